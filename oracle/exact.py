@@ -1,0 +1,126 @@
+"""O-X: full-precision float64 attention with QK-norm, forward and backward (CPU, numpy).
+
+Test infrastructure only (see oracle/__init__.py). No quantisation anywhere.
+
+Forward:  Q^ = RMSNorm(Q), K^ = RMSNorm(K) per token over d (gain 1, when QK-norm is on;
+          SageBwd article, QK-norm paragraph); S = sm * Q^ K^T, masked above the
+          diagonal when causal; P = softmax_rows(S); O = P V; LSE = ln sum_j exp(S_ij).
+Backward: dV = P^T dO; dP = dO V^T; D = rowsum(dO o O); dS = P o (dP - D);
+          dQ^ = sm * dS K^; dK^ = sm * dS^T Q^ (SageBwd article, gradient paragraph);
+          dQ, dK = RMSNorm backward of dQ^, dK^.
+K-smoothing is left out: subtracting any fixed vector from every key adds a per-row
+constant to S, which softmax ignores (pinned by test_oracle_exact.py).
+
+Rows are processed in blocks of query rows so that long sequences never hold the
+N x N matrix; each row of the softmax is computed whole, as the definition says.
+Pinned by: central finite differences (test_oracle_exact.py::test_grad_fd_*), the
+library attention routine (test_forward_matches_sdpa), closed forms (uniform keys,
+single key), and the dS structure (row sums zero, RMS(dS) bound).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+
+def rms_norm(x: np.ndarray, eps: float):
+    """y = x / sqrt(mean_c x^2 + eps); returns (y, rstd) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+    return x * rstd[..., None], rstd
+
+
+def rms_norm_backward(dy: np.ndarray, y: np.ndarray, rstd: np.ndarray) -> np.ndarray:
+    """Backward of y = x * rstd(x): dx = rstd * (dy - y * mean_c(dy * y))."""
+    r = rstd[..., None]
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-6,
+              sm_scale: Optional[float] = None, k_shift: Optional[np.ndarray] = None,
+              row_block: int = 512, want_ds_stats: bool = False) -> Dict[str, np.ndarray]:
+    """Exact attention on [..., N, d] float64 inputs; the backward runs when dO is given.
+
+    k_shift: optional vector (broadcast to [..., d]) subtracted from every normalised key
+    before the scores (used only to check that K-smoothing leaves the output unchanged).
+    want_ds_stats: also return, per query row, sqrt(mean_j dS_ij^2) over the row's
+    visible keys ("ds_rms"), sqrt(sum_j dS_ij^2) ("ds_l2"), max_j |dP_ij| ("dp_max"),
+    the row sum of dS ("ds_rowsum") and max_j |dS_ij| ("ds_max").
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    lead = Q.shape[:-2]
+    N, d = Q.shape[-2], Q.shape[-1]
+    q = Q.reshape((-1, N, d))
+    k = K.reshape((-1, N, d))
+    v = V.reshape((-1, N, d))
+    BH = q.shape[0]
+    sm = sm_scale if sm_scale is not None else 1.0 / np.sqrt(d)
+    if qk_norm:
+        qh, rq = rms_norm(q, eps)
+        kh, rk = rms_norm(k, eps)
+    else:
+        qh, rq = q, np.ones((BH, N))
+        kh, rk = k, np.ones((BH, N))
+    ks = kh if k_shift is None else kh - np.broadcast_to(np.asarray(k_shift, np.float64),
+                                                         lead + (d,)).reshape(BH, 1, d)
+    O = np.empty((BH, N, d))
+    LSE = np.empty((BH, N))
+    have_bwd = dO is not None
+    if have_bwd:
+        do = np.asarray(dO, dtype=np.float64).reshape((-1, N, d))
+        dqh = np.empty((BH, N, d))
+        dkh = np.zeros((BH, N, d))
+        dv = np.zeros((BH, N, d))
+    stats = {name: np.empty((BH, N)) for name in ("ds_rms", "ds_l2", "dp_max", "ds_rowsum", "ds_max")}
+    cols = np.arange(N)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        rows = np.arange(r0, r1)
+        S = sm * (qh[:, r0:r1, :] @ ks.transpose(0, 2, 1))
+        if causal:
+            S = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, S)
+        m = S.max(axis=-1, keepdims=True)
+        E = np.exp(S - m)
+        l = E.sum(axis=-1, keepdims=True)
+        P = E / l
+        O[:, r0:r1, :] = P @ v
+        LSE[:, r0:r1] = (m + np.log(l))[..., 0]
+        if have_bwd:
+            dv += P.transpose(0, 2, 1) @ do[:, r0:r1, :]
+            dP = do[:, r0:r1, :] @ v.transpose(0, 2, 1)
+            D = np.sum(do[:, r0:r1, :] * O[:, r0:r1, :], axis=-1, keepdims=True)
+            dS = P * (dP - D)
+            dqh[:, r0:r1, :] = sm * (dS @ kh)
+            dkh += sm * (dS.transpose(0, 2, 1) @ qh[:, r0:r1, :])
+            if want_ds_stats:
+                nvis = (rows + 1).astype(np.float64) if causal else np.full(r1 - r0, float(N))
+                vis = np.ones_like(dS, dtype=bool)
+                if causal:
+                    vis = np.broadcast_to(cols[None, None, :] <= rows[None, :, None], dS.shape)
+                sq = np.sum(dS * dS, axis=-1)
+                stats["ds_l2"][:, r0:r1] = np.sqrt(sq)
+                stats["ds_rms"][:, r0:r1] = np.sqrt(sq / nvis[None, :])
+                stats["dp_max"][:, r0:r1] = np.max(np.where(vis, np.abs(dP), 0.0), axis=-1)
+                stats["ds_rowsum"][:, r0:r1] = dS.sum(axis=-1)
+                stats["ds_max"][:, r0:r1] = np.abs(dS).max(axis=-1)
+    out = dict(O=O.reshape(lead + (N, d)), LSE=LSE.reshape(lead + (N,)))
+    if have_bwd:
+        if qk_norm:
+            dq = rms_norm_backward(dqh, qh, rq)
+            dk = rms_norm_backward(dkh, kh, rk)
+        else:
+            dq, dk = dqh, dkh
+        out.update(dQ=dq.reshape(lead + (N, d)), dK=dk.reshape(lead + (N, d)),
+                   dV=dv.reshape(lead + (N, d)))
+        if want_ds_stats:
+            out.update({k_: v_.reshape(lead + (N,)) for k_, v_ in stats.items()})
+    return out
+
+
+def loss(Q, K, V, dO, **kw) -> float:
+    """L = sum(dO o O): its gradient w.r.t. (Q, K, V) is what attention(..., dO) returns."""
+    out = attention(Q, K, V, None, **kw)
+    return float(np.sum(np.asarray(dO, np.float64) * out["O"]))

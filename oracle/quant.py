@@ -1,0 +1,465 @@
+"""O-Q: the quantised SageBwd-style attention, written plainly (CPU, numpy).
+
+Test infrastructure only (see oracle/__init__.py).
+
+What is computed, in the order of the SageBwd article:
+  1. QK-norm: RMSNorm of every token vector of Q and of K over the head dimension,
+     gain 1 (SageBwd article, QK-norm paragraph).
+  2. K-smoothing: subtract from every key the mean key of its head, i.e. the
+     per-channel mean over all N tokens, right before quantising (SageBwd article,
+     K-smoothing paragraph; the axis follows from the Q-smoothing paragraph, whose
+     bias term (dS^T 1) mu_Q^T needs mu to be a d-vector averaged over tokens).
+  3. Per-block INT8 quantisation of Q^, K~, V (and dO in the backward): one float32
+     scale per block of `blk` tokens x d channels, symmetric absmax/127, codes in
+     [-127, 127], round to nearest even (SageBwd article, per-block kernels
+     paragraph).
+  4. A flash-style forward (TurboQuant blog, FlashAttention section: the T x T score
+     matrix is processed block by block) whose QK^T and PV products are INT8 (SageBwd
+     article, precision split paragraph). P~ is quantised on tiles of fwd_tq query
+     rows x fwd_tk keys.
+  5. The backward with recomputed QK^T, dP = dO V^T from the 16-bit dO and V,
+     dS = P o (dP - D), and INT8 products dV = P^T dO, dK = dS^T Q, dQ = dS K (SageBwd
+     article, precision split and gradient paragraphs). P is quantised on tiles of
+     bwd_tq x bwd_pk, dS on tiles of bwd_tq x bwd_sk.
+  6. Gradients are with respect to the raw Q, K handed to the prologue: the RMSNorm
+     backward closes dQ and dK; K-smoothing contributes nothing, because every row of
+     dS sums to zero.
+
+Precision: steps 1-3 are float32, one IEEE operation at a time, round to nearest
+even, in the order written (sums run over channels, or over tokens, in ascending
+index order). Everything after the prologue is float64, except that each in-kernel
+quantisation (P~, P, dS) takes its decision in float32 exactly as in step 3 (the
+value is rounded to float32 first), so the oracle and the kernels decide codes in
+the same precision. Outputs are rounded to the 16-bit dtype, nearest even.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+F32 = np.float32
+
+
+@dataclasses.dataclass(frozen=True)
+class Spec:
+    """Shape, flags and quantisation tiling of one attention call.
+
+    fwd_tq x fwd_tk : tile on which P~ is quantised in the forward; fwd_tk is also
+                      the online-softmax step (the running max moves once per tile).
+    bwd_tq x bwd_pk : tile on which P is quantised in the backward (for dV).
+    bwd_tq x bwd_sk : tile on which dS is quantised (for dK and dQ).
+    Every tile lies inside one blk x blk block, so the block scales of Q, K, V and dO
+    factor out of every integer product.
+    """
+    N: int
+    d: int
+    blk: int
+    causal: bool
+    qk_norm: bool
+    k_smooth: bool
+    dtype: str = "fp16"
+    eps: float = 1e-6
+    sm_scale: Optional[float] = None
+    fwd_tq: int = 32
+    fwd_tk: Optional[int] = None
+    bwd_tq: int = 64
+    bwd_pk: int = 32
+    bwd_sk: Optional[int] = None
+
+    def __post_init__(self):
+        blk = self.blk
+        fk = self.fwd_tk if self.fwd_tk is not None else blk
+        sk = self.bwd_sk if self.bwd_sk is not None else blk
+        for name, v in (("fwd_tq", self.fwd_tq), ("fwd_tk", fk), ("bwd_tq", self.bwd_tq),
+                        ("bwd_pk", self.bwd_pk), ("bwd_sk", sk)):
+            if v <= 0 or blk % v != 0:
+                raise ValueError(f"{name}={v} must divide blk={blk}")
+        if sk % self.bwd_pk != 0:
+            raise ValueError("bwd_pk must divide bwd_sk")
+        if self.N % blk != 0:
+            raise ValueError("N must be a multiple of blk")
+
+    @property
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale is not None else 1.0 / np.sqrt(self.d)
+
+    @property
+    def tk(self) -> int:
+        return self.fwd_tk if self.fwd_tk is not None else self.blk
+
+    @property
+    def sk(self) -> int:
+        return self.bwd_sk if self.bwd_sk is not None else self.blk
+
+
+# ----------------------------------------------------------------------------
+# Output rounding to the 16-bit dtype (nearest even).
+# ----------------------------------------------------------------------------
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to fp16 or bf16 (nearest even); return them as float64.
+
+    dtype "f64" leaves the values unrounded (used only by the oracle's own pins).
+    bf16 goes through float32 first; the two roundings can only differ from one
+    direct rounding on values within 2^-24 relative of a bf16 tie.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f64":  # no rounding: used by the reduction pins
+        return x
+    if dtype == "fp16":
+        return x.astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+        lsb = (u >> np.uint64(16)) & np.uint64(1)
+        r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+        return r.astype(np.uint32).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Prologue, bit-specified in float32.
+# ----------------------------------------------------------------------------
+
+def rms_norm_f32(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """QK-norm of each token vector (last axis), float32 op by op.
+
+    ss = 0; for c ascending: ss = fl(ss + x_c * x_c)   (x_c * x_c is exact for 16-bit x)
+    ms = fl(ss / d); rstd = fl(1 / fl(sqrt(fl(ms + eps)))); x^ = fl(x * rstd).
+    Returns (x^, rstd). SageBwd article, QK-norm paragraph (RMSNorm per token, gain 1).
+    Pinned by: test_oracle_quant.py::test_rms_norm_* (hand example, error bound).
+    """
+    x = np.asarray(x, dtype=F32)
+    d = x.shape[-1]
+    ss = np.zeros(x.shape[:-1], dtype=F32)
+    for c in range(d):
+        xc = x[..., c]
+        ss = ss + xc * xc
+    ms = ss / F32(d)
+    rstd = F32(1.0) / np.sqrt(ms + F32(eps))
+    return x * rstd[..., None], rstd
+
+
+def k_smooth_f32(khat: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
+    """K-smoothing: K~ = K^ - mu, mu = per-channel mean of K^ over the N tokens of a head.
+
+    Order: per block of blk tokens, part = sum of the block's tokens in ascending
+    order (from 0); tot = sum of the parts in ascending block order (from 0);
+    mu = fl(tot / N); K~ = fl(K^ - mu). Input [..., N, d]; returns (K~, mu [..., d]).
+    SageBwd article, K-smoothing paragraph (axis: see module docstring).
+    Pinned by: test_oracle_quant.py::test_k_smooth_* and the softmax-invariance tests.
+    """
+    khat = np.asarray(khat, dtype=F32)
+    N, d = khat.shape[-2], khat.shape[-1]
+    nb = N // blk
+    kb = khat.reshape(khat.shape[:-2] + (nb, blk, d))
+    part = np.zeros(khat.shape[:-2] + (nb, d), dtype=F32)
+    for t in range(blk):
+        part = part + kb[..., t, :]
+    tot = np.zeros(khat.shape[:-2] + (d,), dtype=F32)
+    for b in range(nb):
+        tot = tot + part[..., b, :]
+    mu = tot / F32(N)
+    return khat - mu[..., None, :], mu
+
+
+def quant_rule_f32(x32: np.ndarray, axes: Tuple[int, ...]) -> Tuple[np.ndarray, np.ndarray]:
+    """The one INT8 rule used for every operand: symmetric absmax over `axes`.
+
+    a = max |x|; if a == 0: scale 0, codes 0; else s = fl(a / 127), inv = fl(127 / a),
+    code = clamp(rint_even(fl(x * inv)), -127, 127). Scales and inverses are correct
+    divisions, never an approximate reciprocal (the NVFP4 page's insight list records
+    training blowing up when an approximate reciprocal flushed subnormals).
+    Returns (codes int8, scales float32 with `axes` removed).
+    Pinned by: test_oracle_quant.py::test_quant_rule_*.
+    """
+    x32 = np.asarray(x32, dtype=F32)
+    a = np.max(np.abs(x32), axis=axes, keepdims=True)
+    zero = a == 0
+    a_safe = np.where(zero, F32(1.0), a)
+    s = np.where(zero, F32(0.0), a_safe / F32(127.0)).astype(F32)
+    inv = np.where(zero, F32(0.0), F32(127.0) / a_safe).astype(F32)
+    q = np.rint(x32 * inv)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, np.squeeze(s, axis=axes)
+
+
+def quant_blocks_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-block quantisation of [..., N, d]: one scale per blk tokens x d channels.
+
+    SageBwd article, per-block kernels paragraph. Returns (codes [..., N, d] int8,
+    scales [..., N // blk] float32).
+    """
+    x = np.asarray(x, dtype=F32)
+    N, d = x.shape[-2], x.shape[-1]
+    xb = x.reshape(x.shape[:-2] + (N // blk, blk, d))
+    nd = xb.ndim
+    q, s = quant_rule_f32(xb, axes=(nd - 2, nd - 1))
+    return q.reshape(x.shape), s
+
+
+BlockQuant = Callable[[np.ndarray, int], Tuple[np.ndarray, np.ndarray]]
+
+
+def identity_block_quant(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
+    """No quantisation: values pass through as float64 "codes" with block scales 1."""
+    x = np.asarray(x, dtype=np.float64)
+    return x, np.ones(x.shape[:-2] + (x.shape[-2] // blk,), dtype=np.float64)
+
+
+def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
+             block_quant: BlockQuant = quant_blocks_f32) -> Dict[str, np.ndarray]:
+    """QK-norm -> K-smoothing -> per-block INT8 quantisation of Q^, K~, V.
+
+    Inputs: float32 arrays [B,H,N,d] holding the exact values of the 16-bit inputs.
+    Returns codes Qc, Kc, Vc (int8 [B,H,N,d], V in natural token-major layout),
+    scales Qs, Ks, Vs (float32 [B,H,N/blk]), q_rstd, k_rstd (float32 [B,H,N], 1 when
+    QK-norm is off), k_mean (float32 [B,H,d], 0 when smoothing is off), and the
+    normalised Qhat, Khat (float32) that the RMSNorm backward needs.
+    """
+    Q = np.asarray(Q, dtype=F32)
+    K = np.asarray(K, dtype=F32)
+    V = np.asarray(V, dtype=F32)
+    if spec.qk_norm:
+        Qh, q_rstd = rms_norm_f32(Q, spec.eps)
+        Kh, k_rstd = rms_norm_f32(K, spec.eps)
+    else:
+        Qh, q_rstd = Q, np.ones(Q.shape[:-1], dtype=F32)
+        Kh, k_rstd = K, np.ones(K.shape[:-1], dtype=F32)
+    if spec.k_smooth:
+        Kt, mu = k_smooth_f32(Kh, spec.blk)
+    else:
+        Kt, mu = Kh, np.zeros(K.shape[:-2] + (K.shape[-1],), dtype=F32)
+    Qc, Qs = block_quant(Qh, spec.blk)
+    Kc, Ks = block_quant(Kt, spec.blk)
+    Vc, Vs = block_quant(V, spec.blk)
+    return dict(Qc=Qc, Kc=Kc, Vc=Vc, Qs=Qs, Ks=Ks, Vs=Vs, q_rstd=q_rstd, k_rstd=k_rstd,
+                k_mean=mu, Qhat=Qh, Khat=Kh)
+
+
+# ----------------------------------------------------------------------------
+# In-kernel tile quantiser (P~, P, dS).
+# ----------------------------------------------------------------------------
+
+TileQuant = Callable[[np.ndarray], Tuple[np.ndarray, np.ndarray]]
+
+
+def int8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise each tile x[h] (leading axis = head) with the INT8 rule, deciding in float32.
+
+    Returns (codes as float64, scales as float64 [BH]).
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(F32)
+    axes = tuple(range(1, x32.ndim))
+    q, s = quant_rule_f32(x32, axes)
+    return q.astype(np.float64), s.astype(np.float64)
+
+
+def identity_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """No quantisation: values pass through with scale 1 (used to pin the tiling logic)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x, np.ones(x.shape[0], dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Forward and backward (float64 after the prologue).
+# ----------------------------------------------------------------------------
+
+def _flat(a: np.ndarray, nlead: int = 2) -> np.ndarray:
+    return a.reshape((-1,) + a.shape[nlead:])
+
+
+def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
+            q_tiles: Optional[Sequence[int]] = None):
+    """Flash-style forward with INT8 QK^T and PV (SageBwd article, precision split).
+
+    Per head, per query tile I of fwd_tq rows: m = -inf, l = 0, acc = 0; for key tiles J
+    of fwd_tk keys in ascending order, skipping tiles wholly above the causal diagonal:
+      S   = Qc_I . Kc_J^T (exact integers),  s = S * sQ(I) * sK(J) * sm_scale,
+            masked (key > query) -> -inf when causal
+      m'  = max(m, rowmax s);  P~ = exp(s - m');  alpha = exp(m - m')
+      l   = l * alpha + rowsum P~                     (P~ before quantisation)
+      qP, sP = quantise P~ on the tile                (INT8 rule, decided in float32)
+      acc = acc * alpha + sP * sV(J) * (qP . Vc_J)    (exact integer product)
+      m   = m'
+    then O = acc / l (rounded to the dtype) and LSE = m + ln l (natural log, float32).
+    Codes may be given as integers or, with identity_tile_quant, as real values.
+    Returns (O [B,H,N,d] float64 of dtype-rounded values, LSE [B,H,N] float32); with
+    q_tiles only those query tiles are computed (rows of other tiles are NaN).
+    Pinned by: test_oracle_quant.py identity and lossless reductions to oracle.exact.
+    """
+    B, H, N, d = Qc.shape
+    blk, tq, tk = spec.blk, spec.fwd_tq, spec.tk
+    sm = spec.scale
+    q = _flat(Qc).astype(np.float64)
+    k = _flat(Kc).astype(np.float64)
+    v = _flat(Vc).astype(np.float64)
+    qs = _flat(np.asarray(Qs, dtype=np.float64))
+    ks = _flat(np.asarray(Ks, dtype=np.float64))
+    vs = _flat(np.asarray(Vs, dtype=np.float64))
+    BH = q.shape[0]
+    O = np.full((BH, N, d), np.nan)
+    LSE = np.full((BH, N), np.nan)
+    tiles = range(N // tq) if q_tiles is None else q_tiles
+    for it in tiles:
+        i0 = it * tq
+        rows = np.arange(i0, i0 + tq)
+        qi = q[:, i0:i0 + tq, :]
+        sq = qs[:, i0 // blk]
+        m = np.full((BH, tq), -np.inf)
+        l = np.zeros((BH, tq))
+        acc = np.zeros((BH, tq, d))
+        for j0 in range(0, N, tk):
+            if spec.causal and j0 > i0 + tq - 1:
+                break
+            cols = np.arange(j0, j0 + tk)
+            S = qi @ k[:, j0:j0 + tk, :].transpose(0, 2, 1)
+            s = S * (sq * ks[:, j0 // blk] * sm)[:, None, None]
+            if spec.causal:
+                s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
+            m_new = np.maximum(m, s.max(axis=-1))
+            Pt = np.exp(s - m_new[..., None])
+            alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+            l = l * alpha + Pt.sum(axis=-1)
+            qP, sP = tile_quant(Pt)
+            pv = qP @ v[:, j0:j0 + tk, :]
+            acc = acc * alpha[..., None] + (sP * vs[:, j0 // blk])[:, None, None] * pv
+            m = m_new
+        O[:, i0:i0 + tq, :] = acc / l[..., None]
+        LSE[:, i0:i0 + tq] = m + np.log(l)
+    O = round_to_dtype(O, spec.dtype)
+    return O.reshape(B, H, N, d), LSE.astype(F32).reshape(B, H, N)
+
+
+def backward_pre(O, dO, spec: Spec, block_quant: BlockQuant = quant_blocks_f32):
+    """D = rowsum(dO o O) (float64, O as stored in the dtype) and the per-block INT8 dO.
+
+    Returns (D [B,H,N] float64, dOc int8 [B,H,N,d], dOs float32 [B,H,N/blk]).
+    """
+    O = np.asarray(O, dtype=np.float64)
+    dO32 = np.asarray(dO, dtype=F32)
+    D = np.sum(dO32.astype(np.float64) * O, axis=-1)
+    dOc, dOs = block_quant(dO32, spec.blk)
+    return D, dOc, dOs
+
+
+def rms_norm_backward(dy: np.ndarray, y: np.ndarray, rstd: np.ndarray) -> np.ndarray:
+    """Backward of y = x * rstd(x) with rstd = (mean_c x^2 + eps)^-1/2 (float64):
+    dx = rstd * (dy - y * mean_c(dy * y)). Pinned by the finite-difference tests."""
+    dy = np.asarray(dy, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(rstd, dtype=np.float64)[..., None]
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
+             tile_quant: TileQuant = int8_tile_quant,
+             block_quant: BlockQuant = quant_blocks_f32,
+             q_tiles: Optional[Sequence[int]] = None,
+             k_tiles: Optional[Sequence[int]] = None):
+    """Backward with recomputed INT8 QK^T, FP dP = dO V^T and INT8 dV, dK, dQ.
+
+    pro: the prologue's dict (codes, scales, rstd, Qhat, Khat). Q, K, V, dO: float32
+    exact 16-bit values; O: the forward's output as stored (dtype values); LSE float32.
+    Per head, for every visible pair of query tile I (bwd_tq rows) and key tile J
+    (bwd_sk keys), in ascending I then J:
+      s  = (Qc_I . Kc_J^T) * sQ(I) * sK(J) * sm_scale (masked -> -inf); P = exp(s - LSE_I)
+      dP = dO_I . V_J^T   (the 16-bit dO and V, never quantised; SageBwd article,
+                           precision split: this product alone stays 16-bit)
+      dS = P o (dP - D_I)
+      qdS, sdS = quantise dS on the tile
+      for each key sub-tile J' of bwd_pk keys: qP, sP = quantise P_{I,J'};
+           dV_J' += sP * sdO(I) * (qP^T . dOc_I)
+      dK_J += sm * sdS * sQ(I) * (qdS^T . Qc_I)
+      dQ_I += sm * sdS * sK(J) * (qdS . Kc_J)          (Kc: the smoothed K codes)
+    Epilogue: dQ = RMSNorm-backward(dQ^, Q^, q_rstd), dK = RMSNorm-backward(dK^, K^,
+    k_rstd) when QK-norm is on (K^ before smoothing; smoothing adds no term because
+    every dS row sums to zero), then all three are rounded to the dtype.
+    With q_tiles / k_tiles only pairs whose I is in q_tiles (bwd_tq units) or whose J
+    is in k_tiles (bwd_sk units) are visited: dQ is then exact for those query tiles,
+    dK and dV for those key tiles, and NaN elsewhere.
+    Returns dict dQ, dK, dV ([B,H,N,d] float64 of dtype-rounded values) plus D, dOc, dOs.
+    """
+    B, H, N, d = pro["Qc"].shape
+    blk, tq, sk, pk = spec.blk, spec.bwd_tq, spec.sk, spec.bwd_pk
+    sm = spec.scale
+    D, dOc, dOs = backward_pre(O, dO, spec, block_quant=block_quant)
+    qc = _flat(pro["Qc"]).astype(np.float64)
+    kc = _flat(pro["Kc"]).astype(np.float64)
+    qs = _flat(np.asarray(pro["Qs"], dtype=np.float64))
+    ks = _flat(np.asarray(pro["Ks"], dtype=np.float64))
+    doc = _flat(dOc).astype(np.float64)
+    dos = _flat(np.asarray(dOs, dtype=np.float64))
+    do = _flat(np.asarray(dO, dtype=F32)).astype(np.float64)
+    vf = _flat(np.asarray(V, dtype=F32)).astype(np.float64)
+    lse = _flat(np.asarray(LSE, dtype=F32)).astype(np.float64)
+    Df = _flat(D)
+    BH = qc.shape[0]
+    dQh = np.zeros((BH, N, d))
+    dKh = np.zeros((BH, N, d))
+    dV = np.zeros((BH, N, d))
+    qsel = None if q_tiles is None else set(q_tiles)
+    ksel = None if k_tiles is None else set(k_tiles)
+    for it in range(N // tq):
+        i0 = it * tq
+        rows = np.arange(i0, i0 + tq)
+        for jt in range(N // sk):
+            j0 = jt * sk
+            if spec.causal and j0 > i0 + tq - 1:
+                break
+            if qsel is not None or ksel is not None:
+                if not ((qsel is not None and it in qsel) or (ksel is not None and jt in ksel)):
+                    continue
+            cols = np.arange(j0, j0 + sk)
+            S = qc[:, i0:i0 + tq, :] @ kc[:, j0:j0 + sk, :].transpose(0, 2, 1)
+            s = S * (qs[:, i0 // blk] * ks[:, j0 // blk] * sm)[:, None, None]
+            if spec.causal:
+                s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
+            P = np.exp(s - lse[:, i0:i0 + tq, None])
+            dP = do[:, i0:i0 + tq, :] @ vf[:, j0:j0 + sk, :].transpose(0, 2, 1)
+            dS = P * (dP - Df[:, i0:i0 + tq, None])
+            qdS, sdS = tile_quant(dS)
+            for p0 in range(0, sk, pk):
+                qP, sP = tile_quant(P[:, :, p0:p0 + pk])
+                dV[:, j0 + p0:j0 + p0 + pk, :] += (sP * dos[:, i0 // blk])[:, None, None] * (
+                    qP.transpose(0, 2, 1) @ doc[:, i0:i0 + tq, :])
+            dKh[:, j0:j0 + sk, :] += (sm * sdS * qs[:, i0 // blk])[:, None, None] * (
+                qdS.transpose(0, 2, 1) @ qc[:, i0:i0 + tq, :])
+            dQh[:, i0:i0 + tq, :] += (sm * sdS * ks[:, j0 // blk])[:, None, None] * (
+                qdS @ kc[:, j0:j0 + sk, :])
+    if spec.qk_norm:
+        dQ = rms_norm_backward(dQh, _flat(pro["Qhat"]), _flat(pro["q_rstd"]))
+        dK = rms_norm_backward(dKh, _flat(pro["Khat"]), _flat(pro["k_rstd"]))
+    else:
+        dQ, dK = dQh, dKh
+    if qsel is not None or ksel is not None:
+        qmask = np.zeros(N, dtype=bool)
+        kmask = np.zeros(N, dtype=bool)
+        for it in (qsel or ()):
+            qmask[it * tq:(it + 1) * tq] = True
+        for jt in (ksel or ()):
+            kmask[jt * sk:(jt + 1) * sk] = True
+        dQ = np.where(qmask[None, :, None], dQ, np.nan)
+        dK = np.where(kmask[None, :, None], dK, np.nan)
+        dV = np.where(kmask[None, :, None], dV, np.nan)
+    out = dict(
+        dQ=round_to_dtype(dQ, spec.dtype).reshape(B, H, N, d),
+        dK=round_to_dtype(dK, spec.dtype).reshape(B, H, N, d),
+        dV=round_to_dtype(dV, spec.dtype).reshape(B, H, N, d),
+        D=D, dOc=dOc, dOs=dOs,
+    )
+    return out
+
+
+def run(Q, K, V, dO, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
+        block_quant: BlockQuant = quant_blocks_f32):
+    """Prologue -> forward -> backward on whole tensors. Returns one dict of everything."""
+    pro = prologue(Q, K, V, spec, block_quant=block_quant)
+    O, LSE = forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec,
+                     tile_quant=tile_quant)
+    g = backward(pro, Q, K, V, O, LSE, dO, spec, tile_quant=tile_quant, block_quant=block_quant)
+    out = dict(pro)
+    out.update(O=O, LSE=LSE)
+    out.update(g)
+    return out

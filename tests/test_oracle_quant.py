@@ -1,0 +1,296 @@
+"""Pins for the quantised oracle (oracle.quant) against things other than itself.
+
+- hand-worked examples of the float32 prologue (exact values, rounding ties, the
+  ascending summation order that bit-exactness depends on), stored as small text
+  fixtures under tests/golden/ with the reasoning that gives each number,
+- error bounds of the float32 steps against exact float64,
+- the quantisation rule's closed-form properties,
+- identity-quantiser reduction: with every quantisation replaced by the identity the
+  tiled online-softmax forward and the tiled backward must equal oracle.exact,
+- lossless-quantiser reduction: inputs built as code * 2^e per block quantise without
+  loss, so with the real per-block rule (and identity tiles) the result must again
+  equal oracle.exact; this pins which block scale multiplies which product,
+- planted mistakes: a dropped or misplaced term in a copy of the oracle must break
+  one of these pins.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import exact
+from oracle import quant as oq
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- prologue
+
+def test_rms_norm_hand_examples():
+    g = _golden("prologue_hand_examples.json")
+    for case in g["rms_norm"]:
+        x = np.array(case["x"], dtype=F32)[None, :]
+        xh, r = oq.rms_norm_f32(x, case["eps"])
+        assert r[0] == F32(case["rstd"]), case
+        np.testing.assert_array_equal(xh[0], np.array(case["xhat"], dtype=F32))
+
+
+def test_rms_norm_ascending_order():
+    """4096^2 = 2^24 absorbs each later 1 (round-half-even), so ss stays 2^24; an exact
+    or reordered sum would give 2^24 + 7 and a different float32 rstd."""
+    x = np.array([[4096.0, 1, 1, 1, 1, 1, 1, 1]], dtype=F32)
+    y = np.array([[4096.0, 0, 0, 0, 0, 0, 0, 0]], dtype=F32)
+    _, rx = oq.rms_norm_f32(x, 0.0)
+    _, ry = oq.rms_norm_f32(y, 0.0)
+    assert rx[0] == ry[0]
+    exact_ms = (2.0 ** 24 + 7) / 8
+    assert F32(1.0 / np.sqrt(exact_ms)) != rx[0]
+
+
+def test_rms_norm_error_bound():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((64, 128)).astype(np.float16).astype(F32)
+    x[:3] *= 100
+    xh, r = oq.rms_norm_f32(x, 1e-6)
+    r64 = 1.0 / np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=-1) + 1e-6)
+    assert np.max(np.abs(r / r64 - 1)) < 4e-7      # a few float32 roundings
+    assert np.max(np.abs(xh / (x * r64[:, None] + 1e-30) - 1)[x != 0]) < 6e-7
+
+
+def test_k_smooth_hand_examples():
+    g = _golden("prologue_hand_examples.json")
+    for case in g["k_smooth"]:
+        k = np.array(case["khat"], dtype=F32)[:, None]  # [N, 1]
+        kt, mu = oq.k_smooth_f32(k, case["blk"])
+        assert mu[0] == F32(case["mu"]), case
+        np.testing.assert_array_equal(kt[:, 0], np.array(case["ktilde"], dtype=F32))
+
+
+def test_k_smooth_mean_zero():
+    rng = np.random.default_rng(1)
+    kh = (rng.standard_normal((2, 512, 64)) + 5).astype(F32)
+    kt, mu = oq.k_smooth_f32(kh, 64)
+    np.testing.assert_allclose(mu, kh.astype(np.float64).mean(axis=1), rtol=2e-6)
+    assert np.max(np.abs(kt.astype(np.float64).mean(axis=1))) < 1e-5
+
+
+def test_quant_rule_hand_examples():
+    g = _golden("prologue_hand_examples.json")
+    for case in g["quant"]:
+        x = np.array(case["x"], dtype=F32)[None]  # one block
+        q, s = oq.quant_blocks_f32(x, x.shape[1])
+        np.testing.assert_array_equal(q[0], np.array(case["codes"], dtype=np.int8))
+        assert s[0] == F32(case["scale"]), case
+
+
+def test_quant_rule_properties():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((3, 4, 256, 64)) * rng.uniform(1e-3, 1e3, (3, 4, 1, 1))).astype(F32)
+    x[0, 0, :64] = 0.0                                  # an all-zero block
+    x[0, 1, 64:128] = -np.abs(x[0, 1, 64:128])          # a block whose absmax is negative
+    q, s = oq.quant_blocks_f32(x, 64)
+    qb = q.reshape(3, 4, 4, 64, 64).astype(np.int32)
+    xb = x.reshape(3, 4, 4, 64, 64).astype(np.float64)
+    amax = np.max(np.abs(qb), axis=(-1, -2))
+    assert s[0, 0, 0] == 0 and amax[0, 0, 0] == 0
+    nz = s > 0
+    assert np.all(amax[nz] == 127)                       # absmax element maps to +-127
+    assert q.min() >= -127                               # never -128
+    err = np.abs(xb - qb * s[..., None, None].astype(np.float64))
+    assert np.all(err <= 0.5 * s[..., None, None] * (1 + 2e-5) + 1e-38)
+    np.testing.assert_allclose(s[nz], (np.max(np.abs(xb), axis=(-1, -2)) / 127)[nz], rtol=6e-8)
+
+
+def test_integer_products_exact():
+    rng = np.random.default_rng(3)
+    a = rng.integers(-127, 128, (64, 128))
+    b = rng.integers(-127, 128, (64, 128))
+    a[0] = 127; b[0] = 127
+    assert np.array_equal(a @ b.T, (a.astype(np.float64) @ b.T.astype(np.float64)).astype(np.int64))
+    assert np.max(np.abs(a @ b.T)) == 128 * 127 * 127 < 2 ** 24
+
+
+# ----------------------------------------------------------------------------- reductions
+
+def _exact_all(Q, K, V, dO, spec, **kw):
+    return exact.attention(Q, K, V, dO, causal=spec.causal, qk_norm=spec.qk_norm, eps=spec.eps,
+                           sm_scale=spec.scale, **kw)
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tiles", [dict(blk=64, fwd_tq=32, bwd_tq=64, bwd_pk=32),
+                                   dict(blk=128, fwd_tq=32, fwd_tk=64, bwd_tq=32, bwd_pk=16, bwd_sk=64)])
+def test_identity_quant_equals_exact(causal, tiles):
+    """All quantisers = identity, QK-norm and smoothing off: the tiled online-softmax
+    forward and the tiled backward are exactly attention (to float64 rounding)."""
+    rng = np.random.default_rng(4)
+    B, H, N, d = 1, 2, 256, 16
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=N, d=d, causal=causal, qk_norm=False, k_smooth=False, dtype="f64", **tiles)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant,
+                 block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    assert _rel(got["O"], ref["O"]) < 1e-12
+    # LSE is stored as float32, and the backward reads it back, so P (and the gradients)
+    # carry a relative error up to |LSE| * 2^-24.
+    assert _rel(got["LSE"], ref["LSE"]) < 1e-7
+    for name in ("dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 2e-6, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_quant_with_norm_and_smoothing(causal):
+    """Identity quantisers with QK-norm and K-smoothing on: equal to exact attention up to
+    the float32 prologue; smoothing changes nothing and needs no gradient correction."""
+    rng = np.random.default_rng(5)
+    B, H, N, d = 1, 2, 128, 32
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    K = (K + 4 * rng.standard_normal((1, H, 1, d))).astype(F32)
+    spec = oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64")
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant,
+                 block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    for name in ("O", "dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 3e-6, name
+
+
+def _lossless(rng, shape, blk, emin=-6, emax=3):
+    """Values code * 2^e with one exponent per block and one element at +-127 per block."""
+    B, H, N, d = shape
+    codes = rng.integers(-127, 128, shape).astype(np.float64)
+    codes.reshape(B, H, N // blk, blk * d)[..., 0] = 127.0 * rng.choice([-1, 1], (B, H, N // blk))
+    e = rng.integers(emin, emax + 1, (B, H, N // blk))
+    x = codes * np.repeat(np.exp2(e.astype(np.float64)), blk, axis=-1)[..., None]
+    return x.astype(F32), e
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lossless_block_quant_equals_exact(causal):
+    """Per-block exponents differ, so a scale applied to the wrong block breaks this."""
+    rng = np.random.default_rng(6)
+    shape = (1, 2, 256, 16)
+    blk = 64
+    Q, eq = _lossless(rng, shape, blk, -7, -5)
+    K, ek = _lossless(rng, shape, blk, -7, -5)
+    V, ev = _lossless(rng, shape, blk)
+    dO, ed = _lossless(rng, shape, blk)
+    spec = oq.Spec(N=256, d=16, blk=blk, causal=causal, qk_norm=False, k_smooth=False, dtype="f64")
+    pro = oq.prologue(Q, K, V, spec)
+    np.testing.assert_array_equal(pro["Qs"], np.exp2(eq).astype(F32))
+    np.testing.assert_array_equal(pro["Vs"], np.exp2(ev).astype(F32))
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant)
+    np.testing.assert_array_equal(got["dOs"], np.exp2(ed).astype(F32))
+    ref = _exact_all(Q, K, V, dO, spec)
+    assert _rel(got["O"], ref["O"]) < 1e-12
+    # LSE is stored as float32, and the backward reads it back, so P (and the gradients)
+    # carry a relative error up to |LSE| * 2^-24.
+    assert _rel(got["LSE"], ref["LSE"]) < 1e-7
+    for name in ("dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 2e-6, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_close_to_exact(causal):
+    """The real INT8 path stays close to exact attention (a gross indexing error would not)."""
+    rng = np.random.default_rng(7)
+    B, H, N, d = 1, 2, 256, 64
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(np.float16).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64")
+    got = oq.run(Q, K, V, dO, spec)
+    ref = _exact_all(Q, K, V, dO, spec)
+
+    def cos(a, b):
+        a = a.ravel(); b = b.ravel()
+        return a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+    assert cos(got["O"], ref["O"]) > 0.999
+    for name in ("dQ", "dK", "dV"):
+        assert cos(got[name], ref[name]) > 0.99, name
+
+
+def test_sampled_tiles_match_full():
+    """Restricting the oracle to some query/key tiles gives the same values there."""
+    rng = np.random.default_rng(8)
+    B, H, N, d = 1, 1, 256, 32
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(np.float16).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=N, d=d, blk=64, causal=True, qk_norm=True, k_smooth=True, dtype="fp16")
+    full = oq.run(Q, K, V, dO, spec)
+    pro = oq.prologue(Q, K, V, spec)
+    O, L = oq.forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec, q_tiles=[1, 6])
+    for it in (1, 6):
+        sl = slice(it * 32, it * 32 + 32)
+        np.testing.assert_array_equal(O[..., sl, :], full["O"][..., sl, :])
+        np.testing.assert_array_equal(L[..., sl], full["LSE"][..., sl])
+    g = oq.backward(pro, Q, K, V, full["O"], full["LSE"], dO, spec, q_tiles=[2], k_tiles=[1])
+    np.testing.assert_allclose(g["dQ"][..., 128:192, :], full["dQ"][..., 128:192, :], rtol=0, atol=0)
+    np.testing.assert_allclose(g["dK"][..., 64:128, :], full["dK"][..., 64:128, :], rtol=0, atol=0)
+    np.testing.assert_allclose(g["dV"][..., 64:128, :], full["dV"][..., 64:128, :], rtol=0, atol=0)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _identity_case(causal=True):
+    rng = np.random.default_rng(9)
+    Q, K, V, dO = (rng.standard_normal((1, 1, 128, 16)).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=128, d=16, blk=64, causal=causal, qk_norm=True, k_smooth=False, dtype="f64")
+    return Q, K, V, dO, spec
+
+
+def _identity_pin_passes(Q, K, V, dO, spec):
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant,
+                 block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    return all(_rel(got[n], ref[n]) < 3e-6 for n in ("O", "dQ", "dK", "dV"))
+
+
+def test_pins_pass_unplanted():
+    assert _identity_pin_passes(*_identity_case())
+
+
+@pytest.mark.parametrize("mistake", ["rmsnorm_bwd_drop_mean", "rmsnorm_bwd_sign",
+                                     "ds_drop_D", "dk_transposed"])
+def test_planted_mistake_is_caught(monkeypatch, mistake):
+    if mistake == "rmsnorm_bwd_drop_mean":
+        monkeypatch.setattr(oq, "rms_norm_backward",
+                            lambda dy, y, r: np.asarray(r)[..., None] * np.asarray(dy))
+    elif mistake == "rmsnorm_bwd_sign":
+        monkeypatch.setattr(oq, "rms_norm_backward",
+                            lambda dy, y, r: np.asarray(r)[..., None] * (dy + y * np.mean(dy * y, -1, keepdims=True)))
+    elif mistake == "tile_scale_dropped":
+        Q, K, V, dO, spec = _identity_case()
+        got = oq.run(Q, K, V, dO, spec, tile_quant=lambda x: (np.asarray(x, np.float64) / 2, np.ones(np.shape(x)[0])),
+                     block_quant=oq.identity_block_quant)
+        ref = _exact_all(Q, K, V, dO, spec)
+        assert not all(_rel(got[n], ref[n]) < 3e-6 for n in ("O", "dQ", "dK", "dV"))
+        return
+    elif mistake == "ds_drop_D":
+        real_bp = oq.backward_pre
+        monkeypatch.setattr(oq, "backward_pre",
+                            lambda O, dO, spec, block_quant=oq.quant_blocks_f32: (
+                                0 * real_bp(O, dO, spec, block_quant)[0],) + tuple(real_bp(O, dO, spec, block_quant)[1:]))
+    elif mistake == "dk_transposed":
+        real_tq = oq.identity_tile_quant
+
+        def tq_T(x):
+            x = np.asarray(x, np.float64)
+            if x.shape[-1] == x.shape[-2] and x.shape[-1] == 64:  # dS tiles: swap axes
+                return x.transpose(0, 2, 1), np.ones(x.shape[0])
+            return real_tq(x)
+        Q, K, V, dO, spec = _identity_case()
+        spec = oq.Spec(N=128, d=16, blk=64, causal=False, qk_norm=True, k_smooth=False, dtype="f64")
+        got = oq.run(Q, K, V, dO, spec, tile_quant=tq_T, block_quant=oq.identity_block_quant)
+        ref = _exact_all(Q, K, V, dO, spec)
+        assert not all(_rel(got[n], ref[n]) < 3e-6 for n in ("dQ", "dK"))
+        return
+    assert not _identity_pin_passes(*_identity_case())
