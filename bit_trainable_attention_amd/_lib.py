@@ -1,0 +1,65 @@
+"""ctypes loader for libsagebwd.so (the HIP kernels behind the C ABI in include/sagebwd.h).
+
+There is no fallback: if the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagebwd.so")
+
+SAGEBWD_FP16 = 0
+SAGEBWD_BF16 = 1
+
+# Quantisation tile shapes of the kernels (include/sagebwd.h).
+FWD_TILE_Q = 32
+BWD_TILE_Q = 64
+BWD_P_TILE_K = 32
+
+STATUS = {
+    0: "SAGEBWD_OK", -1: "SAGEBWD_ERR_NULL", -2: "SAGEBWD_ERR_SHAPE", -3: "SAGEBWD_ERR_UNSUPPORTED",
+    -4: "SAGEBWD_ERR_ALIGN", -5: "SAGEBWD_ERR_WORKSPACE", -6: "SAGEBWD_ERR_HIP",
+}
+
+
+class Params(ctypes.Structure):
+    """Mirror of sagebwd_params."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("blk", ctypes.c_int32), ("causal", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+        ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_SIZE = ctypes.c_size_t
+_ST = ctypes.c_int
+
+SIGNATURES = {
+    "sagebwd_prologue_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
+    "sagebwd_quant_prologue": (_ST, [ctypes.POINTER(Params)] + [_P] * 12 + [_P, _SIZE, _P]),
+    "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 8 + [_P]),
+    "sagebwd_backward_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
+    "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 15 + [_P, _SIZE, _P]),
+    "sagebwd_status_string": (ctypes.c_char_p, [_ST]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsagebwd.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m bit_trainable_attention_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

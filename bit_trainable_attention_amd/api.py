@@ -1,0 +1,175 @@
+"""Thin Python binding of the C ABI (include/sagebwd.h); names follow the C entry points.
+
+Argument marshalling only: every step of the attention runs in the HIP kernels of
+libsagebwd.so. PyTorch provides device memory and the stream. Before a call is made,
+each tensor is checked on the host against the shape, dtype, device and layout that the
+parameters imply, so a kernel is never launched on a buffer of the wrong size.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+
+_TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloat16}
+
+
+def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
+                dtype: str, eps: float = 1e-6, sm_scale: float = 0.0) -> _lib.Params:
+    dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
+    return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt)
+
+
+def sagebwd_status_string(status: int) -> str:
+    return _lib.load().sagebwd_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise RuntimeError(f"{what}: {_lib.STATUS.get(status, status)} ({sagebwd_status_string(status)})")
+
+
+def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _want(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _shapes(p: _lib.Params):
+    bhnd = (p.B, p.H, p.N, p.d)
+    return dict(x=bhnd, xt=(p.B, p.H, p.d, p.N), s=(p.B, p.H, p.N // p.blk), r=(p.B, p.H, p.N),
+                m=(p.B, p.H, p.d))
+
+
+def sagebwd_prologue_workspace_bytes(p: _lib.Params) -> int:
+    return int(_lib.load().sagebwd_prologue_workspace_bytes(ctypes.byref(p)))
+
+
+def sagebwd_backward_workspace_bytes(p: _lib.Params) -> int:
+    return int(_lib.load().sagebwd_backward_workspace_bytes(ctypes.byref(p)))
+
+
+def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
+    """Byte offsets of the backward workspace regions, as documented in include/sagebwd.h."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    n = p.B * p.H * p.N * p.d
+    bhn = p.B * p.H * p.N
+    off = {"dq_acc": 0}
+    off["D"] = off["dq_acc"] + up(4 * n)
+    off["dOtc"] = off["D"] + up(4 * bhn)
+    off["dOs"] = off["dOtc"] + up(n)
+    off["Qtc"] = off["dOs"] + up(4 * (bhn // p.blk))
+    off["total"] = off["Qtc"] + up(n)
+    return off
+
+
+def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                           out: Optional[Dict[str, torch.Tensor]] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
+    """QK-norm -> K-smoothing -> per-block INT8 codes/scales. Returns the prologue tensors."""
+    dev = Q.device
+    sh = _shapes(p)
+    dt = _TORCH_DTYPE[p.dtype]
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _want(t, name, sh["x"], dt, dev)
+    if out is None:
+        out = dict(
+            Qc=torch.empty(sh["x"], dtype=torch.int8, device=dev),
+            Kc=torch.empty(sh["x"], dtype=torch.int8, device=dev),
+            Vtc=torch.empty(sh["xt"], dtype=torch.int8, device=dev),
+            Qs=torch.empty(sh["s"], dtype=torch.float32, device=dev),
+            Ks=torch.empty(sh["s"], dtype=torch.float32, device=dev),
+            Vs=torch.empty(sh["s"], dtype=torch.float32, device=dev),
+            q_rstd=torch.empty(sh["r"], dtype=torch.float32, device=dev),
+            k_rstd=torch.empty(sh["r"], dtype=torch.float32, device=dev),
+            k_mean=torch.empty(sh["m"], dtype=torch.float32, device=dev),
+        )
+    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
+                           ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32),
+                           ("q_rstd", "r", torch.float32), ("k_rstd", "r", torch.float32),
+                           ("k_mean", "m", torch.float32)):
+        _want(out[name], name, sh[key], tdt, dev)
+    need = sagebwd_prologue_workspace_bytes(p)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().sagebwd_quant_prologue(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
+        _ptr(out["Qc"]), _ptr(out["Kc"]), _ptr(out["Vtc"]), _ptr(out["Qs"]), _ptr(out["Ks"]), _ptr(out["Vs"]),
+        _ptr(out["q_rstd"]), _ptr(out["k_rstd"]), _ptr(out["k_mean"]),
+        _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _check(st, "sagebwd_quant_prologue")
+    return out
+
+
+def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None):
+    """INT8 forward from the prologue tensors. Returns (O, lse)."""
+    dev = pro["Qc"].device
+    sh = _shapes(p)
+    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
+                           ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32)):
+        _want(pro[name], name, sh[key], tdt, dev)
+    if O is None:
+        O = torch.empty(sh["x"], dtype=_TORCH_DTYPE[p.dtype], device=dev)
+    if lse is None:
+        lse = torch.empty(sh["r"], dtype=torch.float32, device=dev)
+    _want(O, "O", sh["x"], _TORCH_DTYPE[p.dtype], dev)
+    _want(lse, "lse", sh["r"], torch.float32, dev)
+    st = _lib.load().sagebwd_forward(
+        ctypes.byref(p), _ptr(pro["Qc"]), _ptr(pro["Kc"]), _ptr(pro["Vtc"]),
+        _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["Vs"]), _ptr(O), _ptr(lse), _stream(dev, stream))
+    _check(st, "sagebwd_forward")
+    return O, lse
+
+
+def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                     pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
+                     grads: Optional[Dict[str, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
+    """Backward. Returns dict(dQ, dK, dV, workspace)."""
+    dev = Q.device
+    sh = _shapes(p)
+    dt = _TORCH_DTYPE[p.dtype]
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
+        _want(t, name, sh["x"], dt, dev)
+    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Qs", "s", torch.float32),
+                           ("Ks", "s", torch.float32), ("q_rstd", "r", torch.float32),
+                           ("k_rstd", "r", torch.float32)):
+        _want(pro[name], name, sh[key], tdt, dev)
+    _want(lse, "lse", sh["r"], torch.float32, dev)
+    if grads is None:
+        grads = {n: torch.empty(sh["x"], dtype=dt, device=dev) for n in ("dQ", "dK", "dV")}
+    for n in ("dQ", "dK", "dV"):
+        _want(grads[n], n, sh["x"], dt, dev)
+    need = sagebwd_backward_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.load().sagebwd_backward(
+        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(pro["Qc"]), _ptr(pro["Kc"]),
+        _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["q_rstd"]), _ptr(pro["k_rstd"]),
+        _ptr(O), _ptr(lse), _ptr(dO), _ptr(grads["dQ"]), _ptr(grads["dK"]), _ptr(grads["dV"]),
+        _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _check(st, "sagebwd_backward")
+    out = dict(grads)
+    out["workspace"] = workspace
+    return out

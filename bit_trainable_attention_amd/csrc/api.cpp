@@ -1,0 +1,179 @@
+// C ABI of the SageBwd-style INT8 attention (declared in include/sagebwd.h).
+// Validates arguments without touching the HIP runtime, then enqueues the kernels.
+#include "sagebwd.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+using sagebwd::BackwardArgs;
+using sagebwd::ForwardArgs;
+using sagebwd::PrologueArgs;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape / option checks shared by every entry point.
+sagebwd_status check_params(const sagebwd_params* p) {
+  if (!p) return SAGEBWD_ERR_NULL;
+  if (p->B < 0 || p->H < 0 || p->N < 0) return SAGEBWD_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->blk != 64 && p->blk != 128) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->dtype != SAGEBWD_FP16 && p->dtype != SAGEBWD_BF16) return SAGEBWD_ERR_UNSUPPORTED;
+  if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
+  // index arithmetic inside the kernels: token rows fit in 32 bits per head, grids in 2^31
+  if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 26)) return SAGEBWD_ERR_SHAPE;
+  if ((long long)p->B * p->H * (p->N / p->blk) * 3 >= (1LL << 31)) return SAGEBWD_ERR_SHAPE;
+  return SAGEBWD_OK;
+}
+
+bool empty(const sagebwd_params* p) { return p->B == 0 || p->H == 0 || p->N == 0; }
+
+size_t elems(const sagebwd_params* p) { return (size_t)p->B * p->H * p->N * p->d; }
+
+float sm_scale_of(const sagebwd_params* p) {
+  return p->sm_scale > 0.0f ? p->sm_scale : 1.0f / __builtin_sqrtf((float)p->d);
+}
+
+template <typename... Ptrs>
+sagebwd_status check_ptrs(Ptrs... ptrs) {
+  const void* arr[] = {static_cast<const void*>(ptrs)...};
+  for (const void* q : arr)
+    if (!q) return SAGEBWD_ERR_NULL;
+  for (const void* q : arr)
+    if (!aligned16(q)) return SAGEBWD_ERR_ALIGN;
+  return SAGEBWD_OK;
+}
+
+struct BwdLayout {
+  size_t dq, D, dOtc, dOs, Qtc, total;
+};
+
+BwdLayout bwd_layout(const sagebwd_params* p) {
+  const size_t bhn = (size_t)p->B * p->H * p->N;
+  BwdLayout L;
+  L.dq = 0;
+  L.D = L.dq + round_up(4 * elems(p));
+  L.dOtc = L.D + round_up(4 * bhn);
+  L.dOs = L.dOtc + round_up(elems(p));
+  L.Qtc = L.dOs + round_up(4 * (bhn / (size_t)p->blk));
+  L.total = L.Qtc + round_up(elems(p));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sagebwd_status_string(sagebwd_status s) {
+  switch (s) {
+    case SAGEBWD_OK: return "ok";
+    case SAGEBWD_ERR_NULL: return "null pointer argument";
+    case SAGEBWD_ERR_SHAPE: return "invalid shape (negative size, or N not a multiple of blk)";
+    case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype or eps)";
+    case SAGEBWD_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
+    case SAGEBWD_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p) {
+  if (check_params(p) != SAGEBWD_OK) return 0;
+  if (!p->k_smooth || empty(p)) return 0;
+  return round_up(4 * (size_t)p->B * p->H * (p->N / p->blk) * p->d);
+}
+
+size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
+  if (check_params(p) != SAGEBWD_OK) return 0;
+  if (empty(p)) return 0;
+  return bwd_layout(p).total;
+}
+
+sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
+                                      int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
+                                      float* q_rstd, float* k_rstd, float* k_mean, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  sagebwd_status st = check_params(p);
+  if (st != SAGEBWD_OK) return st;
+  if (empty(p)) return SAGEBWD_OK;
+  st = check_ptrs(Q, K, V, Qc, Kc, Vtc, Qs, Ks, Vs, q_rstd, k_rstd, k_mean);
+  if (st != SAGEBWD_OK) return st;
+  const size_t need = sagebwd_prologue_workspace_bytes(p);
+  if (need > 0) {
+    if (!workspace) return SAGEBWD_ERR_NULL;
+    if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
+    if (workspace_bytes < need) return SAGEBWD_ERR_WORKSPACE;
+  }
+  PrologueArgs a{};
+  a.Q = static_cast<const unsigned short*>(Q);
+  a.K = static_cast<const unsigned short*>(K);
+  a.V = static_cast<const unsigned short*>(V);
+  a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc;
+  a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
+  a.q_rstd = q_rstd; a.k_rstd = k_rstd; a.k_mean = k_mean;
+  a.kpart = static_cast<float*>(workspace);
+  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.eps = p->eps;
+  return sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+}
+
+sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
+                               const float* Qs, const float* Ks, const float* Vs, void* O, float* lse,
+                               void* stream) {
+  sagebwd_status st = check_params(p);
+  if (st != SAGEBWD_OK) return st;
+  if (empty(p)) return SAGEBWD_OK;
+  st = check_ptrs(Qc, Kc, Vtc, Qs, Ks, Vs, O, lse);
+  if (st != SAGEBWD_OK) return st;
+  ForwardArgs a{};
+  a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc; a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
+  a.O = static_cast<unsigned short*>(O); a.lse = lse;
+  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
+  return sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+}
+
+sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,
+                                const int8_t* Qc, const int8_t* Kc, const float* Qs, const float* Ks,
+                                const float* q_rstd, const float* k_rstd, const void* O, const float* lse,
+                                const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sagebwd_status st = check_params(p);
+  if (st != SAGEBWD_OK) return st;
+  if (empty(p)) return SAGEBWD_OK;
+  st = check_ptrs(Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV);
+  if (st != SAGEBWD_OK) return st;
+  if (!workspace) return SAGEBWD_ERR_NULL;
+  if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
+  const BwdLayout L = bwd_layout(p);
+  if (workspace_bytes < L.total) return SAGEBWD_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  BackwardArgs a{};
+  a.Q = static_cast<const unsigned short*>(Q);
+  a.K = static_cast<const unsigned short*>(K);
+  a.V = static_cast<const unsigned short*>(V);
+  a.O = static_cast<const unsigned short*>(O);
+  a.dO = static_cast<const unsigned short*>(dO);
+  a.Qc = Qc; a.Kc = Kc; a.Qs = Qs; a.Ks = Ks;
+  a.q_rstd = q_rstd; a.k_rstd = k_rstd; a.lse = lse;
+  a.dQ = static_cast<unsigned short*>(dQ);
+  a.dK = static_cast<unsigned short*>(dK);
+  a.dV = static_cast<unsigned short*>(dV);
+  a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
+  a.Dvec = reinterpret_cast<float*>(ws + L.D);
+  a.dOtc = reinterpret_cast<int8_t*>(ws + L.dOtc);
+  a.dOs = reinterpret_cast<float*>(ws + L.dOs);
+  a.Qtc = reinterpret_cast<int8_t*>(ws + L.Qtc);
+  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
+  return sagebwd::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+}
+
+}  // extern "C"

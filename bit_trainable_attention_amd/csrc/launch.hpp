@@ -1,0 +1,71 @@
+// Kernel argument blocks and launch entry points (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace sagebwd {
+
+struct PrologueArgs {
+  const unsigned short *Q, *K, *V;   // 16-bit [BH, N, D]
+  int8_t *Qc, *Kc, *Vtc;             // [BH, N, D], [BH, N, D], [BH, D, N]
+  float *Qs, *Ks, *Vs;               // [BH, N/BLK]
+  float *q_rstd, *k_rstd;            // [BH, N]
+  float* k_mean;                     // [BH, D]
+  float* kpart;                      // [BH, N/BLK, D] (smoothing only)
+  int BH, N, D, BLK, dtype;
+  int qk_norm, k_smooth;
+  float eps;
+};
+
+struct ForwardArgs {
+  const int8_t *Qc, *Kc, *Vtc;
+  const float *Qs, *Ks, *Vs;
+  unsigned short* O;                 // [BH, N, D]
+  float* lse;                        // [BH, N]
+  int BH, N, D, BLK, dtype;
+  int causal;
+  float sm_scale;
+};
+
+struct BackwardArgs {
+  const unsigned short *Q, *K, *V, *O, *dO;  // 16-bit [BH, N, D]
+  const int8_t *Qc, *Kc;                     // [BH, N, D]
+  const float *Qs, *Ks;                      // [BH, N/BLK]
+  const float *q_rstd, *k_rstd, *lse;        // [BH, N]
+  unsigned short *dQ, *dK, *dV;              // [BH, N, D]
+  // workspace regions
+  float* dq_acc;                             // [BH, N, D]
+  float* Dvec;                               // [BH, N]
+  int8_t* dOtc;                              // [BH, D, N]
+  float* dOs;                                // [BH, N/BLK]
+  int8_t* Qtc;                               // [BH, D, N]
+  int BH, N, D, BLK, dtype;
+  int causal, qk_norm;
+  float sm_scale;
+};
+
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t st);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
+
+// Calls f(dtype, d, blk) with std::integral_constant arguments for the supported
+// combinations (dtype in {fp16, bf16}, d in {64, 128}, blk in {64, 128}).
+template <typename F>
+hipError_t dispatch_dt_d_blk(int dtype, int d, int blk, F&& f) {
+  using I = std::integral_constant<int, 0>;
+  (void)sizeof(I);
+#define SAGEBWD_CASE(DTV, DV, BV)                                                    \
+  if (dtype == DTV && d == DV && blk == BV)                                          \
+    return f(std::integral_constant<int, DTV>{}, std::integral_constant<int, DV>{},  \
+             std::integral_constant<int, BV>{});
+  SAGEBWD_CASE(0, 64, 64) SAGEBWD_CASE(0, 64, 128) SAGEBWD_CASE(0, 128, 64) SAGEBWD_CASE(0, 128, 128)
+  SAGEBWD_CASE(1, 64, 64) SAGEBWD_CASE(1, 64, 128) SAGEBWD_CASE(1, 128, 64) SAGEBWD_CASE(1, 128, 128)
+#undef SAGEBWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sagebwd

@@ -1,0 +1,150 @@
+/*
+ * sagebwd.h - C ABI of a SageBwd-style trainable INT8 attention for AMD MI355X (gfx950).
+ *
+ * The method (SageBwd article, "SageBwd: a trainable low-bit attention mechanism",
+ * aitrends.kr article 8227):
+ *   - QK-norm: every token vector of Q and K is RMS-normalised over the head dim, gain 1
+ *     (article, QK-norm paragraph);
+ *   - K-smoothing: the per-channel mean of the normalised keys over all N tokens of a head
+ *     is subtracted right before quantisation (article, K-smoothing paragraph; the axis is
+ *     fixed by the Q-smoothing paragraph's bias term (dS^T 1) mu_Q^T, a d-vector over tokens);
+ *   - per-block INT8 quantisation (article, per-block kernels paragraph): one float32 scale
+ *     per `blk` tokens x d channels, scale = absmax/127, codes = round-to-nearest-even of
+ *     x * (127/absmax) clamped to [-127, 127]; an all-zero block has scale 0 and codes 0;
+ *   - six of attention's seven matmuls in INT8 with int32 accumulation (forward QK^T, PV;
+ *     backward recomputed QK^T, dV = P^T dO, dK = dS^T Q, dQ = dS K) and dP = dO V^T in the
+ *     16-bit input type with float32 accumulation (article, precision-split paragraph);
+ *   - a flash-style forward and backward that never writes the N x N scores to memory
+ *     (TurboQuant blog, FlashAttention section).
+ *
+ * In-kernel quantisation tiles (P~ in the forward, P and dS in the backward) use the same
+ * absmax/127 rule, decided in float32:
+ *   P~ (forward)   : SAGEBWD_FWD_TILE_Q query rows x blk keys; the online-softmax running
+ *                    max moves once per such tile and P~ = exp(s - running max); the row
+ *                    sum l accumulates P~ before quantisation.
+ *   P  (backward)  : SAGEBWD_BWD_TILE_Q query rows x SAGEBWD_BWD_P_TILE_K keys.
+ *   dS (backward)  : SAGEBWD_BWD_TILE_Q query rows x blk keys.
+ * Every tile lies inside one blk x blk block, so the block scales factor out of each
+ * integer product.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors), contiguous,
+ *     16-byte aligned. Shapes are given in [B,H,N,d] order, last index fastest.
+ *   - The caller owns every buffer. The library allocates nothing, keeps no state between
+ *     calls, never synchronises, and is re-entrant; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream). Calls sharing a workspace must be
+ *     ordered on one stream.
+ *   - Inputs are never written. Outputs are fully overwritten.
+ *   - Argument errors are reported before anything is enqueued and before any HIP call.
+ *     A failed launch returns SAGEBWD_ERR_HIP. Faults inside kernels surface at the
+ *     caller's next synchronisation, as usual in HIP. NaN/Inf inputs give unspecified
+ *     (but memory-safe) results. No exception crosses this boundary.
+ *   - N == 0 (or B == 0 or H == 0) is valid and enqueues nothing.
+ */
+#ifndef SAGEBWD_H
+#define SAGEBWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGEBWD_FWD_TILE_Q 32
+#define SAGEBWD_BWD_TILE_Q 64
+#define SAGEBWD_BWD_P_TILE_K 32
+
+typedef enum {
+  SAGEBWD_OK = 0,
+  SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
+  SAGEBWD_ERR_SHAPE = -2,       /* negative size, or N not a multiple of blk                */
+  SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, eps < 0        */
+  SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
+  SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
+  SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
+} sagebwd_status;
+
+typedef enum { SAGEBWD_FP16 = 0, SAGEBWD_BF16 = 1 } sagebwd_dtype;
+
+typedef struct {
+  int32_t B, H, N, d;   /* batch, heads, tokens, head dim (d in {64, 128})                  */
+  int32_t blk;          /* quantisation block, tokens (64 or 128); N % blk == 0             */
+  int32_t causal;       /* nonzero: key j is visible to query i iff j <= i                  */
+  int32_t qk_norm;      /* nonzero: RMSNorm Q and K per token (gain 1)                      */
+  int32_t k_smooth;     /* nonzero: subtract K's per-channel mean before quantising         */
+  float eps;            /* RMSNorm epsilon (>= 0), e.g. 1e-6                                */
+  float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(d)                            */
+  int32_t dtype;        /* sagebwd_dtype of Q, K, V, dO, O, dQ, dK, dV                       */
+} sagebwd_params;
+
+/* Bytes of scratch sagebwd_quant_prologue needs: the per-block channel sums of the
+ * normalised keys, float32 [B,H,N/blk,d] (0 when k_smooth is off). Returns 0 for
+ * invalid params. */
+size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
+
+/* Quantisation prologue: QK-norm -> K-smoothing -> per-block INT8 codes and scales.
+ * The codes, scales and statistics are the "quantised views" both passes reuse (the
+ * Full-Stack FP4 page, section 2.4, reuses quantised Q, K, V between the passes).
+ *   Q, K, V  in : dtype [B,H,N,d]
+ *   Qc, Kc   out: int8 [B,H,N,d]   codes of Q^ and of K~ = K^ - mean (smoothed keys)
+ *   Vtc      out: int8 [B,H,d,N]   codes of V, stored TRANSPOSED (channel-major)
+ *   Qs,Ks,Vs out: float32 [B,H,N/blk]  block scales
+ *   q_rstd, k_rstd out: float32 [B,H,N]  1/sqrt(mean(x^2)+eps) per token (1 if !qk_norm)
+ *   k_mean   out: float32 [B,H,d]  the subtracted mean (0 if !k_smooth)
+ *   workspace   : >= sagebwd_prologue_workspace_bytes(p) bytes (may be NULL if that is 0)
+ * Bit-exact contract: per token, ss = sum over channels in ascending order of x*x in
+ * float32; rstd = 1/sqrt(ss/d + eps) with correctly rounded float32 division and square
+ * root; x^ = x*rstd; the mean sums each block's tokens in ascending order, then the block
+ * sums in ascending order, then divides by N; K~ = K^ - mean; then the INT8 rule above. */
+sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
+                                      const void* Q, const void* K, const void* V,
+                                      int8_t* Qc, int8_t* Kc, int8_t* Vtc,
+                                      float* Qs, float* Ks, float* Vs,
+                                      float* q_rstd, float* k_rstd, float* k_mean,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* Forward: O = softmax(sm_scale * Q^ K~^T [causal mask]) V with INT8 QK^T and PV.
+ *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs
+ *   O   out: dtype [B,H,N,d]
+ *   lse out: float32 [B,H,N], natural-log logsumexp of each row of the scaled scores */
+sagebwd_status sagebwd_forward(const sagebwd_params* p,
+                               const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
+                               const float* Qs, const float* Ks, const float* Vs,
+                               void* O, float* lse, void* stream);
+
+/* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
+ * boundary, in this order; sizes in bytes):
+ *   dq_acc float32 [B,H,N,d]    (4*B*H*N*d)   dQ of the normalised queries, accumulated
+ *   D      float32 [B,H,N]      (4*B*H*N)     rowsum(dO o O)
+ *   dOtc   int8    [B,H,d,N]    (B*H*N*d)     INT8 codes of dO, transposed
+ *   dOs    float32 [B,H,N/blk]  (4*B*H*N/blk) block scales of dO
+ *   Qtc    int8    [B,H,d,N]    (B*H*N*d)     Qc transposed
+ * Returns 0 for invalid params. */
+size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
+
+/* Backward. Gradients are with respect to the RAW Q, K, V given to the prologue (the
+ * RMSNorm backward is applied; K-smoothing adds no term because every row of dS sums to 0).
+ *   Q, K, V       in : dtype [B,H,N,d], the prologue's inputs
+ *   Qc, Kc, Qs, Ks, q_rstd, k_rstd in: the prologue's outputs
+ *   O, lse        in : the forward's outputs
+ *   dO            in : dtype [B,H,N,d]
+ *   dQ, dK, dV    out: dtype [B,H,N,d]
+ *   workspace        : >= sagebwd_backward_workspace_bytes(p) bytes, layout above */
+sagebwd_status sagebwd_backward(const sagebwd_params* p,
+                                const void* Q, const void* K, const void* V,
+                                const int8_t* Qc, const int8_t* Kc,
+                                const float* Qs, const float* Ks,
+                                const float* q_rstd, const float* k_rstd,
+                                const void* O, const float* lse, const void* dO,
+                                void* dQ, void* dK, void* dV,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* sagebwd_status_string(sagebwd_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGEBWD_H */

@@ -1,0 +1,131 @@
+"""Shared helpers for the parity tests: build the oracle's Spec from a workload and the
+tile constants documented in include/sagebwd.h, move seeded inputs to the GPU, run the
+HIP path through the C ABI, and compare."""
+from __future__ import annotations
+
+import os
+import re
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from bit_trainable_attention_amd import workloads as wl
+from oracle import quant as oq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sagebwd.h")
+
+
+def header_constants() -> Dict[str, int]:
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+SAGEBWD_(\w+)\s+(\d+)", text)}
+
+
+def header_functions() -> list:
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|sagebwd_status|const char\*)\s+(sagebwd_\w+)\s*\(", text, re.M)))
+
+
+def spec_for(w: wl.Workload, dtype: Optional[str] = None) -> oq.Spec:
+    c = header_constants()
+    return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
+                   dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
+                   fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=c["BWD_TILE_Q"], bwd_pk=c["BWD_P_TILE_K"],
+                   bwd_sk=w.blk)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def cosine(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / max(np.linalg.norm(a) * np.linalg.norm(b), 1e-300))
+
+
+def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
+    x = wl.make_inputs(w)
+    out = {k: x[k] for k in ("Q", "K", "V", "dO")}
+    for k in ("Q", "K", "V", "dO"):
+        out[k + "f"] = wl.bits_to_f32(x[k], w.dtype)
+    return out
+
+
+# ------------------------------------------------------------------------------- GPU side
+
+def params_for(w: wl.Workload):
+    from bit_trainable_attention_amd import api
+    return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+
+
+def to_device(bits: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.float16 if dtype == "fp16" else torch.bfloat16)
+    return t.to("cuda:0")
+
+
+def f32_to_device_dtype(x: np.ndarray, dtype: str):
+    """float64/32 values already representable in dtype -> device tensor of dtype."""
+    return to_device(wl.f32_to_bits(np.asarray(x, np.float32), dtype), dtype)
+
+
+def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
+            pro_in=None, O_in=None, lse_in=None) -> Dict[str, np.ndarray]:
+    """Run the HIP path and return host copies (numpy) of everything it produced."""
+    import torch
+    from bit_trainable_attention_amd import api
+    p = params_for(w)
+    Q, K, V, dO = (to_device(x[k], w.dtype) for k in ("Q", "K", "V", "dO"))
+    res: Dict[str, np.ndarray] = {}
+    pro = pro_in
+    if "prologue" in stages:
+        pro = api.sagebwd_quant_prologue(p, Q, K, V)
+    O, lse = O_in, lse_in
+    if "forward" in stages:
+        O, lse = api.sagebwd_forward(p, pro)
+    if "backward" in stages:
+        g = api.sagebwd_backward(p, Q, K, V, pro, O, lse, dO)
+    torch.cuda.synchronize()
+    if "prologue" in stages:
+        for k, v in pro.items():
+            res[k] = v.cpu().numpy()
+    if "forward" in stages:
+        res["O"] = O.float().cpu().numpy().astype(np.float64)
+        res["LSE"] = lse.cpu().numpy()
+    if "backward" in stages:
+        for k in ("dQ", "dK", "dV"):
+            res[k] = g[k].float().cpu().numpy().astype(np.float64)
+        lay = api.backward_workspace_layout(p)
+        ws = g["workspace"].cpu().numpy()
+        n = w.B * w.H * w.N * w.d
+        res["dOtc"] = ws[lay["dOtc"]:lay["dOtc"] + n].view(np.int8).reshape(w.B, w.H, w.d, w.N)
+        res["dOs"] = ws[lay["dOs"]:lay["dOs"] + 4 * w.B * w.H * (w.N // w.blk)].view(np.float32).reshape(
+            w.B, w.H, w.N // w.blk)
+        res["Dvec"] = ws[lay["D"]:lay["D"] + 4 * w.B * w.H * w.N].view(np.float32).reshape(w.B, w.H, w.N)
+    return res
+
+
+def pro_to_device(pro: Dict[str, np.ndarray]):
+    """The oracle's prologue outputs as device tensors in the C ABI layout (for staged tests)."""
+    import torch
+    out = {}
+    for k in ("Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"):
+        out[k] = torch.from_numpy(np.ascontiguousarray(pro[k])).to("cuda:0")
+    out["Vtc"] = torch.from_numpy(np.ascontiguousarray(np.swapaxes(pro["Vc"], -1, -2))).to("cuda:0")
+    return out
+
+
+def slice_heads(x: Dict[str, np.ndarray], w: wl.Workload, heads: Sequence[int]) -> Dict[str, np.ndarray]:
+    """Select flattened heads (b*H + h) of every [B,H,...] array, as a B=1, H=len(heads) set."""
+    out = {}
+    for k, v in x.items():
+        if isinstance(v, np.ndarray) and v.ndim >= 2 and v.shape[:2] == (w.B, w.H):
+            f = v.reshape((w.B * w.H,) + v.shape[2:])[list(heads)]
+            out[k] = f.reshape((1, len(heads)) + v.shape[2:])
+        else:
+            out[k] = v
+    return out

@@ -1,0 +1,99 @@
+"""The C ABI library loads, exports every entry point include/sagebwd.h declares, and
+rejects bad arguments before doing anything on a device. No call here reaches a kernel:
+every call either fails validation or is a documented no-op (N == 0)."""
+import ctypes
+
+import pytest
+
+from bit_trainable_attention_amd import _lib
+from tests.harness import header_constants, header_functions
+
+lib = _lib.load()  # fails loudly if the library was not built
+
+
+def P(**kw):
+    base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
+                dtype=_lib.SAGEBWD_FP16)
+    base.update(kw)
+    return _lib.Params(**base)
+
+
+FAKE = 0x10000  # an aligned, never dereferenced address
+MIS = 0x10001   # misaligned
+
+
+def test_exports_every_header_symbol():
+    names = header_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_header_tile_constants_match_binding():
+    c = header_constants()
+    assert (c["FWD_TILE_Q"], c["BWD_TILE_Q"], c["BWD_P_TILE_K"]) == (_lib.FWD_TILE_Q, _lib.BWD_TILE_Q, _lib.BWD_P_TILE_K)
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS.items():
+        s = lib.sagebwd_status_string(code).decode()
+        assert s and s != "unknown status", (code, name)
+    assert lib.sagebwd_status_string(12345).decode() == "unknown status"
+
+
+def _prologue(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 12), ws, ws_bytes, None)
+
+
+def _forward(p, ptr=FAKE):
+    return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 8), None)
+
+
+def _backward(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 15), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call", [_prologue, _forward, _backward])
+def test_invalid_params_rejected(call):
+    assert call(P(d=96)) == -3
+    assert call(P(d=32)) == -3
+    assert call(P(blk=32)) == -3
+    assert call(P(dtype=7)) == -3
+    assert call(P(eps=-1.0)) == -3
+    assert call(P(N=200)) == -2            # not a multiple of blk
+    assert call(P(B=-1)) == -2
+    assert call(P(N=-64)) == -2
+    assert call(P(B=1 << 13, H=1 << 12)) == -2
+    assert call(P(), ptr=0) == -1          # null tensors
+    assert call(P(), ptr=MIS) == -4        # misaligned tensors
+
+
+def test_null_params_rejected():
+    assert lib.sagebwd_forward(None, *([FAKE] * 8), None) == -1
+    assert lib.sagebwd_backward_workspace_bytes(None) == 0
+    assert lib.sagebwd_prologue_workspace_bytes(None) == 0
+
+
+def test_workspace_checks():
+    p = P()
+    need = lib.sagebwd_backward_workspace_bytes(ctypes.byref(p))
+    n = 1 * 2 * 256 * 64
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == up(4 * n) + up(4 * 512) + up(n) + up(4 * 8) + up(n)
+    assert _backward(p, ws_bytes=need - 1) == -5
+    assert _backward(p, ws=0) == -1
+    assert _backward(p, ws=MIS) == -4
+    pw = lib.sagebwd_prologue_workspace_bytes(ctypes.byref(p))
+    assert pw == up(4 * 2 * 4 * 64)
+    assert _prologue(p, ws_bytes=pw - 1) == -5
+    assert _prologue(p, ws=0) == -1
+    # smoothing off: the prologue needs no scratch
+    assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(k_smooth=0))) == 0
+
+
+def test_empty_is_a_noop():
+    # N == 0 (or B == 0 / H == 0): nothing is enqueued and pointers are not inspected
+    for p in (P(N=0), P(B=0), P(H=0)):
+        assert _prologue(p, ptr=0, ws=0, ws_bytes=0) == 0
+        assert _forward(p, ptr=0) == 0
+        assert _backward(p, ptr=0, ws=0, ws_bytes=0) == 0
