@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the SageBwd-style INT8 attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input resident in HBM:
+quantisation prologue -> INT8 forward -> INT8/FP16 backward (all kernels). The workload is
+B2 H16 N8192 d128, causal, fp16, QK-norm and K-smoothing on, 128-token quantisation blocks.
+Throughput counts the seven attention matmuls: 14*d operations per visible (query, key) pair
+(12*d in INT8, 2*d in FP16), for the whole step.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TOP/s): INT8 5.0 POPS, FP16/BF16 2.5 PFLOPS.
+PEAK_I8 = 5000.0
+PEAK_F16 = 2500.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_main_n8192_d128_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_trainable_attention_amd", "csrc", f)
+                  for f in ("backward.hip", "common.hpp")]
+
+
+def weighted_peak(n_i8: int, n_f16: int) -> float:
+    tot = n_i8 + n_f16
+    return 1.0 / ((n_i8 / tot) / PEAK_I8 + (n_f16 / tot) / PEAK_F16)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per bwd_main launch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    with open(PROFILE_TRAFFIC) as f:
+        d = json.load(f)
+    if d.get("source_sha256") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, heads: int):
+    """The plain CPU oracle (as it stands) on `heads` heads of the same workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import quant as oq
+    from tests.harness import spec_for
+    from bit_trainable_attention_amd import workloads as wl
+    ws = w.with_shape(B=1, H=heads)
+    sl = lambda a: np.ascontiguousarray(a.reshape((-1,) + a.shape[2:])[:heads].reshape((1, heads) + a.shape[2:]))
+    Qf, Kf, Vf, dOf = (wl.bits_to_f32(sl(x[k]), w.dtype) for k in ("Q", "K", "V", "dO"))
+    spec = spec_for(ws)
+    t0 = time.perf_counter()
+    oq.run(Qf, Kf, Vf, dOf, spec)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=ws.algorithmic_ops() / dt / 1e12, unit="TOPS", cores=int(threads), kind="oracle",
+                sample=f"{heads} of {w.B * w.H} heads (B1 H{heads} N{w.N} d{w.d}), quantised oracle "
+                       f"prologue+forward+backward, float64 numpy, {dt:.1f} s",
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n8192_d128")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards over heads with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_trainable_attention_amd import api
+    from bit_trainable_attention_amd import workloads as wl
+    w = wl.WORKLOADS[args.workload]
+
+    def to_device(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.float16 if w.dtype == "fp16" else torch.bfloat16).to("cuda:0")
+
+    log(f"[bench] workload {w.name}: B{w.B} H{w.H} N{w.N} d{w.d} {w.dtype} causal={w.causal} "
+        f"qk_norm={w.qk_norm} k_smooth={w.k_smooth} blk={w.blk}")
+    x = wl.make_inputs(w)
+    p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+    dev = torch.device("cuda:0")
+    Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
+    pro = api.sagebwd_quant_prologue(p, Q, K, V)
+    pro_ws = torch.empty(max(api.sagebwd_prologue_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+    O, lse = api.sagebwd_forward(p, pro)
+    grads = {n: torch.empty_like(Q) for n in ("dQ", "dK", "dV")}
+    bws = torch.empty(api.sagebwd_backward_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stages = ["prologue", "forward", "bwd_pre", "bwd_main", "dq_finalize"]
+
+    def step(ev):
+        ev[0].record()
+        api.sagebwd_quant_prologue(p, Q, K, V, out=pro, workspace=pro_ws)
+        ev[1].record()
+        api.sagebwd_forward(p, pro, O=O, lse=lse)
+        ev[2].record()
+        for part in range(3):
+            api.sagebwd_backward_part(p, part, Q, K, V, pro, O, lse, dO, grads, bws)
+            ev[3 + part].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, s in enumerate(stages)}
+
+    pairs = w.visible_pairs()
+    ops = w.algorithmic_ops()
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    peak_step = weighted_peak(6, 1)
+    ops_main = 10 * w.d * pairs       # bwd_main: recomputed QK^T, dV, dK, dQ (INT8) + dP (FP16)
+    ach_main = ops_main / (stage_ms["bwd_main"] * 1e-3) / 1e12
+    peak_main = weighted_peak(4, 1)
+    traffic = traffic_from_profile()
+    log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TOPS = {100 * value / peak_step:.1f}% of the "
+        f"{peak_step:.0f} TOPS INT8/FP16 (6:1) dense peak; stages (ms): "
+        + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+    fwd_ops = 4 * w.d * pairs
+    log(f"[bench] forward {fwd_ops / (stage_ms['forward'] * 1e-3) / 1e12:.1f} TOPS (INT8 peak {PEAK_I8:.0f}); "
+        f"bwd_main {ach_main:.1f} TOPS (4:1 INT8/FP16 peak {peak_main:.0f})")
+
+    out = {
+        "metric": "INT8 attention fwd+bwd TOPS at B2 H16 N8192 d128 causal; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} H{w.H} N{w.N} d{w.d} causal {w.dtype} QK-norm "
+                               f"K-smoothing blk{w.blk} (prologue+fwd+bwd)",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "blk": w.blk,
+                   "dtype": w.dtype, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / peak_step, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "bwd_main", "bound": "mfma", "achieved": round(ach_main, 2),
+                     "peak": round(peak_main, 1), "unit": "TFLOP/s", "frac": round(ach_main / peak_main, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_heads} head(s)...")
+        cb = cpu_baseline(w, x, args.cpu_heads)
+        log(f"[bench] CPU oracle: {cb['seconds']:.1f} s, {cb['value']:.5f} TOPS, {cb['cores']} threads")
+        cb.pop("seconds")
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

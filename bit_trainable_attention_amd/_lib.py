@@ -43,6 +43,7 @@ SIGNATURES = {
     "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 8 + [_P]),
     "sagebwd_backward_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
     "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 15 + [_P, _SIZE, _P]),
+    "sagebwd_backward_part": (_ST, [ctypes.POINTER(Params), ctypes.c_int32] + [_P] * 15 + [_P, _SIZE, _P]),
     "sagebwd_status_string": (ctypes.c_char_p, [_ST]),
 }
 

@@ -71,7 +71,8 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     bhn = p.B * p.H * p.N
     off = {"dq_acc": 0}
     off["D"] = off["dq_acc"] + up(4 * n)
-    off["dOtc"] = off["D"] + up(4 * bhn)
+    off["lse2"] = off["D"] + up(4 * bhn)
+    off["dOtc"] = off["lse2"] + up(4 * bhn)
     off["dOs"] = off["dOtc"] + up(n)
     off["Qtc"] = off["dOs"] + up(4 * (bhn // p.blk))
     off["total"] = off["Qtc"] + up(n)
@@ -140,12 +141,7 @@ def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[to
     return O, lse
 
 
-def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
-                     pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
-                     grads: Optional[Dict[str, torch.Tensor]] = None,
-                     workspace: Optional[torch.Tensor] = None,
-                     stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
-    """Backward. Returns dict(dQ, dK, dV, workspace)."""
+def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
     dev = Q.device
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
@@ -164,12 +160,32 @@ def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = _lib.load().sagebwd_backward(
-        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(pro["Qc"]), _ptr(pro["Kc"]),
-        _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["q_rstd"]), _ptr(pro["k_rstd"]),
-        _ptr(O), _ptr(lse), _ptr(dO), _ptr(grads["dQ"]), _ptr(grads["dK"]), _ptr(grads["dV"]),
-        _ptr(workspace), ws_bytes, _stream(dev, stream))
+    args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(pro["Qc"]), _ptr(pro["Kc"]),
+            _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["q_rstd"]), _ptr(pro["k_rstd"]),
+            _ptr(O), _ptr(lse), _ptr(dO), _ptr(grads["dQ"]), _ptr(grads["dK"]), _ptr(grads["dV"]),
+            _ptr(workspace), ws_bytes]
+    return args, grads, workspace
+
+
+def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                     pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
+                     grads: Optional[Dict[str, torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
+    """Backward. Returns dict(dQ, dK, dV, workspace)."""
+    args, grads, workspace = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace)
+    st = _lib.load().sagebwd_backward(ctypes.byref(p), *args, _stream(Q.device, stream))
     _check(st, "sagebwd_backward")
     out = dict(grads)
     out["workspace"] = workspace
     return out
+
+
+def sagebwd_backward_part(p: _lib.Params, part: int, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                          pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
+                          grads: Dict[str, torch.Tensor], workspace: torch.Tensor,
+                          stream: Optional[torch.cuda.Stream] = None) -> None:
+    """One stage (0: pre, 1: main, 2: finalize) of the backward; see include/sagebwd.h."""
+    args, _, _ = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace)
+    st = _lib.load().sagebwd_backward_part(ctypes.byref(p), int(part), *args, _stream(Q.device, stream))
+    _check(st, f"sagebwd_backward_part({part})")

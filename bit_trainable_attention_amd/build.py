@@ -51,6 +51,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every symbol must resolve (a missing kernel stub would otherwise only show at load time)
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    bad = [ln for ln in nm.splitlines() if "sagebwd" in ln]
+    if bad:
+        raise RuntimeError("unresolved library symbols:\n" + "\n".join(bad))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -27,8 +27,9 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->dtype != SAGEBWD_FP16 && p->dtype != SAGEBWD_BF16) return SAGEBWD_ERR_UNSUPPORTED;
   if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
-  // index arithmetic inside the kernels: token rows fit in 32 bits per head, grids in 2^31
-  if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 26)) return SAGEBWD_ERR_SHAPE;
+  // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
+  // (N * d * 4 < 2^31), grids in 2^31 workgroups
+  if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 22)) return SAGEBWD_ERR_SHAPE;
   if ((long long)p->B * p->H * (p->N / p->blk) * 3 >= (1LL << 31)) return SAGEBWD_ERR_SHAPE;
   return SAGEBWD_OK;
 }
@@ -52,7 +53,7 @@ sagebwd_status check_ptrs(Ptrs... ptrs) {
 }
 
 struct BwdLayout {
-  size_t dq, D, dOtc, dOs, Qtc, total;
+  size_t dq, D, lse2, dOtc, dOs, Qtc, total;
 };
 
 BwdLayout bwd_layout(const sagebwd_params* p) {
@@ -60,7 +61,8 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
   BwdLayout L;
   L.dq = 0;
   L.D = L.dq + round_up(4 * elems(p));
-  L.dOtc = L.D + round_up(4 * bhn);
+  L.lse2 = L.D + round_up(4 * bhn);
+  L.dOtc = L.lse2 + round_up(4 * bhn);
   L.dOs = L.dOtc + round_up(elems(p));
   L.Qtc = L.dOs + round_up(4 * (bhn / (size_t)p->blk));
   L.total = L.Qtc + round_up(elems(p));
@@ -140,13 +142,14 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
   return sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
 }
 
-sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,
-                                const int8_t* Qc, const int8_t* Kc, const float* Qs, const float* Ks,
-                                const float* q_rstd, const float* k_rstd, const void* O, const float* lse,
-                                const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static sagebwd_status backward_impl(const sagebwd_params* p, int part, const void* Q, const void* K,
+                                    const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
+                                    const float* Ks, const float* q_rstd, const float* k_rstd, const void* O,
+                                    const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
+  if (part < -1 || part > 2) return SAGEBWD_ERR_UNSUPPORTED;
   if (empty(p)) return SAGEBWD_OK;
   st = check_ptrs(Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV);
   if (st != SAGEBWD_OK) return st;
@@ -168,12 +171,33 @@ sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const vo
   a.dV = static_cast<unsigned short*>(dV);
   a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
   a.Dvec = reinterpret_cast<float*>(ws + L.D);
+  a.lse2 = reinterpret_cast<float*>(ws + L.lse2);
   a.dOtc = reinterpret_cast<int8_t*>(ws + L.dOtc);
   a.dOs = reinterpret_cast<float*>(ws + L.dOs);
   a.Qtc = reinterpret_cast<int8_t*>(ws + L.Qtc);
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
-  return sagebwd::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+  return sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK
+                                                                                          : SAGEBWD_ERR_HIP;
+}
+
+sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,
+                                const int8_t* Qc, const int8_t* Kc, const float* Qs, const float* Ks,
+                                const float* q_rstd, const float* k_rstd, const void* O, const float* lse,
+                                const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return backward_impl(p, -1, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV, workspace,
+                       workspace_bytes, stream);
+}
+
+sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part, const void* Q, const void* K,
+                                     const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
+                                     const float* Ks, const float* q_rstd, const float* k_rstd, const void* O,
+                                     const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (part < 0) return check_params(p) != SAGEBWD_OK ? check_params(p) : SAGEBWD_ERR_UNSUPPORTED;
+  return backward_impl(p, part, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,7 @@ struct BackwardArgs {
   // workspace regions
   float* dq_acc;                             // [BH, N, D]
   float* Dvec;                               // [BH, N]
+  float* lse2;                               // [BH, N] lse * log2(e)
   int8_t* dOtc;                              // [BH, D, N]
   float* dOs;                                // [BH, N/BLK]
   int8_t* Qtc;                               // [BH, D, N]
@@ -50,7 +51,7 @@ struct BackwardArgs {
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st);
-hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
+hipError_t launch_backward(const BackwardArgs& a, int part, hipStream_t st);  // part -1 = all
 
 // Calls f(dtype, d, blk) with std::integral_constant arguments for the supported
 // combinations (dtype in {fp16, bf16}, d in {64, 128}, blk in {64, 128}).

@@ -58,7 +58,8 @@ extern "C" {
 typedef enum {
   SAGEBWD_OK = 0,
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
-  SAGEBWD_ERR_SHAPE = -2,       /* negative size, or N not a multiple of blk                */
+  SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
+                                   B*H > 2^24                                               */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, eps < 0        */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
@@ -118,9 +119,12 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  * boundary, in this order; sizes in bytes):
  *   dq_acc float32 [B,H,N,d]    (4*B*H*N*d)   dQ of the normalised queries, accumulated
  *   D      float32 [B,H,N]      (4*B*H*N)     rowsum(dO o O)
- *   dOtc   int8    [B,H,d,N]    (B*H*N*d)     INT8 codes of dO, transposed
+ *   lse2   float32 [B,H,N]      (4*B*H*N)     lse * log2(e)
+ *   dOtc   int8    [B,H,d,N]    (B*H*N*d)     INT8 codes of dO, transposed; inside each group of
+ *                                             32 tokens, token t sits at position
+ *                                             16*((t>>2)&1) + 4*(t>>3) + (t&3)
  *   dOs    float32 [B,H,N/blk]  (4*B*H*N/blk) block scales of dO
- *   Qtc    int8    [B,H,d,N]    (B*H*N*d)     Qc transposed
+ *   Qtc    int8    [B,H,d,N]    (B*H*N*d)     Qc transposed, same token order as dOtc
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 
@@ -140,6 +144,22 @@ sagebwd_status sagebwd_backward(const sagebwd_params* p,
                                 const void* O, const float* lse, const void* dO,
                                 void* dQ, void* dK, void* dV,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* One stage of sagebwd_backward, for callers that schedule or time the stages apart:
+ *   part 0: D = rowsum(dO o O), dO codes/scales, Qc transposed, dq_acc zeroed
+ *   part 1: the fused key-block kernel (S, P, dP, dS; dV, dK final; dQ^ accumulated)
+ *   part 2: dQ = RMSNorm backward of dq_acc, rounded to the dtype
+ * Arguments as for sagebwd_backward. Running parts 0, 1, 2 in order on one stream with the
+ * same workspace is exactly sagebwd_backward; any other order gives undefined results.
+ * part outside 0..2 -> SAGEBWD_ERR_UNSUPPORTED. */
+sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part,
+                                     const void* Q, const void* K, const void* V,
+                                     const int8_t* Qc, const int8_t* Kc,
+                                     const float* Qs, const float* Ks,
+                                     const float* q_rstd, const float* k_rstd,
+                                     const void* O, const float* lse, const void* dO,
+                                     void* dQ, void* dK, void* dV,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* sagebwd_status_string(sagebwd_status s);

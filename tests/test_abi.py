@@ -64,6 +64,7 @@ def test_invalid_params_rejected(call):
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
     assert call(P(B=1 << 13, H=1 << 12)) == -2
+    assert call(P(N=(1 << 22) + 64)) == -2   # per-head byte offsets must fit in 31 bits
     assert call(P(), ptr=0) == -1          # null tensors
     assert call(P(), ptr=MIS) == -4        # misaligned tensors
 
@@ -79,7 +80,7 @@ def test_workspace_checks():
     need = lib.sagebwd_backward_workspace_bytes(ctypes.byref(p))
     n = 1 * 2 * 256 * 64
     up = lambda x: (x + 255) // 256 * 256
-    assert need == up(4 * n) + up(4 * 512) + up(n) + up(4 * 8) + up(n)
+    assert need == up(4 * n) + up(4 * 512) + up(4 * 512) + up(n) + up(4 * 8) + up(n)
     assert _backward(p, ws_bytes=need - 1) == -5
     assert _backward(p, ws=0) == -1
     assert _backward(p, ws=MIS) == -4
@@ -97,3 +98,11 @@ def test_empty_is_a_noop():
         assert _prologue(p, ptr=0, ws=0, ws_bytes=0) == 0
         assert _forward(p, ptr=0) == 0
         assert _backward(p, ptr=0, ws=0, ws_bytes=0) == 0
+
+
+def test_backward_part_rejects_bad_part():
+    p = P()
+    for part in (-1, 3, 99):
+        assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 15), FAKE, 0, None) == -5
