@@ -116,7 +116,7 @@ def main():
     bws = torch.empty(api.sagebwd_backward_workspace_bytes(p), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    stages = ["prologue", "forward", "bwd_pre", "bwd_main", "dq_finalize"]
+    stages = ["prologue", "forward", "bwd_pre", "bwd_main", "bwd_dq"]
 
     def step(ev):
         ev[0].record()

@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagebwd.
 
 SAGEBWD_FP16 = 0
 SAGEBWD_BF16 = 1
+DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 
 # Quantisation tile shapes of the kernels (include/sagebwd.h).
 FWD_TILE_Q = 32
@@ -29,7 +30,7 @@ class Params(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
         ("blk", ctypes.c_int32), ("causal", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
-        ("dtype", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32),
     ]
 
 

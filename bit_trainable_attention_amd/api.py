@@ -18,9 +18,10 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 
 
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
-                dtype: str, eps: float = 1e-6, sm_scale: float = 0.0) -> _lib.Params:
+                dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0) -> _lib.Params:
+    """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
-    return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt)
+    return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode)
 
 
 def sagebwd_status_string(status: int) -> str:
@@ -63,19 +64,32 @@ def sagebwd_backward_workspace_bytes(p: _lib.Params) -> int:
     return int(_lib.load().sagebwd_backward_workspace_bytes(ctypes.byref(p)))
 
 
+PACKET_BYTES = {64: 21504, 128: 41984}
+
+
+SPILL_LIMIT = 16 << 30
+
+
 def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     """Byte offsets of the backward workspace regions, as documented in include/sagebwd.h."""
     def up(x):
         return (x + 255) // 256 * 256
-    n = p.B * p.H * p.N * p.d
-    bhn = p.B * p.H * p.N
-    off = {"dq_acc": 0}
-    off["D"] = off["dq_acc"] + up(4 * n)
-    off["lse2"] = off["D"] + up(4 * bhn)
-    off["dOtc"] = off["lse2"] + up(4 * bhn)
-    off["dOs"] = off["dOtc"] + up(n)
-    off["Qtc"] = off["dOs"] + up(4 * (bhn // p.blk))
-    off["total"] = off["Qtc"] + up(n)
+    bh, nt, nb = p.B * p.H, p.N // 64, p.N // p.blk
+    r = p.blk // 64
+    tiles = nb * nt - r * nb * (nb - 1) // 2 if p.causal else nb * nt
+    off = {"packet_bytes": PACKET_BYTES[p.d], "packets": 0, "tiles_per_head": tiles}
+    after = up(bh * nt * PACKET_BYTES[p.d])
+    ktp, dsp, dsm = up(bh * nb * p.d * p.blk), up(bh * tiles * 64 * p.blk), up(bh * tiles * 4)
+    spill = p.dq_mode == 1 or (p.dq_mode == 0 and ktp + dsp + dsm <= SPILL_LIMIT)
+    off["spill"] = int(spill)
+    if spill:
+        off["ktp"] = after
+        off["dsp"] = after + ktp
+        off["dsm"] = after + ktp + dsp
+        off["total"] = after + ktp + dsp + dsm
+    else:
+        off["dq_acc"] = after
+        off["total"] = after + up(4 * bh * p.N * p.d)
     return off
 
 

@@ -25,6 +25,7 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->d != 64 && p->d != 128) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->blk != 64 && p->blk != 128) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->dtype != SAGEBWD_FP16 && p->dtype != SAGEBWD_BF16) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->dq_mode < SAGEBWD_DQ_AUTO || p->dq_mode > SAGEBWD_DQ_ATOMIC) return SAGEBWD_ERR_UNSUPPORTED;
   if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
@@ -53,19 +54,32 @@ sagebwd_status check_ptrs(Ptrs... ptrs) {
 }
 
 struct BwdLayout {
-  size_t dq, D, lse2, dOtc, dOs, Qtc, total;
+  bool spill;
+  long long tiles;  // dS tiles per head (spill mode)
+  size_t pk, dq, ktp, dsp, dsm, total;
 };
 
 BwdLayout bwd_layout(const sagebwd_params* p) {
-  const size_t bhn = (size_t)p->B * p->H * p->N;
-  BwdLayout L;
-  L.dq = 0;
-  L.D = L.dq + round_up(4 * elems(p));
-  L.lse2 = L.D + round_up(4 * bhn);
-  L.dOtc = L.lse2 + round_up(4 * bhn);
-  L.dOs = L.dOtc + round_up(elems(p));
-  L.Qtc = L.dOs + round_up(4 * (bhn / (size_t)p->blk));
-  L.total = L.Qtc + round_up(elems(p));
+  BwdLayout L{};
+  const size_t bh = (size_t)p->B * p->H;
+  L.pk = 0;
+  const size_t after_pk = round_up(bh * (p->N / 64) * sagebwd::packet_bytes(p->d));
+  L.tiles = sagebwd::spill_tiles_per_head(p->N, p->blk, p->causal != 0);
+  const size_t ktp_bytes = round_up(bh * (p->N / p->blk) * (size_t)p->d * p->blk);
+  const size_t dsp_bytes = round_up(bh * (size_t)L.tiles * 64 * p->blk);
+  const size_t dsm_bytes = round_up(bh * (size_t)L.tiles * 4);
+  const size_t spill_bytes = ktp_bytes + dsp_bytes + dsm_bytes;
+  L.spill = p->dq_mode == SAGEBWD_DQ_SPILL ||
+            (p->dq_mode == SAGEBWD_DQ_AUTO && spill_bytes <= SAGEBWD_DQ_AUTO_SPILL_LIMIT);
+  if (L.spill) {
+    L.ktp = after_pk;
+    L.dsp = L.ktp + ktp_bytes;
+    L.dsm = L.dsp + dsp_bytes;
+    L.total = L.dsm + dsm_bytes;
+  } else {
+    L.dq = after_pk;
+    L.total = L.dq + round_up(4 * elems(p));
+  }
   return L;
 }
 
@@ -169,12 +183,16 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   a.dQ = static_cast<unsigned short*>(dQ);
   a.dK = static_cast<unsigned short*>(dK);
   a.dV = static_cast<unsigned short*>(dV);
-  a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
-  a.Dvec = reinterpret_cast<float*>(ws + L.D);
-  a.lse2 = reinterpret_cast<float*>(ws + L.lse2);
-  a.dOtc = reinterpret_cast<int8_t*>(ws + L.dOtc);
-  a.dOs = reinterpret_cast<float*>(ws + L.dOs);
-  a.Qtc = reinterpret_cast<int8_t*>(ws + L.Qtc);
+  a.pk = reinterpret_cast<int8_t*>(ws + L.pk);
+  a.spill = L.spill;
+  if (L.spill) {
+    a.ktp = reinterpret_cast<int8_t*>(ws + L.ktp);
+    a.dsp = reinterpret_cast<int8_t*>(ws + L.dsp);
+    a.dsm = reinterpret_cast<float*>(ws + L.dsm);
+    a.spill_tiles = L.tiles;
+  } else {
+    a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
+  }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
   return sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK

@@ -5,22 +5,29 @@
 // with, so it is quantised on its own tile with its own absmax scale, in registers).
 //
 // Kernels:
-//   bwd_pre      one workgroup per (head, block of BLK tokens): D = rowsum(dO o O),
-//                lse * log2(e), block absmax and INT8 codes of dO written channel-major,
-//                Qc transposed to channel-major, and the float32 dQ accumulator rows zeroed.
-//   bwd_main     one workgroup per (head, key block of BLK keys); a pair of waves owns
-//                each 32 keys. Streams query tiles of 64 rows (the P / dS quantisation
-//                tile height), double-buffered in LDS with the next tile's global loads
-//                in flight while the current one is computed.
-//                S = Q K~^T with v_mfma_i32_32x32x32_i8 in the layout lane = key,
-//                registers = queries, which is directly the B operand of the two products
-//                that contract over queries: dV^T = dO^T P and dK^T = Q^T dS. dP = dO V^T
-//                uses v_mfma_f32_32x32x16_{f16,bf16} on the raw dO and V. dS codes go
-//                through LDS once (transposed) for dQ = dS K, accumulated with float32
-//                atomics into the workspace.
-//   dq_finalize  RMSNorm backward of dQ and rounding to the dtype.
+//   bwd_pre      one workgroup per (head, block of BLK tokens). Computes D = rowsum(dO o O),
+//                lse * log2(e), the block absmax and INT8 codes of dO, and writes, for every
+//                64-query tile, a "packet": the exact LDS image the main kernel needs for that
+//                tile (Q codes, dO, dO^T codes, Q^T codes, lse2, D, block scales), already
+//                swizzled and permuted. Also zeroes the float32 dQ accumulator rows.
+//   bwd_main     one workgroup per (head, key block of BLK keys); a pair of waves owns each
+//                32 keys. Streams the query tiles' packets into double-buffered LDS with
+//                buffer->LDS copies (the next tile is in flight while the current one is
+//                computed). S = Q K~^T with v_mfma_i32_32x32x32_i8 in the layout lane = key,
+//                registers = queries, which is directly the B operand of the two products that
+//                contract over queries: dV^T = dO^T P and dK^T = Q^T dS. dP = dO V^T uses
+//                v_mfma_f32_32x32x16_{f16,bf16} on the raw dO and V. dS codes go through LDS
+//                once (query-major) for dQ = dS K, accumulated with float32 atomics.
+//   bwd_dq       (dS spill mode) query-major dQ = dS K over the spilled dS tiles, fused with the
+//                RMSNorm backward and the dtype rounding.
+//   dq_finalize  (atomic mode) RMSNorm backward of the accumulated dQ and dtype rounding.
+// dQ mode: in dS spill mode (the default while its O(N^2) scratch stays moderate) bwd_main
+// writes each dS tile's INT8 codes once to the workspace (the split-reduction pass); in atomic
+// mode it accumulates dQ with float32 atomics instead.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace sagebwd {
 
@@ -29,13 +36,10 @@ namespace {
 constexpr int kTq = 64;  // query rows per P / dS quantisation tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int perm_dword_pos(int kd) {
-  // Byte position of token-dword kd (tokens 4kd..4kd+3) in a channel-major row: inside each
-  // group of 32 tokens, lane group g of an MFMA operand needs tokens {8j + 4g + i}
-  // (j, i = 0..3), which this places at bytes 16g..16g+15 of the group.
-  const int c32 = kd >> 3, k8 = kd & 7;
-  return 32 * c32 + 16 * (k8 & 1) + 4 * (k8 >> 1);
-}
+// Byte position, inside a group of 32 tokens of a channel-major row, of token-dword kd
+// (tokens 4kd..4kd+3, kd = 0..7): lane group g of an MFMA operand needs tokens {8j + 4g + i}
+// (j, i = 0..3), which lands at bytes 16g..16g+15. Token t sits at 16*((t>>2)&1) + 4*(t>>3) + (t&3).
+__device__ __forceinline__ int perm_dword_pos(int kd) { return 16 * (kd & 1) + 4 * (kd >> 1); }
 
 // XOR swizzles of the 16-byte chunks of LDS rows: 8 consecutive rows read at the same
 // logical chunk land in 8 different bank groups.
@@ -47,7 +51,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
-// outstanding vector-memory operations (dQ atomics, direct-to-LDS copies in flight, whose
+// outstanding vector-memory operations (dQ atomics, buffer->LDS copies in flight, whose
 // completion is awaited explicitly where their data is published). The memory clobber keeps
 // the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -59,27 +63,87 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Direct buffer -> LDS copy (buffer_load ... lds): lane l reads 16 bytes at byte offset
+// voff + soff of the buffer [base, base + bytes) (reads past the end return zeros) and the
+// hardware writes them to LDS at lds + 16*l (the 4-byte form: 4 bytes at lds + 4*l). The
+// bodies are compiled for the device only:
+// this compiler's host pass cannot type-check the LDS-DMA builtin and, instead of reporting
+// it, silently omits the host launch stubs of kernels that reach it.
+__device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
+                                                uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                                      0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
+                                               uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                                      0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+#endif
+}
+
 }  // namespace
+
+// Layout of one 64-query tile packet (= of one LDS tile buffer), bytes.
+template <int D>
+struct Packet {
+  static constexpr int bQ = 0;                // Q codes [64][D], chunk j of row r at slot swz<D>(r, j)
+  static constexpr int bDO = 64 * D;          // dO [64][D] 16-bit, chunk j of row r at slot swz<2D>(r, j)
+  static constexpr int bDOT = bDO + 128 * D;  // dO codes [D][64], tokens permuted, chunk swz<64>(c, j)
+  static constexpr int bQT = bDOT + 64 * D;   // Q codes [D][64], same order as dO^T
+  static constexpr int bLSE = bQT + 64 * D;   // lse * log2(e) [64] f32
+  static constexpr int bDV = bLSE + 256;      // D = rowsum(dO o O) [64] f32
+  static constexpr int bSQ = bDV + 256;       // Q block scale f32
+  static constexpr int bSDO = bSQ + 4;        // dO block scale f32
+  static constexpr int kBytes = (bSDO + 4 + 1023) / 1024 * 1024;
+  static constexpr int kCopies = kBytes / 1024;  // 1 KB wave copies per packet
+};
+
+size_t packet_bytes(int d) { return d == 64 ? Packet<64>::kBytes : Packet<128>::kBytes; }
+
+// dS spill: (query tile, key block) tiles of one head, causal ones packed key block by key
+// block (key block kb holds query tiles kb*BLK/64 .. N/64-1).
+long long spill_tiles_per_head(int N, int blk, int causal) {
+  const long long nt = N / 64, nb = N / blk, r = blk / 64;
+  return causal ? nb * nt - r * nb * (nb - 1) / 2 : nb * nt;
+}
+__device__ __forceinline__ long long spill_tile_index(int N, int blk, int causal, int kb, int qt) {
+  const long long nt = N / 64, r = blk / 64;
+  return causal ? (long long)kb * nt - r * (long long)kb * (kb - 1) / 2 + (qt - (long long)kb * r)
+                : (long long)kb * nt + qt;
+}
 
 // ------------------------------------------------------------------------------ bwd_pre
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
+  using P = Packet<D>;
   __shared__ float xs[BLK][D + 1];
   __shared__ __attribute__((aligned(16))) int8_t qs[BLK][D + 4];
+  __shared__ __attribute__((aligned(16))) int8_t ks[BLK][D + 4];
   __shared__ float red[4];
   const int nb = a.N / BLK;
   const int blk_id = blockIdx.x % nb;
   const int bh = blockIdx.x / nb;
   const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;
   const int tid = threadIdx.x;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int CPR = D / 8;  // 16-byte dO chunks per row
+  // packet of the block's first 64-token tile
+  int8_t* pk0 = a.pk + ((size_t)bh * (a.N / kTq) + (size_t)blk_id * (BLK / kTq)) * P::kBytes;
 
   // dO, O: coalesced 8-element chunks; D via a segmented reduction over each row's chunks
   float amax = 0.0f;
   for (int ch = tid; ch < BLK * CPR; ch += 256) {
-    const int t = ch / CPR, c = (ch % CPR) * 8;
+    const int t = ch / CPR, j = ch % CPR, c = j * 8;
     const u16x8 dv = *reinterpret_cast<const u16x8*>(a.dO + (tok0 + t) * D + c);
     const u16x8 ov = *reinterpret_cast<const u16x8*>(a.O + (tok0 + t) * D + c);
+    int8_t* pk = pk0 + (t / kTq) * P::kBytes;
+    const int r = t % kTq;
+    *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, j)) = dv;
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -91,39 +155,68 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
     // CPR consecutive lanes share a row (CPR divides 64 and 256)
 #pragma unroll
     for (int o = CPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    if ((ch % CPR) == 0) {
-      a.Dvec[tok0 + t] = part;
-      a.lse2[tok0 + t] = a.lse[tok0 + t] * kLog2e;
+    if (j == 0) {
+      reinterpret_cast<float*>(pk + P::bDV)[r] = part;
+      reinterpret_cast<float*>(pk + P::bLSE)[r] = a.lse[tok0 + t] * kLog2e;
     }
   }
-  // Qc block into LDS (bytes) for the transpose
+  // Q codes: token-major into the packets, and into LDS for the transpose
   for (int ch = tid; ch < BLK * D / 16; ch += 256) {
-    const int t = (ch * 16) / D, c = (ch * 16) % D;
+    const int t = (ch * 16) / D, j = ch % (D / 16), c = 16 * j;
     const i32x4 v = *reinterpret_cast<const i32x4*>(a.Qc + (tok0 + t) * D + c);
+    const int r = t % kTq;
+    *reinterpret_cast<i32x4*>(pk0 + (t / kTq) * P::kBytes + P::bQ + r * D + 16 * swz<D>(r, j)) = v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<int*>(&qs[t][c + 4 * i]) = v[i];
   }
-  // zero the dQ accumulator rows of this block
-  for (int e = tid; e < BLK * D / 4; e += 256)
-    reinterpret_cast<float4*>(a.dq_acc + tok0 * D)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.spill) {
+    // K codes of this key block, into LDS for the channel-major K^T packet
+    for (int ch = tid; ch < BLK * D / 16; ch += 256) {
+      const int t = (ch * 16) / D, c = (ch * 16) % D;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(a.Kc + (tok0 + t) * D + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<int*>(&ks[t][c + 4 * i]) = v[i];
+    }
+  } else {
+    // zero the dQ accumulator rows of this block
+    for (int e = tid; e < BLK * D / 4; e += 256)
+      reinterpret_cast<float4*>(a.dq_acc + tok0 * D)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 
   amax = wave_max(amax);
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   const float am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = am > 0.0f ? 127.0f / am : 0.0f;
-  if (tid == 0) a.dOs[(size_t)bh * nb + blk_id] = am > 0.0f ? am / 127.0f : 0.0f;
-  // channel-major codes of dO and transposed Qc: word = 4 consecutive tokens of channel c,
-  // stored at its permuted position inside the 32-token group (see perm_dword_pos)
+  if (tid < BLK / kTq) {
+    int8_t* pk = pk0 + tid * P::kBytes;
+    *reinterpret_cast<float*>(pk + P::bSDO) = am > 0.0f ? am / 127.0f : 0.0f;
+    *reinterpret_cast<float*>(pk + P::bSQ) = a.Qs[(size_t)bh * nb + blk_id];
+  }
+  // channel-major codes of dO and of Q: word = 4 consecutive tokens of channel c, placed at
+  // its permuted position inside the 32-token group and its swizzled 16-byte chunk
   for (int w = tid; w < BLK * D / 4; w += 256) {
     const int c = w / (BLK / 4), t = 4 * (w % (BLK / 4));
     const unsigned word = pack4_lo_bytes(quant_word(xs[t][c], inv), quant_word(xs[t + 1][c], inv),
                                          quant_word(xs[t + 2][c], inv), quant_word(xs[t + 3][c], inv));
-    const size_t off = ((size_t)bh * D + c) * a.N + (size_t)blk_id * BLK + perm_dword_pos(t / 4);
-    *reinterpret_cast<unsigned*>(a.dOtc + off) = word;
     const unsigned qw = (unsigned)(uint8_t)qs[t][c] | ((unsigned)(uint8_t)qs[t + 1][c] << 8) |
                         ((unsigned)(uint8_t)qs[t + 2][c] << 16) | ((unsigned)(uint8_t)qs[t + 3][c] << 24);
-    *reinterpret_cast<unsigned*>(a.Qtc + off) = qw;
+    const int tl = t % kTq;
+    const int p = 32 * (tl / 32) + perm_dword_pos((tl % 32) / 4);  // byte position in the 64-token row
+    const int off = c * kTq + 16 * swz<kTq>(c, p / 16) + p % 16;
+    int8_t* pk = pk0 + (t / kTq) * P::kBytes;
+    *reinterpret_cast<unsigned*>(pk + P::bDOT + off) = word;
+    *reinterpret_cast<unsigned*>(pk + P::bQT + off) = qw;
+  }
+  if (a.spill) {
+    // K^T packet of this key block: [D][BLK] codes, chunk j of row c at slot swz<BLK>(c, j)
+    int8_t* kt = a.ktp + ((size_t)bh * nb + blk_id) * (size_t)(D * BLK);
+    for (int w = tid; w < BLK * D / 4; w += 256) {
+      const int c = w / (BLK / 4), t = 4 * (w % (BLK / 4));
+      const unsigned kw = (unsigned)(uint8_t)ks[t][c] | ((unsigned)(uint8_t)ks[t + 1][c] << 8) |
+                          ((unsigned)(uint8_t)ks[t + 2][c] << 16) | ((unsigned)(uint8_t)ks[t + 3][c] << 24);
+      *reinterpret_cast<unsigned*>(kt + c * BLK + 16 * swz<BLK>(c, t / 16) + t % 16) = kw;
+    }
   }
 }
 
@@ -135,22 +228,11 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 // B operands of dV^T = dO^T P and dK^T = Q^T dS for all 64 queries.
 template <int D, int BLK>
 struct BwdLds {
+  using P = Packet<D>;
   static constexpr int NKG = BLK / 32;        // 32-key groups
   static constexpr int NW = 2 * NKG;          // waves
-  static constexpr int NT = NW * 64;
   static constexpr int kRowS = BLK + 16;      // dS codes [query][key]; K^T codes [channel][key]
-  // one query-tile buffer (double-buffered), rows unpadded and chunk-swizzled:
-  //   Q codes [kTq][D], dO [kTq][D] 16-bit, dO^T and Q^T codes [D][kTq], lse2 [kTq], D [kTq],
-  //   and the tile's Q and dO block scales
-  static constexpr int bQ = 0;
-  static constexpr int bDO = bQ + kTq * D;
-  static constexpr int bDOT = bDO + kTq * 2 * D;
-  static constexpr int bQT = bDOT + D * kTq;
-  static constexpr int bLSE = bQT + D * kTq;
-  static constexpr int bDV = bLSE + kTq * 4;
-  static constexpr int bSQ = bDV + kTq * 4;     // Q block scale of the tile (first word)
-  static constexpr int bSDO = bSQ + 256;        // dO block scale of the tile (first word)
-  static constexpr int kBuf = bSDO + 256;
+  static constexpr int kBuf = P::kBytes;      // one tile buffer (double-buffered)
   static constexpr int offDS = 2 * kBuf;
   static constexpr int offKT = offDS + kTq * kRowS;
   static constexpr int offK = offKT + D * kRowS;    // K codes [BLK][D], token-major, swizzled
@@ -159,111 +241,16 @@ struct BwdLds {
   static constexpr int offRED = offXD + NW * 1024;  // redP[NW], redD[NW]
   static constexpr int offDOT = offRED + 2 * NW * 4;  // epilogue: per-lane dK.K^ partial dots [NW][64]
   static constexpr int kBytes = offDOT + NW * 64 * 4;
-  // 1 KB direct-to-LDS wave copies of the Q, dO, dO^T, Q^T parts of a tile
-  static constexpr int kCopies = (bLSE - bQ) / 1024;
-  static constexpr int kCopiesPerWave = (kCopies + NW - 1) / NW;
-  static_assert((bLSE - bQ) % 1024 == 0, "tile parts are whole 1 KB copies");
+  static constexpr int kCopiesPerWave = (P::kCopies + NW - 1) / NW;
 };
 
-// Direct buffer -> LDS copies (buffer_load ... lds): lane l reads 16 (or 4) bytes at byte
-// offset voff + soff of the buffer [base, base + bytes) (reads past the end return zeros)
-// and the hardware writes them to LDS at lds + 16*l (or 4*l). The bodies are compiled for
-// the device only: this compiler's host pass cannot type-check the LDS-DMA builtin and,
-// instead of reporting it, silently omits the host launch stubs of kernels that reach it.
-__device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
-                                                uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                                                      0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-#endif
-}
-__device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
-                                               uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                                                      0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
-#endif
-}
-
-// Direct global -> LDS copies of one query tile. Each wave copy fills 1 KB of LDS, lane l
-// the 16 bytes at 16*l; each lane's source is chosen so that the LDS image is the swizzled
-// layout. Sources are addressed through buffer resources of the head's arrays: a per-lane
-// 32-bit offset that does not depend on the query tile (computed once) plus a wave-uniform
-// offset for the query tile and the copy.
-template <int D, int BLK>
-struct TileDma {
-  using L = BwdLds<D, BLK>;
-  static constexpr int nQc = kTq * D / 1024;       // copies of the Q codes part
-  static constexpr int nDOc = kTq * 2 * D / 1024;  // copies of the dO part
-  static constexpr int nTc = D * kTq / 1024;       // copies of each of dO^T, Q^T
-  // head bases of the arrays (the buffer resources are built from these where they are used)
-  const void *pQ, *pDO, *pDOT, *pQT, *pLSE, *pDV, *pQs, *pDOs;
-  uint32_t loff[L::kCopiesPerWave];
-  int N;
-
-  __device__ __forceinline__ void init(const BackwardArgs& a, size_t hrow, int bh, int w, int l) {
-    N = a.N;
-    pQ = a.Qc + hrow * D;
-    pDO = a.dO + hrow * D;
-    pDOT = a.dOtc + (size_t)bh * D * a.N;
-    pQT = a.Qtc + (size_t)bh * D * a.N;
-    pLSE = a.lse2 + hrow;
-    pDV = a.Dvec + hrow;
-    pQs = a.Qs + (size_t)bh * (a.N / BLK);
-    pDOs = a.dOs + (size_t)bh * (a.N / BLK);
-#pragma unroll
-    for (int j = 0; j < L::kCopiesPerWave; ++j) {
-      const int cp = w + L::NW * j;
-      uint32_t off = 0;
-      if (cp < nQc) {
-        const int q = (16 * l) / D, p = l % (D / 16);
-        off = q * D + 16 * swz<D>(cp * (1024 / D) + q, p);
-      } else if (cp < nQc + nDOc) {
-        const int cd = cp - nQc, q = (16 * l) / (2 * D), p = l % (D / 8);
-        off = 2 * (q * D + 8 * swz<2 * D>(cd * (512 / D) + q, p));
-      } else if (cp < L::kCopies) {
-        const int c3 = (cp - nQc - nDOc) % nTc, c = l / 4, p = l % 4;
-        off = (uint32_t)c * (uint32_t)a.N + 16 * swz<kTq>(16 * c3 + c, p);
-      }
-      loff[j] = off;
-    }
-  }
-
-  __device__ __forceinline__ void issue(int q0, int8_t* buf, int w) const {
-    const uint32_t nd = (uint32_t)N * D;
-#pragma unroll
-    for (int j = 0; j < L::kCopiesPerWave; ++j) {
-      const int cp = w + L::NW * j;
-      int8_t* dst = buf + cp * 1024;
-      if (cp < nQc) {
-        buffer_to_lds16(pQ, nd, dst, loff[j], q0 * D + cp * 1024);
-      } else if (cp < nQc + nDOc) {
-        buffer_to_lds16(pDO, 2 * nd, dst, loff[j], 2 * q0 * D + (cp - nQc) * 1024);
-      } else if (cp < nQc + nDOc + nTc) {
-        buffer_to_lds16(pDOT, nd, dst, loff[j], 16 * (cp - nQc - nDOc) * N + q0);
-      } else if (cp < L::kCopies) {
-        buffer_to_lds16(pQT, nd, dst, loff[j], 16 * (cp - nQc - nDOc - nTc) * N + q0);
-      }
-    }
-    if (w == L::NW - 1) {
-      buffer_to_lds4(pLSE, 4 * (uint32_t)N, buf + L::bLSE, 4 * lane_id(), 4 * q0);
-      buffer_to_lds4(pDV, 4 * (uint32_t)N, buf + L::bDV, 4 * lane_id(), 4 * q0);
-    }
-    if (w == L::NW - 2) {  // lane 0 carries the tile's block scale; lanes past the row read 0
-      buffer_to_lds4(pQs, 4 * (uint32_t)(N / BLK), buf + L::bSQ, 4 * lane_id(), 4 * (q0 / BLK));
-      buffer_to_lds4(pDOs, 4 * (uint32_t)(N / BLK), buf + L::bSDO, 4 * lane_id(), 4 * (q0 / BLK));
-    }
-  }
-};
-
-template <int DT, int D, int BLK>
+template <int DT, int D, int BLK, bool SPILL>
 __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   using L = BwdLds<D, BLK>;
+  using P = Packet<D>;
   constexpr int NKG = L::NKG;      // 32-key groups (wave pairs)
   constexpr int NW = L::NW;        // waves per workgroup
-  constexpr int NT = L::NT;        // threads
+  constexpr int NT = NW * 64;      // threads
   constexpr int DC = D / 32;       // 32-channel chunks (int8 contraction / output tiles)
   constexpr int DCH = DC / 2;      // 32-channel output tiles per channel half
   constexpr int DH = D / 16;       // 16-channel chunks (16-bit contraction)
@@ -279,7 +266,11 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   const int tid = threadIdx.x;
   const int k0 = kb * BLK;
   const int key = k0 + 32 * kg + lk;           // this lane's key
+  const int kl = 32 * kg + lk;                 // ... inside the block
   const size_t hrow = (size_t)bh * a.N;
+  const int ntile = a.N / kTq;
+  const int8_t* pkh = a.pk + (size_t)bh * ntile * P::kBytes;   // this head's packets
+  const uint32_t pkh_bytes = (uint32_t)ntile * P::kBytes;
 
   // ---- per-wave constant operand: V (B of dP) for this lane's key
   u16x8 vreg[DH];
@@ -291,8 +282,10 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     const int t = (ch * 16) / D, c = (ch * 16) % D;
     const i32x4 v = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + k0 + t) * D + c);
     *reinterpret_cast<i32x4*>(lds + L::offK + t * D + 16 * swz<D>(t, c / 16)) = v;
+    if constexpr (!SPILL) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lds[L::offKT + (c + i) * L::kRowS + t] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
+      for (int i = 0; i < 16; ++i) lds[L::offKT + (c + i) * L::kRowS + t] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
+    }
   }
   const float sK = a.Ks[(size_t)bh * nb + kb];
   const float smc = a.sm_scale;
@@ -303,56 +296,66 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < DCH; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  const int nqt = a.N / kTq;
-  const int qt0 = a.causal ? k0 / kTq : 0;
-  TileDma<D, BLK> dma;
-  dma.init(a, hrow, bh, w, l);
-  dma.issue(qt0 * kTq, lds, w);
-  wait_vmcnt<0>();
-  lds_barrier();
+  // copies of packet qt into an LDS tile buffer: wave w moves KB cp = w, w + NW, ...
+  auto issue = [&](int qt, int8_t* dst) {
+#pragma unroll
+    for (int j = 0; j < L::kCopiesPerWave; ++j) {
+      const int cp = w + NW * j;
+      if (cp < P::kCopies) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * P::kBytes + cp * 1024);
+    }
+  };
 
-  for (int qt = qt0; qt < nqt; ++qt) {
+  const int qt0 = a.causal ? k0 / kTq : 0;
+  issue(qt0, lds);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int qt = qt0; qt < ntile; ++qt) {
     const int q0 = qt * kTq;
-    const bool has_next = qt + 1 < nqt;
+    const bool has_next = qt + 1 < ntile;
     int8_t* buf = lds + ((qt - qt0) & 1) * L::kBuf;
     int8_t* nbuf = lds + (((qt - qt0) & 1) ^ 1) * L::kBuf;
-    if (has_next) dma.issue(q0 + kTq, nbuf, w);
+    if (has_next) issue(qt + 1, nbuf);
 
-    const float sQ = *reinterpret_cast<const float*>(buf + L::bSQ);
-    const float sdO = *reinterpret_cast<const float*>(buf + L::bSDO);
+    const float sQ = *reinterpret_cast<const float*>(buf + P::bSQ);
+    const float sdO = *reinterpret_cast<const float*>(buf + P::bSDO);
     const float c2 = (sQ * sK) * (smc * kLog2e);
-    const bool diag = a.causal && (k0 + BLK - 1 > q0);
 
     // ---- S, P, dP, dS for query rows 32h..32h+31 of the tile and this pair's 32 keys
+    const int q = 32 * h + lk;
     i32x16 s = i32x16{};
 #pragma unroll
     for (int kk = 0; kk < DC; ++kk) {
-      const int q = 32 * h + lk, kl = 32 * kg + lk;
-      const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + L::bQ + q * D + 16 * swz<D>(q, 2 * kk + g));
+      const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + P::bQ + q * D + 16 * swz<D>(q, 2 * kk + g));
       const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offK + kl * D + 16 * swz<D>(kl, 2 * kk + g));
       s = mfma_i8_32x32x32(aq, bk, s);
     }
     f32x16 dp = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < DH; ++kk) {
-      const int q = 32 * h + lk;
-      const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + L::bDO + q * 2 * D + 16 * swz<2 * D>(q, 2 * kk + g));
+      const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + P::bDO + q * 2 * D + 16 * swz<2 * D>(q, 2 * kk + g));
       dp = mfma_16b_32x32x16<DT>(ad, vreg[kk], dp);
     }
-    const float* lse2 = reinterpret_cast<const float*>(buf + L::bLSE) + 32 * h + 4 * g;
-    const float* dvv = reinterpret_cast<const float*>(buf + L::bDV) + 32 * h + 4 * g;
+    const float* lse2 = reinterpret_cast<const float*>(buf + P::bLSE) + 32 * h + 4 * g;
+    const float* dvv = reinterpret_cast<const float*>(buf + P::bDV) + 32 * h + 4 * g;
     float pf[16], dsf[16];
     float pm = 0.0f, dm = 0.0f;
+    auto elems = [&](auto masked) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = 8 * (r >> 2) + (r & 3);  // query offset inside the 32 rows, minus 4g
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c2, -lse2[qi]));
-      if (diag && key > q0 + 32 * h + 4 * g + qi) p = 0.0f;
-      pf[r] = p;
-      dsf[r] = p * (dp[r] - dvv[qi]);
-      pm = fmaxf(pm, p);
-      dm = fmaxf(dm, fabsf(dsf[r]));
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 8 * (r >> 2) + (r & 3);  // query offset inside the 32 rows, minus 4g
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c2, -lse2[qi]));
+        if constexpr (decltype(masked)::value) {
+          if (key > q0 + 32 * h + 4 * g + qi) p = 0.0f;
+        }
+        pf[r] = p;
+        dsf[r] = p * (dp[r] - dvv[qi]);
+        pm = fmaxf(pm, p);
+        dm = fmaxf(dm, fabsf(dsf[r]));
+      }
+    };
+    if (a.causal && k0 + BLK - 1 > q0) elems(std::true_type{});
+    else elems(std::false_type{});
     pm = wave_max(pm);
     dm = wave_max(dm);
     if (l == 0) { redP[w] = pm; redD[w] = dm; }
@@ -366,10 +369,9 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     const float sP = pa > 0.0f ? pa / 127.0f : 0.0f;
     const float dinv = da > 0.0f ? 127.0f / da : 0.0f;
     const float sdS = da > 0.0f ? da / 127.0f : 0.0f;
-    i32x4 pcode[2], dcode[2];
+    i32x4 pc, dc;  // this wave's codes (queries 32h..32h+31)
     {
-      i32x4 pc, dc;
-      int8_t* col = lds + L::offDS + (32 * kg + lk);
+      int8_t* col = lds + L::offDS + kl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pc[j] = (int)pack4_lo_bytes(quant_word(pf[4 * j], pinv), quant_word(pf[4 * j + 1], pinv),
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         const unsigned w0 = quant_word(dsf[4 * j], dinv), w1 = quant_word(dsf[4 * j + 1], dinv);
         const unsigned w2 = quant_word(dsf[4 * j + 2], dinv), w3 = quant_word(dsf[4 * j + 3], dinv);
         dc[j] = (int)pack4_lo_bytes(w0, w1, w2, w3);
-        // dS codes, query-major, for dQ: query 32h + 8j + 4g + i, key 32kg + lk
+        // dS codes, query-major, for dQ: query 32h + 8j + 4g + i, key kl
         const int qb = 32 * h + 8 * j + 4 * g;
         col[(qb + 0) * L::kRowS] = (int8_t)w0;
         col[(qb + 1) * L::kRowS] = (int8_t)w1;
@@ -386,25 +388,23 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
       }
       *reinterpret_cast<i32x4*>(lds + L::offXP + w * 1024 + l * 16) = pc;
       *reinterpret_cast<i32x4*>(lds + L::offXD + w * 1024 + l * 16) = dc;
-      pcode[h] = pc;
-      dcode[h] = dc;
     }
     lds_barrier();
-    pcode[1 - h] = *reinterpret_cast<const i32x4*>(lds + L::offXP + partner * 1024 + l * 16);
-    dcode[1 - h] = *reinterpret_cast<const i32x4*>(lds + L::offXD + partner * 1024 + l * 16);
+    // the partner's codes cover queries 32(1-h)..32(1-h)+31
+    const i32x4 pco = *reinterpret_cast<const i32x4*>(lds + L::offXP + partner * 1024 + l * 16);
+    const i32x4 dco = *reinterpret_cast<const i32x4*>(lds + L::offXD + partner * 1024 + l * 16);
 
-    // ---- dV^T += dO^T P and dK^T += Q^T dS for channel half h (int32 over the 64 queries)
+    // ---- dV^T += dO^T P and dK^T += Q^T dS for channel half h (int32 over the 64 queries):
+    //      own codes pair with the A-operand chunk of query half h, the partner's with 1-h
     {
       const float sv = sP * sdO;
 #pragma unroll
       for (int i = 0; i < DCH; ++i) {
         const int c = 32 * (DCH * h + i) + lk;
-        i32x16 acc = i32x16{};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + L::bDOT + c * kTq + 16 * swz<kTq>(c, 2 * u + g));
-          acc = mfma_i8_32x32x32(ao, pcode[u], acc);
-        }
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, 2 * h + g));
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, 2 * (1 - h) + g));
+        i32x16 acc = mfma_i8_32x32x32(a0, pc, i32x16{});
+        acc = mfma_i8_32x32x32(a1, pco, acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) dv[i][r] += sv * (float)acc[r];
       }
@@ -412,19 +412,32 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 #pragma unroll
       for (int i = 0; i < DCH; ++i) {
         const int c = 32 * (DCH * h + i) + lk;
-        i32x16 acc = i32x16{};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + L::bQT + c * kTq + 16 * swz<kTq>(c, 2 * u + g));
-          acc = mfma_i8_32x32x32(aq, dcode[u], acc);
-        }
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, 2 * h + g));
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, 2 * (1 - h) + g));
+        i32x16 acc = mfma_i8_32x32x32(a0, dc, i32x16{});
+        acc = mfma_i8_32x32x32(a1, dco, acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) dk[i][r] += sk * (float)acc[r];
       }
     }
 
-    // ---- dQ = dS K over the BLK keys: 2 x DC output tiles of 32 x 32, split over the waves
-    {
+    if constexpr (SPILL) {
+      // ---- spill the dS tile (query-major, rows swizzled) and its dQ multiplier; the
+      //      query-major dQ pass contracts it with K
+      const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt);
+      int8_t* dst = a.dsp + ti * (kTq * BLK);
+      for (int ch = tid; ch < kTq * BLK / 16; ch += NT) {
+        const int r = ch / (BLK / 16), j = ch % (BLK / 16);
+        *reinterpret_cast<i32x4*>(dst + r * BLK + 16 * swz<BLK>(r, j)) =
+            *reinterpret_cast<const i32x4*>(lds + L::offDS + r * L::kRowS + 16 * j);
+      }
+      if (tid == 0) a.dsm[ti] = smc * sdS * sK;
+      // the next tile's copies were issued before these (at most 2) stores; in-order
+      // completion makes this wait for every copy
+      wait_vmcnt<2>();
+    } else {
+      // ---- dQ = dS K over the BLK keys: 2 x DC output tiles of 32 x 32, split over the
+      //      waves, added to the float32 accumulator with atomics
       const float sc = smc * sdS * sK;
       for (int tile = w; tile < 2 * DC; tile += NW) {
         const int u = tile / DC, ct = tile % DC;
@@ -441,15 +454,15 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         for (int r = 0; r < 16; ++r)
           unsafeAtomicAdd(dst + (size_t)(8 * (r >> 2) + (r & 3)) * D, sc * (float)acc[r]);
       }
-    }
-    // The next tile's copies were issued before this iteration's dQ atomics; vector memory
-    // operations complete in issue order, so allowing the atomics (16 per dQ tile) to stay
-    // outstanding still waits for every copy.
-    if constexpr (2 * DC <= NW) {
-      if (w < 2 * DC) wait_vmcnt<16>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<16 * ((2 * DC) / NW)>();
+      // The next tile's copies were issued before this iteration's dQ atomics; vector memory
+      // operations complete in issue order, so allowing the atomics (16 per dQ tile) to stay
+      // outstanding still waits for every copy.
+      if constexpr (2 * DC <= NW) {
+        if (w < 2 * DC) wait_vmcnt<16>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<16 * ((2 * DC) / NW)>();
+      }
     }
     lds_barrier();
   }
@@ -504,6 +517,122 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------ bwd_dq
+// Query-major dQ pass over the spilled dS tiles: one workgroup (4 waves) per (head, 64-query
+// tile). For every key block up to the diagonal, the tile's dS codes [64][BLK] and the block's
+// K^T codes [D][BLK] stream through double-buffered LDS (buffer->LDS copies), and
+// dQ^ += m(kb) * (dS_codes . K_codes) runs on v_mfma_i32_32x32x32_i8 with float32 accumulation
+// in registers (m = sm_scale * s_dS * s_K of the tile). The epilogue applies the RMSNorm
+// backward and writes dQ in the dtype; no float32 dQ buffer and no atomics.
+template <int D, int BLK>
+struct DqLds {
+  static constexpr int bDS = 0;                     // dS codes [64][BLK], rows swizzled
+  static constexpr int bKT = 64 * BLK;              // K^T codes [D][BLK], rows swizzled
+  static constexpr int bM = bKT + D * BLK;          // tile multiplier (first word)
+  static constexpr int kBuf = bM + 1024;
+  static constexpr int kCopiesDS = 64 * BLK / 1024;
+  static constexpr int kCopiesKT = D * BLK / 1024;
+  // the epilogue reuses the buffers for the dQ^ tile [64][D] f32
+  static constexpr int kBytes = 2 * kBuf > 64 * D * 4 ? 2 * kBuf : 64 * D * 4;
+};
+
+template <int DT, int D, int BLK>
+__global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
+  using L = DqLds<D, BLK>;
+  constexpr int DC = D / 32, KC = BLK / 32;
+  constexpr int TPW = (2 * DC) / 4;                 // 32 x 32 output tiles per wave
+  __shared__ __attribute__((aligned(16))) int8_t lds[L::kBytes];
+  const int ntile = a.N / kTq, nb = a.N / BLK;
+  const int bh = blockIdx.x % a.BH;
+  const int qt = a.causal ? ntile - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);
+  const int q0 = qt * kTq;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 5, lk = l & 31;
+  const int kb_last = a.causal ? (q0 + kTq - 1) / BLK : nb - 1;
+  const int8_t* dsh = a.dsp + (size_t)bh * a.spill_tiles * (kTq * BLK);
+  const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kTq * BLK));
+  const float* dmh = a.dsm + (size_t)bh * a.spill_tiles;
+  const int8_t* kth = a.ktp + (size_t)bh * nb * (D * BLK);
+  const uint32_t kth_bytes = (uint32_t)nb * (D * BLK);
+
+  auto issue = [&](int kb, int8_t* buf) {
+    const long long ti = spill_tile_index(a.N, BLK, a.causal, kb, qt);
+    for (int cp = w; cp < L::kCopiesDS + L::kCopiesKT; cp += 4) {
+      if (cp < L::kCopiesDS)
+        buffer_to_lds16(dsh, dsh_bytes, buf + L::bDS + cp * 1024, 16 * l, (uint32_t)(ti * (kTq * BLK)) + cp * 1024);
+      else
+        buffer_to_lds16(kth, kth_bytes, buf + L::bKT + (cp - L::kCopiesDS) * 1024, 16 * l,
+                        (uint32_t)kb * (D * BLK) + (cp - L::kCopiesDS) * 1024);
+    }
+    if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4), buf + L::bM, 4 * l, (uint32_t)(ti * 4));
+  };
+
+  f32x16 dq[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) dq[i] = f32x16{};
+  issue(0, lds);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int kb = 0; kb <= kb_last; ++kb) {
+    int8_t* buf = lds + (kb & 1) * L::kBuf;
+    if (kb < kb_last) issue(kb + 1, lds + ((kb & 1) ^ 1) * L::kBuf);
+    const float m = *reinterpret_cast<const float*>(buf + L::bM);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tile = w + 4 * i, u = tile / DC, ct = tile % DC;
+      const int qr = 32 * u + lk, cr = 32 * ct + lk;
+      i32x16 acc = i32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const i32x4 as = *reinterpret_cast<const i32x4*>(buf + L::bDS + qr * BLK + 16 * swz<BLK>(qr, 2 * kc + g));
+        const i32x4 bk = *reinterpret_cast<const i32x4*>(buf + L::bKT + cr * BLK + 16 * swz<BLK>(cr, 2 * kc + g));
+        acc = mfma_i8_32x32x32(as, bk, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[i][r] += m * (float)acc[r];
+    }
+    wait_vmcnt<0>();   // the next key block's copies (the only vector-memory operations here)
+    lds_barrier();
+  }
+  // ---- epilogue: dQ^ tile to LDS [64][D] f32, then RMSNorm backward row by row
+  float* t = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = w + 4 * i, u = tile / DC, ct = tile % DC;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[(32 * u + 8 * (r >> 2) + 4 * g + (r & 3)) * D + 32 * ct + lk] = dq[i][r];
+  }
+  __syncthreads();
+  constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
+  const size_t hrow = (size_t)bh * a.N;
+  for (int e = threadIdx.x; e < kTq * CPR; e += 256) {
+    const int r = e / CPR, c = (e % CPR) * 8;
+    const size_t tok = hrow + q0 + r;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = t[r * D + c + i];
+    u16x8 out;
+    if (a.qk_norm) {
+      const float rs = a.q_rstd[tok];
+      const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + tok * D + c);
+      float qh[8], dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qh[i] = to_f32<DT>(qv[i]) * rs;
+        dot = __builtin_fmaf(v[i], qh[i], dot);
+      }
+#pragma unroll
+      for (int o = CPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+      const float mean = dot / (float)D;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(rs * (v[i] - qh[i] * mean));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(v[i]);
+    }
+    *reinterpret_cast<u16x8*>(a.dQ + tok * D + c) = out;
+  }
+}
+
 // ------------------------------------------------------------------------------ dq_finalize
 // One group of D/8 lanes per token: dQ = rstd * (dQ^ - Q^ * mean_c(dQ^ o Q^)), Q^ = Q * rstd.
 template <int DT, int D>
@@ -549,13 +678,20 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 1) {
-    hipLaunchKernelGGL((bwd_main<DT, D, BLK>), dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), 0, st, a);
+    if (a.spill)
+      hipLaunchKernelGGL((bwd_main<DT, D, BLK, true>), dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_main<DT, D, BLK, false>), dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {
-    const long long threads = (long long)a.BH * a.N * (D / 8);
-    hipLaunchKernelGGL((dq_finalize<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+    if (a.spill) {
+      hipLaunchKernelGGL((bwd_dq<DT, D, BLK>), dim3((unsigned)((long long)(a.N / kTq) * a.BH)), dim3(256), 0, st, a);
+    } else {
+      const long long threads = (long long)a.BH * a.N * (D / 8);
+      hipLaunchKernelGGL((dq_finalize<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
   }
   return hipSuccess;

@@ -38,12 +38,13 @@ struct BackwardArgs {
   const float *q_rstd, *k_rstd, *lse;        // [BH, N]
   unsigned short *dQ, *dK, *dV;              // [BH, N, D]
   // workspace regions
-  float* dq_acc;                             // [BH, N, D]
-  float* Dvec;                               // [BH, N]
-  float* lse2;                               // [BH, N] lse * log2(e)
-  int8_t* dOtc;                              // [BH, D, N]
-  float* dOs;                                // [BH, N/BLK]
-  int8_t* Qtc;                               // [BH, D, N]
+  int8_t* pk;                                // [BH, N/64] tile packets
+  float* dq_acc;                             // atomic mode: [BH, N, D]
+  int8_t* ktp;                               // spill mode: K^T packets [BH, N/BLK][D*BLK]
+  int8_t* dsp;                               // spill mode: dS tiles [BH, spill_tiles][64*BLK]
+  float* dsm;                                // spill mode: dQ multipliers [BH, spill_tiles]
+  long long spill_tiles;                     // dS tiles per head
+  int spill;
   int BH, N, D, BLK, dtype;
   int causal, qk_norm;
   float sm_scale;
@@ -52,6 +53,8 @@ struct BackwardArgs {
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st);
 hipError_t launch_backward(const BackwardArgs& a, int part, hipStream_t st);  // part -1 = all
+size_t packet_bytes(int d);  // bytes of one 64-query backward tile packet
+long long spill_tiles_per_head(int N, int blk, int causal);
 
 // Calls f(dtype, d, blk) with std::integral_constant arguments for the supported
 // combinations (dtype in {fp16, bf16}, d in {64, 128}, blk in {64, 128}).

@@ -60,7 +60,8 @@ typedef enum {
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
                                    B*H > 2^24                                               */
-  SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, eps < 0        */
+  SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype or dq_mode,
+                                   eps < 0                                                  */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
@@ -77,7 +78,18 @@ typedef struct {
   float eps;            /* RMSNorm epsilon (>= 0), e.g. 1e-6                                */
   float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(d)                            */
   int32_t dtype;        /* sagebwd_dtype of Q, K, V, dO, O, dQ, dK, dV                       */
+  int32_t dq_mode;      /* how the backward reduces dQ over key blocks (sagebwd_dq_mode)     */
 } sagebwd_params;
+
+/* dQ = dS K sums over every key block. SAGEBWD_DQ_SPILL writes each (64-query, blk-key) tile
+ * of INT8 dS codes once to the workspace and contracts them with K in a query-major pass
+ * (plain stores, O(N^2/2) bytes of scratch per head when causal). SAGEBWD_DQ_ATOMIC adds
+ * each tile's float32 dQ contribution with atomics (O(N) scratch, but the atomic traffic is
+ * (N/blk) * N * d * 4 bytes per head). SAGEBWD_DQ_AUTO picks SPILL while its scratch is at
+ * most SAGEBWD_DQ_AUTO_SPILL_LIMIT bytes, else ATOMIC. Both give the same dQ up to float32
+ * summation order. */
+typedef enum { SAGEBWD_DQ_AUTO = 0, SAGEBWD_DQ_SPILL = 1, SAGEBWD_DQ_ATOMIC = 2 } sagebwd_dq_mode;
+#define SAGEBWD_DQ_AUTO_SPILL_LIMIT (16ull << 30)
 
 /* Bytes of scratch sagebwd_quant_prologue needs: the per-block channel sums of the
  * normalised keys, float32 [B,H,N/blk,d] (0 when k_smooth is off). Returns 0 for
@@ -116,15 +128,31 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
                                void* O, float* lse, void* stream);
 
 /* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
- * boundary, in this order; sizes in bytes):
- *   dq_acc float32 [B,H,N,d]    (4*B*H*N*d)   dQ of the normalised queries, accumulated
- *   D      float32 [B,H,N]      (4*B*H*N)     rowsum(dO o O)
- *   lse2   float32 [B,H,N]      (4*B*H*N)     lse * log2(e)
- *   dOtc   int8    [B,H,d,N]    (B*H*N*d)     INT8 codes of dO, transposed; inside each group of
- *                                             32 tokens, token t sits at position
- *                                             16*((t>>2)&1) + 4*(t>>3) + (t&3)
- *   dOs    float32 [B,H,N/blk]  (4*B*H*N/blk) block scales of dO
- *   Qtc    int8    [B,H,d,N]    (B*H*N*d)     Qc transposed, same token order as dOtc
+ * boundary, in this order; "chunk" = 16 bytes):
+ *   packets [B,H,N/64] x P bytes     P = 21504 for d = 64, 41984 for d = 128: for each head
+ *           and each 64-token tile, the tile's data in the order the key-block kernel copies
+ *           it into LDS (r = token inside the tile, c = channel):
+ *     [0, 64d)      Q codes [64][d]; chunk j of row r stored at chunk j^(r&7) (d = 128) or
+ *                   j^((r>>1)&3) (d = 64)
+ *     [64d, 192d)   dO [64][d], 16-bit; chunk j of row r stored at chunk j^(r&7)
+ *     [192d, 256d)  dO INT8 codes, channel-major [d][64]: token u of row c at byte
+ *                   32*(u>>5) + 16*((u>>2)&1) + 4*((u&31)>>3) + (u&3), then chunk j of
+ *                   row c stored at chunk j^((c>>1)&3)
+ *     [256d, 320d)  Q codes, channel-major, same order as the dO codes
+ *     [320d, +256)  lse * log2(e), float32 [64]
+ *     [+256, +512)  D = rowsum(dO o O), float32 [64]
+ *     [+512, +516)  the Q block scale; [+516, +520) the dO block scale (float32); padding
+ * then, with dq_mode ATOMIC:
+ *   dq_acc  float32 [B,H,N,d]        dQ of the normalised queries, accumulated
+ * or, with dq_mode SPILL (T = tiles per head = nb*nt - (blk/64)*nb*(nb-1)/2 when causal,
+ * nb*nt otherwise, nb = N/blk, nt = N/64; tile (kb, t) of key block kb and query tile t has
+ * index kb*nt - (blk/64)*kb*(kb-1)/2 + t - kb*blk/64 when causal, kb*nt + t otherwise):
+ *   ktp     [B,H,N/blk] x d*blk      K codes of each key block, channel-major [d][blk];
+ *                                    chunk j of row c stored at chunk j^(c&7) (blk = 128)
+ *                                    or j^((c>>1)&3) (blk = 64)
+ *   dsp     [B,H,T] x 64*blk         INT8 dS codes of each tile, query-major [64][blk],
+ *                                    chunk j of row r stored as for ktp
+ *   dsm     float32 [B,H,T]          sm_scale * (dS tile scale) * (K block scale)
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 

@@ -56,9 +56,10 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 
 # ------------------------------------------------------------------------------- GPU side
 
-def params_for(w: wl.Workload):
+def params_for(w: wl.Workload, dq_mode: int = 0):
     from bit_trainable_attention_amd import api
-    return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+    return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
+                           dq_mode=dq_mode)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -74,11 +75,11 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
-            pro_in=None, O_in=None, lse_in=None) -> Dict[str, np.ndarray]:
+            pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0) -> Dict[str, np.ndarray]:
     """Run the HIP path and return host copies (numpy) of everything it produced."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w)
+    p = params_for(w, dq_mode)
     Q, K, V, dO = (to_device(x[k], w.dtype) for k in ("Q", "K", "V", "dO"))
     res: Dict[str, np.ndarray] = {}
     pro = pro_in
@@ -101,12 +102,28 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
             res[k] = g[k].float().cpu().numpy().astype(np.float64)
         lay = api.backward_workspace_layout(p)
         ws = g["workspace"].cpu().numpy()
-        n = w.B * w.H * w.N * w.d
-        res["dOtc"] = ws[lay["dOtc"]:lay["dOtc"] + n].view(np.int8).reshape(w.B, w.H, w.d, w.N)
-        res["dOs"] = ws[lay["dOs"]:lay["dOs"] + 4 * w.B * w.H * (w.N // w.blk)].view(np.float32).reshape(
-            w.B, w.H, w.N // w.blk)
-        res["Dvec"] = ws[lay["D"]:lay["D"] + 4 * w.B * w.H * w.N].view(np.float32).reshape(w.B, w.H, w.N)
+        res.update(decode_packets(ws, lay, w))
     return res
+
+
+def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[str, np.ndarray]:
+    """Read the dO codes (channel-major, natural token order), the dO block scales and D
+    back out of the backward workspace's tile packets (layout in include/sagebwd.h)."""
+    d, P, nt = w.d, lay["packet_bytes"], w.N // 64
+    pk = ws[lay["packets"]:lay["packets"] + w.B * w.H * nt * P].reshape(w.B, w.H, nt, P)
+    rows = pk[..., 192 * d:256 * d].view(np.int8).reshape(w.B, w.H, nt, d, 4, 16)  # [.., c, slot, 16]
+    c = np.arange(d)
+    slot_of = np.arange(4)[None, :] ^ ((c[:, None] >> 1) & 3)                        # logical chunk -> slot
+    logical = np.take_along_axis(rows, slot_of[None, None, None, :, :, None], axis=-2).reshape(w.B, w.H, nt, d, 64)
+    u = np.arange(64)
+    pos = 32 * (u >> 5) + 16 * ((u >> 2) & 1) + 4 * ((u & 31) >> 3) + (u & 3)
+    codes = logical[..., pos]                                                         # [B,H,nt,d,64]
+    dOtc = np.moveaxis(codes, 2, 3).reshape(w.B, w.H, d, w.N)
+    base = 320 * d
+    Dv = pk[..., base + 256:base + 512].copy().view(np.float32).reshape(w.B, w.H, w.N)
+    sdo_tiles = pk[..., base + 516:base + 520].copy().view(np.float32).reshape(w.B, w.H, nt)
+    dOs = sdo_tiles[..., :: w.blk // 64]
+    return {"dOtc": dOtc, "dOs": dOs, "Dvec": Dv}
 
 
 def pro_to_device(pro: Dict[str, np.ndarray]):

@@ -13,7 +13,7 @@ lib = _lib.load()  # fails loudly if the library was not built
 
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
-                dtype=_lib.SAGEBWD_FP16)
+                dtype=_lib.SAGEBWD_FP16, dq_mode=0)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -60,6 +60,7 @@ def test_invalid_params_rejected(call):
     assert call(P(blk=32)) == -3
     assert call(P(dtype=7)) == -3
     assert call(P(eps=-1.0)) == -3
+    assert call(P(dq_mode=3)) == -3
     assert call(P(N=200)) == -2            # not a multiple of blk
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
@@ -80,7 +81,11 @@ def test_workspace_checks():
     need = lib.sagebwd_backward_workspace_bytes(ctypes.byref(p))
     n = 1 * 2 * 256 * 64
     up = lambda x: (x + 255) // 256 * 256
-    assert need == up(4 * n) + up(4 * 512) + up(4 * 512) + up(n) + up(4 * 8) + up(n)
+    # auto -> dS spill at this size: packets, K^T packets, dS tiles, multipliers
+    tiles = 4 * 4 - 4 * 3 // 2          # nb * nt - (blk/64) * nb * (nb - 1) / 2, causal
+    assert need == up(2 * 4 * 21504) + up(2 * 4 * 64 * 64) + up(2 * tiles * 64 * 64) + up(2 * tiles * 4)
+    atomic = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=2)))
+    assert atomic == up(2 * 4 * 21504) + up(4 * n)
     assert _backward(p, ws_bytes=need - 1) == -5
     assert _backward(p, ws=0) == -1
     assert _backward(p, ws=MIS) == -4
