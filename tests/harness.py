@@ -101,7 +101,8 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
         for k in ("dQ", "dK", "dV"):
             res[k] = g[k].float().cpu().numpy().astype(np.float64)
         lay = api.backward_workspace_layout(p)
-        ws = g["workspace"].cpu().numpy()
+        npk = w.B * w.H * (w.N // 64) * lay["packet_bytes"]   # only the packet region is decoded
+        ws = g["workspace"][:npk].cpu().numpy()
         res.update(decode_packets(ws, lay, w))
     return res
 
