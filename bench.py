@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks (TOP/s): INT8 5.0 POPS, FP16/BF16 2.5 PFLOPS.
 PEAK_I8 = 5000.0
 PEAK_F16 = 2500.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_main_n8192_d128_traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_main_n8192_d128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_trainable_attention_amd", "csrc", f)
                   for f in ("backward.hip", "common.hpp")]
 
@@ -86,7 +86,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="n8192_d128")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="before warm-up, run one plain device-to-device copy of this many MiB "
+                         "(a known-traffic kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -115,6 +118,14 @@ def main():
     grads = {n: torch.empty_like(Q) for n in ("dQ", "dK", "dV")}
     bws = torch.empty(api.sagebwd_backward_workspace_bytes(p), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     stages = ["prologue", "forward", "bwd_pre", "bwd_main", "bwd_dq"]
 
