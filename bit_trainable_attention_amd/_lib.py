@@ -46,18 +46,26 @@ SIGNATURES = {
     "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 15 + [_P, _SIZE, _P]),
     "sagebwd_backward_part": (_ST, [ctypes.POINTER(Params), ctypes.c_int32] + [_P] * 15 + [_P, _SIZE, _P]),
     "sagebwd_status_string": (ctypes.c_char_p, [_ST]),
+    "sagebwd_last_error": (ctypes.c_char_p, []),
 }
 
 _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libsagebwd.so once; raise if it has not been built."""
+    """Load libsagebwd.so once; raise if it has not been built.
+
+    torch is imported first so that the library binds to the HIP runtime torch already
+    loaded. Both runtimes carry the soname libamdhip64.so.7, but torch asks for it as
+    libamdhip64.so; if the library were loaded first, torch would bring a second HIP/HSA
+    runtime into the process and the library's runtime would find no device.
+    """
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m bit_trainable_attention_amd.build`")
+        import torch  # noqa: F401  (binds the HIP runtime; see above)
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

@@ -28,9 +28,15 @@ def sagebwd_status_string(status: int) -> str:
     return _lib.load().sagebwd_status_string(status).decode()
 
 
+def sagebwd_last_error() -> str:
+    """Detail of the last SAGEBWD_ERR_HIP on this thread ("" if none)."""
+    return _lib.load().sagebwd_last_error().decode()
+
+
 def _check(status: int, what: str) -> None:
     if status != 0:
-        raise RuntimeError(f"{what}: {_lib.STATUS.get(status, status)} ({sagebwd_status_string(status)})")
+        detail = f"; {sagebwd_last_error()}" if _lib.STATUS.get(status) == "SAGEBWD_ERR_HIP" else ""
+        raise RuntimeError(f"{what}: {_lib.STATUS.get(status, status)} ({sagebwd_status_string(status)}){detail}")
 
 
 def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:

@@ -2,6 +2,8 @@
 // Validates arguments without touching the HIP runtime, then enqueues the kernels.
 #include "sagebwd.h"
 
+#include <stdio.h>
+
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
@@ -100,6 +102,17 @@ const char* sagebwd_status_string(sagebwd_status s) {
   return "unknown status";
 }
 
+// Text of the last HIP failure on this host thread ("" if none since the thread started).
+static thread_local char g_last_error[192];
+
+static sagebwd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SAGEBWD_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  return SAGEBWD_ERR_HIP;
+}
+
+const char* sagebwd_last_error(void) { return g_last_error; }
+
 size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p) {
   if (check_params(p) != SAGEBWD_OK) return 0;
   if (!p->k_smooth || empty(p)) return 0;
@@ -137,7 +150,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
   a.kpart = static_cast<float*>(workspace);
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.eps = p->eps;
-  return sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+  return hip_status(sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)), "sagebwd_quant_prologue");
 }
 
 sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
@@ -153,7 +166,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
-  return sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP;
+  return hip_status(sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)), "sagebwd_forward");
 }
 
 static sagebwd_status backward_impl(const sagebwd_params* p, int part, const void* Q, const void* K,
@@ -195,8 +208,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
-  return sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)) == hipSuccess ? SAGEBWD_OK
-                                                                                          : SAGEBWD_ERR_HIP;
+  return hip_status(sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)), "sagebwd_backward");
 }
 
 sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,

@@ -673,26 +673,20 @@ template <int DT, int D, int BLK>
 static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t st) {
   const long long nb = a.N / BLK;
   if (part < 0 || part == 0) {
-    hipLaunchKernelGGL((bwd_pre<DT, D, BLK>), dim3((unsigned)(nb * a.BH)), dim3(256), 0, st, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(&bwd_pre<DT, D, BLK>, dim3((unsigned)(nb * a.BH)), dim3(256), st, a);
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 1) {
-    if (a.spill)
-      hipLaunchKernelGGL((bwd_main<DT, D, BLK, true>), dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_main<DT, D, BLK, false>), dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), 0, st, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        a.spill ? launch_kernel(&bwd_main<DT, D, BLK, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
+                : launch_kernel(&bwd_main<DT, D, BLK, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a);
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {
-    if (a.spill) {
-      hipLaunchKernelGGL((bwd_dq<DT, D, BLK>), dim3((unsigned)((long long)(a.N / kTq) * a.BH)), dim3(256), 0, st, a);
-    } else {
-      const long long threads = (long long)a.BH * a.N * (D / 8);
-      hipLaunchKernelGGL((dq_finalize<DT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
-    }
-    return hipGetLastError();
+    if (a.spill)
+      return launch_kernel(&bwd_dq<DT, D, BLK>, dim3((unsigned)((long long)(a.N / kTq) * a.BH)), dim3(256), st, a);
+    const long long threads = (long long)a.BH * a.N * (D / 8);
+    return launch_kernel(&dq_finalize<DT, D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), st, a);
   }
   return hipSuccess;
 }

@@ -16,8 +16,12 @@
 // Per key tile (the online-softmax step and the P~ quantisation tile, 32 rows x BLK keys):
 //   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); alpha = 2^(m - m'); l = l*alpha + sum P~;
 //   a = max P~ over the wave's tile; codes = rne(P~ * (127/a)); O = O*alpha + (a/127)*sV*int(PV).
+// P~ * 127/a is produced by one exponential, 2^(s*log2e - m' + log2(127/a)), and rounded and
+// packed by v_cvt_pk_u8_f32 (nearest even); only tiles on the diagonal carry masking work.
 #include "common.hpp"
 #include "launch.hpp"
+
+#include <type_traits>
 
 namespace sagebwd {
 
@@ -28,6 +32,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
 
 template <int D, int BLK>
 struct FwdLds {
@@ -124,7 +129,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
     const int k0 = kt * BLK;
     const int8_t* kl = lds[kt & 1];
     const int8_t* vl = lds[kt & 1] + L::kBytesK;
-    if (active && (!a.causal || k0 <= q0w + kRowsPerWave - 1)) {
+    // One key tile. DIAG: the tile crosses this wave's causal diagonal (keys above it are
+    // masked); every other visited tile is wholly visible and carries no masking work.
+    auto tile = [&](auto diag_c) {
+      constexpr bool DIAG = decltype(diag_c)::value;
       // ---- S^T = K Q^T (exact int32)
       i32x16 s[NSUB];
 #pragma unroll
@@ -136,9 +144,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           s[t] = mfma_i8_32x32x32(ak, qreg[kk], s[t]);
         }
       }
-      // ---- causal mask on the tile that crosses the diagonal
-      const bool diag = a.causal && (k0 + BLK - 1 > q0w);
-      if (diag) {
+      if constexpr (DIAG) {
 #pragma unroll
         for (int t = 0; t < NSUB; ++t)
 #pragma unroll
@@ -157,41 +163,49 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       const size_t sidx = (size_t)bh * nb + kt;
       const float sK = a.Ks[sidx], sV = a.Vs[sidx];
       const float c2 = (sQ * sK) * (a.sm_scale * kLog2e);
-      const float m_new = fmaxf(m, (float)rmax * c2);
+      // row max over the visible keys (a row with none in this tile keeps its old max)
+      float rowmax = (float)rmax * c2;
+      if constexpr (DIAG) rowmax = rmax == INT32_MIN ? -INFINITY : rowmax;
+      const float m_new = fmaxf(m, rowmax);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      // P~ tile absmax a = max over rows of 2^(rowmax - m'); in log2 it is one wave max.
+      // The quantisation factor 127/a is folded into the exponent, so the exponential
+      // yields P~ * 127/a directly and its nearest-even integer is the code.
+      const float pa_log = wave_max(rowmax - m_new);
+      const float bias = kLog2_127 - pa_log - m_new;
+      const float sP = __builtin_amdgcn_exp2f(pa_log) * (1.0f / 127.0f);
 
-      // ---- P~ = 2^(s - m'), row sums before quantisation
-      float p[NSUB][16];
-      float psum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, -m_new));
-          if (diag && s[t][r] == INT32_MIN) v = 0.0f;
-          p[t][r] = v;
-          psum += v;
-        }
-      lsum_run = lsum_run * alpha + psum;
-
-      // ---- P~ tile absmax (32 rows x BLK keys): the largest element of each row is the
-      // row max, so the tile max is the max over rows of 2^(rowmax - m').
-      const float pmax_row = __builtin_amdgcn_exp2f(__builtin_fmaf((float)rmax, c2, -m_new));
-      const float pa = wave_max(pmax_row);
-      const float inv = pa > 0.0f ? 127.0f / pa : 0.0f;
-      const float sP = pa > 0.0f ? pa / 127.0f : 0.0f;
-
-      // ---- quantise P~ into the B-operand layout (slot s = register s of the subtile)
+      float tsum = 0.0f;
       i32x4 pc[NSUB];
 #pragma unroll
       for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pc[t][j] = (int)pack4_lo_bytes(quant_word(p[t][4 * j], inv), quant_word(p[t][4 * j + 1], inv),
-                                         quant_word(p[t][4 * j + 2], inv), quant_word(p[t][4 * j + 3], inv));
+        for (int j = 0; j < 4; ++j) {
+          float u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = __builtin_fmaf((float)s[t][4 * j + i], c2, bias);
+            if constexpr (DIAG) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
+            u[i] = __builtin_amdgcn_exp2f(x);
+            tsum += u[i];
+          }
+          unsigned wd = __builtin_amdgcn_cvt_pk_u8_f32(u[0], 0, 0u);
+          wd = __builtin_amdgcn_cvt_pk_u8_f32(u[1], 1, wd);
+          wd = __builtin_amdgcn_cvt_pk_u8_f32(u[2], 2, wd);
+          pc[t][j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, wd);
+        }
+      // l accumulates P~ before quantisation: sum(P~ * 127/a) * a/127
+      lsum_run = lsum_run * alpha + tsum * sP;
 
-      // ---- O^T += V^T P~^T (int32 over the BLK keys of one V block), then rescale
+      // ---- O^T = O^T * alpha + (a/127) sV (V^T P~^T), int32 over the BLK keys of one V block.
+      // The rescale is skipped when no row of the wave moved its max (alpha == 1 exactly).
       const float spv = sP * sV;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < DC; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+      }
 #pragma unroll
       for (int ct = 0; ct < DC; ++ct) {
         i32x16 acc = i32x16{};
@@ -201,9 +215,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           acc = mfma_i8_32x32x32(av, pc[t], acc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[ct][r] = o[ct][r] * alpha + spv * (float)acc[r];
+        for (int r = 0; r < 16; ++r) o[ct][r] = __builtin_fmaf(spv, (float)acc[r], o[ct][r]);
       }
       m = m_new;
+    };
+    if (active && (!a.causal || k0 <= q0w + kRowsPerWave - 1)) {
+      if (a.causal && k0 + BLK - 1 > q0w) tile(std::true_type{});
+      else tile(std::false_type{});
     }
     if (has_next) store_tile_lds<D, BLK>(lds[(kt + 1) & 1], kreg, vreg);
     __syncthreads();
@@ -228,8 +246,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 template <int DT, int D, int BLK>
 static hipError_t launch_forward_t(const ForwardArgs& a, hipStream_t st) {
   const long long nq = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((fwd_kernel<DT, D, BLK>), dim3((unsigned)(nq * a.BH)), dim3(kWaves * 64), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(&fwd_kernel<DT, D, BLK>, dim3((unsigned)(nq * a.BH)), dim3(kWaves * 64), st, a);
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st) {

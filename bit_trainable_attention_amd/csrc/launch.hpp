@@ -50,6 +50,15 @@ struct BackwardArgs {
   float sm_scale;
 };
 
+// Enqueue one kernel and return the status of this launch itself (hipLaunchKernel reports
+// it directly, so an error left pending by an unrelated runtime call is not picked up).
+template <typename Args>
+hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, dim3 block, hipStream_t st, const Args& a) {
+  Args copy = a;
+  void* params[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, params, 0, st);
+}
+
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st);
 hipError_t launch_backward(const BackwardArgs& a, int part, hipStream_t st);  // part -1 = all

@@ -200,11 +200,9 @@ template <int DT, int D, int BLK>
 static hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st) {
   const int nb = a.N / BLK;
   const long long nblocks = (long long)a.BH * nb;
-  hipLaunchKernelGGL((prologue_pass1<DT, D, BLK>), dim3((unsigned)(nblocks * 3)), dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(&prologue_pass1<DT, D, BLK>, dim3((unsigned)(nblocks * 3)), dim3(kThreads), st, a);
   if (e != hipSuccess || !a.k_smooth) return e;
-  hipLaunchKernelGGL((prologue_pass2<DT, D, BLK>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)nblocks), dim3(kThreads), st, a);
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st) {

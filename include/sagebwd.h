@@ -192,6 +192,12 @@ sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part,
 /* Static description of a status code (never NULL). */
 const char* sagebwd_status_string(sagebwd_status s);
 
+/* Detail of the last SAGEBWD_ERR_HIP returned on the calling host thread: the entry point
+ * and the HIP runtime's error name and text for the enqueue that failed. The string is
+ * owned by the library, stays valid until the next failing call on the same thread, and
+ * is empty if no call on this thread has failed. Never NULL; makes no HIP call. */
+const char* sagebwd_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,12 @@ def test_status_strings():
     assert lib.sagebwd_status_string(12345).decode() == "unknown status"
 
 
+def test_last_error_empty_without_failures():
+    # argument errors are reported by status alone; only a failed enqueue records detail
+    assert _prologue(P(d=96)) == -3
+    assert lib.sagebwd_last_error().decode() == ""
+
+
 def _prologue(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 12), ws, ws_bytes, None)
 
