@@ -27,6 +27,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <float.h>
+
 #include <type_traits>
 
 namespace sagebwd {
@@ -350,8 +352,12 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         }
         pf[r] = p;
         dsf[r] = p * (dp[r] - dvv[qi]);
-        pm = fmaxf(pm, p);
-        dm = fmaxf(dm, fabsf(dsf[r]));
+      }
+      // tile maxima as three-input max trees (v_max3_f32, |x| as an operand modifier)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        pm = fmaxf(pm, fmaxf(pf[r], pf[r + 1]));
+        dm = fmaxf(dm, fmaxf(fabsf(dsf[r]), fabsf(dsf[r + 1])));
       }
     };
     if (a.causal && k0 + BLK - 1 > q0) elems(std::true_type{});
@@ -365,19 +371,20 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     float da = redD[0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) da = fmaxf(da, redD[i]);
-    const float pinv = pa > 0.0f ? 127.0f / pa : 0.0f;
-    const float sP = pa > 0.0f ? pa / 127.0f : 0.0f;
-    const float dinv = da > 0.0f ? 127.0f / da : 0.0f;
-    const float sdS = da > 0.0f ? da / 127.0f : 0.0f;
+    // Tile scales a/127 and inverses 127/a (hardware reciprocal; a tile whose absmax is below
+    // the smallest normal float is quantised against that bound so the reciprocal stays finite).
+    const float pa_n = fmaxf(pa, FLT_MIN), da_n = fmaxf(da, FLT_MIN);
+    const float pinv = 127.0f * __builtin_amdgcn_rcpf(pa_n), sP = pa_n * (1.0f / 127.0f);
+    const float dinv = 127.0f * __builtin_amdgcn_rcpf(da_n), sdS = da_n * (1.0f / 127.0f);
     i32x4 pc, dc;  // this wave's codes (queries 32h..32h+31)
     {
       int8_t* col = lds + L::offDS + kl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pc[j] = (int)pack4_lo_bytes(quant_word(pf[4 * j], pinv), quant_word(pf[4 * j + 1], pinv),
-                                    quant_word(pf[4 * j + 2], pinv), quant_word(pf[4 * j + 3], pinv));
-        const unsigned w0 = quant_word(dsf[4 * j], dinv), w1 = quant_word(dsf[4 * j + 1], dinv);
-        const unsigned w2 = quant_word(dsf[4 * j + 2], dinv), w3 = quant_word(dsf[4 * j + 3], dinv);
+        pc[j] = (int)pack4_lo_bytes(quant_word_fma(pf[4 * j], pinv), quant_word_fma(pf[4 * j + 1], pinv),
+                                    quant_word_fma(pf[4 * j + 2], pinv), quant_word_fma(pf[4 * j + 3], pinv));
+        const unsigned w0 = quant_word_fma(dsf[4 * j], dinv), w1 = quant_word_fma(dsf[4 * j + 1], dinv);
+        const unsigned w2 = quant_word_fma(dsf[4 * j + 2], dinv), w3 = quant_word_fma(dsf[4 * j + 3], dinv);
         dc[j] = (int)pack4_lo_bytes(w0, w1, w2, w3);
         // dS codes, query-major, for dQ: query 32h + 8j + 4g + i, key kl
         const int qb = 32 * h + 8 * j + 4 * g;

@@ -79,4 +79,10 @@ __device__ __forceinline__ unsigned quant_word(float x, float inv) {
   return __float_as_uint(t + 12582912.0f);
 }
 
+// In-kernel tile codes (P, dS): nearest-even integer of the exact product x * inv, rounded
+// once by the fused multiply-add with 1.5 * 2^23 (|x * inv| <= 127.5); low byte = code.
+__device__ __forceinline__ unsigned quant_word_fma(float x, float inv) {
+  return __float_as_uint(__builtin_fmaf(x, inv, 12582912.0f));
+}
+
 }  // namespace sagebwd
