@@ -16,7 +16,7 @@ DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 # Quantisation tile shapes of the kernels (include/sagebwd.h).
 FWD_TILE_Q = 32
 BWD_TILE_Q = 64
-BWD_P_TILE_K = 32
+BWD_P_TILE_K = 16
 
 STATUS = {
     0: "SAGEBWD_OK", -1: "SAGEBWD_ERR_NULL", -2: "SAGEBWD_ERR_SHAPE", -3: "SAGEBWD_ERR_UNSUPPORTED",

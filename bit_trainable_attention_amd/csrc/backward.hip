@@ -10,14 +10,14 @@
 //                64-query tile, a "packet": the exact LDS image the main kernel needs for that
 //                tile (Q codes, dO, dO^T codes, Q^T codes, lse2, D, block scales), already
 //                swizzled and permuted. Also zeroes the float32 dQ accumulator rows.
-//   bwd_main     one workgroup per (head, key block of BLK keys); a pair of waves owns each
-//                32 keys. Streams the query tiles' packets into double-buffered LDS with
-//                buffer->LDS copies (the next tile is in flight while the current one is
-//                computed). S = Q K~^T with v_mfma_i32_32x32x32_i8 in the layout lane = key,
-//                registers = queries, which is directly the B operand of the two products that
-//                contract over queries: dV^T = dO^T P and dK^T = Q^T dS. dP = dO V^T uses
-//                v_mfma_f32_32x32x16_{f16,bf16} on the raw dO and V. dS codes go through LDS
-//                once (query-major) for dQ = dS K, accumulated with float32 atomics.
+//   bwd_main     one workgroup per (head, key block of BLK keys); each wave owns 16 keys.
+//                Streams the query tiles' packets into triple-buffered LDS with buffer->LDS
+//                copies (issued two tiles ahead). S = Q K~^T on v_mfma_i32_16x16x64_i8 and
+//                dP = dO V^T on v_mfma_f32_16x16x32_{f16,bf16}, in the layout lane = key,
+//                registers = queries, which is directly the B operand of the two products
+//                that contract over queries: dV^T = dO^T P and dK^T = Q^T dS. dS codes leave
+//                key-major (spill mode) or go through LDS once for dQ = dS K with float32
+//                atomics (atomic mode).
 //   bwd_dq       (dS spill mode) query-major dQ = dS K over the spilled dS tiles, fused with the
 //                RMSNorm backward and the dtype rounding.
 //   dq_finalize  (atomic mode) RMSNorm backward of the accumulated dQ and dtype rounding.
@@ -38,10 +38,10 @@ namespace {
 constexpr int kTq = 64;  // query rows per P / dS quantisation tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Byte position, inside a group of 32 tokens of a channel-major row, of token-dword kd
-// (tokens 4kd..4kd+3, kd = 0..7): lane group g of an MFMA operand needs tokens {8j + 4g + i}
-// (j, i = 0..3), which lands at bytes 16g..16g+15. Token t sits at 16*((t>>2)&1) + 4*(t>>3) + (t&3).
-__device__ __forceinline__ int perm_dword_pos(int kd) { return 16 * (kd & 1) + 4 * (kd >> 1); }
+// Byte position, inside a 64-token channel-major row of a tile packet, of token u: the
+// backward's lane group g holds tokens {16t + 4g + r} (t, r = 0..3) as contraction slots
+// 4t + r, so token 16t + 4g + r sits at byte 16g + 4t + r.
+__device__ __forceinline__ int tile_token_pos(int u) { return 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3); }
 
 // XOR swizzles of the 16-byte chunks of LDS rows: 8 consecutive rows read at the same
 // logical chunk land in 8 different bank groups.
@@ -96,7 +96,7 @@ template <int D>
 struct Packet {
   static constexpr int bQ = 0;                // Q codes [64][D], chunk j of row r at slot swz<D>(r, j)
   static constexpr int bDO = 64 * D;          // dO [64][D] 16-bit, chunk j of row r at slot swz<2D>(r, j)
-  static constexpr int bDOT = bDO + 128 * D;  // dO codes [D][64], tokens permuted, chunk swz<64>(c, j)
+  static constexpr int bDOT = bDO + 128 * D;  // dO codes [D][64], token u at tile_token_pos(u), chunk swz<64>(c, j)
   static constexpr int bQT = bDOT + 64 * D;   // Q codes [D][64], same order as dO^T
   static constexpr int bLSE = bQT + 64 * D;   // lse * log2(e) [64] f32
   static constexpr int bDV = bLSE + 256;      // D = rowsum(dO o O) [64] f32
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
     const unsigned qw = (unsigned)(uint8_t)qs[t][c] | ((unsigned)(uint8_t)qs[t + 1][c] << 8) |
                         ((unsigned)(uint8_t)qs[t + 2][c] << 16) | ((unsigned)(uint8_t)qs[t + 3][c] << 24);
     const int tl = t % kTq;
-    const int p = 32 * (tl / 32) + perm_dword_pos((tl % 32) / 4);  // byte position in the 64-token row
+    const int p = tile_token_pos(tl);  // byte position in the 64-token row (tl..tl+3 stay together)
     const int off = c * kTq + 16 * swz<kTq>(c, p / 16) + p % 16;
     int8_t* pk = pk0 + (t / kTq) * P::kBytes;
     *reinterpret_cast<unsigned*>(pk + P::bDOT + off) = word;
@@ -223,317 +223,339 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 }
 
 // ------------------------------------------------------------------------------ bwd_main
-// Workgroup = one key block of BLK keys, 2*BLK/32 waves (two per SIMD). The waves come in
-// pairs: both waves of pair kg own the same 32 keys; wave half h = 0/1 computes S, P, dP and
-// dS for query rows 32h..32h+31 of each 64-row query tile, and accumulates dK and dV for
-// channel half h. The pair swaps its P and dS codes through LDS, so each wave holds the
-// B operands of dV^T = dO^T P and dK^T = Q^T dS for all 64 queries.
+// Workgroup = one key block of BLK keys, NW = BLK/16 waves; wave w owns keys 16w..16w+15 of
+// the block for every 64-query tile (lane l: key 16w + (l & 15), lane group g = l >> 4). The
+// products run on gfx950's 16 x 16 MFMAs. S and dP of query sub-tile t (queries 16t..16t+15)
+// leave query 16t + 4g + r and this lane's key in register r, so each lane ends up holding P
+// and dS of its key for 16 of the tile's queries: the B operand (columns = keys, contraction
+// = the 64 queries) of dV^T = dO^T P and dK^T = Q^T dS, contraction slot 4t + r of lane
+// group g standing for query 16t + 4g + r. The packets store dO^T and Q^T codes in that
+// query order, so no data moves between lanes.
+//   P is quantised on the wave's own 64 x 16 tile (no cross-wave step), so dV runs before
+//   the one workgroup barrier of the tile, which publishes the waves' |dS| maxima (dS is
+//   quantised on the 64 x BLK tile). After that barrier nothing reads the tile buffer (the
+//   Q^T operands of dK are loaded into registers before it), and with three tile buffers the
+//   same barrier also hands over the tile two steps ahead: the copies of tile qt+2 are issued
+//   at the top of step qt into the buffer that step qt-1 released.
+//   dS leaves as this lane's 16 codes in one 16-byte store: the spilled tile is dS^T, key-major.
 template <int D, int BLK>
 struct BwdLds {
   using P = Packet<D>;
-  static constexpr int NKG = BLK / 32;        // 32-key groups
-  static constexpr int NW = 2 * NKG;          // waves
-  static constexpr int kRowS = BLK + 16;      // dS codes [query][key]; K^T codes [channel][key]
-  static constexpr int kBuf = P::kBytes;      // one tile buffer (double-buffered)
-  static constexpr int offDS = 2 * kBuf;
-  static constexpr int offKT = offDS + kTq * kRowS;
-  static constexpr int offK = offKT + D * kRowS;    // K codes [BLK][D], token-major, swizzled
-  static constexpr int offXP = offK + BLK * D;      // P codes exchanged inside a pair [NW][64][16 B]
-  static constexpr int offXD = offXP + NW * 1024;   // dS codes exchanged inside a pair
-  static constexpr int offRED = offXD + NW * 1024;  // redP[NW], redD[NW]
-  static constexpr int offDOT = offRED + 2 * NW * 4;  // epilogue: per-lane dK.K^ partial dots [NW][64]
-  static constexpr int kBytes = offDOT + NW * 64 * 4;
-  static constexpr int kCopiesPerWave = (P::kCopies + NW - 1) / NW;
+  static constexpr int NW = BLK / 16;             // waves
+  static constexpr int kBuf = P::kBytes;          // one tile buffer (three of them)
+  static constexpr int offRED = 3 * kBuf;         // |dS| maxima [2][NW] (by step parity)
+  static constexpr int offDST = offRED + 2 * NW * 4;  // atomic mode: dS^T codes [BLK][64]
+  static constexpr int offKT = offDST + BLK * 64;     // atomic mode: K^T codes [D][BLK]
+  static constexpr int kBytesSpill = offDST;
+  static constexpr int kBytesAtomic = offKT + D * BLK;
+  // copies per wave of one packet: kCpHi for waves w < kCpSplit, one fewer for the rest
+  static constexpr int kCpHi = (P::kCopies + NW - 1) / NW;
+  static constexpr int kCpSplit = P::kCopies - (kCpHi - 1) * NW;
 };
+
+// wait until at most S + C (C = copies of this wave in the current step, if any) vector-memory
+// operations are outstanding: S and C are per-wave-uniform, so the immediate is chosen by branches
+template <int S, int CHI>
+__device__ __forceinline__ void wait_copies_then(bool issued, bool hi) {
+  if (!issued) wait_vmcnt<S>();
+  else if (hi) wait_vmcnt<S + CHI>();
+  else wait_vmcnt<S + CHI - 1>();
+}
 
 template <int DT, int D, int BLK, bool SPILL>
 __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   using L = BwdLds<D, BLK>;
   using P = Packet<D>;
-  constexpr int NKG = L::NKG;      // 32-key groups (wave pairs)
   constexpr int NW = L::NW;        // waves per workgroup
   constexpr int NT = NW * 64;      // threads
-  constexpr int DC = D / 32;       // 32-channel chunks (int8 contraction / output tiles)
-  constexpr int DCH = DC / 2;      // 32-channel output tiles per channel half
-  constexpr int DH = D / 16;       // 16-channel chunks (16-bit contraction)
-  constexpr int KC = BLK / 32;     // 32-key chunks of the workgroup
-  __shared__ __attribute__((aligned(16))) int8_t lds[L::kBytes];
+  constexpr int KCH = D / 64;      // 64-channel chunks (INT8 contraction of S)
+  constexpr int HCH = D / 32;      // 32-channel chunks (16-bit contraction of dP)
+  constexpr int NCT = D / 16;      // 16-channel output tiles of dV^T and dK^T
+  __shared__ __attribute__((aligned(16))) int8_t lds[SPILL ? L::kBytesSpill : L::kBytesAtomic];
 
   const int nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;            // key block; 0 first (most work when causal)
-  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 5, lk = l & 31;
-  const int kg = w % NKG, h = w / NKG;         // key group, query half / channel half
-  const int partner = kg + NKG * (1 - h);
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 4, lr = l & 15;
   const int tid = threadIdx.x;
   const int k0 = kb * BLK;
-  const int key = k0 + 32 * kg + lk;           // this lane's key
-  const int kl = 32 * kg + lk;                 // ... inside the block
+  const int kl = 16 * w + lr;                  // this lane's key inside the block
+  const int key = k0 + kl;
   const size_t hrow = (size_t)bh * a.N;
   const int ntile = a.N / kTq;
   const int8_t* pkh = a.pk + (size_t)bh * ntile * P::kBytes;   // this head's packets
   const uint32_t pkh_bytes = (uint32_t)ntile * P::kBytes;
+  const bool cp_hi = w < L::kCpSplit;
 
-  // ---- per-wave constant operand: V (B of dP) for this lane's key
-  u16x8 vreg[DH];
+  // ---- per-lane constant operands: K codes (B of S) and V (B of dP) of this lane's key
+  i32x4 kreg[KCH];
 #pragma unroll
-  for (int kk = 0; kk < DH; ++kk) vreg[kk] = *reinterpret_cast<const u16x8*>(a.V + (hrow + key) * D + 16 * kk + 8 * g);
-  // ---- K codes of the key block in LDS: token-major (B operand of S = Q K^T) and
-  //      channel-major (B operand of dQ = dS K)
-  for (int ch = tid; ch < BLK * D / 16; ch += NT) {
-    const int t = (ch * 16) / D, c = (ch * 16) % D;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + k0 + t) * D + c);
-    *reinterpret_cast<i32x4*>(lds + L::offK + t * D + 16 * swz<D>(t, c / 16)) = v;
-    if constexpr (!SPILL) {
+  for (int c = 0; c < KCH; ++c) kreg[c] = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + key) * D + 64 * c + 16 * g);
+  u16x8 vreg[HCH];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lds[L::offKT + (c + i) * L::kRowS + t] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
+  for (int c = 0; c < HCH; ++c) vreg[c] = *reinterpret_cast<const u16x8*>(a.V + (hrow + key) * D + 32 * c + 8 * g);
+  if constexpr (!SPILL) {
+    // K^T codes of the block for dQ = dS K: [D][BLK], chunk j of row c at slot swz<BLK>(c, j)
+    for (int ch = tid; ch < BLK * D / 16; ch += NT) {
+      const int t = (ch * 16) / D, c = (ch * 16) % D;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + k0 + t) * D + c);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cc = c + i;
+        lds[L::offKT + cc * BLK + 16 * swz<BLK>(cc, t / 16) + t % 16] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
+      }
     }
   }
   const float sK = a.Ks[(size_t)bh * nb + kb];
   const float smc = a.sm_scale;
-  float* redP = reinterpret_cast<float*>(lds + L::offRED);
-  float* redD = redP + NW;
+  float* redD = reinterpret_cast<float*>(lds + L::offRED);
 
-  f32x16 dk[DCH], dv[DCH];
+  f32x4 dk[NCT], dv[NCT];
 #pragma unroll
-  for (int i = 0; i < DCH; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+  for (int i = 0; i < NCT; ++i) { dk[i] = f32x4{}; dv[i] = f32x4{}; }
 
-  // copies of packet qt into an LDS tile buffer: wave w moves KB cp = w, w + NW, ...
-  auto issue = [&](int qt, int8_t* dst) {
+  // copies of packet qt into an LDS tile buffer: wave w moves KB cp = w, w + NW, ... (copies
+  // j in [J0, J1) of this wave)
+  auto issue = [&](int qt, int8_t* dst, auto j0_c, auto j1_c) {
+    constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
 #pragma unroll
-    for (int j = 0; j < L::kCopiesPerWave; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int cp = w + NW * j;
       if (cp < P::kCopies) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * P::kBytes + cp * 1024);
     }
   };
+  constexpr int kC = L::kCpHi;
+  using G0 = std::integral_constant<int, 0>;
+  using G1 = std::integral_constant<int, (kC + 2) / 3>;
+  using G2 = std::integral_constant<int, (2 * kC + 2) / 3>;
+  using G3 = std::integral_constant<int, kC>;
+  // vector-memory operations a wave issues per step after the step's copies: the dS^T store
+  // and the dQ multiplier (spill), or the dQ atomics
+  constexpr int WPU = NW / 4;                       // atomic mode: waves per 16-query group
+  constexpr int NCTW = NCT / WPU;                   // ... and their 16-channel dQ tiles
+  constexpr int kStores = SPILL ? 2 : NCTW * 4;
 
   const int qt0 = a.causal ? k0 / kTq : 0;
-  issue(qt0, lds);
+  issue(qt0, lds, G0{}, G3{});
+  if (qt0 + 1 < ntile) issue(qt0 + 1, lds + L::kBuf, G0{}, G3{});
   wait_vmcnt<0>();
   __syncthreads();
 
+  int bi = 0;  // buffer of the current tile
   for (int qt = qt0; qt < ntile; ++qt) {
     const int q0 = qt * kTq;
-    const bool has_next = qt + 1 < ntile;
-    int8_t* buf = lds + ((qt - qt0) & 1) * L::kBuf;
-    int8_t* nbuf = lds + (((qt - qt0) & 1) ^ 1) * L::kBuf;
-    if (has_next) issue(qt + 1, nbuf);
+    const int step = qt - qt0;
+    const bool issue_next = qt + 2 < ntile;
+    int8_t* buf = lds + bi * L::kBuf;
+    const int bn = bi == 0 ? 2 : bi - 1;             // (bi + 2) % 3: released by the previous step
+    int8_t* nbuf = lds + bn * L::kBuf;
+    if (issue_next) issue(qt + 2, nbuf, G0{}, G1{});
 
     const float sQ = *reinterpret_cast<const float*>(buf + P::bSQ);
     const float sdO = *reinterpret_cast<const float*>(buf + P::bSDO);
     const float c2 = (sQ * sK) * (smc * kLog2e);
 
-    // ---- S, P, dP, dS for query rows 32h..32h+31 of the tile and this pair's 32 keys
-    const int q = 32 * h + lk;
-    i32x16 s = i32x16{};
+    // ---- S = Q K~^T and dP = dO V^T for the four 16-query sub-tiles
+    i32x4 s[4];
+    f32x4 dp[4];
 #pragma unroll
-    for (int kk = 0; kk < DC; ++kk) {
-      const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + P::bQ + q * D + 16 * swz<D>(q, 2 * kk + g));
-      const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offK + kl * D + 16 * swz<D>(kl, 2 * kk + g));
-      s = mfma_i8_32x32x32(aq, bk, s);
-    }
-    f32x16 dp = f32x16{};
+    for (int t = 0; t < 4; ++t) {
+      const int q = 16 * t + lr;
+      s[t] = i32x4{};
 #pragma unroll
-    for (int kk = 0; kk < DH; ++kk) {
-      const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + P::bDO + q * 2 * D + 16 * swz<2 * D>(q, 2 * kk + g));
-      dp = mfma_16b_32x32x16<DT>(ad, vreg[kk], dp);
+      for (int c = 0; c < KCH; ++c) {
+        const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + P::bQ + q * D + 16 * swz<D>(q, 4 * c + g));
+        s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
+      }
+      dp[t] = f32x4{};
+#pragma unroll
+      for (int c = 0; c < HCH; ++c) {
+        const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + P::bDO + q * 2 * D + 16 * swz<2 * D>(q, 4 * c + g));
+        dp[t] = mfma_16b_16x16x32<DT>(ad, vreg[c], dp[t]);
+      }
     }
-    const float* lse2 = reinterpret_cast<const float*>(buf + P::bLSE) + 32 * h + 4 * g;
-    const float* dvv = reinterpret_cast<const float*>(buf + P::bDV) + 32 * h + 4 * g;
-    float pf[16], dsf[16];
-    float pm = 0.0f, dm = 0.0f;
+    // ---- P = 2^(S c - lse2), dS = P (dP - D): register r of sub-tile t is query 16t + 4g + r
+    float pf[4][4], dsf[4][4];
     auto elems = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 8 * (r >> 2) + (r & 3);  // query offset inside the 32 rows, minus 4g
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], c2, -lse2[qi]));
-        if constexpr (decltype(masked)::value) {
-          if (key > q0 + 32 * h + 4 * g + qi) p = 0.0f;
-        }
-        pf[r] = p;
-        dsf[r] = p * (dp[r] - dvv[qi]);
-      }
-      // tile maxima as three-input max trees (v_max3_f32, |x| as an operand modifier)
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 lse2 = *reinterpret_cast<const f32x4*>(buf + P::bLSE + 4 * (16 * t + 4 * g));
+        const f32x4 dvv = *reinterpret_cast<const f32x4*>(buf + P::bDV + 4 * (16 * t + 4 * g));
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        pm = fmaxf(pm, fmaxf(pf[r], pf[r + 1]));
-        dm = fmaxf(dm, fmaxf(fabsf(dsf[r]), fabsf(dsf[r + 1])));
+        for (int r = 0; r < 4; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, -lse2[r]));
+          if constexpr (decltype(masked)::value) {
+            if (key > q0 + 16 * t + 4 * g + r) p = 0.0f;
+          }
+          pf[t][r] = p;
+          dsf[t][r] = p * (dp[t][r] - dvv[r]);
+        }
       }
     };
     if (a.causal && k0 + BLK - 1 > q0) elems(std::true_type{});
     else elems(std::false_type{});
-    pm = wave_max(pm);
-    dm = wave_max(dm);
-    if (l == 0) { redP[w] = pm; redD[w] = dm; }
-    lds_barrier();
-    // P tile: 64 queries x this pair's 32 keys; dS tile: 64 queries x the block's BLK keys
-    const float pa = fmaxf(redP[kg], redP[kg + NKG]);
-    float da = redD[0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) da = fmaxf(da, redD[i]);
-    // Tile scales a/127 and inverses 127/a (hardware reciprocal; a tile whose absmax is below
-    // the smallest normal float is quantised against that bound so the reciprocal stays finite).
-    const float pa_n = fmaxf(pa, FLT_MIN), da_n = fmaxf(da, FLT_MIN);
-    const float pinv = 127.0f * __builtin_amdgcn_rcpf(pa_n), sP = pa_n * (1.0f / 127.0f);
-    const float dinv = 127.0f * __builtin_amdgcn_rcpf(da_n), sdS = da_n * (1.0f / 127.0f);
-    i32x4 pc, dc;  // this wave's codes (queries 32h..32h+31)
-    {
-      int8_t* col = lds + L::offDS + kl;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pc[j] = (int)pack4_lo_bytes(quant_word_fma(pf[4 * j], pinv), quant_word_fma(pf[4 * j + 1], pinv),
-                                    quant_word_fma(pf[4 * j + 2], pinv), quant_word_fma(pf[4 * j + 3], pinv));
-        const unsigned w0 = quant_word_fma(dsf[4 * j], dinv), w1 = quant_word_fma(dsf[4 * j + 1], dinv);
-        const unsigned w2 = quant_word_fma(dsf[4 * j + 2], dinv), w3 = quant_word_fma(dsf[4 * j + 3], dinv);
-        dc[j] = (int)pack4_lo_bytes(w0, w1, w2, w3);
-        // dS codes, query-major, for dQ: query 32h + 8j + 4g + i, key kl
-        const int qb = 32 * h + 8 * j + 4 * g;
-        col[(qb + 0) * L::kRowS] = (int8_t)w0;
-        col[(qb + 1) * L::kRowS] = (int8_t)w1;
-        col[(qb + 2) * L::kRowS] = (int8_t)w2;
-        col[(qb + 3) * L::kRowS] = (int8_t)w3;
-      }
-      *reinterpret_cast<i32x4*>(lds + L::offXP + w * 1024 + l * 16) = pc;
-      *reinterpret_cast<i32x4*>(lds + L::offXD + w * 1024 + l * 16) = dc;
-    }
-    lds_barrier();
-    // the partner's codes cover queries 32(1-h)..32(1-h)+31
-    const i32x4 pco = *reinterpret_cast<const i32x4*>(lds + L::offXP + partner * 1024 + l * 16);
-    const i32x4 dco = *reinterpret_cast<const i32x4*>(lds + L::offXD + partner * 1024 + l * 16);
+    if (issue_next) issue(qt + 2, nbuf, G1{}, G2{});
 
-    // ---- dV^T += dO^T P and dK^T += Q^T dS for channel half h (int32 over the 64 queries):
-    //      own codes pair with the A-operand chunk of query half h, the partner's with 1-h
+    // ---- tile maxima (three-input max trees; the |dS| maximum goes to the workgroup)
+    float pm = 0.0f, dm = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pm = fmaxf(pm, fmaxf(fmaxf(pf[t][0], pf[t][1]), fmaxf(pf[t][2], pf[t][3])));
+      dm = fmaxf(dm, fmaxf(fmaxf(fabsf(dsf[t][0]), fabsf(dsf[t][1])), fmaxf(fabsf(dsf[t][2]), fabsf(dsf[t][3]))));
+    }
+    wave_max2(pm, dm);
+    if (l == 0) redD[(step & 1) * NW + w] = dm;
+
+    // ---- P codes on this wave's 64 x 16 tile, then dV^T += dO^T P (int32 over the 64 queries)
     {
-      const float sv = sP * sdO;
+      const float pa = fmaxf(pm, FLT_MIN);
+      const float pinv = 127.0f * __builtin_amdgcn_rcpf(pa);
+      const float sv = pa * (1.0f / 127.0f) * sdO;
+      i32x4 pc;
 #pragma unroll
-      for (int i = 0; i < DCH; ++i) {
-        const int c = 32 * (DCH * h + i) + lk;
-        const i32x4 a0 = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, 2 * h + g));
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, 2 * (1 - h) + g));
-        i32x16 acc = mfma_i8_32x32x32(a0, pc, i32x16{});
-        acc = mfma_i8_32x32x32(a1, pco, acc);
+      for (int t = 0; t < 4; ++t)
+        pc[t] = (int)pack4_lo_bytes(quant_word_fma(pf[t][0], pinv), quant_word_fma(pf[t][1], pinv),
+                                    quant_word_fma(pf[t][2], pinv), quant_word_fma(pf[t][3], pinv));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dv[i][r] += sv * (float)acc[r];
+      for (int n = 0; n < NCT; ++n) {
+        const int c = 16 * n + lr;
+        const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, g));
+        const i32x4 acc = mfma_i8_16x16x64(ao, pc, i32x4{});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
       }
+    }
+    // Q^T operands of dK, read before the barrier (after it the buffer may be refilled)
+    i32x4 qtr[NCT];
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) {
+      const int c = 16 * n + lr;
+      qtr[n] = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, g));
+    }
+    if (issue_next) issue(qt + 2, nbuf, G2{}, G3{});
+    // the copies of tile qt+1 (issued one step ago) must have landed before the barrier that
+    // publishes them; issued after them: last step's stores, this step's copies
+    wait_copies_then<kStores, L::kCpHi>(issue_next, cp_hi);
+    lds_barrier();
+
+    // ---- dS codes on the 64 x BLK tile, dK^T += Q^T dS
+    float da = redD[(step & 1) * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) da = fmaxf(da, redD[(step & 1) * NW + i]);
+    da = fmaxf(da, FLT_MIN);
+    const float dinv = 127.0f * __builtin_amdgcn_rcpf(da);
+    const float sdS = da * (1.0f / 127.0f);
+    i32x4 dc;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      dc[t] = (int)pack4_lo_bytes(quant_word_fma(dsf[t][0], dinv), quant_word_fma(dsf[t][1], dinv),
+                                  quant_word_fma(dsf[t][2], dinv), quant_word_fma(dsf[t][3], dinv));
+    {
       const float sk = smc * sdS * sQ;
 #pragma unroll
-      for (int i = 0; i < DCH; ++i) {
-        const int c = 32 * (DCH * h + i) + lk;
-        const i32x4 a0 = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, 2 * h + g));
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, 2 * (1 - h) + g));
-        i32x16 acc = mfma_i8_32x32x32(a0, dc, i32x16{});
-        acc = mfma_i8_32x32x32(a1, dco, acc);
+      for (int n = 0; n < NCT; ++n) {
+        const i32x4 acc = mfma_i8_16x16x64(qtr[n], dc, i32x4{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dk[i][r] += sk * (float)acc[r];
+        for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(sk, (float)acc[r], dk[n][r]);
       }
     }
 
     if constexpr (SPILL) {
-      // ---- spill the dS tile (query-major, rows swizzled) and its dQ multiplier; the
-      //      query-major dQ pass contracts it with K
+      // ---- the dS^T tile [BLK][64] for the query-major dQ pass: key row kl, chunk g (queries
+      //      in the contraction order above) at slot swz<64>(kl, g); and its dQ multiplier
       const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt);
-      int8_t* dst = a.dsp + ti * (kTq * BLK);
-      for (int ch = tid; ch < kTq * BLK / 16; ch += NT) {
-        const int r = ch / (BLK / 16), j = ch % (BLK / 16);
-        *reinterpret_cast<i32x4*>(dst + r * BLK + 16 * swz<BLK>(r, j)) =
-            *reinterpret_cast<const i32x4*>(lds + L::offDS + r * L::kRowS + 16 * j);
-      }
-      if (tid == 0) a.dsm[ti] = smc * sdS * sK;
-      // the next tile's copies were issued before these (at most 2) stores; in-order
-      // completion makes this wait for every copy
-      wait_vmcnt<2>();
+      *reinterpret_cast<i32x4*>(a.dsp + ti * (kTq * BLK) + kl * kTq + 16 * swz<kTq>(kl, g)) = dc;
+      if (l == 0) a.dsm[ti] = smc * sdS * sK;   // every wave stores the same value
     } else {
-      // ---- dQ = dS K over the BLK keys: 2 x DC output tiles of 32 x 32, split over the
-      //      waves, added to the float32 accumulator with atomics
-      const float sc = smc * sdS * sK;
-      for (int tile = w; tile < 2 * DC; tile += NW) {
-        const int u = tile / DC, ct = tile % DC;
-        i32x16 acc = i32x16{};
+      // ---- dQ = dS K on the 64 x BLK tile, added to the float32 accumulator with atomics:
+      //      the dS^T tile goes through LDS once and is read back query by query (transposing
+      //      reads); wave w computes query group u = w % 4 for its share of the channel tiles
+      *reinterpret_cast<i32x4*>(lds + L::offDST + kl * kTq + 16 * swz<kTq>(kl, g)) = dc;
+      lds_barrier();
+      const int u = w % 4, n0 = (w / 4) * NCTW;
+      i32x4 acc[NCTW];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const i32x4 as = *reinterpret_cast<const i32x4*>(lds + L::offDS + (32 * u + lk) * L::kRowS + 32 * kc + 16 * g);
-          const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + (32 * ct + lk) * L::kRowS + 32 * kc + 16 * g);
-          acc = mfma_i8_32x32x32(as, bk, acc);
+      for (int n = 0; n < NCTW; ++n) acc[n] = i32x4{};
+#pragma unroll
+      for (int kc = 0; kc < BLK / 64; ++kc) {
+        const int i = lr >> 1, hh = l & 1;
+        const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
+        const i32x2 x0 = lds_read_tr8(lds + L::offDST + r0 * kTq + 16 * swz<kTq>(r0, u) + 8 * hh);
+        const i32x2 x1 = lds_read_tr8(lds + L::offDST + r1 * kTq + 16 * swz<kTq>(r1, u) + 8 * hh);
+        const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+        for (int n = 0; n < NCTW; ++n) {
+          const int c = 16 * (n0 + n) + lr;
+          const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
+          acc[n] = mfma_i8_16x16x64(as, bk, acc[n]);
         }
-        // result lane: channel 32ct + lk, query 32u + 8(r/4) + 4g + r%4
-        float* dst = a.dq_acc + (hrow + q0 + 32 * u + 4 * g) * D + 32 * ct + lk;
+      }
+      // result: query position 16u + 4g + r = query 16g + 4u + r of the tile, channel 16n + lr
+      const float sc = smc * sdS * sK;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          unsafeAtomicAdd(dst + (size_t)(8 * (r >> 2) + (r & 3)) * D, sc * (float)acc[r]);
-      }
-      // The next tile's copies were issued before this iteration's dQ atomics; vector memory
-      // operations complete in issue order, so allowing the atomics (16 per dQ tile) to stay
-      // outstanding still waits for every copy.
-      if constexpr (2 * DC <= NW) {
-        if (w < 2 * DC) wait_vmcnt<16>();
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<16 * ((2 * DC) / NW)>();
-      }
+      for (int n = 0; n < NCTW; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          unsafeAtomicAdd(a.dq_acc + (hrow + q0 + 16 * g + 4 * u + r) * D + 16 * (n0 + n) + lr, sc * (float)acc[n][r]);
     }
-    lds_barrier();
+    bi = bi == 2 ? 0 : bi + 1;
   }
 
-  // ---- epilogue: dV and dK (RMSNorm backward with K^ = K * rstd) for this lane's key, half h
+  // ---- epilogue: dV and dK (RMSNorm backward with K^ = K * rstd) for this lane's key;
+  //      lane group g holds channels 16n + 4g + r
   unsigned short* dvrow = a.dV + (hrow + key) * D;
 #pragma unroll
-  for (int i = 0; i < DCH; ++i)
+  for (int n = 0; n < NCT; ++n) {
+    u16x4 v;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = from_f32<DT>(dv[i][4 * j + e]);
-      *reinterpret_cast<u16x4*>(dvrow + 32 * (DCH * h + i) + 8 * j + 4 * g) = v;
-    }
+    for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dv[n][r]);
+    *reinterpret_cast<u16x4*>(dvrow + 16 * n + 4 * g) = v;
+  }
   unsigned short* dkrow = a.dK + (hrow + key) * D;
   if (a.qk_norm) {
     const float rs = a.k_rstd[hrow + key];
     const unsigned short* krow = a.K + (hrow + key) * D;
-    float kh[DCH][16];
+    float kh[NCT][4];
     float dot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < DCH; ++i)
+    for (int n = 0; n < NCT; ++n) {
+      const u16x4 kv = *reinterpret_cast<const u16x4*>(krow + 16 * n + 4 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u16x4 kv = *reinterpret_cast<const u16x4*>(krow + 32 * (DCH * h + i) + 8 * j + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kh[i][4 * j + e] = to_f32<DT>(kv[e]) * rs;
-          dot = __builtin_fmaf(dk[i][4 * j + e], kh[i][4 * j + e], dot);
-        }
+      for (int r = 0; r < 4; ++r) {
+        kh[n][r] = to_f32<DT>(kv[r]) * rs;
+        dot = __builtin_fmaf(dk[n][r], kh[n][r], dot);
       }
-    float* dots = reinterpret_cast<float*>(lds + L::offDOT);
-    dots[w * 64 + l] = dot;
-    lds_barrier();
-    dot += dots[partner * 64 + l];
+    }
+    dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
     const float mean = dot / (float)D;
 #pragma unroll
-    for (int i = 0; i < DCH; ++i)
+    for (int n = 0; n < NCT; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dk[i][r] = rs * (dk[i][r] - kh[i][r] * mean);
+      for (int r = 0; r < 4; ++r) dk[n][r] = rs * (dk[n][r] - kh[n][r] * mean);
   }
 #pragma unroll
-  for (int i = 0; i < DCH; ++i)
+  for (int n = 0; n < NCT; ++n) {
+    u16x4 v;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = from_f32<DT>(dk[i][4 * j + e]);
-      *reinterpret_cast<u16x4*>(dkrow + 32 * (DCH * h + i) + 8 * j + 4 * g) = v;
-    }
+    for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dk[n][r]);
+    *reinterpret_cast<u16x4*>(dkrow + 16 * n + 4 * g) = v;
+  }
 }
 
 // ------------------------------------------------------------------------------ bwd_dq
-// Query-major dQ pass over the spilled dS tiles: one workgroup (4 waves) per (head, 64-query
-// tile). For every key block up to the diagonal, the tile's dS codes [64][BLK] and the block's
-// K^T codes [D][BLK] stream through double-buffered LDS (buffer->LDS copies), and
-// dQ^ += m(kb) * (dS_codes . K_codes) runs on v_mfma_i32_32x32x32_i8 with float32 accumulation
-// in registers (m = sm_scale * s_dS * s_K of the tile). The epilogue applies the RMSNorm
+// Query-major dQ pass over the spilled dS^T tiles: one workgroup (4 waves) per (head, 64-query
+// tile). For every key block up to the diagonal, the tile's dS^T codes [BLK][64] and the
+// block's K^T codes [D][BLK] stream through double-buffered LDS (buffer->LDS copies), and
+// dQ^ += m(kb) * (dS_codes . K_codes) runs on v_mfma_i32_16x16x64_i8 with float32
+// accumulation in registers (m = sm_scale * s_dS * s_K of the tile). The A operand (rows =
+// queries, contraction = keys) comes from the key-major dS^T tile through transposing LDS
+// reads. Wave w computes query positions 16w..16w+15 of the spilled order (position
+// 16g + 4t + r is query 16t + 4g + r) against all channels. The epilogue applies the RMSNorm
 // backward and writes dQ in the dtype; no float32 dQ buffer and no atomics.
 template <int D, int BLK>
 struct DqLds {
-  static constexpr int bDS = 0;                     // dS codes [64][BLK], rows swizzled
+  static constexpr int bDS = 0;                     // dS^T codes [BLK][64], rows swizzled
   static constexpr int bKT = 64 * BLK;              // K^T codes [D][BLK], rows swizzled
   static constexpr int bM = bKT + D * BLK;          // tile multiplier (first word)
   static constexpr int kBuf = bM + 1024;
@@ -546,14 +568,13 @@ struct DqLds {
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   using L = DqLds<D, BLK>;
-  constexpr int DC = D / 32, KC = BLK / 32;
-  constexpr int TPW = (2 * DC) / 4;                 // 32 x 32 output tiles per wave
+  constexpr int NCT = D / 16;                       // 16-channel output tiles
   __shared__ __attribute__((aligned(16))) int8_t lds[L::kBytes];
   const int ntile = a.N / kTq, nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
   const int qt = a.causal ? ntile - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);
   const int q0 = qt * kTq;
-  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 5, lk = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 4, lr = l & 15;
   const int kb_last = a.causal ? (q0 + kTq - 1) / BLK : nb - 1;
   const int8_t* dsh = a.dsp + (size_t)bh * a.spill_tiles * (kTq * BLK);
   const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kTq * BLK));
@@ -573,9 +594,9 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
     if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4), buf + L::bM, 4 * l, (uint32_t)(ti * 4));
   };
 
-  f32x16 dq[TPW];
+  f32x4 dq[NCT];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) dq[i] = f32x16{};
+  for (int i = 0; i < NCT; ++i) dq[i] = f32x4{};
   issue(0, lds);
   wait_vmcnt<0>();
   __syncthreads();
@@ -583,31 +604,38 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
     int8_t* buf = lds + (kb & 1) * L::kBuf;
     if (kb < kb_last) issue(kb + 1, lds + ((kb & 1) ^ 1) * L::kBuf);
     const float m = *reinterpret_cast<const float*>(buf + L::bM);
+    i32x4 acc[NCT];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tile = w + 4 * i, u = tile / DC, ct = tile % DC;
-      const int qr = 32 * u + lk, cr = 32 * ct + lk;
-      i32x16 acc = i32x16{};
+    for (int n = 0; n < NCT; ++n) acc[n] = i32x4{};
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const i32x4 as = *reinterpret_cast<const i32x4*>(buf + L::bDS + qr * BLK + 16 * swz<BLK>(qr, 2 * kc + g));
-        const i32x4 bk = *reinterpret_cast<const i32x4*>(buf + L::bKT + cr * BLK + 16 * swz<BLK>(cr, 2 * kc + g));
-        acc = mfma_i8_32x32x32(as, bk, acc);
+    for (int kc = 0; kc < BLK / 64; ++kc) {
+      // A: keys 64kc + 16g .. +15 of query position 16w + lr, two transposing reads of 8 keys
+      const int i = lr >> 1, hh = l & 1;
+      const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
+      const i32x2 x0 = lds_read_tr8(buf + L::bDS + r0 * kTq + 16 * swz<kTq>(r0, w) + 8 * hh);
+      const i32x2 x1 = lds_read_tr8(buf + L::bDS + r1 * kTq + 16 * swz<kTq>(r1, w) + 8 * hh);
+      const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+      for (int n = 0; n < NCT; ++n) {
+        const int c = 16 * n + lr;
+        const i32x4 bk = *reinterpret_cast<const i32x4*>(buf + L::bKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
+        acc[n] = mfma_i8_16x16x64(as, bk, acc[n]);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dq[i][r] += m * (float)acc[r];
     }
+#pragma unroll
+    for (int n = 0; n < NCT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dq[n][r] = __builtin_fmaf(m, (float)acc[n][r], dq[n][r]);
     wait_vmcnt<0>();   // the next key block's copies (the only vector-memory operations here)
     lds_barrier();
   }
-  // ---- epilogue: dQ^ tile to LDS [64][D] f32, then RMSNorm backward row by row
+  // ---- epilogue: dQ^ tile to LDS [64][D] f32 (position 16w + 4g + r = query 16g + 4w + r),
+  //      then RMSNorm backward row by row
   float* t = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tile = w + 4 * i, u = tile / DC, ct = tile % DC;
+  for (int n = 0; n < NCT; ++n)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[(32 * u + 8 * (r >> 2) + 4 * g + (r & 3)) * D + 32 * ct + lk] = dq[i][r];
-  }
+    for (int r = 0; r < 4; ++r) t[(16 * g + 4 * w + r) * D + 16 * n + lr] = dq[n][r];
   __syncthreads();
   constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
   const size_t hrow = (size_t)bh * a.N;

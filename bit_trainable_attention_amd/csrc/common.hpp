@@ -8,8 +8,10 @@
 
 namespace sagebwd {
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,14 +54,71 @@ template <> __device__ __forceinline__ f32x16 mfma_16b_32x32x16<DT_BF16>(u16x8 a
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16 x 16 products (checked on the hardware): lane l, register r of the result hold row
+// 4*(l/16) + r and column l%16. Operand A: lane l holds row l%16; operand B: column l%16;
+// lane group l/16 supplies the same contraction slots to both (16 bytes for the INT8 form,
+// 8 16-bit values for the 16-bit form).
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+template <int DT> __device__ __forceinline__ f32x4 mfma_16b_16x16x32(u16x8 a, u16x8 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mfma_16b_16x16x32<DT_FP16>(u16x8 a, u16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma_16b_16x16x32<DT_BF16>(u16x8 a, u16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b8). Inside each group of 16 lanes, lanes 2i and 2i+1
+// name the two 8-byte halves of "row" i (i = 0..7); lane j of the group receives byte j of
+// every row: result byte i = byte (j % 8) at the address of lane 2i + j/8 (checked on the
+// hardware). Reading a 16-byte column block of 8 rows thus hands each lane one column.
+__device__ __forceinline__ i32x2 lds_read_tr8(const int8_t* p) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Max over the 64 lanes (wave-uniform result). Floats are compared as integers: flipping
+// the magnitude bits of negative values makes signed-integer order equal float order (for
+// everything but NaN), so each butterfly step is one v_max_i32 with a DPP source (quad swaps,
+// then row rotations by 4 and 8) and needs no NaN canonicalisation. The four row maxima are
+// read out with v_readlane and combined on the scalar unit.
+__device__ __forceinline__ int float_order_key(float x) {
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+template <int CTRL>
+__device__ __forceinline__ int imax_dpp(int v) {
+  return max(v, __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  int v = float_order_key(x);
+  v = imax_dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = imax_dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = imax_dpp<0x124>(v);  // row_ror:4
+  v = imax_dpp<0x128>(v);  // row_ror:8 -> every lane of a row holds the row max
+  const int m = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                    max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return __int_as_float(m ^ ((m >> 31) & 0x7FFFFFFF));
+}
+// Two independent wave maxima, their butterfly steps interleaved so that each chain's DPP
+// wait states are filled by the other chain.
+__device__ __forceinline__ void wave_max2(float& x, float& y) {
+  int u = float_order_key(x), v = float_order_key(y);
+  u = imax_dpp<0xB1>(u);  v = imax_dpp<0xB1>(v);
+  u = imax_dpp<0x4E>(u);  v = imax_dpp<0x4E>(v);
+  u = imax_dpp<0x124>(u); v = imax_dpp<0x124>(v);
+  u = imax_dpp<0x128>(u); v = imax_dpp<0x128>(v);
+  const int mu = max(max(__builtin_amdgcn_readlane(u, 0), __builtin_amdgcn_readlane(u, 16)),
+                     max(__builtin_amdgcn_readlane(u, 32), __builtin_amdgcn_readlane(u, 48)));
+  const int mv = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                     max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  x = __int_as_float(mu ^ ((mu >> 31) & 0x7FFFFFFF));
+  y = __int_as_float(mv ^ ((mv >> 31) & 0x7FFFFFFF));
 }
 
 // Pack the low bytes of four 32-bit words into one word (byte i <- word i).

@@ -18,7 +18,9 @@
  *     (TurboQuant blog, FlashAttention section).
  *
  * In-kernel quantisation tiles (P~ in the forward, P and dS in the backward) use the same
- * absmax/127 rule, decided in float32:
+ * absmax/127 rule in float32, except that the kernels take 127/absmax from the hardware
+ * reciprocal and round x * (127/absmax) once (fused), so a code can differ from the rule's
+ * by one at a near-tie; these codes stay inside the kernels:
  *   P~ (forward)   : SAGEBWD_FWD_TILE_Q query rows x blk keys; the online-softmax running
  *                    max moves once per such tile and P~ = exp(s - running max); the row
  *                    sum l accumulates P~ before quantisation.
@@ -53,7 +55,7 @@ extern "C" {
 
 #define SAGEBWD_FWD_TILE_Q 32
 #define SAGEBWD_BWD_TILE_Q 64
-#define SAGEBWD_BWD_P_TILE_K 32
+#define SAGEBWD_BWD_P_TILE_K 16
 
 typedef enum {
   SAGEBWD_OK = 0,
@@ -136,8 +138,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *                   j^((r>>1)&3) (d = 64)
  *     [64d, 192d)   dO [64][d], 16-bit; chunk j of row r stored at chunk j^(r&7)
  *     [192d, 256d)  dO INT8 codes, channel-major [d][64]: token u of row c at byte
- *                   32*(u>>5) + 16*((u>>2)&1) + 4*((u&31)>>3) + (u&3), then chunk j of
- *                   row c stored at chunk j^((c>>1)&3)
+ *                   16*((u>>2)&3) + 4*(u>>4) + (u&3), then chunk j of row c stored at
+ *                   chunk j^((c>>1)&3)
  *     [256d, 320d)  Q codes, channel-major, same order as the dO codes
  *     [320d, +256)  lse * log2(e), float32 [64]
  *     [+256, +512)  D = rowsum(dO o O), float32 [64]
@@ -150,8 +152,10 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *   ktp     [B,H,N/blk] x d*blk      K codes of each key block, channel-major [d][blk];
  *                                    chunk j of row c stored at chunk j^(c&7) (blk = 128)
  *                                    or j^((c>>1)&3) (blk = 64)
- *   dsp     [B,H,T] x 64*blk         INT8 dS codes of each tile, query-major [64][blk],
- *                                    chunk j of row r stored as for ktp
+ *   dsp     [B,H,T] x 64*blk         INT8 dS codes of each tile, key-major [blk][64]:
+ *                                    token u of the query tile at byte position
+ *                                    16*((u>>2)&3) + 4*(u>>4) + (u&3) of the key's row,
+ *                                    then chunk j of row k stored at chunk j^((k>>1)&3)
  *   dsm     float32 [B,H,T]          sm_scale * (dS tile scale) * (K block scale)
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);

@@ -65,7 +65,7 @@ class Spec:
     fwd_tq: int = 32
     fwd_tk: Optional[int] = None
     bwd_tq: int = 64
-    bwd_pk: int = 32
+    bwd_pk: int = 16
     bwd_sk: Optional[int] = None
 
     def __post_init__(self):

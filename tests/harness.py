@@ -117,7 +117,7 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
     slot_of = np.arange(4)[None, :] ^ ((c[:, None] >> 1) & 3)                        # logical chunk -> slot
     logical = np.take_along_axis(rows, slot_of[None, None, None, :, :, None], axis=-2).reshape(w.B, w.H, nt, d, 64)
     u = np.arange(64)
-    pos = 32 * (u >> 5) + 16 * ((u >> 2) & 1) + 4 * ((u & 31) >> 3) + (u & 3)
+    pos = 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
     codes = logical[..., pos]                                                         # [B,H,nt,d,64]
     dOtc = np.moveaxis(codes, 2, 3).reshape(w.B, w.H, d, w.N)
     base = 320 * d
