@@ -5,17 +5,25 @@
 //
 // The results are specified bit for bit (include/sagebwd.h): every float32 operation
 // below is one IEEE operation with round-to-nearest-even, no contraction into FMA,
-// sums in ascending index order, correctly rounded division and square root.
+// correctly rounded division and square root, and every sum runs in the stated order.
 //
-// Pass 1, one workgroup per (head, token block, tensor):
-//   Q: rstd per token, Q^ = Q*rstd, block absmax, codes (token-major).
-//   K: rstd per token; with smoothing, the block's per-channel sums of K^ (pass 2
-//      quantises); without smoothing, codes of K^ as for Q.
-//   V: block absmax, codes written channel-major (V^T), as the forward's PV product reads it.
-// Pass 2 (smoothing only), one workgroup per (head, token block): mean = sum of the block
-//   sums / N, K~ = K^ - mean, block absmax, codes.
-// Each block is staged once through LDS as float32 rows of D+1 words, so that a thread
-// walking its own token row and a thread walking a channel column both hit distinct banks.
+// Thread layout of a (head, block of BLK tokens) workgroup, 256 threads: thread (j, ch),
+// j = tid / 16 (token slot), ch = tid % 16 (channel chunk), owns channels
+// ch*CW .. ch*CW + CW - 1 (CW = D/16) of tokens t = 16p + j, p = 0 .. BLK/16 - 1, in
+// registers. The 16 chunks of a token sit in one 16-lane row, so the token's sum of squares
+// is each lane's chunk sum (ascending) followed by a pairwise tree across the row (DPP):
+// xor 1, xor 2, then the half-row and row mirrors, which pair chunk blocks {0-3, 4-7} and
+// {0-7, 8-15}. Float addition is commutative, so both lanes of a pair compute the same sum
+// and every lane ends with the tree's result.
+//
+// pass1  one workgroup per (head, block, tensor):
+//          Q: rstd, Q^ = Q*rstd, block absmax, codes (token-major);
+//          K: rstd; with smoothing, the block's per-channel sums of K^ (group t mod 16 in
+//             ascending order, then the pairwise tree over the 16 groups); without, codes;
+//          V: block absmax, codes written channel-major (V^T) through an LDS byte tile.
+// k_mean (smoothing only) one thread per (head, channel): block sums in ascending block
+//          order, / N.
+// pass2  (smoothing only) one workgroup per (head, block): K~ = K^ - mean, absmax, codes.
 #pragma clang fp contract(off)
 
 #include "common.hpp"
@@ -27,181 +35,244 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Per-thread slice of a block: P tokens x CW channels.
 template <int D, int BLK>
-struct ProLds {
-  float x[BLK][D + 1];
-  float rstd[BLK];
-  float red[kThreads / 64];
-  float mu[D];
+struct Slice {
+  static constexpr int CW = D / 16;
+  static constexpr int P = BLK / 16;
+  float x[P][CW];
 };
 
-// Block absmax over the whole workgroup (exact: max is order independent).
-__device__ __forceinline__ float block_absmax(float v, float* red) {
-  v = wave_max(v);
-  if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
-  float r = red[0];
+template <int DT, int CW>
+__device__ __forceinline__ void load_chunk(const unsigned short* __restrict__ src, float* x) {
+  if constexpr (CW == 8) {
+    const u16x8 v = *reinterpret_cast<const u16x8*>(src);
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
-  return r;
-}
-
-// Coalesced load of a BLK x D block of 16-bit values into LDS as float32.
-template <int DT, int D, int BLK>
-__device__ __forceinline__ void load_block(const unsigned short* __restrict__ src, ProLds<D, BLK>& s) {
-  constexpr int kChunks = BLK * D / 8;  // 8 values (16 bytes) per chunk
+    for (int i = 0; i < 8; ++i) x[i] = to_f32<DT>(v[i]);
+  } else {
+    static_assert(CW == 4, "chunk width");
+    const u16x4 v = *reinterpret_cast<const u16x4*>(src);
 #pragma unroll
-  for (int ch = threadIdx.x; ch < kChunks; ch += kThreads) {
-    u16x8 v = *reinterpret_cast<const u16x8*>(src + (size_t)ch * 8);
-    const int t = (ch * 8) / D, c = (ch * 8) % D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s.x[t][c + i] = to_f32<DT>(v[i]);
+    for (int i = 0; i < 4; ++i) x[i] = to_f32<DT>(v[i]);
   }
 }
 
-// rstd of every token row of s.x (threads t < BLK), ascending channel order.
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void load_slice(const unsigned short* __restrict__ blk_src, Slice<D, BLK>& s, int j,
+                                           int ch) {
+#pragma unroll
+  for (int p = 0; p < Slice<D, BLK>::P; ++p)
+    load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * D + ch * Slice<D, BLK>::CW, s.x[p]);
+}
+
+// Sum of the 16 lanes of each row by the pairwise tree (xor 1, xor 2, half mirror, mirror).
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_tree_sum(float v) {
+  v = add_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = add_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = add_dpp<0x141>(v);  // row_half_mirror: chunks 0-3 with 4-7 (and 8-11 with 12-15)
+  v = add_dpp<0x140>(v);  // row_mirror: chunks 0-7 with 8-15
+  return v;
+}
+
+// QK-norm of the thread's tokens in place; lane ch == 0 writes rstd of each token.
 template <int D, int BLK>
-__device__ __forceinline__ void token_rstd(ProLds<D, BLK>& s, float eps, float* __restrict__ rstd_out) {
-  const int t = threadIdx.x;
-  if (t < BLK) {
-    float ss = 0.0f;
-    for (int c = 0; c < D; ++c) {
-      const float v = s.x[t][c];
-      ss = ss + v * v;
+__device__ __forceinline__ void qk_norm_slice(Slice<D, BLK>& s, float eps, float* __restrict__ rstd_out, int j,
+                                              int ch) {
+  using S = Slice<D, BLK>;
+#pragma unroll
+  for (int p = 0; p < S::P; ++p) {
+    float cs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) {
+      const float sq = s.x[p][i] * s.x[p][i];
+      cs = cs + sq;
     }
+    const float ss = row_tree_sum(cs);
     const float ms = ss / (float)D;
     const float r = 1.0f / __builtin_sqrtf(ms + eps);
-    s.rstd[t] = r;
-    rstd_out[t] = r;
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) s.x[p][i] = s.x[p][i] * r;
+    if (ch == 0) rstd_out[16 * p + j] = r;
   }
 }
 
-// Quantise s.x (already the values to quantise) as one block; codes token-major.
+// Block absmax over the workgroup (exact: max is order independent).
 template <int D, int BLK>
-__device__ __forceinline__ void quant_token_major(ProLds<D, BLK>& s, int8_t* __restrict__ codes,
-                                                  float* __restrict__ scale_out) {
-  constexpr int kWords = BLK * D / 4;
+__device__ __forceinline__ float slice_absmax(const Slice<D, BLK>& s, float* red) {
   float m = 0.0f;
-  for (int w = threadIdx.x; w < kWords; w += kThreads) {
-    const int t = (w * 4) / D, c = (w * 4) % D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(s.x[t][c + i]));
-  }
-  const float a = block_absmax(m, s.red);
+  for (int p = 0; p < Slice<D, BLK>::P; ++p)
+#pragma unroll
+    for (int i = 0; i < Slice<D, BLK>::CW; ++i) m = fmaxf(m, fabsf(s.x[p][i]));
+  m = wave_max(m);
+  if (lane_id() == 0) red[wave_id()] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Codes of the thread's values under the block's absmax a, token-major; scale a/127.
+template <int D, int BLK>
+__device__ __forceinline__ void quant_slice_token_major(const Slice<D, BLK>& s, float a, int8_t* __restrict__ blk_codes,
+                                                        float* __restrict__ scale_out, int j, int ch) {
+  using S = Slice<D, BLK>;
   const float inv = a > 0.0f ? 127.0f / a : 0.0f;
   if (threadIdx.x == 0) *scale_out = a > 0.0f ? a / 127.0f : 0.0f;
-  for (int w = threadIdx.x; w < kWords; w += kThreads) {
-    const int t = (w * 4) / D, c = (w * 4) % D;
-    const unsigned word = pack4_lo_bytes(quant_word(s.x[t][c], inv), quant_word(s.x[t][c + 1], inv),
-                                         quant_word(s.x[t][c + 2], inv), quant_word(s.x[t][c + 3], inv));
-    reinterpret_cast<unsigned*>(codes)[w] = word;
+#pragma unroll
+  for (int p = 0; p < S::P; ++p) {
+    int8_t* dst = blk_codes + (size_t)(16 * p + j) * D + ch * S::CW;
+    const unsigned w0 = pack4_lo_bytes(quant_word(s.x[p][0], inv), quant_word(s.x[p][1], inv),
+                                       quant_word(s.x[p][2], inv), quant_word(s.x[p][3], inv));
+    if constexpr (S::CW == 8) {
+      const unsigned w1 = pack4_lo_bytes(quant_word(s.x[p][4], inv), quant_word(s.x[p][5], inv),
+                                         quant_word(s.x[p][6], inv), quant_word(s.x[p][7], inv));
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else {
+      *reinterpret_cast<unsigned*>(dst) = w0;
+    }
   }
 }
+
+template <int D, int BLK>
+struct Pass1Lds {
+  float red[kThreads / 64];
+  union {
+    float gs[16][D];                               // K: group sums per token slot
+    int8_t vt[D][BLK + 16];                        // V: codes, channel-major
+  };
+};
 
 }  // namespace
 
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
-  __shared__ ProLds<D, BLK> s;
+  using S = Slice<D, BLK>;
+  __shared__ __attribute__((aligned(16))) Pass1Lds<D, BLK> lds;
   const int nb = a.N / BLK;
   const int tensor = blockIdx.x % 3;          // 0 = Q, 1 = K, 2 = V
   const int blk_id = (blockIdx.x / 3) % nb;
   const int bh = (blockIdx.x / 3) / nb;
   const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;   // first token row of the block
   const size_t sidx = (size_t)bh * nb + blk_id;                    // scale index
+  const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
-  const unsigned short* src = (tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + tok0 * D;
-  load_block<DT, D, BLK>(src, s);
-  __syncthreads();
+  S s;
+  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + tok0 * D, s, j, ch);
 
   if (tensor == 2) {
     // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token].
-    constexpr int kWords = BLK * D / 4;
-    float m = 0.0f;
-    for (int w = threadIdx.x; w < kWords; w += kThreads) {
-      const int t = (w * 4) / D, c = (w * 4) % D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(s.x[t][c + i]));
-    }
-    const float amax = block_absmax(m, s.red);
+    const float amax = slice_absmax<D, BLK>(s, lds.red);
     const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
     if (threadIdx.x == 0) a.Vs[sidx] = amax > 0.0f ? amax / 127.0f : 0.0f;
-    for (int w = threadIdx.x; w < kWords; w += kThreads) {
-      const int c = w / (BLK / 4), t = 4 * (w % (BLK / 4));
-      const unsigned word = pack4_lo_bytes(quant_word(s.x[t][c], inv), quant_word(s.x[t + 1][c], inv),
-                                           quant_word(s.x[t + 2][c], inv), quant_word(s.x[t + 3][c], inv));
-      int8_t* dst = a.Vtc + ((size_t)bh * D + c) * a.N + (size_t)blk_id * BLK + t;
-      *reinterpret_cast<unsigned*>(dst) = word;
+#pragma unroll
+    for (int p = 0; p < S::P; ++p)
+#pragma unroll
+      for (int i = 0; i < S::CW; ++i)
+        lds.vt[ch * S::CW + i][16 * p + j] = (int8_t)quant_word(s.x[p][i], inv);
+    __syncthreads();
+    constexpr int kRowChunks = BLK / 16;
+    for (int e = threadIdx.x; e < D * kRowChunks; e += kThreads) {
+      const int c = e / kRowChunks, q = e % kRowChunks;
+      *reinterpret_cast<i32x4*>(a.Vtc + ((size_t)bh * D + c) * a.N + (size_t)blk_id * BLK + 16 * q) =
+          *reinterpret_cast<const i32x4*>(&lds.vt[c][16 * q]);
     }
     return;
   }
 
   float* rstd_out = (tensor == 0 ? a.q_rstd : a.k_rstd) + tok0;
   if (a.qk_norm) {
-    token_rstd<D, BLK>(s, a.eps, rstd_out);
-    __syncthreads();
-    for (int e = threadIdx.x; e < BLK * D; e += kThreads) {
-      const int t = e / D, c = e % D;
-      s.x[t][c] = s.x[t][c] * s.rstd[t];
-    }
-  } else {
-    if (threadIdx.x < BLK) rstd_out[threadIdx.x] = 1.0f;
+    qk_norm_slice<D, BLK>(s, a.eps, rstd_out, j, ch);
+  } else if (ch == 0) {
+#pragma unroll
+    for (int p = 0; p < S::P; ++p) rstd_out[16 * p + j] = 1.0f;
   }
-  __syncthreads();
 
   if (tensor == 1 && a.k_smooth) {
-    // Per-channel sum of the block's normalised keys, tokens in ascending order.
+    // Per-channel block sums of K^: group j (tokens t = j mod 16) in ascending order ...
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) {
+      float g = 0.0f;
+#pragma unroll
+      for (int p = 0; p < S::P; ++p) g = g + s.x[p][i];
+      lds.gs[j][ch * S::CW + i] = g;
+    }
+    __syncthreads();
+    // ... then the pairwise tree over the 16 groups.
     for (int c = threadIdx.x; c < D; c += kThreads) {
-      float part = 0.0f;
-      for (int t = 0; t < BLK; ++t) part = part + s.x[t][c];
-      a.kpart[sidx * D + c] = part;
+      float t8[8], t4[4], t2[2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t8[u] = lds.gs[2 * u][c] + lds.gs[2 * u + 1][c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t4[u] = t8[2 * u] + t8[2 * u + 1];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) t2[u] = t4[2 * u] + t4[2 * u + 1];
+      a.kpart[sidx * D + c] = t2[0] + t2[1];
     }
     return;
   }
-  if (tensor == 1) {
-    for (int c = threadIdx.x; c < D; c += kThreads)
-      if (blk_id == 0) a.k_mean[(size_t)bh * D + c] = 0.0f;
+  if (tensor == 1 && blk_id == 0) {
+    for (int c = threadIdx.x; c < D; c += kThreads) a.k_mean[(size_t)bh * D + c] = 0.0f;
   }
-  quant_token_major<D, BLK>(s, (tensor == 0 ? a.Qc : a.Kc) + tok0 * D, (tensor == 0 ? a.Qs : a.Ks) + sidx);
+  const float amax = slice_absmax<D, BLK>(s, lds.red);
+  quant_slice_token_major<D, BLK>(s, amax, (tensor == 0 ? a.Qc : a.Kc) + tok0 * D,
+                                  (tensor == 0 ? a.Qs : a.Ks) + sidx, j, ch);
+}
+
+// Mean over all tokens of the head: block sums in ascending block order, then / N.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prologue_k_mean(PrologueArgs a) {
+  const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= (size_t)a.BH * D) return;
+  const size_t bh = e / D;
+  const int c = (int)(e % D);
+  const int nb = a.N / a.BLK;
+  const float* part = a.kpart + bh * nb * D + c;
+  float tot = 0.0f;
+  for (int b = 0; b < nb; ++b) tot = tot + part[(size_t)b * D];
+  a.k_mean[e] = tot / (float)a.N;
 }
 
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
-  __shared__ ProLds<D, BLK> s;
+  using S = Slice<D, BLK>;
+  __shared__ float red[kThreads / 64];
   const int nb = a.N / BLK;
   const int blk_id = blockIdx.x % nb;
   const int bh = blockIdx.x / nb;
   const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;
   const size_t sidx = (size_t)bh * nb + blk_id;
+  const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
-  // Mean over all tokens of the head: block sums in ascending block order, then / N.
-  for (int c = threadIdx.x; c < D; c += kThreads) {
-    const float* part = a.kpart + (size_t)bh * nb * D + c;
-    float tot = 0.0f;
-    for (int b = 0; b < nb; ++b) tot = tot + part[(size_t)b * D];
-    const float mu = tot / (float)a.N;
-    s.mu[c] = mu;
-    if (blk_id == 0) a.k_mean[(size_t)bh * D + c] = mu;
+  S s;
+  load_slice<DT, D, BLK>(a.K + tok0 * D, s, j, ch);
+  float mu[S::CW];
+#pragma unroll
+  for (int i = 0; i < S::CW; ++i) mu[i] = a.k_mean[(size_t)bh * D + ch * S::CW + i];
+#pragma unroll
+  for (int p = 0; p < S::P; ++p) {
+    const float r = a.qk_norm ? a.k_rstd[tok0 + 16 * p + j] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) {
+      const float kh = s.x[p][i] * r;
+      s.x[p][i] = kh - mu[i];
+    }
   }
-  load_block<DT, D, BLK>(a.K + tok0 * D, s);
-  if (threadIdx.x < BLK) s.rstd[threadIdx.x] = a.qk_norm ? a.k_rstd[tok0 + threadIdx.x] : 1.0f;
-  __syncthreads();
-  for (int e = threadIdx.x; e < BLK * D; e += kThreads) {
-    const int t = e / D, c = e % D;
-    const float kh = s.x[t][c] * s.rstd[t];
-    s.x[t][c] = kh - s.mu[c];
-  }
-  __syncthreads();
-  quant_token_major<D, BLK>(s, a.Kc + tok0 * D, a.Ks + sidx);
+  const float amax = slice_absmax<D, BLK>(s, red);
+  quant_slice_token_major<D, BLK>(s, amax, a.Kc + tok0 * D, a.Ks + sidx, j, ch);
 }
 
 template <int DT, int D, int BLK>
 static hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st) {
   const int nb = a.N / BLK;
   const long long nblocks = (long long)a.BH * nb;
-  const hipError_t e = launch_kernel(&prologue_pass1<DT, D, BLK>, dim3((unsigned)(nblocks * 3)), dim3(kThreads), st, a);
+  hipError_t e = launch_kernel(&prologue_pass1<DT, D, BLK>, dim3((unsigned)(nblocks * 3)), dim3(kThreads), st, a);
   if (e != hipSuccess || !a.k_smooth) return e;
+  const long long mthreads = (long long)a.BH * D;
+  e = launch_kernel(&prologue_k_mean<D>, dim3((unsigned)((mthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, a);
+  if (e != hipSuccess) return e;
   return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)nblocks), dim3(kThreads), st, a);
 }
 

@@ -108,10 +108,14 @@ size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
  *   q_rstd, k_rstd out: float32 [B,H,N]  1/sqrt(mean(x^2)+eps) per token (1 if !qk_norm)
  *   k_mean   out: float32 [B,H,d]  the subtracted mean (0 if !k_smooth)
  *   workspace   : >= sagebwd_prologue_workspace_bytes(p) bytes (may be NULL if that is 0)
- * Bit-exact contract: per token, ss = sum over channels in ascending order of x*x in
- * float32; rstd = 1/sqrt(ss/d + eps) with correctly rounded float32 division and square
- * root; x^ = x*rstd; the mean sums each block's tokens in ascending order, then the block
- * sums in ascending order, then divides by N; K~ = K^ - mean; then the INT8 rule above. */
+ * Bit-exact contract: per token, the d channels form 16 chunks of d/16 consecutive
+ * channels; each chunk sums x*x in ascending channel order in float32, and ss is the
+ * pairwise tree of the 16 chunk sums ((c0+c1), (c2+c3), ..., then pairs of those, down to
+ * one); rstd = 1/sqrt(ss/d + eps) with correctly rounded float32 division and square
+ * root; x^ = x*rstd; the mean: inside each block, token t joins group t mod 16, each group
+ * sums its tokens in ascending order and the block sum is the same pairwise tree of the 16
+ * group sums; the block sums are then added in ascending block order and divided by N;
+ * K~ = K^ - mean; then the INT8 rule above. */
 sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
                                       const void* Q, const void* K, const void* V,
                                       int8_t* Qc, int8_t* Kc, int8_t* Vtc,

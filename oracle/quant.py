@@ -122,20 +122,41 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
 # Prologue, bit-specified in float32.
 # ----------------------------------------------------------------------------
 
+def tree_f32(s: np.ndarray) -> np.ndarray:
+    """Sum over the last axis (a power of two long) by a pairwise tree over consecutive
+    entries: (s0+s1), (s2+s3), ... then ((s0+s1)+(s2+s3)), ... down to one value, float32."""
+    s = np.asarray(s, dtype=F32)
+    n = s.shape[-1]
+    assert n >= 1 and n & (n - 1) == 0
+    while s.shape[-1] > 1:
+        s = s[..., 0::2] + s[..., 1::2]
+    return s[..., 0]
+
+
 def rms_norm_f32(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
     """QK-norm of each token vector (last axis), float32 op by op.
 
-    ss = 0; for c ascending: ss = fl(ss + x_c * x_c)   (x_c * x_c is exact for 16-bit x)
+    The d channels (a power of two) form n = min(16, d) chunks of d/n consecutive channels;
+    each chunk sum runs in ascending channel order, cs_j = fl(... fl(x_a*x_a +
+    x_{a+1}*x_{a+1}) ...) (each x*x is exact for 16-bit x), and ss = tree(cs_0..cs_{n-1}),
+    the pairwise tree of tree_f32. The pages fix no summation order;
+    this one is the one a 16-lane row of the GPU computes (each lane one chunk, then a
+    butterfly across the row).
     ms = fl(ss / d); rstd = fl(1 / fl(sqrt(fl(ms + eps)))); x^ = fl(x * rstd).
     Returns (x^, rstd). SageBwd article, QK-norm paragraph (RMSNorm per token, gain 1).
-    Pinned by: test_oracle_quant.py::test_rms_norm_* (hand example, error bound).
+    Pinned by: test_oracle_quant.py::test_rms_norm_* (hand example, order, error bound).
     """
     x = np.asarray(x, dtype=F32)
     d = x.shape[-1]
-    ss = np.zeros(x.shape[:-1], dtype=F32)
-    for c in range(d):
-        xc = x[..., c]
-        ss = ss + xc * xc
+    n = min(16, d)
+    cw = d // n
+    assert cw * n == d and n & (n - 1) == 0
+    xc = x.reshape(x.shape[:-1] + (n, cw))
+    cs = np.zeros(x.shape[:-1] + (n,), dtype=F32)
+    for i in range(cw):
+        v = xc[..., i]
+        cs = cs + v * v
+    ss = tree_f32(cs)
     ms = ss / F32(d)
     rstd = F32(1.0) / np.sqrt(ms + F32(eps))
     return x * rstd[..., None], rstd
@@ -144,19 +165,24 @@ def rms_norm_f32(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
 def k_smooth_f32(khat: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
     """K-smoothing: K~ = K^ - mu, mu = per-channel mean of K^ over the N tokens of a head.
 
-    Order: per block of blk tokens, part = sum of the block's tokens in ascending
-    order (from 0); tot = sum of the parts in ascending block order (from 0);
-    mu = fl(tot / N); K~ = fl(K^ - mu). Input [..., N, d]; returns (K~, mu [..., d]).
+    Order: inside each block of blk tokens (a power of two), token t joins group t mod G,
+    G = min(16, blk); each group sums its tokens in ascending order and part = tree of
+    the G group sums (tree_f32); then tot = sum of the
+    parts in ascending block order (from 0); mu = fl(tot / N); K~ = fl(K^ - mu). The
+    pages fix no order; this is the one the GPU's 16 token slots per pass compute.
+    Input [..., N, d]; returns (K~, mu [..., d]).
     SageBwd article, K-smoothing paragraph (axis: see module docstring).
     Pinned by: test_oracle_quant.py::test_k_smooth_* and the softmax-invariance tests.
     """
     khat = np.asarray(khat, dtype=F32)
     N, d = khat.shape[-2], khat.shape[-1]
     nb = N // blk
-    kb = khat.reshape(khat.shape[:-2] + (nb, blk, d))
-    part = np.zeros(khat.shape[:-2] + (nb, d), dtype=F32)
-    for t in range(blk):
-        part = part + kb[..., t, :]
+    G = min(16, blk)
+    kb = khat.reshape(khat.shape[:-2] + (nb, blk // G, G, d))    # [..., block, pass, slot, d]
+    gs = np.zeros(khat.shape[:-2] + (nb, G, d), dtype=F32)
+    for p_ in range(blk // G):
+        gs = gs + kb[..., p_, :, :]
+    part = tree_f32(np.moveaxis(gs, -2, -1))                       # [..., nb, d]
     tot = np.zeros(khat.shape[:-2] + (d,), dtype=F32)
     for b in range(nb):
         tot = tot + part[..., b, :]

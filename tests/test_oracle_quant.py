@@ -42,16 +42,28 @@ def test_rms_norm_hand_examples():
         np.testing.assert_array_equal(xh[0], np.array(case["xhat"], dtype=F32))
 
 
-def test_rms_norm_ascending_order():
-    """4096^2 = 2^24 absorbs each later 1 (round-half-even), so ss stays 2^24; an exact
-    or reordered sum would give 2^24 + 7 and a different float32 rstd."""
-    x = np.array([[4096.0, 1, 1, 1, 1, 1, 1, 1]], dtype=F32)
-    y = np.array([[4096.0, 0, 0, 0, 0, 0, 0, 0]], dtype=F32)
-    _, rx = oq.rms_norm_f32(x, 0.0)
-    _, ry = oq.rms_norm_f32(y, 0.0)
-    assert rx[0] == ry[0]
-    exact_ms = (2.0 ** 24 + 7) / 8
-    assert F32(1.0 / np.sqrt(exact_ms)) != rx[0]
+def test_rms_norm_chunk_tree_order():
+    """d = 128, x = [4096, 1 x 127]: chunk 0 (channels 0..7) starts at 4096^2 = 2^24 and
+    absorbs each of its seven 1s (2^24 + 1 rounds to even, 2^24); chunks 1..15 sum to 8.
+    The pairwise tree then stays exact: 2^24 + 8, + 16, + 32, + 64 -> ss = 2^24 + 120,
+    ms = 2^17 + 15/16 exactly. An ascending sum would give 2^24 and the exact sum
+    2^24 + 127; both give a different float32 rstd."""
+    x = np.ones((1, 128), dtype=F32)
+    x[0, 0] = 4096.0
+    _, r = oq.rms_norm_f32(x, 0.0)
+    ms = F32(2.0 ** 17 + 15.0 / 16.0)
+    assert r[0] == F32(1.0) / np.sqrt(ms)
+    assert r[0] != F32(1.0) / np.sqrt(F32(2.0 ** 17))               # ascending order
+    assert r[0] != F32(1.0 / np.sqrt((2.0 ** 24 + 127) / 128))       # exact sum
+
+
+def test_rms_norm_small_d_tree():
+    """d = 16 (one channel per chunk), x = [4096, 1 x 15]: the tree's first pair absorbs
+    the 1 (2^24), the others pair to 2, then 2^24 + 2, + 4, + 8 -> ss = 2^24 + 14."""
+    x = np.ones((1, 16), dtype=F32)
+    x[0, 0] = 4096.0
+    _, r = oq.rms_norm_f32(x, 0.0)
+    assert r[0] == F32(1.0) / np.sqrt(F32((2.0 ** 24 + 14) / 16))
 
 
 def test_rms_norm_error_bound():
@@ -71,6 +83,18 @@ def test_k_smooth_hand_examples():
         kt, mu = oq.k_smooth_f32(k, case["blk"])
         assert mu[0] == F32(case["mu"]), case
         np.testing.assert_array_equal(kt[:, 0], np.array(case["ktilde"], dtype=F32))
+
+
+def test_k_smooth_group_tree_order():
+    """One block of 32 tokens of one channel: token 0 = 2^24, tokens 1..31 = 1. Groups
+    t mod 16: group 0 = 2^24 + 1 -> 2^24 (tie to even), groups 1..15 = 2. The tree then
+    stays exact: 2^24 + 2, + 4, + 8, + 16 -> 2^24 + 30, so mu = (2^24 + 30) / 32 =
+    2^19 + 15/16 exactly (an ascending sum would give 2^24 / 32 = 2^19)."""
+    k = np.ones((32, 1), dtype=F32)
+    k[0, 0] = 2.0 ** 24
+    kt, mu = oq.k_smooth_f32(k, 32)
+    assert mu[0] == F32(2.0 ** 19 + 15.0 / 16.0)
+    assert kt[1, 0] == F32(1.0) - mu[0]
 
 
 def test_k_smooth_mean_zero():
