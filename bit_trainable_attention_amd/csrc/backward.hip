@@ -58,6 +58,18 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Sum over each 16-lane row, returned to every lane of the row (DPP butterfly).
+template <int CTRL>
+__device__ __forceinline__ float add_dpp_row(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = add_dpp_row<0xB1>(v);
+  v = add_dpp_row<0x4E>(v);
+  v = add_dpp_row<0x141>(v);
+  return add_dpp_row<0x140>(v);
+}
+
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -121,104 +133,180 @@ __device__ __forceinline__ long long spill_tile_index(int N, int blk, int causal
 }
 
 // ------------------------------------------------------------------------------ bwd_pre
+// One workgroup per (head, block of BLK tokens), 256 threads: thread (j, ch), j = tid / 16,
+// ch = tid % 16, owns channels ch*CW .. ch*CW + CW - 1 (CW = D/16) of the four consecutive
+// tokens 64q + 4j + k (k = 0..3) of every 64-token tile q of the block, in registers. The
+// 16 lanes of a row share their tokens, so D = rowsum(dO o O) is a DPP tree across the row,
+// and a thread's four codes of one channel are one word at the packet's permuted token
+// position. Channel-major rows (dO^T, Q^T, K^T codes) are assembled in an LDS byte tile.
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
   using P = Packet<D>;
-  __shared__ float xs[BLK][D + 1];
-  __shared__ __attribute__((aligned(16))) int8_t qs[BLK][D + 4];
-  __shared__ __attribute__((aligned(16))) int8_t ks[BLK][D + 4];
+  constexpr int CW = D / 16;                 // channels per thread
+  constexpr int NQ = BLK / kTq;              // 64-token tiles of the block
+  constexpr int TR = kTq + 4;                // LDS row stride of a transposed tile row (bytes)
+  constexpr int KR = BLK + 4;                // ... of the block's K^T rows
+  constexpr int kTile = NQ * D * TR > D * KR ? NQ * D * TR : D * KR;
+  __shared__ __attribute__((aligned(16))) int8_t tt[kTile];
   __shared__ float red[4];
   const int nb = a.N / BLK;
   const int blk_id = blockIdx.x % nb;
   const int bh = blockIdx.x / nb;
   const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 8;  // 16-byte dO chunks per row
+  const int tid = threadIdx.x, j = tid >> 4, ch = tid & 15;
+  const int c0 = ch * CW;
+  const int wpos = tile_token_pos(4 * j);    // packet position of tokens 4j..4j+3 (one word)
   // packet of the block's first 64-token tile
-  int8_t* pk0 = a.pk + ((size_t)bh * (a.N / kTq) + (size_t)blk_id * (BLK / kTq)) * P::kBytes;
+  int8_t* pk0 = a.pk + ((size_t)bh * (a.N / kTq) + (size_t)blk_id * NQ) * P::kBytes;
 
-  // dO, O: coalesced 8-element chunks; D via a segmented reduction over each row's chunks
+  // ---- dO (16-bit, straight into the packets), D = rowsum(dO o O), lse * log2(e)
+  float x[NQ][4][CW];
   float amax = 0.0f;
-  for (int ch = tid; ch < BLK * CPR; ch += 256) {
-    const int t = ch / CPR, j = ch % CPR, c = j * 8;
-    const u16x8 dv = *reinterpret_cast<const u16x8*>(a.dO + (tok0 + t) * D + c);
-    const u16x8 ov = *reinterpret_cast<const u16x8*>(a.O + (tok0 + t) * D + c);
-    int8_t* pk = pk0 + (t / kTq) * P::kBytes;
-    const int r = t % kTq;
-    *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, j)) = dv;
-    float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = to_f32<DT>(dv[i]);
-      xs[t][c + i] = x;
-      amax = fmaxf(amax, fabsf(x));
-      part = __builtin_fmaf(x, to_f32<DT>(ov[i]), part);
-    }
-    // CPR consecutive lanes share a row (CPR divides 64 and 256)
+  for (int q = 0; q < NQ; ++q) {
+    int8_t* pk = pk0 + q * P::kBytes;
 #pragma unroll
-    for (int o = CPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    if (j == 0) {
-      reinterpret_cast<float*>(pk + P::bDV)[r] = part;
-      reinterpret_cast<float*>(pk + P::bLSE)[r] = a.lse[tok0 + t] * kLog2e;
+    for (int k = 0; k < 4; ++k) {
+      const int r = 4 * j + k;                       // token inside the tile
+      const size_t tok = tok0 + kTq * q + r;
+      const unsigned short* dsrc = a.dO + tok * D + c0;
+      const unsigned short* osrc = a.O + tok * D + c0;
+      float part = 0.0f;
+      if constexpr (CW == 8) {
+        const u16x8 dv = *reinterpret_cast<const u16x8*>(dsrc);
+        const u16x8 ov = *reinterpret_cast<const u16x8*>(osrc);
+        *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, ch)) = dv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[q][k][i] = to_f32<DT>(dv[i]);
+          part = __builtin_fmaf(x[q][k][i], to_f32<DT>(ov[i]), part);
+        }
+      } else {
+        const u16x4 dv = *reinterpret_cast<const u16x4*>(dsrc);
+        const u16x4 ov = *reinterpret_cast<const u16x4*>(osrc);
+        *reinterpret_cast<u16x4*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, ch >> 1) + 8 * (ch & 1)) = dv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[q][k][i] = to_f32<DT>(dv[i]);
+          part = __builtin_fmaf(x[q][k][i], to_f32<DT>(ov[i]), part);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CW; ++i) amax = fmaxf(amax, fabsf(x[q][k][i]));
+      const float dsum = row_sum16(part);
+      if (ch == 0) {
+        reinterpret_cast<float*>(pk + P::bDV)[r] = dsum;
+        reinterpret_cast<float*>(pk + P::bLSE)[r] = a.lse[tok] * kLog2e;
+      }
     }
   }
-  // Q codes: token-major into the packets, and into LDS for the transpose
-  for (int ch = tid; ch < BLK * D / 16; ch += 256) {
-    const int t = (ch * 16) / D, j = ch % (D / 16), c = 16 * j;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(a.Qc + (tok0 + t) * D + c);
-    const int r = t % kTq;
-    *reinterpret_cast<i32x4*>(pk0 + (t / kTq) * P::kBytes + P::bQ + r * D + 16 * swz<D>(r, j)) = v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<int*>(&qs[t][c + 4 * i]) = v[i];
-  }
-  if (a.spill) {
-    // K codes of this key block, into LDS for the channel-major K^T packet
-    for (int ch = tid; ch < BLK * D / 16; ch += 256) {
-      const int t = (ch * 16) / D, c = (ch * 16) % D;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(a.Kc + (tok0 + t) * D + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<int*>(&ks[t][c + 4 * i]) = v[i];
-    }
-  } else {
-    // zero the dQ accumulator rows of this block
-    for (int e = tid; e < BLK * D / 4; e += 256)
-      reinterpret_cast<float4*>(a.dq_acc + tok0 * D)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-
   amax = wave_max(amax);
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   const float am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = am > 0.0f ? 127.0f / am : 0.0f;
-  if (tid < BLK / kTq) {
+  if (tid < NQ) {
     int8_t* pk = pk0 + tid * P::kBytes;
     *reinterpret_cast<float*>(pk + P::bSDO) = am > 0.0f ? am / 127.0f : 0.0f;
     *reinterpret_cast<float*>(pk + P::bSQ) = a.Qs[(size_t)bh * nb + blk_id];
   }
-  // channel-major codes of dO and of Q: word = 4 consecutive tokens of channel c, placed at
-  // its permuted position inside the 32-token group and its swizzled 16-byte chunk
-  for (int w = tid; w < BLK * D / 4; w += 256) {
-    const int c = w / (BLK / 4), t = 4 * (w % (BLK / 4));
-    const unsigned word = pack4_lo_bytes(quant_word(xs[t][c], inv), quant_word(xs[t + 1][c], inv),
-                                         quant_word(xs[t + 2][c], inv), quant_word(xs[t + 3][c], inv));
-    const unsigned qw = (unsigned)(uint8_t)qs[t][c] | ((unsigned)(uint8_t)qs[t + 1][c] << 8) |
-                        ((unsigned)(uint8_t)qs[t + 2][c] << 16) | ((unsigned)(uint8_t)qs[t + 3][c] << 24);
-    const int tl = t % kTq;
-    const int p = tile_token_pos(tl);  // byte position in the 64-token row (tl..tl+3 stay together)
-    const int off = c * kTq + 16 * swz<kTq>(c, p / 16) + p % 16;
-    int8_t* pk = pk0 + (t / kTq) * P::kBytes;
-    *reinterpret_cast<unsigned*>(pk + P::bDOT + off) = word;
-    *reinterpret_cast<unsigned*>(pk + P::bQT + off) = qw;
-  }
-  if (a.spill) {
-    // K^T packet of this key block: [D][BLK] codes, chunk j of row c at slot swz<BLK>(c, j)
-    int8_t* kt = a.ktp + ((size_t)bh * nb + blk_id) * (size_t)(D * BLK);
-    for (int w = tid; w < BLK * D / 4; w += 256) {
-      const int c = w / (BLK / 4), t = 4 * (w % (BLK / 4));
-      const unsigned kw = (unsigned)(uint8_t)ks[t][c] | ((unsigned)(uint8_t)ks[t + 1][c] << 8) |
-                          ((unsigned)(uint8_t)ks[t + 2][c] << 16) | ((unsigned)(uint8_t)ks[t + 3][c] << 24);
-      *reinterpret_cast<unsigned*>(kt + c * BLK + 16 * swz<BLK>(c, t / 16) + t % 16) = kw;
+
+  // channel-major rows of a tile from the LDS tile [q][c][TR]: chunk g of row c (positions
+  // 16g..16g+15) is stored at chunk swz<64>(c, g) of the packet region at offset `region`
+  auto write_rows = [&](int region) {
+    for (int e = tid; e < NQ * D * 4; e += 256) {
+      const int q = e / (D * 4), c = (e / 4) % D, g = e % 4;
+      const int8_t* src = tt + (q * D + c) * TR + 16 * g;
+      i32x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const int*>(src + 4 * u);
+      *reinterpret_cast<i32x4*>(pk0 + q * P::kBytes + region + c * kTq + 16 * swz<kTq>(c, g)) = v;
     }
+  };
+
+  // ---- dO codes, channel-major (dO^T), tokens at their permuted positions
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < CW; ++i)
+      *reinterpret_cast<unsigned*>(tt + (q * D + c0 + i) * TR + wpos) =
+          pack4_lo_bytes(quant_word(x[q][0][i], inv), quant_word(x[q][1][i], inv), quant_word(x[q][2][i], inv),
+                         quant_word(x[q][3][i], inv));
+  __syncthreads();
+  write_rows(P::bDOT);
+  __syncthreads();
+
+  // ---- Q codes: token-major into the packets, channel-major (Q^T) through LDS
+  unsigned qb[NQ][4][CW / 4];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    int8_t* pk = pk0 + q * P::kBytes;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 4 * j + k;
+      const int8_t* src = a.Qc + (tok0 + kTq * q + r) * D + c0;
+      if constexpr (CW == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        qb[q][k][0] = v.x; qb[q][k][1] = v.y;
+        *reinterpret_cast<uint2*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 1) + 8 * (ch & 1)) = v;
+      } else {
+        const unsigned v = *reinterpret_cast<const unsigned*>(src);
+        qb[q][k][0] = v;
+        *reinterpret_cast<unsigned*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 2) + 4 * (ch & 3)) = v;
+      }
+    }
+  }
+  // byte i of the thread's four tokens -> one word per channel
+  auto transpose4 = [&](const unsigned* w0, const unsigned* w1, const unsigned* w2, const unsigned* w3, int i) {
+    const int wi = i >> 2, sh = 8 * (i & 3);
+    return ((w0[wi] >> sh) & 0xFFu) | (((w1[wi] >> sh) & 0xFFu) << 8) | (((w2[wi] >> sh) & 0xFFu) << 16) |
+           (((w3[wi] >> sh) & 0xFFu) << 24);
+  };
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int i = 0; i < CW; ++i)
+      *reinterpret_cast<unsigned*>(tt + (q * D + c0 + i) * TR + wpos) =
+          transpose4(qb[q][0], qb[q][1], qb[q][2], qb[q][3], i);
+  __syncthreads();
+  write_rows(P::bQT);
+
+  if (a.spill) {
+    // ---- K^T packet of this key block: [D][BLK] codes, chunk j of row c at slot swz<BLK>(c, j)
+    unsigned kbw[NQ][4][CW / 4];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int8_t* src = a.Kc + (tok0 + kTq * q + 4 * j + k) * D + c0;
+        if constexpr (CW == 8) {
+          const uint2 v = *reinterpret_cast<const uint2*>(src);
+          kbw[q][k][0] = v.x; kbw[q][k][1] = v.y;
+        } else {
+          kbw[q][k][0] = *reinterpret_cast<const unsigned*>(src);
+        }
+      }
+    __syncthreads();   // the Q^T rows have been read out of the LDS tile
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < CW; ++i)
+        *reinterpret_cast<unsigned*>(tt + (c0 + i) * KR + kTq * q + 4 * j) =
+            transpose4(kbw[q][0], kbw[q][1], kbw[q][2], kbw[q][3], i);
+    __syncthreads();
+    int8_t* kt = a.ktp + ((size_t)bh * nb + blk_id) * (size_t)(D * BLK);
+    for (int e = tid; e < D * (BLK / 16); e += 256) {
+      const int c = e / (BLK / 16), g = e % (BLK / 16);
+      const int8_t* src = tt + c * KR + 16 * g;
+      i32x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const int*>(src + 4 * u);
+      *reinterpret_cast<i32x4*>(kt + c * BLK + 16 * swz<BLK>(c, g)) = v;
+    }
+  } else {
+    // zero the dQ accumulator rows of this block
+    for (int e = tid; e < BLK * D / 4; e += 256)
+      reinterpret_cast<float4*>(a.dq_acc + tok0 * D)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
