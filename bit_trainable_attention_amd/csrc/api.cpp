@@ -57,6 +57,7 @@ sagebwd_status check_ptrs(Ptrs... ptrs) {
 
 struct BwdLayout {
   bool spill;
+  bool spill_fits;  // one head's dS tiles stay below 4 GiB
   long long tiles;  // dS tiles per head (spill mode)
   size_t pk, dq, ktp, dsp, dsm, total;
 };
@@ -71,8 +72,10 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
   const size_t dsp_bytes = round_up(bh * (size_t)L.tiles * 64 * p->blk);
   const size_t dsm_bytes = round_up(bh * (size_t)L.tiles * 4);
   const size_t spill_bytes = ktp_bytes + dsp_bytes + dsm_bytes;
-  L.spill = p->dq_mode == SAGEBWD_DQ_SPILL ||
-            (p->dq_mode == SAGEBWD_DQ_AUTO && spill_bytes <= SAGEBWD_DQ_AUTO_SPILL_LIMIT);
+  // the dQ pass addresses one head's dS tiles with 32-bit buffer offsets
+  L.spill_fits = (size_t)L.tiles * 64 * p->blk < (1ull << 32);
+  L.spill = L.spill_fits && (p->dq_mode == SAGEBWD_DQ_SPILL ||
+                             (p->dq_mode == SAGEBWD_DQ_AUTO && spill_bytes <= SAGEBWD_DQ_AUTO_SPILL_LIMIT));
   if (L.spill) {
     L.ktp = after_pk;
     L.dsp = L.ktp + ktp_bytes;
@@ -122,7 +125,9 @@ size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p) {
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
   if (check_params(p) != SAGEBWD_OK) return 0;
   if (empty(p)) return 0;
-  return bwd_layout(p).total;
+  const BwdLayout L = bwd_layout(p);
+  if (p->dq_mode == SAGEBWD_DQ_SPILL && !L.spill_fits) return 0;
+  return L.total;
 }
 
 sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
@@ -183,6 +188,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   if (!workspace) return SAGEBWD_ERR_NULL;
   if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
   const BwdLayout L = bwd_layout(p);
+  if (p->dq_mode == SAGEBWD_DQ_SPILL && !L.spill_fits) return SAGEBWD_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return SAGEBWD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   BackwardArgs a{};

@@ -89,7 +89,9 @@ typedef struct {
  * each tile's float32 dQ contribution with atomics (O(N) scratch, but the atomic traffic is
  * (N/blk) * N * d * 4 bytes per head). SAGEBWD_DQ_AUTO picks SPILL while its scratch is at
  * most SAGEBWD_DQ_AUTO_SPILL_LIMIT bytes, else ATOMIC. Both give the same dQ up to float32
- * summation order. */
+ * summation order. SPILL also needs one head's dS tiles (T * 64 * blk bytes, T below) under
+ * 4 GiB: AUTO picks ATOMIC beyond that, and an explicit SPILL is rejected
+ * (SAGEBWD_ERR_UNSUPPORTED from the backward, 0 from the workspace query). */
 typedef enum { SAGEBWD_DQ_AUTO = 0, SAGEBWD_DQ_SPILL = 1, SAGEBWD_DQ_ATOMIC = 2 } sagebwd_dq_mode;
 #define SAGEBWD_DQ_AUTO_SPILL_LIMIT (16ull << 30)
 

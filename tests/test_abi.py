@@ -103,6 +103,19 @@ def test_workspace_checks():
     assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(k_smooth=0))) == 0
 
 
+def test_spill_needs_per_head_tiles_below_4gib():
+    # causal N = 131072, blk 128: one head's dS tiles need 8.6 GB > 4 GiB of 32-bit offsets
+    big = dict(B=1, H=1, N=131072, d=128, blk=128)
+    assert lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=1, **big))) == 0
+    assert _backward(P(dq_mode=1, **big)) == -3
+    # auto falls back to the atomic layout (packets + float32 dQ accumulator)
+    up = lambda x: (x + 255) // 256 * 256
+    auto = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=0, **big)))
+    assert auto == up(131072 // 64 * 41984) + up(4 * 131072 * 128)
+    # N = 65536 still spills (2.1 GB per head)
+    assert lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=1, B=1, H=1, N=65536, d=128, blk=128))) > 0
+
+
 def test_empty_is_a_noop():
     # N == 0 (or B == 0 / H == 0): nothing is enqueued and pointers are not inspected
     for p in (P(N=0), P(B=0), P(H=0)):
