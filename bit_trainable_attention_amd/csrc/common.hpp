@@ -144,4 +144,46 @@ __device__ __forceinline__ unsigned quant_word_fma(float x, float inv) {
   return __float_as_uint(__builtin_fmaf(x, inv, 12582912.0f));
 }
 
+// ---------------------------------------------------------------- LDS staging helpers
+// XOR swizzles of the 16-byte chunks of LDS rows: 8 consecutive rows read at the same
+// logical chunk land in 8 different bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (ROWB >= 128) return chunk ^ (row & 7);
+  else if constexpr (ROWB == 64) return chunk ^ ((row >> 1) & 3);
+  else return chunk;
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct buffer -> LDS copy (buffer_load ... lds): lane l reads 16 bytes at byte offset
+// voff + soff of the buffer [base, base + bytes) (reads past the end return zeros) and the
+// hardware writes them to LDS at lds + 16*l (the 4-byte form: 4 bytes at lds + 4*l). voff is
+// the per-lane offset; soff and lds must be the same in every lane of the wave. The
+// bodies are compiled for the device only:
+// this compiler's host pass cannot type-check the LDS-DMA builtin and, instead of reporting
+// it, silently omits the host launch stubs of kernels that reach it.
+__device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
+                                                uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                                      0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
+                                               uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                                      0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+#endif
+}
+
 }  // namespace sagebwd

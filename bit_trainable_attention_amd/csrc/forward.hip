@@ -5,14 +5,15 @@
 //
 // Work decomposition (gfx950, 64-lane waves):
 //   workgroup = 4 waves = 128 query rows of one head; wave w owns 32 rows.
-//   Key tiles of BLK keys (one quantisation block of K and V) stream through LDS,
-//   double-buffered: K codes token-major (rows padded to D+16 bytes) and V^T codes
-//   channel-major (rows padded to BLK+16 bytes); the padding makes the 16-byte MFMA
-//   operand reads of 8 consecutive rows fall on distinct banks.
+//   Key tiles of BLK keys (one quantisation block of K and V) stream into double-buffered
+//   LDS by buffer->LDS copies: K codes token-major and V^T codes channel-major, both with
+//   their 16-byte chunks XOR-swizzled by row so the MFMA operand reads of 8 consecutive
+//   rows hit distinct banks (the copies take the permutation on their source addresses).
 //   S^T = K Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 16 keys per
 //   32-key subtile, so the row max / row sum are lane-local plus one exchange with lane
-//   l^32, and the quantised P~^T is already in the B-operand layout of O^T = V^T P~^T.
-//   The V^T tile is permuted in LDS so that each A-operand read is one 16-byte load.
+//   l^32 (v_permlane32_swap). The quantised P~^T becomes the B operand of O^T = V^T P~^T
+//   after two v_permlane32_swap per subtile, which put keys 16g..16g+15 in lane group g,
+//   the order in which the V^T rows are stored.
 // Per key tile (the online-softmax step and the P~ quantisation tile, 32 rows x BLK keys):
 //   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); alpha = 2^(m - m'); l = l*alpha + sum P~;
 //   a = max P~ over the wave's tile; codes = rne(P~ * (127/a)); O = O*alpha + (a/127)*sV*int(PV).
@@ -36,48 +37,37 @@ constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
 
 template <int D, int BLK>
 struct FwdLds {
-  static constexpr int kRowK = D + 16;      // bytes per K row in LDS
-  static constexpr int kRowV = BLK + 16;    // bytes per V^T row in LDS
-  static constexpr int kBytesK = BLK * kRowK;
-  static constexpr int kBytesV = D * kRowV;
+  static constexpr int kBytesK = BLK * D;   // K codes [BLK][D], chunk j of row r at swz<D>(r, j)
+  static constexpr int kBytesV = D * BLK;   // V^T codes [D][BLK], chunk j of row c at swz<BLK>(c, j)
   static constexpr int kBytes = kBytesK + kBytesV;
-  // 16-byte chunks of one K tile and of one V^T tile, and per thread
-  static constexpr int kChunks = BLK * D / 16;
-  static constexpr int kPerThread = kChunks / (kWaves * 64);
+  static constexpr int kCopies = kBytes / 1024;              // 1 KB copies per tile
+  static constexpr int kCopiesPerWave = kCopies / kWaves;
+  static_assert(kCopies % kWaves == 0, "copies per wave");
 };
 
-// Byte offset, inside a V^T LDS row, of key-dword kd (keys 4kd..4kd+3): within each
-// group of 32 keys, lane group g reads keys {8j + 4g + i} (j, i = 0..3) as one 16-byte load.
-__device__ __forceinline__ int vt_dword_pos(int kd) {
-  const int c32 = kd >> 3, k8 = kd & 7;
-  return 32 * c32 + 16 * (k8 & 1) + 4 * (k8 >> 1);
-}
-
+// Copies of key tile k0 into an LDS tile buffer: copy cp = w + kWaves*i moves LDS bytes
+// [1024 cp, 1024 cp + 1024); lane l fills the chunk at 1024 cp + 16 l and reads the logical
+// chunk that the swizzle puts there.
 template <int D, int BLK>
-__device__ __forceinline__ void load_tile_regs(const ForwardArgs& a, size_t bh, int k0, i32x4* kreg, i32x4* vreg) {
+__device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int k0, int8_t* dst, int w, int l) {
   using L = FwdLds<D, BLK>;
-  const int8_t* kbase = a.Kc + ((size_t)bh * a.N + k0) * D;
+  const int8_t* kh = a.Kc + (size_t)bh * a.N * D;     // this head's K codes
+  const int8_t* vh = a.Vtc + (size_t)bh * D * a.N;    // this head's V^T codes
+  const uint32_t hbytes = (uint32_t)a.N * D;
 #pragma unroll
-  for (int j = 0; j < L::kPerThread; ++j) {
-    const int ci = threadIdx.x + j * kWaves * 64;
-    kreg[j] = *reinterpret_cast<const i32x4*>(kbase + (size_t)ci * 16);
-    const int c = ci / (BLK / 16), cc = ci % (BLK / 16);
-    vreg[j] = *reinterpret_cast<const i32x4*>(a.Vtc + ((size_t)bh * D + c) * a.N + k0 + cc * 16);
-  }
-}
-
-template <int D, int BLK>
-__device__ __forceinline__ void store_tile_lds(int8_t* lds, const i32x4* kreg, const i32x4* vreg) {
-  using L = FwdLds<D, BLK>;
-#pragma unroll
-  for (int j = 0; j < L::kPerThread; ++j) {
-    const int ci = threadIdx.x + j * kWaves * 64;
-    const int row = (ci * 16) / D, col = (ci * 16) % D;
-    *reinterpret_cast<i32x4*>(lds + row * L::kRowK + col) = kreg[j];
-    const int c = ci / (BLK / 16), cc = ci % (BLK / 16);
-    int8_t* vrow = lds + L::kBytesK + c * L::kRowV;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) *reinterpret_cast<int*>(vrow + vt_dword_pos(4 * cc + w)) = vreg[j][w];
+  for (int i = 0; i < L::kCopiesPerWave; ++i) {
+    const int cp = w + kWaves * i;
+    const int e = 64 * cp + l;                          // 16-byte chunk index inside the tile
+    if (cp * 1024 < L::kBytesK) {
+      const int r = e / (D / 16), pc = e % (D / 16);
+      const int j = swz<D>(r, pc);                      // the swizzle is an involution
+      buffer_to_lds16(kh, hbytes, dst + cp * 1024, (uint32_t)((k0 + r) * D + 16 * j), 0u);
+    } else {
+      const int ev = e - L::kBytesK / 16;
+      const int c = ev / (BLK / 16), pc = ev % (BLK / 16);
+      const int j = swz<BLK>(c, pc);
+      buffer_to_lds16(vh, hbytes, dst + cp * 1024, (uint32_t)(c * a.N + k0 + 16 * j), 0u);
+    }
   }
 }
 
@@ -118,14 +108,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
   for (int ct = 0; ct < DC; ++ct) o[ct] = f32x16{};
 
-  i32x4 kreg[L::kPerThread], vreg[L::kPerThread];
-  load_tile_regs<D, BLK>(a, bh, 0, kreg, vreg);
-  store_tile_lds<D, BLK>(lds[0], kreg, vreg);
+  issue_tile<D, BLK>(a, bh, 0, lds[0], w, l);
+  wait_vmcnt<0>();
   __syncthreads();
+  // block scales of the current key tile, loaded one tile ahead
+  float sK_n = a.Ks[(size_t)bh * nb], sV_n = a.Vs[(size_t)bh * nb];
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) load_tile_regs<D, BLK>(a, bh, (kt + 1) * BLK, kreg, vreg);
+    if (has_next) issue_tile<D, BLK>(a, bh, (kt + 1) * BLK, lds[(kt + 1) & 1], w, l);
+    const float sK = sK_n, sV = sV_n;
+    if (has_next) {
+      sK_n = a.Ks[(size_t)bh * nb + kt + 1];
+      sV_n = a.Vs[(size_t)bh * nb + kt + 1];
+    }
     const int k0 = kt * BLK;
     const int8_t* kl = lds[kt & 1];
     const int8_t* vl = lds[kt & 1] + L::kBytesK;
@@ -140,7 +136,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         s[t] = i32x16{};
 #pragma unroll
         for (int kk = 0; kk < DC; ++kk) {
-          const i32x4 ak = *reinterpret_cast<const i32x4*>(kl + (32 * t + lq) * L::kRowK + 32 * kk + 16 * g);
+          const int kr = 32 * t + lq;
+          const i32x4 ak = *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz<D>(kr, 2 * kk + g));
           s[t] = mfma_i8_32x32x32(ak, qreg[kk], s[t]);
         }
       }
@@ -158,10 +155,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       for (int t = 0; t < NSUB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) rmax = max(rmax, s[t][r]);
-      rmax = max(rmax, __shfl_xor(rmax, 32));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(rmax, rmax, false, false);
+        rmax = max((int)sw[0], (int)sw[1]);   // lanes l and l^32 hold the same query row (signed)
+      }
 
-      const size_t sidx = (size_t)bh * nb + kt;
-      const float sK = a.Ks[sidx], sV = a.Vs[sidx];
       const float c2 = (sQ * sK) * (a.sm_scale * kLog2e);
       // row max over the visible keys (a row with none in this tile keeps its old max)
       float rowmax = (float)rmax * c2;
@@ -194,6 +192,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           wd = __builtin_amdgcn_cvt_pk_u8_f32(u[2], 2, wd);
           pc[t][j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, wd);
         }
+      // word j of lane group g holds keys 8j + 4g .. +3; group 0 needs keys 0..15 and group
+      // 1 keys 16..31: swap words (0, 2) and (1, 3) across the lane halves
+#pragma unroll
+      for (int t = 0; t < NSUB; ++t) {
+        const auto x02 = __builtin_amdgcn_permlane32_swap(pc[t][0], pc[t][2], false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(pc[t][1], pc[t][3], false, false);
+        pc[t] = i32x4{(int)x02[0], (int)x02[1], (int)x13[0], (int)x13[1]};
+      }
       // l accumulates P~ before quantisation: sum(P~ * 127/a) * a/127
       lsum_run = lsum_run * alpha + tsum * sP;
 
@@ -211,7 +217,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         i32x16 acc = i32x16{};
 #pragma unroll
         for (int t = 0; t < NSUB; ++t) {
-          const i32x4 av = *reinterpret_cast<const i32x4*>(vl + (32 * ct + lq) * L::kRowV + 32 * t + 16 * g);
+          const int vr = 32 * ct + lq;
+          const i32x4 av = *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz<BLK>(vr, 2 * t + g));
           acc = mfma_i8_32x32x32(av, pc[t], acc);
         }
 #pragma unroll
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       if (a.causal && k0 + BLK - 1 > q0w) tile(std::true_type{});
       else tile(std::false_type{});
     }
-    if (has_next) store_tile_lds<D, BLK>(lds[(kt + 1) & 1], kreg, vreg);
+    wait_vmcnt<0>();   // the next tile's copies (the only vector-memory operations in the loop)
     __syncthreads();
   }
 
