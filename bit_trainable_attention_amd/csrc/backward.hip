@@ -362,6 +362,16 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < NCT; ++i) { dk[i] = f32x4{}; dv[i] = f32x4{}; }
 
+  // per-lane byte offsets of the operands inside a tile buffer. The swizzle of row r depends
+  // on r & 7 (or on (r >> 1) & 3), which rows 16t + lr share for every t, so each operand
+  // address is buffer + one of these offsets + a compile-time constant.
+  int oQ[KCH], oDO[HCH];
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) oQ[c] = P::bQ + lr * D + 16 * swz<D>(lr, 4 * c + g);
+#pragma unroll
+  for (int c = 0; c < HCH; ++c) oDO[c] = P::bDO + lr * 2 * D + 16 * swz<2 * D>(lr, 4 * c + g);
+  const int oT = lr * kTq + 16 * swz<kTq>(lr, g);   // dO^T / Q^T codes, channel 16n + lr
+
   // copies of packet qt into an LDS tile buffer: wave w moves KB cp = w, w + NW, ... (copies
   // j in [J0, J1) of this wave)
   auto issue = [&](int qt, int8_t* dst, auto j0_c, auto j1_c) {
@@ -408,17 +418,16 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     f32x4 dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int q = 16 * t + lr;
       s[t] = i32x4{};
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
-        const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + P::bQ + q * D + 16 * swz<D>(q, 4 * c + g));
+        const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + oQ[c] + 16 * t * D);
         s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
       }
       dp[t] = f32x4{};
 #pragma unroll
       for (int c = 0; c < HCH; ++c) {
-        const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + P::bDO + q * 2 * D + 16 * swz<2 * D>(q, 4 * c + g));
+        const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + oDO[c] + 32 * t * D);
         dp[t] = mfma_16b_16x16x32<DT>(ad, vreg[c], dp[t]);
       }
     }
@@ -466,8 +475,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
                                     quant_word_fma(pf[t][2], pinv), quant_word_fma(pf[t][3], pinv));
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        const int c = 16 * n + lr;
-        const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + P::bDOT + c * kTq + 16 * swz<kTq>(c, g));
+        const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + P::bDOT + oT + 16 * n * kTq);
         const i32x4 acc = mfma_i8_16x16x64(ao, pc, i32x4{});
 #pragma unroll
         for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
@@ -477,8 +485,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     i32x4 qtr[NCT];
 #pragma unroll
     for (int n = 0; n < NCT; ++n) {
-      const int c = 16 * n + lr;
-      qtr[n] = *reinterpret_cast<const i32x4*>(buf + P::bQT + c * kTq + 16 * swz<kTq>(c, g));
+      qtr[n] = *reinterpret_cast<const i32x4*>(buf + P::bQT + oT + 16 * n * kTq);
     }
     if (issue_next) issue(qt + 2, nbuf, G2{}, G3{});
     // the copies of tile qt+1 (issued one step ago) must have landed before the barrier that
