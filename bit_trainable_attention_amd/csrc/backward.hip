@@ -453,14 +453,15 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     else elems(std::false_type{});
     if (issue_next) issue(qt + 2, nbuf, G1{}, G2{});
 
-    // ---- tile maxima (three-input max trees; the |dS| maximum goes to the workgroup)
-    float pm = 0.0f, dm = 0.0f;
+    // ---- tile maxima (chains of three-input maxima; the |dS| maximum goes to the workgroup)
+    float pm = pf[0][0], dm = fabsf(dsf[0][0]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pm = fmaxf(pm, fmaxf(fmaxf(pf[t][0], pf[t][1]), fmaxf(pf[t][2], pf[t][3])));
-      dm = fmaxf(dm, fmaxf(fmaxf(fabsf(dsf[t][0]), fabsf(dsf[t][1])), fmaxf(fabsf(dsf[t][2]), fabsf(dsf[t][3]))));
+    for (int i = 1; i < 16; i += 2) {
+      const int t0 = i / 4, r0 = i % 4, t1 = (i + 1) / 4, r1 = (i + 1) % 4;
+      pm = fmaxf(fmaxf(pm, pf[t0][r0]), i + 1 < 16 ? pf[t1][r1] : 0.0f);
+      dm = fmaxf(fmaxf(dm, fabsf(dsf[t0][r0])), i + 1 < 16 ? fabsf(dsf[t1][r1]) : 0.0f);
     }
-    wave_max2(pm, dm);
+    wave_max2_nonneg(pm, dm);
     if (l == 0) redD[(step & 1) * NW + w] = dm;
 
     // ---- P codes on this wave's 64 x 16 tile, then dV^T += dO^T P (int32 over the 64 queries)

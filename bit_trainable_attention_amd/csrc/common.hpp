@@ -120,6 +120,26 @@ __device__ __forceinline__ void wave_max2(float& x, float& y) {
   x = __int_as_float(mu ^ ((mu >> 31) & 0x7FFFFFFF));
   y = __int_as_float(mv ^ ((mv >> 31) & 0x7FFFFFFF));
 }
+// Two wave maxima of non-negative floats. The row steps are float max with a DPP operand
+// (every source lane exists for these controls, so no lane reads the bound value); the four
+// row maxima are combined as integers, which order non-negative floats like the floats.
+template <int CTRL>
+__device__ __forceinline__ float fmax_dpp(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true)));
+}
+__device__ __forceinline__ int rows_max(float v) {
+  const int b = __float_as_int(v);
+  return max(max(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
+             max(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+}
+__device__ __forceinline__ void wave_max2_nonneg(float& x, float& y) {
+  x = fmax_dpp<0xB1>(x);  y = fmax_dpp<0xB1>(y);    // lane ^ 1
+  x = fmax_dpp<0x4E>(x);  y = fmax_dpp<0x4E>(y);    // lane ^ 2
+  x = fmax_dpp<0x124>(x); y = fmax_dpp<0x124>(y);   // row_ror:4
+  x = fmax_dpp<0x128>(x); y = fmax_dpp<0x128>(y);   // row_ror:8
+  x = __int_as_float(rows_max(x));
+  y = __int_as_float(rows_max(y));
+}
 
 // Pack the low bytes of four 32-bit words into one word (byte i <- word i).
 __device__ __forceinline__ unsigned pack4_lo_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
