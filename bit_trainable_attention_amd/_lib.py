@@ -13,9 +13,9 @@ SAGEBWD_FP16 = 0
 SAGEBWD_BF16 = 1
 DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 
-# Quantisation tile shapes of the kernels (include/sagebwd.h).
+# Quantisation tile shapes of the kernels (include/sagebwd.h); the backward's P and dS tiles
+# span one query block (blk rows).
 FWD_TILE_Q = 32
-BWD_TILE_Q = 64
 BWD_P_TILE_K = 16
 
 STATUS = {

@@ -70,7 +70,7 @@ def sagebwd_backward_workspace_bytes(p: _lib.Params) -> int:
     return int(_lib.load().sagebwd_backward_workspace_bytes(ctypes.byref(p)))
 
 
-PACKET_BYTES = {64: 21504, 128: 41984}
+PACKET_BYTES = {64: 17408, 128: 33792}
 
 
 SPILL_LIMIT = 16 << 30

@@ -8,10 +8,11 @@
 //   bwd_pre      one workgroup per (head, block of BLK tokens). Computes D = rowsum(dO o O),
 //                lse * log2(e), the block absmax and INT8 codes of dO, and writes, for every
 //                64-query tile, a "packet": the exact LDS image the main kernel needs for that
-//                tile (Q codes, dO, dO^T codes, Q^T codes, lse2, D, block scales), already
-//                swizzled and permuted. Also zeroes the float32 dQ accumulator rows.
+//                tile (Q codes, dO, dO^T codes, lse2, D, block scales), already swizzled and
+//                permuted. Also writes the key blocks' K^T codes (spill mode) or zeroes the
+//                float32 dQ accumulator rows (atomic mode).
 //   bwd_main     one workgroup per (head, key block of BLK keys); each wave owns 16 keys.
-//                Streams the query tiles' packets into triple-buffered LDS with buffer->LDS
+//                Streams the query blocks' packets into double-buffered LDS with buffer->LDS
 //                copies (issued two tiles ahead). S = Q K~^T on v_mfma_i32_16x16x64_i8 and
 //                dP = dO V^T on v_mfma_f32_16x16x32_{f16,bf16}, in the layout lane = key,
 //                registers = queries, which is directly the B operand of the two products
@@ -35,7 +36,7 @@ namespace sagebwd {
 
 namespace {
 
-constexpr int kTq = 64;  // query rows per P / dS quantisation tile
+constexpr int kPq = 64;  // query rows of a tile packet and of a spilled dS^T tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Byte position, inside a 64-token channel-major row of a tile packet, of token u: the
@@ -69,8 +70,7 @@ struct Packet {
   static constexpr int bQ = 0;                // Q codes [64][D], chunk j of row r at slot swz<D>(r, j)
   static constexpr int bDO = 64 * D;          // dO [64][D] 16-bit, chunk j of row r at slot swz<2D>(r, j)
   static constexpr int bDOT = bDO + 128 * D;  // dO codes [D][64], token u at tile_token_pos(u), chunk swz<64>(c, j)
-  static constexpr int bQT = bDOT + 64 * D;   // Q codes [D][64], same order as dO^T
-  static constexpr int bLSE = bQT + 64 * D;   // lse * log2(e) [64] f32
+  static constexpr int bLSE = bDOT + 64 * D;  // lse * log2(e) [64] f32
   static constexpr int bDV = bLSE + 256;      // D = rowsum(dO o O) [64] f32
   static constexpr int bSQ = bDV + 256;       // Q block scale f32
   static constexpr int bSDO = bSQ + 4;        // dO block scale f32
@@ -98,13 +98,13 @@ __device__ __forceinline__ long long spill_tile_index(int N, int blk, int causal
 // tokens 64q + 4j + k (k = 0..3) of every 64-token tile q of the block, in registers. The
 // 16 lanes of a row share their tokens, so D = rowsum(dO o O) is a DPP tree across the row,
 // and a thread's four codes of one channel are one word at the packet's permuted token
-// position. Channel-major rows (dO^T, Q^T, K^T codes) are assembled in an LDS byte tile.
+// position. Channel-major rows (dO^T, K^T codes) are assembled in an LDS byte tile.
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
   using P = Packet<D>;
   constexpr int CW = D / 16;                 // channels per thread
-  constexpr int NQ = BLK / kTq;              // 64-token tiles of the block
-  constexpr int TR = kTq + 4;                // LDS row stride of a transposed tile row (bytes)
+  constexpr int NQ = BLK / kPq;              // 64-token tiles of the block
+  constexpr int TR = kPq + 4;                // LDS row stride of a transposed tile row (bytes)
   constexpr int KR = BLK + 4;                // ... of the block's K^T rows
   constexpr int kTile = NQ * D * TR > D * KR ? NQ * D * TR : D * KR;
   __shared__ __attribute__((aligned(16))) int8_t tt[kTile];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
   const int c0 = ch * CW;
   const int wpos = tile_token_pos(4 * j);    // packet position of tokens 4j..4j+3 (one word)
   // packet of the block's first 64-token tile
-  int8_t* pk0 = a.pk + ((size_t)bh * (a.N / kTq) + (size_t)blk_id * NQ) * P::kBytes;
+  int8_t* pk0 = a.pk + ((size_t)bh * (a.N / kPq) + (size_t)blk_id * NQ) * P::kBytes;
 
   // ---- dO (16-bit, straight into the packets), D = rowsum(dO o O), lse * log2(e)
   float x[NQ][4][CW];
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * j + k;                       // token inside the tile
-      const size_t tok = tok0 + kTq * q + r;
+      const size_t tok = tok0 + kPq * q + r;
       const unsigned short* dsrc = a.dO + tok * D + c0;
       const unsigned short* osrc = a.O + tok * D + c0;
       float part = 0.0f;
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
       i32x4 v;
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const int*>(src + 4 * u);
-      *reinterpret_cast<i32x4*>(pk0 + q * P::kBytes + region + c * kTq + 16 * swz<kTq>(c, g)) = v;
+      *reinterpret_cast<i32x4*>(pk0 + q * P::kBytes + region + c * kPq + 16 * swz<kPq>(c, g)) = v;
     }
   };
 
@@ -196,40 +196,23 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
   write_rows(P::bDOT);
   __syncthreads();
 
-  // ---- Q codes: token-major into the packets, channel-major (Q^T) through LDS
-  unsigned qb[NQ][4][CW / 4];
+  // ---- Q codes, token-major into the packets (the key-block kernel reads its Q^T operands
+  //      out of them with transposing reads)
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     int8_t* pk = pk0 + q * P::kBytes;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * j + k;
-      const int8_t* src = a.Qc + (tok0 + kTq * q + r) * D + c0;
-      if constexpr (CW == 8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        qb[q][k][0] = v.x; qb[q][k][1] = v.y;
-        *reinterpret_cast<uint2*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 1) + 8 * (ch & 1)) = v;
-      } else {
-        const unsigned v = *reinterpret_cast<const unsigned*>(src);
-        qb[q][k][0] = v;
-        *reinterpret_cast<unsigned*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 2) + 4 * (ch & 3)) = v;
-      }
+      const int8_t* src = a.Qc + (tok0 + kPq * q + r) * D + c0;
+      if constexpr (CW == 8)
+        *reinterpret_cast<uint2*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 1) + 8 * (ch & 1)) =
+            *reinterpret_cast<const uint2*>(src);
+      else
+        *reinterpret_cast<unsigned*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 2) + 4 * (ch & 3)) =
+            *reinterpret_cast<const unsigned*>(src);
     }
   }
-  // byte i of the thread's four tokens -> one word per channel
-  auto transpose4 = [&](const unsigned* w0, const unsigned* w1, const unsigned* w2, const unsigned* w3, int i) {
-    const int wi = i >> 2, sh = 8 * (i & 3);
-    return ((w0[wi] >> sh) & 0xFFu) | (((w1[wi] >> sh) & 0xFFu) << 8) | (((w2[wi] >> sh) & 0xFFu) << 16) |
-           (((w3[wi] >> sh) & 0xFFu) << 24);
-  };
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int i = 0; i < CW; ++i)
-      *reinterpret_cast<unsigned*>(tt + (q * D + c0 + i) * TR + wpos) =
-          transpose4(qb[q][0], qb[q][1], qb[q][2], qb[q][3], i);
-  __syncthreads();
-  write_rows(P::bQT);
 
   if (a.spill) {
     // ---- K^T packet of this key block: [D][BLK] codes, chunk j of row c at slot swz<BLK>(c, j)
@@ -238,7 +221,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int8_t* src = a.Kc + (tok0 + kTq * q + 4 * j + k) * D + c0;
+        const int8_t* src = a.Kc + (tok0 + kPq * q + 4 * j + k) * D + c0;
         if constexpr (CW == 8) {
           const uint2 v = *reinterpret_cast<const uint2*>(src);
           kbw[q][k][0] = v.x; kbw[q][k][1] = v.y;
@@ -246,12 +229,18 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
           kbw[q][k][0] = *reinterpret_cast<const unsigned*>(src);
         }
       }
-    __syncthreads();   // the Q^T rows have been read out of the LDS tile
+    // byte i of the thread's four tokens -> one word per channel
+    auto transpose4 = [&](const unsigned* w0, const unsigned* w1, const unsigned* w2, const unsigned* w3, int i) {
+      const int wi = i >> 2, sh = 8 * (i & 3);
+      return ((w0[wi] >> sh) & 0xFFu) | (((w1[wi] >> sh) & 0xFFu) << 8) | (((w2[wi] >> sh) & 0xFFu) << 16) |
+             (((w3[wi] >> sh) & 0xFFu) << 24);
+    };
+    // (the LDS tile is free: the barrier after the dO^T rows)
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
       for (int i = 0; i < CW; ++i)
-        *reinterpret_cast<unsigned*>(tt + (c0 + i) * KR + kTq * q + 4 * j) =
+        *reinterpret_cast<unsigned*>(tt + (c0 + i) * KR + kPq * q + 4 * j) =
             transpose4(kbw[q][0], kbw[q][1], kbw[q][2], kbw[q][3], i);
     __syncthreads();
     int8_t* kt = a.ktp + ((size_t)bh * nb + blk_id) * (size_t)(D * BLK);
@@ -272,54 +261,52 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 
 // ------------------------------------------------------------------------------ bwd_main
 // Workgroup = one key block of BLK keys, NW = BLK/16 waves; wave w owns keys 16w..16w+15 of
-// the block for every 64-query tile (lane l: key 16w + (l & 15), lane group g = l >> 4). The
-// products run on gfx950's 16 x 16 MFMAs. S and dP of query sub-tile t (queries 16t..16t+15)
-// leave query 16t + 4g + r and this lane's key in register r, so each lane ends up holding P
-// and dS of its key for 16 of the tile's queries: the B operand (columns = keys, contraction
-// = the 64 queries) of dV^T = dO^T P and dK^T = Q^T dS, contraction slot 4t + r of lane
-// group g standing for query 16t + 4g + r. The packets store dO^T and Q^T codes in that
-// query order, so no data moves between lanes.
-//   P is quantised on the wave's own 64 x 16 tile (no cross-wave step), so dV runs before
+// the block (lane l: key 16w + (l & 15), lane group g = l >> 4). The query tiles are whole
+// query blocks of BLK rows (one or two 64-row packets, NH = BLK/64), so the block scales of
+// Q and dO are constant over a tile and the int32 products below contract over all of its
+// rows at once. The products run on gfx950's 16 x 16 MFMAs. S and dP of query sub-tile t
+// (rows 16t..16t+15) leave row 16t + 4g + r and this lane's key in register r, so each lane
+// holds P and dS of its key for 16 rows of every packet: the B operand (columns = keys,
+// contraction = queries) of dV^T = dO^T P and dK^T = Q^T dS, contraction slot 4t + r of
+// lane group g standing for row 16t + 4g + r of the packet. The packets store dO^T codes in
+// that order; the Q^T operands come from the row-major Q codes through transposing reads.
+//   P is quantised on the wave's own TQ x 16 tile (no cross-wave step), so dV runs before
 //   the one workgroup barrier of the tile, which publishes the waves' |dS| maxima (dS is
-//   quantised on the 64 x BLK tile). After that barrier nothing reads the tile buffer (the
-//   Q^T operands of dK are loaded into registers before it), and with three tile buffers the
-//   same barrier also hands over the tile two steps ahead: the copies of tile qt+2 are issued
-//   at the top of step qt into the buffer that step qt-1 released.
-//   dS leaves as this lane's 16 codes in one 16-byte store: the spilled tile is dS^T, key-major.
+//   quantised on the TQ x BLK tile, one block). Everything the tile needs from LDS is in
+//   registers before that barrier, so right after it the tile buffer takes the copies of
+//   the tile two steps ahead (two tile buffers); each wave waits for its own copies just
+//   before the next barrier, which publishes them.
+//   dS leaves as this lane's 16 codes per packet in 16-byte stores: the spilled tiles are
+//   dS^T, key-major, one per 64-row packet.
 template <int D, int BLK>
 struct BwdLds {
   using P = Packet<D>;
   static constexpr int NW = BLK / 16;             // waves
-  static constexpr int kBuf = P::kBytes;          // one tile buffer (three of them)
-  static constexpr int offRED = 3 * kBuf;         // |dS| maxima [2][NW] (by step parity)
-  static constexpr int offDST = offRED + 2 * NW * 4;  // atomic mode: dS^T codes [BLK][64]
-  static constexpr int offKT = offDST + BLK * 64;     // atomic mode: K^T codes [D][BLK]
-  static constexpr int kBytesSpill = offDST;
+  static constexpr int NH = BLK / kPq;            // packets per query tile
+  static constexpr int kBuf = NH * P::kBytes;     // one tile buffer (two of them)
+  static constexpr int offRED = 2 * kBuf;         // |dS| maxima [2][NW] (by tile parity)
+  static constexpr int offKT = offRED + 2 * NW * 4;  // atomic mode: K^T codes [D][BLK]
+  static constexpr int kBytesSpill = offKT;
   static constexpr int kBytesAtomic = offKT + D * BLK;
-  // copies per wave of one packet: kCpHi for waves w < kCpSplit, one fewer for the rest
-  static constexpr int kCpHi = (P::kCopies + NW - 1) / NW;
-  static constexpr int kCpSplit = P::kCopies - (kCpHi - 1) * NW;
+  // 1 KB copies of one tile: kCpHi for waves w < kCpSplit, one fewer for the rest
+  static constexpr int kCopies = NH * P::kCopies;
+  static constexpr int kCpHi = (kCopies + NW - 1) / NW;
+  static constexpr int kCpSplit = kCopies - (kCpHi - 1) * NW;
 };
-
-// wait until at most S + C (C = copies of this wave in the current step, if any) vector-memory
-// operations are outstanding: S and C are per-wave-uniform, so the immediate is chosen by branches
-template <int S, int CHI>
-__device__ __forceinline__ void wait_copies_then(bool issued, bool hi) {
-  if (!issued) wait_vmcnt<S>();
-  else if (hi) wait_vmcnt<S + CHI>();
-  else wait_vmcnt<S + CHI - 1>();
-}
 
 template <int DT, int D, int BLK, bool SPILL>
 __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   using L = BwdLds<D, BLK>;
   using P = Packet<D>;
   constexpr int NW = L::NW;        // waves per workgroup
+  constexpr int NH = L::NH;        // packets per query tile
   constexpr int NT = NW * 64;      // threads
+  constexpr int TQ = NH * kPq;     // query rows per tile (= BLK)
+  constexpr int NS = TQ / 16;      // 16-row sub-tiles of a tile
   constexpr int KCH = D / 64;      // 64-channel chunks (INT8 contraction of S)
   constexpr int HCH = D / 32;      // 32-channel chunks (16-bit contraction of dP)
-  constexpr int NCT = D / 16;      // 16-channel output tiles of dV^T and dK^T
-  __shared__ __attribute__((aligned(16))) int8_t lds[SPILL ? L::kBytesSpill : L::kBytesAtomic];
+  constexpr int NCT = D / 16;      // 16-channel output tiles of dV^T, dK^T and dQ
+  __shared__ __attribute__((aligned(1024))) int8_t lds[SPILL ? L::kBytesSpill : L::kBytesAtomic];
 
   const int nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
@@ -330,10 +317,9 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   const int kl = 16 * w + lr;                  // this lane's key inside the block
   const int key = k0 + kl;
   const size_t hrow = (size_t)bh * a.N;
-  const int ntile = a.N / kTq;
-  const int8_t* pkh = a.pk + (size_t)bh * ntile * P::kBytes;   // this head's packets
-  const uint32_t pkh_bytes = (uint32_t)ntile * P::kBytes;
-  const bool cp_hi = w < L::kCpSplit;
+  const int ntq = a.N / TQ;                    // query tiles
+  const int8_t* pkh = a.pk + (size_t)bh * ntq * L::kBuf;    // this head's packets
+  const uint32_t pkh_bytes = (uint32_t)ntq * L::kBuf;
 
   // ---- per-lane constant operands: K codes (B of S) and V (B of dP) of this lane's key
   i32x4 kreg[KCH];
@@ -362,7 +348,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < NCT; ++i) { dk[i] = f32x4{}; dv[i] = f32x4{}; }
 
-  // per-lane byte offsets of the operands inside a tile buffer. The swizzle of row r depends
+  // per-lane byte offsets of the operands inside a packet. The swizzle of row r depends
   // on r & 7 (or on (r >> 1) & 3), which rows 16t + lr share for every t, so each operand
   // address is buffer + one of these offsets + a compile-time constant.
   int oQ[KCH], oDO[HCH];
@@ -370,74 +356,73 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   for (int c = 0; c < KCH; ++c) oQ[c] = P::bQ + lr * D + 16 * swz<D>(lr, 4 * c + g);
 #pragma unroll
   for (int c = 0; c < HCH; ++c) oDO[c] = P::bDO + lr * 2 * D + 16 * swz<2 * D>(lr, 4 * c + g);
-  const int oT = lr * kTq + 16 * swz<kTq>(lr, g);   // dO^T / Q^T codes, channel 16n + lr
+  const int oT = P::bDOT + lr * kPq + 16 * swz<kPq>(lr, g);   // dO^T codes, channel 16n + lr
+  // Q^T operands by transposing reads of the row-major Q codes: for channel tile n, lane
+  // 16g + 2i + h names 8 bytes (channels 16n + 8h ..) of packet row 16(i/4) + 4g + i%4 (and
+  // of that row + 32 for the second read), so lane 16g + m receives channel 16n + m of the
+  // eight rows standing for contraction slots 16g .. 16g+7 (then 16g+8 .. 16g+15). Rows are
+  // D >= 64 bytes with the 16-byte chunks XOR-swizzled, and buffers start on 1 KB
+  // boundaries, so chunk n of the row is this offset XOR 16n.
+  const int oQT = [&] {
+    const int i = lr >> 1, row = 16 * (i >> 2) + 4 * g + (i & 3);
+    return P::bQ + row * D + 16 * swz<D>(row, 0) + 8 * (l & 1);
+  }();
 
-  // copies of packet qt into an LDS tile buffer: wave w moves KB cp = w, w + NW, ... (copies
-  // j in [J0, J1) of this wave)
-  auto issue = [&](int qt, int8_t* dst, auto j0_c, auto j1_c) {
-    constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
+  // copies of query tile qt into a tile buffer: wave w moves KB cp = w, w + NW, ...
+  auto issue = [&](int qt, int8_t* dst) {
 #pragma unroll
-    for (int j = J0; j < J1; ++j) {
+    for (int j = 0; j < L::kCpHi; ++j) {
       const int cp = w + NW * j;
-      if (cp < P::kCopies) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * P::kBytes + cp * 1024);
+      if (cp < L::kCopies) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * L::kBuf + cp * 1024);
     }
   };
-  constexpr int kC = L::kCpHi;
-  using G0 = std::integral_constant<int, 0>;
-  using G1 = std::integral_constant<int, (kC + 2) / 3>;
-  using G2 = std::integral_constant<int, (2 * kC + 2) / 3>;
-  using G3 = std::integral_constant<int, kC>;
-  // vector-memory operations a wave issues per step after the step's copies: the dS^T store
-  // and the dQ multiplier (spill), or the dQ atomics
-  constexpr int WPU = NW / 4;                       // atomic mode: waves per 16-query group
-  constexpr int NCTW = NCT / WPU;                   // ... and their 16-channel dQ tiles
-  constexpr int kStores = SPILL ? 2 : NCTW * 4;
+  // vector-memory operations a wave issues per step after the step's copies: the dS^T
+  // stores and dQ multipliers (spill), or the dQ atomics
+  constexpr int kStores = SPILL ? 2 * NH : NCT * 4;
 
-  const int qt0 = a.causal ? k0 / kTq : 0;
-  issue(qt0, lds, G0{}, G3{});
-  if (qt0 + 1 < ntile) issue(qt0 + 1, lds + L::kBuf, G0{}, G3{});
+  const int qt0 = a.causal ? kb : 0;           // first query tile at or below the diagonal
+  issue(qt0, lds);
+  if (qt0 + 1 < ntq) issue(qt0 + 1, lds + L::kBuf);
   wait_vmcnt<0>();
   __syncthreads();
 
-  int bi = 0;  // buffer of the current tile
-  for (int qt = qt0; qt < ntile; ++qt) {
-    const int q0 = qt * kTq;
+  for (int qt = qt0; qt < ntq; ++qt) {
+    const int q0 = qt * TQ;
     const int step = qt - qt0;
-    const bool issue_next = qt + 2 < ntile;
-    int8_t* buf = lds + bi * L::kBuf;
-    const int bn = bi == 0 ? 2 : bi - 1;             // (bi + 2) % 3: released by the previous step
-    int8_t* nbuf = lds + bn * L::kBuf;
-    if (issue_next) issue(qt + 2, nbuf, G0{}, G1{});
+    const int bofs = (step & 1) * L::kBuf;       // byte offset of this tile's buffer
+    const int8_t* buf = lds + bofs;
 
     const float sQ = *reinterpret_cast<const float*>(buf + P::bSQ);
     const float sdO = *reinterpret_cast<const float*>(buf + P::bSDO);
     const float c2 = (sQ * sK) * (smc * kLog2e);
 
-    // ---- S = Q K~^T and dP = dO V^T for the four 16-query sub-tiles
-    i32x4 s[4];
-    f32x4 dp[4];
+    // ---- S = Q K~^T and dP = dO V^T for the 16-row sub-tiles
+    i32x4 s[NS];
+    f32x4 dp[NS];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NS; ++t) {
+      const int8_t* pb = buf + (t / 4) * P::kBytes;
       s[t] = i32x4{};
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
-        const i32x4 aq = *reinterpret_cast<const i32x4*>(buf + oQ[c] + 16 * t * D);
+        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + oQ[c] + 16 * (t % 4) * D);
         s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
       }
       dp[t] = f32x4{};
 #pragma unroll
       for (int c = 0; c < HCH; ++c) {
-        const u16x8 ad = *reinterpret_cast<const u16x8*>(buf + oDO[c] + 32 * t * D);
+        const u16x8 ad = *reinterpret_cast<const u16x8*>(pb + oDO[c] + 32 * (t % 4) * D);
         dp[t] = mfma_16b_16x16x32<DT>(ad, vreg[c], dp[t]);
       }
     }
-    // ---- P = 2^(S c - lse2), dS = P (dP - D): register r of sub-tile t is query 16t + 4g + r
-    float pf[4][4], dsf[4][4];
+    // ---- P = 2^(S c - lse2), dS = P (dP - D): register r of sub-tile t is row 16t + 4g + r
+    float pf[NS][4], dsf[NS][4];
     auto elems = [&](auto masked) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4 lse2 = *reinterpret_cast<const f32x4*>(buf + P::bLSE + 4 * (16 * t + 4 * g));
-        const f32x4 dvv = *reinterpret_cast<const f32x4*>(buf + P::bDV + 4 * (16 * t + 4 * g));
+      for (int t = 0; t < NS; ++t) {
+        const int8_t* pb = buf + (t / 4) * P::kBytes;
+        const f32x4 lse2 = *reinterpret_cast<const f32x4*>(pb + P::bLSE + 4 * (16 * (t % 4) + 4 * g));
+        const f32x4 dvv = *reinterpret_cast<const f32x4*>(pb + P::bDV + 4 * (16 * (t % 4) + 4 * g));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, -lse2[r]));
@@ -451,110 +436,145 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     };
     if (a.causal && k0 + BLK - 1 > q0) elems(std::true_type{});
     else elems(std::false_type{});
-    if (issue_next) issue(qt + 2, nbuf, G1{}, G2{});
 
     // ---- tile maxima (chains of three-input maxima; the |dS| maximum goes to the workgroup)
     float pm = pf[0][0], dm = fabsf(dsf[0][0]);
 #pragma unroll
-    for (int i = 1; i < 16; i += 2) {
+    for (int i = 1; i < 4 * NS; i += 2) {
       const int t0 = i / 4, r0 = i % 4, t1 = (i + 1) / 4, r1 = (i + 1) % 4;
-      pm = fmaxf(fmaxf(pm, pf[t0][r0]), i + 1 < 16 ? pf[t1][r1] : 0.0f);
-      dm = fmaxf(fmaxf(dm, fabsf(dsf[t0][r0])), i + 1 < 16 ? fabsf(dsf[t1][r1]) : 0.0f);
+      pm = fmaxf(fmaxf(pm, pf[t0][r0]), i + 1 < 4 * NS ? pf[t1][r1] : 0.0f);
+      dm = fmaxf(fmaxf(dm, fabsf(dsf[t0][r0])), i + 1 < 4 * NS ? fabsf(dsf[t1][r1]) : 0.0f);
     }
     wave_max2_nonneg(pm, dm);
     if (l == 0) redD[(step & 1) * NW + w] = dm;
 
-    // ---- P codes on this wave's 64 x 16 tile, then dV^T += dO^T P (int32 over the 64 queries)
+    // ---- P codes on this wave's TQ x 16 tile, then dV^T += dO^T P (int32 over the TQ rows)
     {
       const float pa = fmaxf(pm, FLT_MIN);
       const float pinv = 127.0f * __builtin_amdgcn_rcpf(pa);
       const float sv = pa * (1.0f / 127.0f) * sdO;
-      i32x4 pc;
+      i32x4 pc[NH];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        pc[t] = (int)pack4_lo_bytes(quant_word_fma(pf[t][0], pinv), quant_word_fma(pf[t][1], pinv),
-                                    quant_word_fma(pf[t][2], pinv), quant_word_fma(pf[t][3], pinv));
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float* v = pf[4 * h + t];
+          pc[h][t] = (int)pack4_lo_bytes(quant_word_fma(v[0], pinv), quant_word_fma(v[1], pinv),
+                                         quant_word_fma(v[2], pinv), quant_word_fma(v[3], pinv));
+        }
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + P::bDOT + oT + 16 * n * kTq);
-        const i32x4 acc = mfma_i8_16x16x64(ao, pc, i32x4{});
+        i32x4 acc = i32x4{};
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + h * P::kBytes + oT + 16 * n * kPq);
+          acc = mfma_i8_16x16x64(ao, pc[h], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
       }
     }
-    // Q^T operands of dK, read before the barrier (after it the buffer may be refilled)
-    i32x4 qtr[NCT];
+    // Q^T operands of dK, read before the barrier (after it the buffer is refilled)
+    i32x4 qtr[NH][NCT];
+    {
+      const int qa = bofs + oQT;
 #pragma unroll
-    for (int n = 0; n < NCT; ++n) {
-      qtr[n] = *reinterpret_cast<const i32x4*>(buf + P::bQT + oT + 16 * n * kTq);
+      for (int n = 0; n < NCT; ++n) {
+        const int8_t* pn = lds + (qa ^ (16 * n));
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const i32x2 x0 = lds_read_tr8(pn + h * P::kBytes);
+          const i32x2 x1 = lds_read_tr8(pn + h * P::kBytes + 32 * D);
+          qtr[h][n] = i32x4{x0[0], x0[1], x1[0], x1[1]};
+        }
+      }
     }
-    if (issue_next) issue(qt + 2, nbuf, G2{}, G3{});
     // the copies of tile qt+1 (issued one step ago) must have landed before the barrier that
-    // publishes them; issued after them: last step's stores, this step's copies
-    wait_copies_then<kStores, L::kCpHi>(issue_next, cp_hi);
+    // publishes them; issued after them: last step's stores or atomics
+    wait_vmcnt<kStores>();
     lds_barrier();
+    if constexpr (SPILL) {
+      if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
+    }
 
-    // ---- dS codes on the 64 x BLK tile, dK^T += Q^T dS
+    // ---- dS codes on the TQ x BLK tile (one block), dK^T += Q^T dS
     float da = redD[(step & 1) * NW];
 #pragma unroll
     for (int i = 1; i < NW; ++i) da = fmaxf(da, redD[(step & 1) * NW + i]);
     da = fmaxf(da, FLT_MIN);
     const float dinv = 127.0f * __builtin_amdgcn_rcpf(da);
     const float sdS = da * (1.0f / 127.0f);
-    i32x4 dc;
+    i32x4 dc[NH];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      dc[t] = (int)pack4_lo_bytes(quant_word_fma(dsf[t][0], dinv), quant_word_fma(dsf[t][1], dinv),
-                                  quant_word_fma(dsf[t][2], dinv), quant_word_fma(dsf[t][3], dinv));
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float* v = dsf[4 * h + t];
+        dc[h][t] = (int)pack4_lo_bytes(quant_word_fma(v[0], dinv), quant_word_fma(v[1], dinv),
+                                       quant_word_fma(v[2], dinv), quant_word_fma(v[3], dinv));
+      }
     {
       const float sk = smc * sdS * sQ;
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        const i32x4 acc = mfma_i8_16x16x64(qtr[n], dc, i32x4{});
+        i32x4 acc = i32x4{};
+#pragma unroll
+        for (int h = 0; h < NH; ++h) acc = mfma_i8_16x16x64(qtr[h][n], dc[h], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(sk, (float)acc[r], dk[n][r]);
       }
     }
 
     if constexpr (SPILL) {
-      // ---- the dS^T tile [BLK][64] for the query-major dQ pass: key row kl, chunk g (queries
-      //      in the contraction order above) at slot swz<64>(kl, g); and its dQ multiplier
-      const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt);
-      *reinterpret_cast<i32x4*>(a.dsp + ti * (kTq * BLK) + kl * kTq + 16 * swz<kTq>(kl, g)) = dc;
-      if (l == 0) a.dsm[ti] = smc * sdS * sK;   // every wave stores the same value
-    } else {
-      // ---- dQ = dS K on the 64 x BLK tile, added to the float32 accumulator with atomics:
-      //      the dS^T tile goes through LDS once and is read back query by query (transposing
-      //      reads); wave w computes query group u = w % 4 for its share of the channel tiles
-      *reinterpret_cast<i32x4*>(lds + L::offDST + kl * kTq + 16 * swz<kTq>(kl, g)) = dc;
-      lds_barrier();
-      const int u = w % 4, n0 = (w / 4) * NCTW;
-      i32x4 acc[NCTW];
+      // ---- the dS^T tile of each packet [BLK][64] for the query-major dQ pass: key row kl,
+      //      chunk g (rows in the contraction order above) at slot swz<64>(kl, g); and its
+      //      dQ multiplier (the same for the tile's packets)
+      const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt * NH);
 #pragma unroll
-      for (int n = 0; n < NCTW; ++n) acc[n] = i32x4{};
+      for (int h = 0; h < NH; ++h) {
+        *reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq + 16 * swz<kPq>(kl, g)) = dc[h];
+        if (l == 0) a.dsm[ti + h] = smc * sdS * sK;   // every wave stores the same value
+      }
+    } else {
+      // ---- dQ = dS K on the TQ x BLK tile, added to the float32 accumulator with atomics.
+      //      The dS^T tile [BLK][TQ] goes through the released tile buffer once (chunk
+      //      4h + g of key row kl at slot swz<TQ>(kl, 4h + g)) and is read back query by
+      //      query (transposing reads); wave w computes query chunk w against all channels.
+      int8_t* dst = lds + bofs;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        *reinterpret_cast<i32x4*>(dst + kl * TQ + 16 * swz<TQ>(kl, 4 * h + g)) = dc[h];
+      lds_barrier();
+      i32x4 acc[NCT];
+#pragma unroll
+      for (int n = 0; n < NCT; ++n) acc[n] = i32x4{};
 #pragma unroll
       for (int kc = 0; kc < BLK / 64; ++kc) {
         const int i = lr >> 1, hh = l & 1;
         const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
-        const i32x2 x0 = lds_read_tr8(lds + L::offDST + r0 * kTq + 16 * swz<kTq>(r0, u) + 8 * hh);
-        const i32x2 x1 = lds_read_tr8(lds + L::offDST + r1 * kTq + 16 * swz<kTq>(r1, u) + 8 * hh);
+        const i32x2 x0 = lds_read_tr8(dst + r0 * TQ + 16 * swz<TQ>(r0, w) + 8 * hh);
+        const i32x2 x1 = lds_read_tr8(dst + r1 * TQ + 16 * swz<TQ>(r1, w) + 8 * hh);
         const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
-        for (int n = 0; n < NCTW; ++n) {
-          const int c = 16 * (n0 + n) + lr;
+        for (int n = 0; n < NCT; ++n) {
+          const int c = 16 * n + lr;
           const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
           acc[n] = mfma_i8_16x16x64(as, bk, acc[n]);
         }
       }
-      // result: query position 16u + 4g + r = query 16g + 4u + r of the tile, channel 16n + lr
+      // every wave has read the staged tile: the buffer takes the tile two steps ahead
+      lds_barrier();
+      if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
+      // result: query chunk w = 4h' + u of the tile, position 4g + r = row 16g + 4u + r of
+      // packet h'
       const float sc = smc * sdS * sK;
+      const int qrow = q0 + kPq * (w / 4) + 16 * g + 4 * (w % 4);
 #pragma unroll
-      for (int n = 0; n < NCTW; ++n)
+      for (int n = 0; n < NCT; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          unsafeAtomicAdd(a.dq_acc + (hrow + q0 + 16 * g + 4 * u + r) * D + 16 * (n0 + n) + lr, sc * (float)acc[n][r]);
+          unsafeAtomicAdd(a.dq_acc + (hrow + qrow + r) * D + 16 * n + lr, sc * (float)acc[n][r]);
     }
-    bi = bi == 2 ? 0 : bi + 1;
   }
 
   // ---- epilogue: dV and dK (RMSNorm backward with K^ = K * rstd) for this lane's key;
@@ -626,14 +646,14 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   using L = DqLds<D, BLK>;
   constexpr int NCT = D / 16;                       // 16-channel output tiles
   __shared__ __attribute__((aligned(16))) int8_t lds[L::kBytes];
-  const int ntile = a.N / kTq, nb = a.N / BLK;
+  const int ntile = a.N / kPq, nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
   const int qt = a.causal ? ntile - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);
-  const int q0 = qt * kTq;
+  const int q0 = qt * kPq;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 4, lr = l & 15;
-  const int kb_last = a.causal ? (q0 + kTq - 1) / BLK : nb - 1;
-  const int8_t* dsh = a.dsp + (size_t)bh * a.spill_tiles * (kTq * BLK);
-  const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kTq * BLK));
+  const int kb_last = a.causal ? (q0 + kPq - 1) / BLK : nb - 1;
+  const int8_t* dsh = a.dsp + (size_t)bh * a.spill_tiles * (kPq * BLK);
+  const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kPq * BLK));
   const float* dmh = a.dsm + (size_t)bh * a.spill_tiles;
   const int8_t* kth = a.ktp + (size_t)bh * nb * (D * BLK);
   const uint32_t kth_bytes = (uint32_t)nb * (D * BLK);
@@ -642,7 +662,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
     const long long ti = spill_tile_index(a.N, BLK, a.causal, kb, qt);
     for (int cp = w; cp < L::kCopiesDS + L::kCopiesKT; cp += 4) {
       if (cp < L::kCopiesDS)
-        buffer_to_lds16(dsh, dsh_bytes, buf + L::bDS + cp * 1024, 16 * l, (uint32_t)(ti * (kTq * BLK)) + cp * 1024);
+        buffer_to_lds16(dsh, dsh_bytes, buf + L::bDS + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
       else
         buffer_to_lds16(kth, kth_bytes, buf + L::bKT + (cp - L::kCopiesDS) * 1024, 16 * l,
                         (uint32_t)kb * (D * BLK) + (cp - L::kCopiesDS) * 1024);
@@ -668,8 +688,8 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
       // A: keys 64kc + 16g .. +15 of query position 16w + lr, two transposing reads of 8 keys
       const int i = lr >> 1, hh = l & 1;
       const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
-      const i32x2 x0 = lds_read_tr8(buf + L::bDS + r0 * kTq + 16 * swz<kTq>(r0, w) + 8 * hh);
-      const i32x2 x1 = lds_read_tr8(buf + L::bDS + r1 * kTq + 16 * swz<kTq>(r1, w) + 8 * hh);
+      const i32x2 x0 = lds_read_tr8(buf + L::bDS + r0 * kPq + 16 * swz<kPq>(r0, w) + 8 * hh);
+      const i32x2 x1 = lds_read_tr8(buf + L::bDS + r1 * kPq + 16 * swz<kPq>(r1, w) + 8 * hh);
       const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
@@ -695,7 +715,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   __syncthreads();
   constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
   const size_t hrow = (size_t)bh * a.N;
-  for (int e = threadIdx.x; e < kTq * CPR; e += 256) {
+  for (int e = threadIdx.x; e < kPq * CPR; e += 256) {
     const int r = e / CPR, c = (e % CPR) * 8;
     const size_t tok = hrow + q0 + r;
     float v[8];
@@ -775,7 +795,7 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
   }
   if (part < 0 || part == 2) {
     if (a.spill)
-      return launch_kernel(&bwd_dq<DT, D, BLK>, dim3((unsigned)((long long)(a.N / kTq) * a.BH)), dim3(256), st, a);
+      return launch_kernel(&bwd_dq<DT, D, BLK>, dim3((unsigned)((long long)(a.N / kPq) * a.BH)), dim3(256), st, a);
     const long long threads = (long long)a.BH * a.N * (D / 8);
     return launch_kernel(&dq_finalize<DT, D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), st, a);
   }

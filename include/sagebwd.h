@@ -24,8 +24,8 @@
  *   P~ (forward)   : SAGEBWD_FWD_TILE_Q query rows x blk keys; the online-softmax running
  *                    max moves once per such tile and P~ = exp(s - running max); the row
  *                    sum l accumulates P~ before quantisation.
- *   P  (backward)  : SAGEBWD_BWD_TILE_Q query rows x SAGEBWD_BWD_P_TILE_K keys.
- *   dS (backward)  : SAGEBWD_BWD_TILE_Q query rows x blk keys.
+ *   P  (backward)  : blk query rows (one query block) x SAGEBWD_BWD_P_TILE_K keys.
+ *   dS (backward)  : blk query rows x blk keys (one block of dS).
  * Every tile lies inside one blk x blk block, so the block scales factor out of each
  * integer product.
  *
@@ -54,7 +54,6 @@ extern "C" {
 #endif
 
 #define SAGEBWD_FWD_TILE_Q 32
-#define SAGEBWD_BWD_TILE_Q 64
 #define SAGEBWD_BWD_P_TILE_K 16
 
 typedef enum {
@@ -137,7 +136,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
 
 /* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
  * boundary, in this order; "chunk" = 16 bytes):
- *   packets [B,H,N/64] x P bytes     P = 21504 for d = 64, 41984 for d = 128: for each head
+ *   packets [B,H,N/64] x P bytes     P = 17408 for d = 64, 33792 for d = 128: for each head
  *           and each 64-token tile, the tile's data in the order the key-block kernel copies
  *           it into LDS (r = token inside the tile, c = channel):
  *     [0, 64d)      Q codes [64][d]; chunk j of row r stored at chunk j^(r&7) (d = 128) or
@@ -146,8 +145,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *     [192d, 256d)  dO INT8 codes, channel-major [d][64]: token u of row c at byte
  *                   16*((u>>2)&3) + 4*(u>>4) + (u&3), then chunk j of row c stored at
  *                   chunk j^((c>>1)&3)
- *     [256d, 320d)  Q codes, channel-major, same order as the dO codes
- *     [320d, +256)  lse * log2(e), float32 [64]
+ *     [256d, +256)  lse * log2(e), float32 [64]
  *     [+256, +512)  D = rowsum(dO o O), float32 [64]
  *     [+512, +516)  the Q block scale; [+516, +520) the dO block scale (float32); padding
  * then, with dq_mode ATOMIC:
@@ -184,7 +182,8 @@ sagebwd_status sagebwd_backward(const sagebwd_params* p,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of sagebwd_backward, for callers that schedule or time the stages apart:
- *   part 0: D = rowsum(dO o O), dO codes/scales, Qc transposed, dq_acc zeroed
+ *   part 0: D = rowsum(dO o O), dO codes/scales, the packets (and K^T codes or a zeroed
+ *           dq_acc)
  *   part 1: the fused key-block kernel (S, P, dP, dS; dV, dK final; dQ^ accumulated)
  *   part 2: dQ = RMSNorm backward of dq_acc, rounded to the dtype
  * Arguments as for sagebwd_backward. Running parts 0, 1, 2 in order on one stream with the

@@ -30,7 +30,7 @@ def spec_for(w: wl.Workload, dtype: Optional[str] = None) -> oq.Spec:
     c = header_constants()
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
-                   fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=c["BWD_TILE_Q"], bwd_pk=c["BWD_P_TILE_K"],
+                   fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
                    bwd_sk=w.blk)
 
 
@@ -120,7 +120,7 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
     pos = 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
     codes = logical[..., pos]                                                         # [B,H,nt,d,64]
     dOtc = np.moveaxis(codes, 2, 3).reshape(w.B, w.H, d, w.N)
-    base = 320 * d
+    base = 256 * d
     Dv = pk[..., base + 256:base + 512].copy().view(np.float32).reshape(w.B, w.H, w.N)
     sdo_tiles = pk[..., base + 516:base + 520].copy().view(np.float32).reshape(w.B, w.H, nt)
     dOs = sdo_tiles[..., :: w.blk // 64]

@@ -31,7 +31,7 @@ def test_exports_every_header_symbol():
 
 def test_header_tile_constants_match_binding():
     c = header_constants()
-    assert (c["FWD_TILE_Q"], c["BWD_TILE_Q"], c["BWD_P_TILE_K"]) == (_lib.FWD_TILE_Q, _lib.BWD_TILE_Q, _lib.BWD_P_TILE_K)
+    assert (c["FWD_TILE_Q"], c["BWD_P_TILE_K"]) == (_lib.FWD_TILE_Q, _lib.BWD_P_TILE_K)
 
 
 def test_status_strings():
@@ -89,9 +89,9 @@ def test_workspace_checks():
     up = lambda x: (x + 255) // 256 * 256
     # auto -> dS spill at this size: packets, K^T packets, dS tiles, multipliers
     tiles = 4 * 4 - 4 * 3 // 2          # nb * nt - (blk/64) * nb * (nb - 1) / 2, causal
-    assert need == up(2 * 4 * 21504) + up(2 * 4 * 64 * 64) + up(2 * tiles * 64 * 64) + up(2 * tiles * 4)
+    assert need == up(2 * 4 * 17408) + up(2 * 4 * 64 * 64) + up(2 * tiles * 64 * 64) + up(2 * tiles * 4)
     atomic = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=2)))
-    assert atomic == up(2 * 4 * 21504) + up(4 * n)
+    assert atomic == up(2 * 4 * 17408) + up(4 * n)
     assert _backward(p, ws_bytes=need - 1) == -5
     assert _backward(p, ws=0) == -1
     assert _backward(p, ws=MIS) == -4
@@ -111,7 +111,7 @@ def test_spill_needs_per_head_tiles_below_4gib():
     # auto falls back to the atomic layout (packets + float32 dQ accumulator)
     up = lambda x: (x + 255) // 256 * 256
     auto = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=0, **big)))
-    assert auto == up(131072 // 64 * 41984) + up(4 * 131072 * 128)
+    assert auto == up(131072 // 64 * 33792) + up(4 * 131072 * 128)
     # N = 65536 still spills (2.1 GB per head)
     assert lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=1, B=1, H=1, N=65536, d=128, blk=128))) > 0
 

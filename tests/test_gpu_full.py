@@ -76,7 +76,7 @@ def test_full_shape_long_sequence_sampled():
     pro = oq.prologue(xh["Qf"], xh["Kf"], xh["Vf"], spec)
     N, tq, btq, sk = w.N, spec.fwd_tq, spec.bwd_tq, spec.sk
     k_blocks = [N // sk - 2, N // sk - 1]                   # dK, dV: last two key blocks
-    q_bwd = [3, 170, N // btq - 1]                          # dQ: sampled 64-row query tiles
+    q_bwd = [3, 170, N // btq - 1]                          # dQ: sampled query tiles (btq rows)
     rows = set(range(k_blocks[0] * sk, N))                  # rows the sampled pairs need O/LSE for
     for it in q_bwd:
         rows |= set(range(it * btq, (it + 1) * btq))
