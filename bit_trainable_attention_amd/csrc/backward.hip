@@ -621,31 +621,38 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 
 // ------------------------------------------------------------------------------ bwd_dq
 // Query-major dQ pass over the spilled dS^T tiles: one workgroup (4 waves) per (head, 64-query
-// tile). For every key block up to the diagonal, the tile's dS^T codes [BLK][64] and the
-// block's K^T codes [D][BLK] stream through double-buffered LDS (buffer->LDS copies), and
-// dQ^ += m(kb) * (dS_codes . K_codes) runs on v_mfma_i32_16x16x64_i8 with float32
-// accumulation in registers (m = sm_scale * s_dS * s_K of the tile). The A operand (rows =
-// queries, contraction = keys) comes from the key-major dS^T tile through transposing LDS
-// reads. Wave w computes query positions 16w..16w+15 of the spilled order (position
-// 16g + 4t + r is query 16t + 4g + r) against all channels. The epilogue applies the RMSNorm
-// backward and writes dQ in the dtype; no float32 dQ buffer and no atomics.
+// tile). For every key block up to the diagonal, dQ^ += m(kb) * (dS_codes . K_codes) runs on
+// v_mfma_i32_16x16x64_i8 with float32 accumulation in registers (m = sm_scale * s_dS * s_K of
+// the tile). The tile's dS^T codes [BLK][64] stream through a ring of three LDS buffers
+// (buffer->LDS copies issued two key blocks ahead) and are read back query-major with
+// transposing reads: the A operand (rows = queries, contraction = keys). Wave w computes all
+// 64 queries against its own NPW 16-channel tiles, so it needs only those channels of the
+// block's K^T codes (the B operand), which it loads straight into registers one key block
+// ahead (they come from L2). Positions follow the spilled order (position 16g + 4t + r is
+// query 16t + 4g + r). The epilogue applies the RMSNorm backward and writes dQ in the dtype;
+// no float32 dQ buffer and no atomics.
 template <int D, int BLK>
 struct DqLds {
-  static constexpr int bDS = 0;                     // dS^T codes [BLK][64], rows swizzled
-  static constexpr int bKT = 64 * BLK;              // K^T codes [D][BLK], rows swizzled
-  static constexpr int bM = bKT + D * BLK;          // tile multiplier (first word)
-  static constexpr int kBuf = bM + 1024;
-  static constexpr int kCopiesDS = 64 * BLK / 1024;
-  static constexpr int kCopiesKT = D * BLK / 1024;
-  // the epilogue reuses the buffers for the dQ^ tile [64][D] f32
-  static constexpr int kBytes = 2 * kBuf > 64 * D * 4 ? 2 * kBuf : 64 * D * 4;
+  static constexpr int kTile = kPq * BLK;           // one dS^T tile [BLK][64]
+  static constexpr int bM = kTile;                  // then its dQ multiplier (first word)
+  static constexpr int kBuf = kTile + 1024;         // one ring slot
+  static constexpr int kCopiesPerWave = kTile / 1024 / 4;
+  // slot 0 also holds the epilogue's dQ^ tile [64][D] f32
+  static constexpr int kBytes0 = kBuf > kPq * D * 4 ? kBuf : kPq * D * 4;
 };
 
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   using L = DqLds<D, BLK>;
-  constexpr int NCT = D / 16;                       // 16-channel output tiles
-  __shared__ __attribute__((aligned(16))) int8_t lds[L::kBytes];
+  constexpr int NCT = D / 16;                       // 16-channel tiles of dQ
+  constexpr int NPW = NCT / 4;                      // ... per wave
+  constexpr int KC = BLK / 64;                      // 64-key chunks of a block
+  constexpr int CPW = L::kCopiesPerWave;
+  // The three ring slots are distinct LDS objects, so the compiler sees that the reads of one
+  // slot never alias the copies in flight into another (and inserts no wait for them).
+  __shared__ __attribute__((aligned(1024))) int8_t slot0[L::kBytes0];
+  __shared__ __attribute__((aligned(1024))) int8_t slot1[L::kBuf];
+  __shared__ __attribute__((aligned(1024))) int8_t slot2[L::kBuf];
   const int ntile = a.N / kPq, nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
   const int qt = a.causal ? ntile - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);
@@ -656,62 +663,115 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kPq * BLK));
   const float* dmh = a.dsm + (size_t)bh * a.spill_tiles;
   const int8_t* kth = a.ktp + (size_t)bh * nb * (D * BLK);
-  const uint32_t kth_bytes = (uint32_t)nb * (D * BLK);
-
-  auto issue = [&](int kb, int8_t* buf) {
-    const long long ti = spill_tile_index(a.N, BLK, a.causal, kb, qt);
-    for (int cp = w; cp < L::kCopiesDS + L::kCopiesKT; cp += 4) {
-      if (cp < L::kCopiesDS)
-        buffer_to_lds16(dsh, dsh_bytes, buf + L::bDS + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
-      else
-        buffer_to_lds16(kth, kth_bytes, buf + L::bKT + (cp - L::kCopiesDS) * 1024, 16 * l,
-                        (uint32_t)kb * (D * BLK) + (cp - L::kCopiesDS) * 1024);
-    }
-    if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4), buf + L::bM, 4 * l, (uint32_t)(ti * 4));
+  auto slot = [&](auto s_c) -> int8_t* {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (S == 0) return slot0;
+    else if constexpr (S == 1) return slot1;
+    else return slot2;
   };
 
-  f32x4 dq[NCT];
+  // this wave's share of the copies of key block kb's dS^T tile (and, by wave 3, of its
+  // multiplier) into ring slot S
+  auto issue_ds = [&](int kb, auto s_c) {
+    const long long ti = spill_tile_index(a.N, BLK, a.causal, kb, qt);
+    int8_t* dst = slot(s_c);
 #pragma unroll
-  for (int i = 0; i < NCT; ++i) dq[i] = f32x4{};
-  issue(0, lds);
-  wait_vmcnt<0>();
-  __syncthreads();
-  for (int kb = 0; kb <= kb_last; ++kb) {
-    int8_t* buf = lds + (kb & 1) * L::kBuf;
-    if (kb < kb_last) issue(kb + 1, lds + ((kb & 1) ^ 1) * L::kBuf);
+    for (int j = 0; j < CPW; ++j) {
+      const int cp = w + 4 * j;
+      buffer_to_lds16(dsh, dsh_bytes, dst + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
+    }
+    if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4), dst + L::bM, 4 * l, (uint32_t)(ti * 4));
+  };
+  // K^T operands of key block kb: channel c = 16(NPW w + n) + lr, keys 64kc + 16g .. +15
+  // (chunk 4kc + g of row c, at slot swz<BLK>(c, 4kc + g))
+  i32x4 kt_next[NPW][KC];
+  auto load_kt = [&](int kb) {
+    const int8_t* kbp = kth + (size_t)kb * (D * BLK);
+#pragma unroll
+    for (int n = 0; n < NPW; ++n)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int c = 16 * (NPW * w + n) + lr;
+        kt_next[n][kc] = *reinterpret_cast<const i32x4*>(kbp + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
+      }
+  };
+
+  f32x4 dq[4][NPW];
+#pragma unroll
+  for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) dq[qs][n] = f32x4{};
+
+  // One key block, in ring slot S. Issue order per block: K^T of the next block, then the
+  // copies of the block two ahead, so when a block's operands are awaited only the next
+  // block's copies were issued after them (vector-memory operations complete in order). Past
+  // the last block the same operations are issued for the last block again (into the freed
+  // slot, never read), which keeps that count fixed. The barrier publishes the block's tile
+  // and frees the slot of the previous block for the block two ahead.
+  auto step = [&](int kb, auto s_c) {
+    constexpr int S = decltype(s_c)::value;
+    if (w == 3) wait_vmcnt<CPW + 1>();
+    else wait_vmcnt<CPW>();
+    lds_barrier();
+    i32x4 kt[NPW][KC];
+#pragma unroll
+    for (int n = 0; n < NPW; ++n)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kt[n][kc] = kt_next[n][kc];
+    load_kt(min(kb + 1, kb_last));
+    issue_ds(min(kb + 2, kb_last), std::integral_constant<int, (S + 2) % 3>{});
+    const int8_t* buf = slot(s_c);
     const float m = *reinterpret_cast<const float*>(buf + L::bM);
-    i32x4 acc[NCT];
+    i32x4 acc[4][NPW];
 #pragma unroll
-    for (int n = 0; n < NCT; ++n) acc[n] = i32x4{};
+    for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-    for (int kc = 0; kc < BLK / 64; ++kc) {
-      // A: keys 64kc + 16g .. +15 of query position 16w + lr, two transposing reads of 8 keys
+      for (int n = 0; n < NPW; ++n) acc[qs][n] = i32x4{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      // A: keys 64kc + 16g .. +15 of query position 16qs + lr, two transposing reads of 8 keys
       const int i = lr >> 1, hh = l & 1;
       const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
-      const i32x2 x0 = lds_read_tr8(buf + L::bDS + r0 * kPq + 16 * swz<kPq>(r0, w) + 8 * hh);
-      const i32x2 x1 = lds_read_tr8(buf + L::bDS + r1 * kPq + 16 * swz<kPq>(r1, w) + 8 * hh);
-      const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
-      for (int n = 0; n < NCT; ++n) {
-        const int c = 16 * n + lr;
-        const i32x4 bk = *reinterpret_cast<const i32x4*>(buf + L::bKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
-        acc[n] = mfma_i8_16x16x64(as, bk, acc[n]);
+      for (int qs = 0; qs < 4; ++qs) {
+        const i32x2 x0 = lds_read_tr8(buf + r0 * kPq + 16 * swz<kPq>(r0, qs) + 8 * hh);
+        const i32x2 x1 = lds_read_tr8(buf + r1 * kPq + 16 * swz<kPq>(r1, qs) + 8 * hh);
+        const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+        for (int n = 0; n < NPW; ++n) acc[qs][n] = mfma_i8_16x16x64(as, kt[n][kc], acc[qs][n]);
       }
     }
 #pragma unroll
-    for (int n = 0; n < NCT; ++n)
+    for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dq[n][r] = __builtin_fmaf(m, (float)acc[n][r], dq[n][r]);
-    wait_vmcnt<0>();   // the next key block's copies (the only vector-memory operations here)
-    lds_barrier();
+      for (int n = 0; n < NPW; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[qs][n][r] = __builtin_fmaf(m, (float)acc[qs][n][r], dq[qs][n][r]);
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  issue_ds(0, S0{});
+  load_kt(0);
+  issue_ds(min(1, kb_last), S1{});
+  for (int kb = 0; kb <= kb_last; kb += 3) {
+    step(kb, S0{});
+    if (kb + 1 <= kb_last) step(kb + 1, S1{});
+    if (kb + 2 <= kb_last) step(kb + 2, S2{});
   }
-  // ---- epilogue: dQ^ tile to LDS [64][D] f32 (position 16w + 4g + r = query 16g + 4w + r),
-  //      then RMSNorm backward row by row
-  float* t = reinterpret_cast<float*>(lds);
+  // every wave is done with the ring (and every copy has landed) before slot 0 takes the tile
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // ---- epilogue: dQ^ tile to LDS [64][D] f32, then RMSNorm backward row by row
+  float* t = reinterpret_cast<float*>(slot0);
 #pragma unroll
-  for (int n = 0; n < NCT; ++n)
+  for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) t[(16 * g + 4 * w + r) * D + 16 * n + lr] = dq[n][r];
+    for (int n = 0; n < NPW; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[(16 * g + 4 * qs + r) * D + 16 * (NPW * w + n) + lr] = dq[qs][n][r];
   __syncthreads();
   constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
   const size_t hrow = (size_t)bh * a.N;
