@@ -64,11 +64,27 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 }  // namespace
 
+// Chunk swizzles of the packets' row-major regions (16-byte chunk j of row r is stored at
+// chunk slot swz_q / swz_do). For d = 128 they follow measured LDS rates on gfx950: with
+// j ^ (r & 7), the 256-byte dO rows read at ~117 B/clk per CU (j ^ (r & 15): ~204), and the
+// transposing reads of the Q rows, which name rows r and r + 16 together, at ~116 B/clk
+// (folding bit 4 of the row into the swizzle: ~175). d = 64 keeps the generic swizzle.
+template <int D>
+__device__ __forceinline__ int swz_q(int r, int j) {
+  if constexpr (D == 128) return j ^ (((r >> 1) ^ ((r >> 4) << 2)) & 7);
+  else return swz<D>(r, j);
+}
+template <int D>
+__device__ __forceinline__ int swz_do(int r, int j) {
+  if constexpr (D == 128) return j ^ (r & 15);
+  else return swz<2 * D>(r, j);
+}
+
 // Layout of one 64-query tile packet (= of one LDS tile buffer), bytes.
 template <int D>
 struct Packet {
-  static constexpr int bQ = 0;                // Q codes [64][D], chunk j of row r at slot swz<D>(r, j)
-  static constexpr int bDO = 64 * D;          // dO [64][D] 16-bit, chunk j of row r at slot swz<2D>(r, j)
+  static constexpr int bQ = 0;                // Q codes [64][D], chunk j of row r at slot swz_q<D>(r, j)
+  static constexpr int bDO = 64 * D;          // dO [64][D] 16-bit, chunk j of row r at slot swz_do<D>(r, j)
   static constexpr int bDOT = bDO + 128 * D;  // dO codes [D][64], token u at tile_token_pos(u), chunk swz<64>(c, j)
   static constexpr int bLSE = bDOT + 64 * D;  // lse * log2(e) [64] f32
   static constexpr int bDV = bLSE + 256;      // D = rowsum(dO o O) [64] f32
@@ -135,7 +151,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
       if constexpr (CW == 8) {
         const u16x8 dv = *reinterpret_cast<const u16x8*>(dsrc);
         const u16x8 ov = *reinterpret_cast<const u16x8*>(osrc);
-        *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, ch)) = dv;
+        *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz_do<D>(r, ch)) = dv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           x[q][k][i] = to_f32<DT>(dv[i]);
@@ -144,7 +160,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
       } else {
         const u16x4 dv = *reinterpret_cast<const u16x4*>(dsrc);
         const u16x4 ov = *reinterpret_cast<const u16x4*>(osrc);
-        *reinterpret_cast<u16x4*>(pk + P::bDO + r * 2 * D + 16 * swz<2 * D>(r, ch >> 1) + 8 * (ch & 1)) = dv;
+        *reinterpret_cast<u16x4*>(pk + P::bDO + r * 2 * D + 16 * swz_do<D>(r, ch >> 1) + 8 * (ch & 1)) = dv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[q][k][i] = to_f32<DT>(dv[i]);
@@ -206,10 +222,10 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
       const int r = 4 * j + k;
       const int8_t* src = a.Qc + (tok0 + kPq * q + r) * D + c0;
       if constexpr (CW == 8)
-        *reinterpret_cast<uint2*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 1) + 8 * (ch & 1)) =
+        *reinterpret_cast<uint2*>(pk + P::bQ + r * D + 16 * swz_q<D>(r, ch >> 1) + 8 * (ch & 1)) =
             *reinterpret_cast<const uint2*>(src);
       else
-        *reinterpret_cast<unsigned*>(pk + P::bQ + r * D + 16 * swz<D>(r, ch >> 2) + 4 * (ch & 3)) =
+        *reinterpret_cast<unsigned*>(pk + P::bQ + r * D + 16 * swz_q<D>(r, ch >> 2) + 4 * (ch & 3)) =
             *reinterpret_cast<const unsigned*>(src);
     }
   }
@@ -348,14 +364,15 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int i = 0; i < NCT; ++i) { dk[i] = f32x4{}; dv[i] = f32x4{}; }
 
-  // per-lane byte offsets of the operands inside a packet. The swizzle of row r depends
-  // on r & 7 (or on (r >> 1) & 3), which rows 16t + lr share for every t, so each operand
-  // address is buffer + one of these offsets + a compile-time constant.
+  // per-lane byte offsets of the operands inside a packet. Rows 16t + lr share their
+  // swizzle for every t, except that at d = 128 the Q rows of odd t have bit 2 of the slot
+  // flipped, i.e. their 64-channel chunks swapped (swz_q); so each operand address is
+  // buffer + one of these offsets + a compile-time constant.
   int oQ[KCH], oDO[HCH];
 #pragma unroll
-  for (int c = 0; c < KCH; ++c) oQ[c] = P::bQ + lr * D + 16 * swz<D>(lr, 4 * c + g);
+  for (int c = 0; c < KCH; ++c) oQ[c] = P::bQ + lr * D + 16 * swz_q<D>(lr, 4 * c + g);
 #pragma unroll
-  for (int c = 0; c < HCH; ++c) oDO[c] = P::bDO + lr * 2 * D + 16 * swz<2 * D>(lr, 4 * c + g);
+  for (int c = 0; c < HCH; ++c) oDO[c] = P::bDO + lr * 2 * D + 16 * swz_do<D>(lr, 4 * c + g);
   const int oT = P::bDOT + lr * kPq + 16 * swz<kPq>(lr, g);   // dO^T codes, channel 16n + lr
   // Q^T operands by transposing reads of the row-major Q codes: for channel tile n, lane
   // 16g + 2i + h names 8 bytes (channels 16n + 8h ..) of packet row 16(i/4) + 4g + i%4 (and
@@ -365,7 +382,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   // boundaries, so chunk n of the row is this offset XOR 16n.
   const int oQT = [&] {
     const int i = lr >> 1, row = 16 * (i >> 2) + 4 * g + (i & 3);
-    return P::bQ + row * D + 16 * swz<D>(row, 0) + 8 * (l & 1);
+    return P::bQ + row * D + 16 * swz_q<D>(row, 0) + 8 * (l & 1);
   }();
 
   // copies of query tile qt into a tile buffer: wave w moves KB cp = w, w + NW, ...
@@ -405,7 +422,8 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
       s[t] = i32x4{};
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
-        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + oQ[c] + 16 * (t % 4) * D);
+        const int cq = D == 128 ? c ^ (t & 1) : c;   // (t % 4) & 1 == t & 1
+        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + oQ[cq] + 16 * (t % 4) * D);
         s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
       }
       dp[t] = f32x4{};

@@ -139,9 +139,10 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *   packets [B,H,N/64] x P bytes     P = 17408 for d = 64, 33792 for d = 128: for each head
  *           and each 64-token tile, the tile's data in the order the key-block kernel copies
  *           it into LDS (r = token inside the tile, c = channel):
- *     [0, 64d)      Q codes [64][d]; chunk j of row r stored at chunk j^(r&7) (d = 128) or
- *                   j^((r>>1)&3) (d = 64)
- *     [64d, 192d)   dO [64][d], 16-bit; chunk j of row r stored at chunk j^(r&7)
+ *     [0, 64d)      Q codes [64][d]; chunk j of row r stored at chunk
+ *                   j^(((r>>1)^((r>>4)<<2))&7) (d = 128) or j^((r>>1)&3) (d = 64)
+ *     [64d, 192d)   dO [64][d], 16-bit; chunk j of row r stored at chunk j^(r&15) (d = 128)
+ *                   or j^(r&7) (d = 64)
  *     [192d, 256d)  dO INT8 codes, channel-major [d][64]: token u of row c at byte
  *                   16*((u>>2)&3) + 4*(u>>4) + (u&3), then chunk j of row c stored at
  *                   chunk j^((c>>1)&3)
