@@ -160,7 +160,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *   dsp     [B,H,T] x 64*blk         INT8 dS codes of each tile, key-major [blk][64]:
  *                                    token u of the query tile at byte position
  *                                    16*((u>>2)&3) + 4*(u>>4) + (u&3) of the key's row,
- *                                    then chunk j of row k stored at chunk j^((k>>1)&3)
+ *                                    then chunk j of row k stored at chunk
+ *                                    j^(((k>>1)^(k>>4))&3)
  *   dsm     float32 [B,H,T]          sm_scale * (dS tile scale) * (K block scale)
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
