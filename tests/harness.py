@@ -127,6 +127,14 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
     return {"dOtc": dOtc, "dOs": dOs, "Dvec": Dv}
 
 
+def check_prologue(g: Dict[str, np.ndarray], o: Dict[str, np.ndarray]) -> None:
+    """The GPU prologue's codes, scales, rstd and K mean equal the oracle's bit for bit."""
+    for k in ("Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"):
+        assert g[k].dtype == o[k].dtype, k
+        assert np.array_equal(g[k], o[k]), (k, int(np.sum(g[k] != o[k])))
+    assert np.array_equal(g["Vtc"], np.swapaxes(o["Vc"], -1, -2)), int(np.sum(g["Vtc"] != np.swapaxes(o["Vc"], -1, -2)))
+
+
 def pro_to_device(pro: Dict[str, np.ndarray]):
     """The oracle's prologue outputs as device tensors in the C ABI layout (for staged tests)."""
     import torch

@@ -14,7 +14,7 @@ import pytest
 from bit_trainable_attention_amd import workloads as wl
 from oracle import exact
 from oracle import quant as oq
-from tests.harness import cosine, gpu_run, host_inputs, pro_to_device, rel_l2, spec_for
+from tests.harness import check_prologue, cosine, gpu_run, host_inputs, pro_to_device, rel_l2, spec_for
 
 pytestmark = pytest.mark.gpu
 
@@ -38,13 +38,6 @@ SMALL = {
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def check_prologue(g, o):
-    for k in ("Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"):
-        assert g[k].dtype == o[k].dtype, k
-        assert np.array_equal(g[k], o[k]), (k, int(np.sum(g[k] != o[k])))
-    assert np.array_equal(g["Vtc"], np.swapaxes(o["Vc"], -1, -2)), int(np.sum(g["Vtc"] != np.swapaxes(o["Vc"], -1, -2)))
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
