@@ -21,9 +21,9 @@
 //          K: rstd; with smoothing, the block's per-channel sums of K^ (group t mod 16 in
 //             ascending order, then the pairwise tree over the 16 groups); without, codes;
 //          V: block absmax, codes written channel-major (V^T) through an LDS byte tile.
-// k_mean (smoothing only) one thread per (head, channel): block sums in ascending block
-//          order, / N.
-// pass2  (smoothing only) one workgroup per (head, block): K~ = K^ - mean, absmax, codes.
+// pass2  (smoothing only) one workgroup per (head, block): the head's K mean (block sums in
+//          ascending block order, / N; every workgroup of the head computes it, block 0's
+//          stores it), K~ = K^ - mean, absmax, codes.
 #pragma clang fp contract(off)
 
 #include "common.hpp"
@@ -221,20 +221,6 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
                                   (tensor == 0 ? a.Qs : a.Ks) + sidx, j, ch);
 }
 
-// Mean over all tokens of the head: block sums in ascending block order, then / N.
-template <int D>
-__global__ __launch_bounds__(kThreads) void prologue_k_mean(PrologueArgs a) {
-  const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (e >= (size_t)a.BH * D) return;
-  const size_t bh = e / D;
-  const int c = (int)(e % D);
-  const int nb = a.N / a.BLK;
-  const float* part = a.kpart + bh * nb * D + c;
-  float tot = 0.0f;
-  for (int b = 0; b < nb; ++b) tot = tot + part[(size_t)b * D];
-  a.k_mean[e] = tot / (float)a.N;
-}
-
 template <int DT, int D, int BLK>
 __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
   using S = Slice<D, BLK>;
@@ -248,9 +234,30 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
 
   S s;
   load_slice<DT, D, BLK>(a.K + tok0 * D, s, j, ch);
+  // mean of the head's keys per channel: its blocks' channel sums in ascending block order,
+  // then one division by N (every workgroup of the head computes the same value; the one of
+  // block 0 also stores it)
+  __shared__ float mean[D];
+  if (threadIdx.x < D) {
+    const float* part = a.kpart + (size_t)bh * nb * D + threadIdx.x;
+    float tot = 0.0f;
+    int b = 0;
+    for (; b + 16 <= nb; b += 16) {   // 16 loads in flight, then the additions in block order
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = part[(size_t)(b + i) * D];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tot = tot + v[i];
+    }
+    for (; b < nb; ++b) tot = tot + part[(size_t)b * D];
+    const float m = tot / (float)a.N;
+    mean[threadIdx.x] = m;
+    if (blk_id == 0) a.k_mean[(size_t)bh * D + threadIdx.x] = m;
+  }
+  __syncthreads();
   float mu[S::CW];
 #pragma unroll
-  for (int i = 0; i < S::CW; ++i) mu[i] = a.k_mean[(size_t)bh * D + ch * S::CW + i];
+  for (int i = 0; i < S::CW; ++i) mu[i] = mean[ch * S::CW + i];
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
     const float r = a.qk_norm ? a.k_rstd[tok0 + 16 * p + j] : 1.0f;
@@ -270,9 +277,6 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st) {
   const long long nblocks = (long long)a.BH * nb;
   hipError_t e = launch_kernel(&prologue_pass1<DT, D, BLK>, dim3((unsigned)(nblocks * 3)), dim3(kThreads), st, a);
   if (e != hipSuccess || !a.k_smooth) return e;
-  const long long mthreads = (long long)a.BH * D;
-  e = launch_kernel(&prologue_k_mean<D>, dim3((unsigned)((mthreads + kThreads - 1) / kThreads)), dim3(kThreads), st, a);
-  if (e != hipSuccess) return e;
   return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)nblocks), dim3(kThreads), st, a);
 }
 
