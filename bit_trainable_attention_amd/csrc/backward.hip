@@ -419,7 +419,9 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
     const float sdO = *reinterpret_cast<const float*>(buf + P::bSDO);
     const float c2 = (sQ * sK) * (smc * kLog2e);
 
-    // ---- S = Q K~^T and dP = dO V^T for the 16-row sub-tiles
+    // ---- S = Q K~^T and dP = dO V^T for the 16-row sub-tiles (LLVM's interleaving strategy
+    //      1 for this block: measured 1.7-2.6% faster than the default schedule)
+    __builtin_amdgcn_iglp_opt(1);
     i32x4 s[NS];
     f32x4 dp[NS];
 #pragma unroll
