@@ -129,6 +129,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
     // masked); every other visited tile is wholly visible and carries no masking work.
     auto tile = [&](auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
+      // (LLVM's interleaving strategy 1 on this block and on the PV block: measured 1-5%
+      // faster than the default schedule)
+      __builtin_amdgcn_iglp_opt(1);
       // ---- S^T = K Q^T (exact int32)
       i32x16 s[NSUB];
 #pragma unroll
@@ -203,6 +206,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       // l accumulates P~ before quantisation: sum(P~ * 127/a) * a/127
       lsum_run = lsum_run * alpha + tsum * sP;
 
+      __builtin_amdgcn_iglp_opt(1);
       // ---- O^T = O^T * alpha + (a/127) sV (V^T P~^T), int32 over the BLK keys of one V block.
       // The rescale is skipped when no row of the wave moved its max (alpha == 1 exactly).
       const float spv = sP * sV;
