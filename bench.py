@@ -74,9 +74,15 @@ def cpu_baseline(w, x, heads: int):
     oq.run(Qf, Kf, Vf, dOf, spec)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return dict(value=ws.algorithmic_ops() / dt / 1e12, unit="TOPS", cores=int(threads), kind="oracle",
                 sample=f"{heads} of {w.B * w.H} heads (B1 H{heads} N{w.N} d{w.d}), quantised oracle "
-                       f"prologue+forward+backward, float64 numpy, {dt:.1f} s",
+                       f"prologue+forward+backward, float64 numpy, {dt:.1f} s on {model}",
                 seconds=dt)
 
 
@@ -155,6 +161,9 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, s in enumerate(stages)}
+    per_step = np.array([e[0].elapsed_time(e[5]) for e in evs])
+    step_stats = {"median": float(np.median(per_step)), "min": float(per_step.min()),
+                  "p90": float(np.percentile(per_step, 90))}
 
     pairs = w.visible_pairs()
     ops = w.algorithmic_ops()
@@ -164,6 +173,15 @@ def main():
     ach_main = ops_main / (stage_ms["bwd_main"] * 1e-3) / 1e12
     peak_main = weighted_peak(4, 1)
     traffic = traffic_from_profile()
+    # each stage's own ideal: MFMA-bound stages at their dense peaks, the others at 8 TB/s of
+    # their algorithmic HBM bytes (E = B*H*N*d elements: prologue reads Q,K,V and writes three
+    # code tensors; bwd_pre reads dO, O, Qc, Kc and writes the packets and K^T codes; the dQ pass
+    # reads one dS byte per visible pair, the K^T codes and Q, and writes dQ)
+    E = w.B * w.H * w.N * w.d
+    hbm = 8e12
+    stage_ideal_ms = {"prologue": 9 * E / hbm * 1e3, "forward": 4 * w.d * pairs / (PEAK_I8 * 1e12) * 1e3,
+                      "bwd_pre": 11 * E / hbm * 1e3, "bwd_main": ops_main / (peak_main * 1e12) * 1e3,
+                      "bwd_dq": (pairs + 5 * E) / hbm * 1e3}
     log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TOPS = {100 * value / peak_step:.1f}% of the "
         f"{peak_step:.0f} TOPS INT8/FP16 (6:1) dense peak; stages (ms): "
         + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
@@ -189,7 +207,9 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "blk": w.blk,
                    "dtype": w.dtype, "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak_step, 4),
+        "step_ms": {k: round(v, 4) for k, v in step_stats.items()},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_frac_of_ideal": {k: round(stage_ideal_ms[k] / stage_ms[k], 4) for k in stage_ms},
         "roofline": {"kernel": "bwd_main", "bound": "mfma", "achieved": round(ach_main, 2),
                      "peak": round(peak_main, 1), "unit": "TFLOP/s", "frac": round(ach_main / peak_main, 4),
                      "traffic": traffic},
