@@ -15,8 +15,12 @@
 //   after two v_permlane32_swap per subtile, which put keys 16g..16g+15 in lane group g,
 //   the order in which the V^T rows are stored.
 // Per key tile (the online-softmax step and the P~ quantisation tile, 32 rows x BLK keys):
-//   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); alpha = 2^(m - m'); l = l*alpha + sum P~;
-//   a = max P~ over the wave's tile; codes = rne(P~ * (127/a)); O = O*alpha + (a/127)*sV*int(PV).
+//   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); a = max P~ over the wave's tile;
+//   codes = rne(P~ * (127/a)); l = l*alpha + u*sum P~; O = O*alpha + u*(a/127)*sV*int(PV),
+// with O and l kept relative to a reference r that lags m: r' = m' when some row of the wave
+// has m' > r + 8 (and on the first tile), else r' = r; alpha = 2^(r - r'), u = 2^(m' - r').
+// Most tiles then leave r alone and skip the O rescale; the codes and the final O and LSE are
+// the same as with r = m (only rounding differs).
 // P~ * 127/a is produced by one exponential, 2^(s*log2e - m' + log2(127/a)), and rounded and
 // packed by v_cvt_pk_u8_f32 (nearest even); only tiles on the diagonal carry masking work.
 #include "common.hpp"
@@ -34,6 +38,7 @@ constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
+constexpr float kLazy = 8.0f;  // O and l may lag the running max by up to 2^kLazy
 
 template <int D, int BLK>
 struct FwdLds {
@@ -103,7 +108,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
   const int last_row = min(q0 + kRowsPerBlock, a.N) - 1;
   const int n_kt = a.causal ? last_row / BLK + 1 : nb;
 
-  float m = -INFINITY, lsum_run = 0.0f;
+  // m: running row max (the reference of P~); mo: the reference of O and l, which follows m
+  // only when some row of the wave has moved more than kLazy past it (and on the first tile)
+  float m = -INFINITY, mo = -INFINITY, lsum_run = 0.0f;
   f32x16 o[DC];
 #pragma unroll
   for (int ct = 0; ct < DC; ++ct) o[ct] = f32x16{};
@@ -168,7 +175,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       float rowmax = (float)rmax * c2;
       if constexpr (DIAG) rowmax = rmax == INT32_MIN ? -INFINITY : rowmax;
       const float m_new = fmaxf(m, rowmax);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      const bool moved = __builtin_amdgcn_ballot_w64(m_new > mo + kLazy) != 0;
+      const float mo_new = moved ? m_new : mo;
+      const float alpha = __builtin_amdgcn_exp2f(mo - mo_new);   // 1 exactly when not moved
+      const float up = __builtin_amdgcn_exp2f(m_new - mo_new);   // P~ in units of 2^mo_new
       // P~ tile absmax a = max over rows of 2^(rowmax - m'); in log2 it is one wave max.
       // The quantisation factor 127/a is folded into the exponent, so the exponential
       // yields P~ * 127/a directly and its nearest-even integer is the code.
@@ -204,13 +214,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         pc[t] = i32x4{(int)x02[0], (int)x02[1], (int)x13[0], (int)x13[1]};
       }
       // l accumulates P~ before quantisation: sum(P~ * 127/a) * a/127
-      lsum_run = lsum_run * alpha + tsum * sP;
+      lsum_run = lsum_run * alpha + tsum * (sP * up);
 
       __builtin_amdgcn_iglp_opt(1);
       // ---- O^T = O^T * alpha + (a/127) sV (V^T P~^T), int32 over the BLK keys of one V block.
-      // The rescale is skipped when no row of the wave moved its max (alpha == 1 exactly).
-      const float spv = sP * sV;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      // O is rescaled only when its reference moved.
+      const float spv = (sP * sV) * up;
+      if (moved) {
 #pragma unroll
         for (int ct = 0; ct < DC; ++ct)
 #pragma unroll
@@ -229,6 +239,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         for (int r = 0; r < 16; ++r) o[ct][r] = __builtin_fmaf(spv, (float)acc[r], o[ct][r]);
       }
       m = m_new;
+      mo = mo_new;
     };
     if (active && (!a.causal || k0 <= q0w + kRowsPerWave - 1)) {
       if (a.causal && k0 + BLK - 1 > q0w) tile(std::true_type{});
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       for (int i = 0; i < 4; ++i) v[i] = from_f32<DT>(o[ct][4 * j + i] * linv);
       *reinterpret_cast<u16x4*>(orow + 32 * ct + 8 * j + 4 * g) = v;
     }
-  if (g == 0) a.lse[(size_t)bh * a.N + qrow] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+  if (g == 0) a.lse[(size_t)bh * a.N + qrow] = (mo + __builtin_amdgcn_logf(ltot)) * kLn2;
 }
 
 template <int DT, int D, int BLK>
