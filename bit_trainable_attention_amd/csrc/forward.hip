@@ -7,8 +7,8 @@
 //   workgroup = 4 waves = 128 query rows of one head; wave w owns 32 rows.
 //   Key tiles of BLK keys (one quantisation block of K and V) stream into double-buffered
 //   LDS by buffer->LDS copies: K codes token-major and V^T codes channel-major, both with
-//   their 16-byte chunks XOR-swizzled by row so the MFMA operand reads of 8 consecutive
-//   rows hit distinct banks (the copies take the permutation on their source addresses).
+//   their 16-byte chunks XOR-swizzled by row (swz_f) so the MFMA operand reads spread over
+//   the banks (the copies take the permutation on their source addresses).
 //   S^T = K Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 16 keys per
 //   32-key subtile, so the row max / row sum are lane-local plus one exchange with lane
 //   l^32 (v_permlane32_swap). The quantised P~^T becomes the B operand of O^T = V^T P~^T
@@ -40,10 +40,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
 constexpr float kLazy = 8.0f;  // O and l may lag the running max by up to 2^kLazy
 
+// Chunk swizzle of the K and V^T tiles, rows of RB bytes (an involution in j). The operand
+// reads name rows 32t .. 32t+31 (lane l & 31), one chunk per lane half; on gfx950 they
+// measured ~206 (RB = 128) and ~218 (RB = 64) B/clk per CU with these XORs, against ~117
+// with j ^ (r & 7) and j ^ ((r >> 1) & 3).
+template <int RB>
+__device__ __forceinline__ int swz_f(int r, int j) {
+  if constexpr (RB == 128) return j ^ (((r >> 1) ^ (r >> 4)) & 7);
+  else return j ^ ((r >> 2) & 3);
+}
+
 template <int D, int BLK>
 struct FwdLds {
-  static constexpr int kBytesK = BLK * D;   // K codes [BLK][D], chunk j of row r at swz<D>(r, j)
-  static constexpr int kBytesV = D * BLK;   // V^T codes [D][BLK], chunk j of row c at swz<BLK>(c, j)
+  static constexpr int kBytesK = BLK * D;   // K codes [BLK][D], chunk j of row r at swz_f<D>(r, j)
+  static constexpr int kBytesV = D * BLK;   // V^T codes [D][BLK], chunk j of row c at swz_f<BLK>(c, j)
   static constexpr int kBytes = kBytesK + kBytesV;
   static constexpr int kCopies = kBytes / 1024;              // 1 KB copies per tile
   static constexpr int kCopiesPerWave = kCopies / kWaves;
@@ -65,12 +75,12 @@ __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int 
     const int e = 64 * cp + l;                          // 16-byte chunk index inside the tile
     if (cp * 1024 < L::kBytesK) {
       const int r = e / (D / 16), pc = e % (D / 16);
-      const int j = swz<D>(r, pc);                      // the swizzle is an involution
+      const int j = swz_f<D>(r, pc);                    // the swizzle is an involution
       buffer_to_lds16(kh, hbytes, dst + cp * 1024, (uint32_t)((k0 + r) * D + 16 * j), 0u);
     } else {
       const int ev = e - L::kBytesK / 16;
       const int c = ev / (BLK / 16), pc = ev % (BLK / 16);
-      const int j = swz<BLK>(c, pc);
+      const int j = swz_f<BLK>(c, pc);
       buffer_to_lds16(vh, hbytes, dst + cp * 1024, (uint32_t)(c * a.N + k0 + 16 * j), 0u);
     }
   }
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
         for (int kk = 0; kk < DC; ++kk) {
           const int kr = 32 * t + lq;
-          const i32x4 ak = *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz<D>(kr, 2 * kk + g));
+          const i32x4 ak = *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz_f<D>(kr, 2 * kk + g));
           s[t] = mfma_i8_32x32x32(ak, qreg[kk], s[t]);
         }
       }
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
         for (int t = 0; t < NSUB; ++t) {
           const int vr = 32 * ct + lq;
-          const i32x4 av = *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz<BLK>(vr, 2 * t + g));
+          const i32x4 av = *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz_f<BLK>(vr, 2 * t + g));
           acc = mfma_i8_32x32x32(av, pc[t], acc);
         }
 #pragma unroll
