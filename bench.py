@@ -97,6 +97,8 @@ def main():
                     help="before warm-up, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-autograd", action="store_true",
+                    help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -189,6 +191,34 @@ def main():
     log(f"[bench] forward {fwd_ops / (stage_ms['forward'] * 1e-3) / 1e12:.1f} TOPS (INT8 peak {PEAK_I8:.0f}); "
         f"bwd_main {ach_main:.1f} TOPS (4:1 INT8/FP16 peak {peak_main:.0f})")
 
+    autograd_ms = None
+    if not args.no_autograd:
+        # the same step through torch.autograd (bit_trainable_attention_amd.autograd): the
+        # wrapper's own outputs, workspaces and saved tensors come from torch's allocator
+        from bit_trainable_attention_amd.autograd import sagebwd_attention
+        qg, kg, vg = (t.detach().clone().requires_grad_() for t in (Q, K, V))
+
+        def ag_step():
+            for t in (qg, kg, vg):
+                t.grad = None
+            o = sagebwd_attention(qg, kg, vg, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
+                                  blk=w.blk, eps=w.eps)
+            o.backward(dO)
+
+        for _ in range(2):
+            ag_step()
+        n_ag = max(1, min(args.steps, 10))
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record()
+        for _ in range(n_ag):
+            ag_step()
+        a1.record()
+        torch.cuda.synchronize()
+        autograd_ms = a0.elapsed_time(a1) / n_ag
+        log(f"[bench] autograd wrapper: {autograd_ms:.3f} ms/step over {n_ag} steps")
+        del qg, kg, vg
+
     out = {
         "metric": "INT8 attention fwd+bwd TOPS at B2 H16 N8192 d128 causal; % of MFMA peak",
         "value": round(value, 2),
@@ -214,6 +244,7 @@ def main():
                      "peak": round(peak_main, 1), "unit": "TFLOP/s", "frac": round(ach_main / peak_main, 4),
                      "traffic": traffic},
         "cpu_baseline": None,
+        "autograd_ms_per_step": None if autograd_ms is None else round(autograd_ms, 4),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_heads} head(s)...")

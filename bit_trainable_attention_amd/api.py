@@ -47,6 +47,8 @@ def _stream(device: torch.device, stream: Optional[torch.cuda.Stream]) -> ctypes
 def _want(t: torch.Tensor, name: str, shape, dtype, device) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: the library takes device tensors only, got one on {t.device}")
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
                          f"{t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")

@@ -1,0 +1,72 @@
+"""PyTorch autograd wrapper over the C ABI (argument marshalling only).
+
+`sagebwd_attention(q, k, v, ...)` runs the quantisation prologue and the INT8 forward and
+returns O (and optionally the row logsumexp); `O.backward(dO)` runs the library's backward
+and delivers dQ, dK, dV with respect to the raw q, k, v handed in (the RMSNorm backward of
+QK-norm included; K-smoothing contributes nothing, SageBwd article, K-smoothing paragraph).
+Every step runs in libsagebwd.so; there is no CPU path.
+
+Layouts: "bhnd" takes [B, H, N, d] tensors as they are (contiguous); "bnhd" takes the
+[B, N, H, d] layout of a fused projection output and hands the library a contiguous
+[B, H, N, d] copy (the kernels read head-major rows), returning gradients in [B, N, H, d].
+"""
+from __future__ import annotations
+
+from typing import Tuple, Union
+
+import torch
+
+from . import api
+
+_DTYPES = {torch.float16: "fp16", torch.bfloat16: "bf16"}
+# prologue tensors the backward reads (the V codes are only the forward's)
+_SAVED = ("Qc", "Kc", "Qs", "Ks", "q_rstd", "k_rstd")
+
+
+class SageBwdAttention(torch.autograd.Function):
+    """Autograd node: forward = prologue + INT8 forward, backward = the library's backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal: bool, qk_norm: bool, k_smooth: bool, blk: int, eps: float,
+                sm_scale: float, dq_mode: int):
+        if q.dtype not in _DTYPES:
+            raise TypeError(f"q, k, v must be float16 or bfloat16, got {q.dtype}")
+        if q.dim() != 4:
+            raise ValueError(f"expected [B, H, N, d] tensors, got shape {tuple(q.shape)}")
+        B, H, N, d = q.shape
+        p = api.make_params(B, H, N, d, blk, causal, qk_norm, k_smooth, _DTYPES[q.dtype], eps=eps,
+                            sm_scale=sm_scale, dq_mode=dq_mode)
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        pro = api.sagebwd_quant_prologue(p, q, k, v)
+        O, lse = api.sagebwd_forward(p, pro)
+        ctx.params = p
+        ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in _SAVED))
+        ctx.mark_non_differentiable(lse)
+        return O, lse
+
+    @staticmethod
+    def backward(ctx, dO, _dlse):
+        q, k, v, O, lse, *saved = ctx.saved_tensors
+        pro = dict(zip(_SAVED, saved))
+        g = api.sagebwd_backward(ctx.params, q, k, v, pro, O, lse, dO.contiguous())
+        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None
+
+
+def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                      qk_norm: bool = True, k_smooth: bool = True, blk: int = 128, eps: float = 1e-6,
+                      sm_scale: float = 0.0, layout: str = "bhnd", return_lse: bool = False,
+                      dq_mode: int = 0) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+    """SageBwd-style INT8 attention with gradients (see the module docstring).
+
+    sm_scale <= 0 selects 1/sqrt(d). The lse returned with return_lse is float32 [B, H, N]
+    (natural log) and carries no gradient.
+    """
+    if layout == "bnhd":
+        q, k, v = (t.transpose(1, 2) for t in (q, k, v))
+    elif layout != "bhnd":
+        raise ValueError(f"layout must be 'bhnd' or 'bnhd', got {layout!r}")
+    O, lse = SageBwdAttention.apply(q, k, v, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
+                                    float(eps), float(sm_scale), int(dq_mode))
+    if layout == "bnhd":
+        O = O.transpose(1, 2)
+    return (O, lse) if return_lse else O

@@ -130,3 +130,19 @@ def test_backward_part_rejects_bad_part():
         assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
     assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
     assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 15), FAKE, 0, None) == -5
+
+
+def test_binding_rejects_host_tensors():
+    # host tensors never reach the C ABI (there is no CPU path): the binding and the autograd
+    # wrapper refuse them before any library call
+    import torch
+    from bit_trainable_attention_amd import api
+    from bit_trainable_attention_amd.autograd import sagebwd_attention
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.float16)
+    p = api.make_params(1, 2, 128, 64, 64, True, True, True, "fp16")
+    with pytest.raises(ValueError, match="device tensors only"):
+        api.sagebwd_quant_prologue(p, q, q, q)
+    with pytest.raises(ValueError, match="device tensors only"):
+        sagebwd_attention(q, q, q, blk=64)
+    with pytest.raises(ValueError, match="layout"):
+        sagebwd_attention(q, q, q, blk=64, layout="nhd")
