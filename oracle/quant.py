@@ -24,6 +24,11 @@ What is computed, in the order of the SageBwd article:
   6. Gradients are with respect to the raw Q, K handed to the prologue: the RMSNorm
      backward closes dQ and dK; K-smoothing contributes nothing, because every row of
      dS sums to zero.
+  7. Optional Q-smoothing (Spec.q_smooth; SageBwd article, Q-smoothing paragraph, which
+     names its bias term): the queries' per-channel mean mu_Q (taken like the keys') is
+     subtracted before quantising; every score gets back the per-key bias
+     b_k = (K mu_Q)_k (key_bias), and dK^ gets dK_bias = (dS^T 1) mu_Q^T
+     (q_smooth_dk_bias); dQ is unchanged.
 
 Precision: steps 1-3 are float32, one IEEE operation at a time, round to nearest
 even, in the order written (sums run over channels, or over tokens, in ascending
@@ -67,6 +72,7 @@ class Spec:
     bwd_tq: int = 64
     bwd_pk: int = 16
     bwd_sk: Optional[int] = None
+    q_smooth: bool = False
 
     def __post_init__(self):
         blk = self.blk
@@ -257,11 +263,35 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
         Kt, mu = k_smooth_f32(Kh, spec.blk)
     else:
         Kt, mu = Kh, np.zeros(K.shape[:-2] + (K.shape[-1],), dtype=F32)
-    Qc, Qs = block_quant(Qh, spec.blk)
+    if spec.q_smooth:
+        # Q-smoothing (SageBwd article, Q-smoothing paragraph): the queries' per-channel mean,
+        # taken like the keys' (same order), is subtracted before quantising
+        Qt, mu_q = k_smooth_f32(Qh, spec.blk)
+    else:
+        Qt, mu_q = Qh, np.zeros(Q.shape[:-2] + (Q.shape[-1],), dtype=F32)
+    Qc, Qs = block_quant(Qt, spec.blk)
     Kc, Ks = block_quant(Kt, spec.blk)
     Vc, Vs = block_quant(V, spec.blk)
-    return dict(Qc=Qc, Kc=Kc, Vc=Vc, Qs=Qs, Ks=Ks, Vs=Vs, q_rstd=q_rstd, k_rstd=k_rstd,
-                k_mean=mu, Qhat=Qh, Khat=Kh)
+    out = dict(Qc=Qc, Kc=Kc, Vc=Vc, Qs=Qs, Ks=Ks, Vs=Vs, q_rstd=q_rstd, k_rstd=k_rstd,
+               k_mean=mu, q_mean=mu_q, Qhat=Qh, Khat=Kh)
+    out["kbias"] = key_bias(Kc, Ks, mu_q, spec.blk) if spec.q_smooth else np.zeros(K.shape[:-1])
+    return out
+
+
+def key_bias(Kc, Ks, mu_q, blk: int) -> np.ndarray:
+    """The per-key score bias Q-smoothing adds back: b_k = sK(block of k) * (Kc_k . mu_Q).
+
+    With Q^ = Q~ + mu_Q, Q^ K^T = Q~ K^T + 1 (K mu_Q)^T (SageBwd article, Q-smoothing
+    paragraph); the keys enter as their dequantised codes, the same K the INT8 product uses.
+    float64 (it is computed after the codes, like everything past the prologue's float32
+    steps). Kc [..., N, d] codes (or identity values), Ks [..., N/blk], mu_q [..., d].
+    Returns [..., N] float64.
+    Pinned by: test_oracle_quant.py::test_q_smooth_identity_reduction (with identity
+    quantisation the smoothed scores equal the unsmoothed ones).
+    """
+    kc = np.asarray(Kc, dtype=np.float64)
+    ks = np.repeat(np.asarray(Ks, dtype=np.float64), blk, axis=-1)
+    return ks * np.einsum("...nd,...d->...n", kc, np.asarray(mu_q, dtype=np.float64))
 
 
 # ----------------------------------------------------------------------------
@@ -297,13 +327,14 @@ def _flat(a: np.ndarray, nlead: int = 2) -> np.ndarray:
 
 
 def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
-            q_tiles: Optional[Sequence[int]] = None):
+            q_tiles: Optional[Sequence[int]] = None, kbias: Optional[np.ndarray] = None):
     """Flash-style forward with INT8 QK^T and PV (SageBwd article, precision split).
 
     Per head, per query tile I of fwd_tq rows: m = -inf, l = 0, acc = 0; for key tiles J
     of fwd_tk keys in ascending order, skipping tiles wholly above the causal diagonal:
-      S   = Qc_I . Kc_J^T (exact integers),  s = S * sQ(I) * sK(J) * sm_scale,
-            masked (key > query) -> -inf when causal
+      S   = Qc_I . Kc_J^T (exact integers),  s = S * sQ(I) * sK(J) * sm_scale
+            (+ kbias_J * sm_scale with Q-smoothing: key_bias), masked (key > query)
+            -> -inf when causal
       m'  = max(m, rowmax s);  P~ = exp(s - m');  alpha = exp(m - m')
       l   = l * alpha + rowsum P~                     (P~ before quantisation)
       qP, sP = quantise P~ on the tile                (INT8 rule, decided in float32)
@@ -324,6 +355,7 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
     qs = _flat(np.asarray(Qs, dtype=np.float64))
     ks = _flat(np.asarray(Ks, dtype=np.float64))
     vs = _flat(np.asarray(Vs, dtype=np.float64))
+    kb = None if kbias is None else _flat(np.asarray(kbias, dtype=np.float64), 2)
     BH = q.shape[0]
     O = np.full((BH, N, d), np.nan)
     LSE = np.full((BH, N), np.nan)
@@ -342,6 +374,8 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
             cols = np.arange(j0, j0 + tk)
             S = qi @ k[:, j0:j0 + tk, :].transpose(0, 2, 1)
             s = S * (sq * ks[:, j0 // blk] * sm)[:, None, None]
+            if kb is not None:
+                s = s + sm * kb[:, None, j0:j0 + tk]
             if spec.causal:
                 s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
             m_new = np.maximum(m, s.max(axis=-1))
@@ -390,7 +424,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     exact 16-bit values; O: the forward's output as stored (dtype values); LSE float32.
     Per head, for every visible pair of query tile I (bwd_tq rows) and key tile J
     (bwd_sk keys), in ascending I then J:
-      s  = (Qc_I . Kc_J^T) * sQ(I) * sK(J) * sm_scale (masked -> -inf); P = exp(s - LSE_I)
+      s  = (Qc_I . Kc_J^T) * sQ(I) * sK(J) * sm_scale (+ kbias_J * sm_scale with
+           Q-smoothing) (masked -> -inf); P = exp(s - LSE_I)
       dP = dO_I . V_J^T   (the 16-bit dO and V, never quantised; SageBwd article,
                            precision split: this product alone stays 16-bit)
       dS = P o (dP - D_I)
@@ -398,6 +433,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
       for each key sub-tile J' of bwd_pk keys: qP, sP = quantise P_{I,J'};
            dV_J' += sP * sdO(I) * (qP^T . dOc_I)
       dK_J += sm * sdS * sQ(I) * (qdS^T . Qc_I)
+              (+ sm * sdS * (qdS^T 1) mu_Q^T with Q-smoothing: Q^ = Q~ + mu_Q, so
+               dS^T Q^ = dS^T Q~ + (dS^T 1) mu_Q^T, the pages' dK_bias term)
       dQ_I += sm * sdS * sK(J) * (qdS . Kc_J)          (Kc: the smoothed K codes)
     Epilogue: dQ = RMSNorm-backward(dQ^, Q^, q_rstd), dK = RMSNorm-backward(dK^, K^,
     k_rstd) when QK-norm is on (K^ before smoothing; smoothing adds no term because
@@ -421,6 +458,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     vf = _flat(np.asarray(V, dtype=F32)).astype(np.float64)
     lse = _flat(np.asarray(LSE, dtype=F32)).astype(np.float64)
     Df = _flat(D)
+    qsm = spec.q_smooth
+    kb = _flat(np.asarray(pro["kbias"], dtype=np.float64), 2) if qsm else None
+    muq = _flat(np.asarray(pro["q_mean"], dtype=np.float64)) if qsm else None
     BH = qc.shape[0]
     dQh = np.zeros((BH, N, d))
     dKh = np.zeros((BH, N, d))
@@ -440,6 +480,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             cols = np.arange(j0, j0 + sk)
             S = qc[:, i0:i0 + tq, :] @ kc[:, j0:j0 + sk, :].transpose(0, 2, 1)
             s = S * (qs[:, i0 // blk] * ks[:, j0 // blk] * sm)[:, None, None]
+            if qsm:
+                s = s + sm * kb[:, None, j0:j0 + sk]
             if spec.causal:
                 s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
             P = np.exp(s - lse[:, i0:i0 + tq, None])
@@ -452,6 +494,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
                     qP.transpose(0, 2, 1) @ doc[:, i0:i0 + tq, :])
             dKh[:, j0:j0 + sk, :] += (sm * sdS * qs[:, i0 // blk])[:, None, None] * (
                 qdS.transpose(0, 2, 1) @ qc[:, i0:i0 + tq, :])
+            if qsm:
+                dKh[:, j0:j0 + sk, :] += q_smooth_dk_bias(qdS, sdS, muq, sm)
             dQh[:, i0:i0 + tq, :] += (sm * sdS * ks[:, j0 // blk])[:, None, None] * (
                 qdS @ kc[:, j0:j0 + sk, :])
     if spec.qk_norm:
@@ -478,12 +522,24 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     return out
 
 
+def q_smooth_dk_bias(qdS, sdS, mu_q, sm: float) -> np.ndarray:
+    """Q-smoothing's dK_bias on one tile: sm * (dS^T 1) mu_Q^T (SageBwd article, Q-smoothing
+    paragraph), with dS the tile's dequantised codes (sdS * qdS, the dS the INT8 dK product
+    uses) summed over the tile's queries. qdS [BH, tq, sk], sdS [BH], mu_q [BH, d].
+    Returns the [BH, sk, d] increment of dK^ (float64).
+    Pinned by: test_oracle_quant.py::test_identity_quant_with_q_smoothing and the planted
+    mistake "qs_drop_dk_bias".
+    """
+    csum = np.asarray(sdS, np.float64)[:, None] * np.asarray(qdS, np.float64).sum(axis=1)
+    return sm * csum[:, :, None] * np.asarray(mu_q, np.float64)[:, None, :]
+
+
 def run(Q, K, V, dO, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
         block_quant: BlockQuant = quant_blocks_f32):
     """Prologue -> forward -> backward on whole tensors. Returns one dict of everything."""
     pro = prologue(Q, K, V, spec, block_quant=block_quant)
     O, LSE = forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec,
-                     tile_quant=tile_quant)
+                     tile_quant=tile_quant, kbias=pro["kbias"] if spec.q_smooth else None)
     g = backward(pro, Q, K, V, O, LSE, dO, spec, tile_quant=tile_quant, block_quant=block_quant)
     out = dict(pro)
     out.update(O=O, LSE=LSE)

@@ -318,3 +318,74 @@ def test_planted_mistake_is_caught(monkeypatch, mistake):
         assert not all(_rel(got[n], ref[n]) < 3e-6 for n in ("dQ", "dK"))
         return
     assert not _identity_pin_passes(*_identity_case())
+
+
+# ----------------------------------------------------------------------------- Q-smoothing
+
+def _qs_case(seed, N=128, d=32, causal=True):
+    rng = np.random.default_rng(seed)
+    B, H = 1, 2
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    # a strong per-channel query offset, so mu_Q (and every term it enters) is large
+    Q = (Q + 3 * rng.standard_normal((1, H, 1, d))).astype(F32)
+    K = (K + 2 * rng.standard_normal((1, H, 1, d))).astype(F32)
+    return Q, K, V, dO
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_quant_with_q_smoothing(causal):
+    """With identity quantisers, Q~ K^T + 1 (K mu_Q)^T is Q^ K^T and dS^T Q~ + (dS^T 1) mu_Q^T
+    is dS^T Q^: the Q-smoothed path equals exact attention (to the float32 prologue's
+    rounding). A dropped or mis-signed bias term, or mu_Q over the wrong axis, breaks it."""
+    Q, K, V, dO = _qs_case(11, causal=causal)
+    spec = oq.Spec(N=128, d=32, blk=64, causal=causal, qk_norm=True, k_smooth=True, q_smooth=True, dtype="f64")
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    for name in ("O", "dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 3e-6, name
+    # the bias is not negligible here: without it the scores would be far off
+    assert np.max(np.abs(got["kbias"])) > 0.5
+
+
+def test_q_smooth_removes_query_mean():
+    Q, K, V, dO = _qs_case(12)
+    spec = oq.Spec(N=128, d=32, blk=64, causal=True, qk_norm=True, k_smooth=True, q_smooth=True, dtype="f64")
+    pro = oq.prologue(Q, K, V, spec, block_quant=oq.identity_block_quant)
+    qt = pro["Qc"].astype(np.float64)          # identity "codes" = Q~
+    assert np.max(np.abs(qt.mean(axis=-2))) < 1e-6 * np.max(np.abs(qt))
+    np.testing.assert_allclose(pro["q_mean"], pro["Qhat"].astype(np.float64).mean(axis=-2), rtol=1e-5, atol=1e-6)
+    # off: the mean is zero and the keys carry no bias
+    off = oq.prologue(Q, K, V, oq.Spec(N=128, d=32, blk=64, causal=True, qk_norm=True, k_smooth=True, dtype="f64"))
+    assert not np.any(off["q_mean"]) and not np.any(off["kbias"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_q_smoothing_close_to_exact(causal):
+    Q, K, V, dO = _qs_case(13, N=256, d=64, causal=causal)
+    Q, K, V, dO = (x.astype(np.float16).astype(F32) for x in (Q, K, V, dO))
+    spec = oq.Spec(N=256, d=64, blk=64, causal=causal, qk_norm=True, k_smooth=True, q_smooth=True, dtype="f64")
+    got = oq.run(Q, K, V, dO, spec)
+    ref = _exact_all(Q, K, V, dO, spec)
+
+    def cos(a, b):
+        a = a.ravel(); b = b.ravel()
+        return a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+    assert cos(got["O"], ref["O"]) > 0.999
+    for name in ("dQ", "dK", "dV"):
+        assert cos(got[name], ref[name]) > 0.99, name
+
+
+@pytest.mark.parametrize("mistake", ["qs_drop_kbias", "qs_drop_dk_bias", "qs_dk_bias_sign"])
+def test_q_smoothing_planted_mistake_is_caught(monkeypatch, mistake):
+    if mistake == "qs_drop_kbias":
+        monkeypatch.setattr(oq, "key_bias", lambda Kc, Ks, mu_q, blk: np.zeros(np.shape(Kc)[:-1]))
+    elif mistake == "qs_drop_dk_bias":
+        monkeypatch.setattr(oq, "q_smooth_dk_bias", lambda qdS, sdS, mu_q, sm: 0.0)
+    else:
+        real = oq.q_smooth_dk_bias
+        monkeypatch.setattr(oq, "q_smooth_dk_bias", lambda qdS, sdS, mu_q, sm: -real(qdS, sdS, mu_q, sm))
+    Q, K, V, dO = _qs_case(11)
+    spec = oq.Spec(N=128, d=32, blk=64, causal=True, qk_norm=True, k_smooth=True, q_smooth=True, dtype="f64")
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    assert not all(_rel(got[n], ref[n]) < 3e-6 for n in ("O", "dQ", "dK", "dV"))
