@@ -18,10 +18,12 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 
 
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
-                dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0) -> _lib.Params:
+                dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0,
+                q_smooth: bool = False) -> _lib.Params:
     """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
-    return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode)
+    return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode,
+                       int(q_smooth))
 
 
 def sagebwd_status_string(status: int) -> str:
@@ -105,7 +107,8 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
                            out: Optional[Dict[str, torch.Tensor]] = None,
                            workspace: Optional[torch.Tensor] = None,
                            stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
-    """QK-norm -> K-smoothing -> per-block INT8 codes/scales. Returns the prologue tensors."""
+    """QK-norm -> K-smoothing (and Q-smoothing) -> per-block INT8 codes/scales. Returns the
+    prologue tensors; with q_smooth also q_mean [B,H,d] and kbias [B,H,N]."""
     dev = Q.device
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
@@ -123,10 +126,15 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
             k_rstd=torch.empty(sh["r"], dtype=torch.float32, device=dev),
             k_mean=torch.empty(sh["m"], dtype=torch.float32, device=dev),
         )
-    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
-                           ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32),
-                           ("q_rstd", "r", torch.float32), ("k_rstd", "r", torch.float32),
-                           ("k_mean", "m", torch.float32)):
+        if p.q_smooth:
+            out["q_mean"] = torch.empty(sh["m"], dtype=torch.float32, device=dev)
+            out["kbias"] = torch.empty(sh["r"], dtype=torch.float32, device=dev)
+    wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
+              ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32),
+              ("q_rstd", "r", torch.float32), ("k_rstd", "r", torch.float32), ("k_mean", "m", torch.float32)]
+    if p.q_smooth:
+        wanted += [("q_mean", "m", torch.float32), ("kbias", "r", torch.float32)]
+    for name, key, tdt in wanted:
         _want(out[name], name, sh[key], tdt, dev)
     need = sagebwd_prologue_workspace_bytes(p)
     if need and workspace is None:
@@ -136,6 +144,7 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
         ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
         _ptr(out["Qc"]), _ptr(out["Kc"]), _ptr(out["Vtc"]), _ptr(out["Qs"]), _ptr(out["Ks"]), _ptr(out["Vs"]),
         _ptr(out["q_rstd"]), _ptr(out["k_rstd"]), _ptr(out["k_mean"]),
+        _ptr(out.get("q_mean") if p.q_smooth else None), _ptr(out.get("kbias") if p.q_smooth else None),
         _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(st, "sagebwd_quant_prologue")
     return out
@@ -144,11 +153,14 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
 def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None,
                     stream: Optional[torch.cuda.Stream] = None):
-    """INT8 forward from the prologue tensors. Returns (O, lse)."""
+    """INT8 forward from the prologue tensors (and their kbias with q_smooth). Returns (O, lse)."""
     dev = pro["Qc"].device
     sh = _shapes(p)
-    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
-                           ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32)):
+    wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
+              ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32)]
+    if p.q_smooth:
+        wanted.append(("kbias", "r", torch.float32))
+    for name, key, tdt in wanted:
         _want(pro[name], name, sh[key], tdt, dev)
     if O is None:
         O = torch.empty(sh["x"], dtype=_TORCH_DTYPE[p.dtype], device=dev)
@@ -158,7 +170,8 @@ def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[to
     _want(lse, "lse", sh["r"], torch.float32, dev)
     st = _lib.load().sagebwd_forward(
         ctypes.byref(p), _ptr(pro["Qc"]), _ptr(pro["Kc"]), _ptr(pro["Vtc"]),
-        _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["Vs"]), _ptr(O), _ptr(lse), _stream(dev, stream))
+        _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["Vs"]), _ptr(pro["kbias"] if p.q_smooth else None),
+        _ptr(O), _ptr(lse), _stream(dev, stream))
     _check(st, "sagebwd_forward")
     return O, lse
 
@@ -169,9 +182,11 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
     dt = _TORCH_DTYPE[p.dtype]
     for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
         _want(t, name, sh["x"], dt, dev)
-    for name, key, tdt in (("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Qs", "s", torch.float32),
-                           ("Ks", "s", torch.float32), ("q_rstd", "r", torch.float32),
-                           ("k_rstd", "r", torch.float32)):
+    wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Qs", "s", torch.float32),
+              ("Ks", "s", torch.float32), ("q_rstd", "r", torch.float32), ("k_rstd", "r", torch.float32)]
+    if p.q_smooth:
+        wanted += [("q_mean", "m", torch.float32), ("kbias", "r", torch.float32)]
+    for name, key, tdt in wanted:
         _want(pro[name], name, sh[key], tdt, dev)
     _want(lse, "lse", sh["r"], torch.float32, dev)
     if grads is None:
@@ -184,6 +199,7 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
     ws_bytes = workspace.numel() * workspace.element_size()
     args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(pro["Qc"]), _ptr(pro["Kc"]),
             _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["q_rstd"]), _ptr(pro["k_rstd"]),
+            _ptr(pro["q_mean"] if p.q_smooth else None), _ptr(pro["kbias"] if p.q_smooth else None),
             _ptr(O), _ptr(lse), _ptr(dO), _ptr(grads["dQ"]), _ptr(grads["dK"]), _ptr(grads["dV"]),
             _ptr(workspace), ws_bytes]
     return args, grads, workspace

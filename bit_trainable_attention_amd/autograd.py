@@ -21,6 +21,7 @@ from . import api
 _DTYPES = {torch.float16: "fp16", torch.bfloat16: "bf16"}
 # prologue tensors the backward reads (the V codes are only the forward's)
 _SAVED = ("Qc", "Kc", "Qs", "Ks", "q_rstd", "k_rstd")
+_SAVED_QS = _SAVED + ("q_mean", "kbias")
 
 
 class SageBwdAttention(torch.autograd.Function):
@@ -28,37 +29,39 @@ class SageBwdAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal: bool, qk_norm: bool, k_smooth: bool, blk: int, eps: float,
-                sm_scale: float, dq_mode: int):
+                sm_scale: float, dq_mode: int, q_smooth: bool):
         if q.dtype not in _DTYPES:
             raise TypeError(f"q, k, v must be float16 or bfloat16, got {q.dtype}")
         if q.dim() != 4:
             raise ValueError(f"expected [B, H, N, d] tensors, got shape {tuple(q.shape)}")
         B, H, N, d = q.shape
         p = api.make_params(B, H, N, d, blk, causal, qk_norm, k_smooth, _DTYPES[q.dtype], eps=eps,
-                            sm_scale=sm_scale, dq_mode=dq_mode)
+                            sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth)
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         pro = api.sagebwd_quant_prologue(p, q, k, v)
         O, lse = api.sagebwd_forward(p, pro)
         ctx.params = p
-        ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in _SAVED))
+        ctx.saved_names = _SAVED_QS if q_smooth else _SAVED
+        ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in ctx.saved_names))
         ctx.mark_non_differentiable(lse)
         return O, lse
 
     @staticmethod
     def backward(ctx, dO, _dlse):
         q, k, v, O, lse, *saved = ctx.saved_tensors
-        pro = dict(zip(_SAVED, saved))
+        pro = dict(zip(ctx.saved_names, saved))
         g = api.sagebwd_backward(ctx.params, q, k, v, pro, O, lse, dO.contiguous())
-        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None
+        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None, None
 
 
 def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                       qk_norm: bool = True, k_smooth: bool = True, blk: int = 128, eps: float = 1e-6,
                       sm_scale: float = 0.0, layout: str = "bhnd", return_lse: bool = False,
-                      dq_mode: int = 0) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+                      dq_mode: int = 0, q_smooth: bool = False) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
     """SageBwd-style INT8 attention with gradients (see the module docstring).
 
-    sm_scale <= 0 selects 1/sqrt(d). The lse returned with return_lse is float32 [B, H, N]
+    sm_scale <= 0 selects 1/sqrt(d); q_smooth selects the Q-smoothing variant (the query
+    mean is subtracted before quantising and added back through the key bias and dK_bias). The lse returned with return_lse is float32 [B, H, N]
     (natural log) and carries no gradient.
     """
     if layout == "bnhd":
@@ -66,7 +69,7 @@ def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     elif layout != "bhnd":
         raise ValueError(f"layout must be 'bhnd' or 'bnhd', got {layout!r}")
     O, lse = SageBwdAttention.apply(q, k, v, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
-                                    float(eps), float(sm_scale), int(dq_mode))
+                                    float(eps), float(sm_scale), int(dq_mode), bool(q_smooth))
     if layout == "bnhd":
         O = O.transpose(1, 2)
     return (O, lse) if return_lse else O

@@ -88,6 +88,12 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
   return L;
 }
 
+// Prologue scratch: the keys' per-block channel sums (K-smoothing), then the queries'
+// (Q-smoothing), each 256-byte aligned.
+size_t prologue_part_bytes(const sagebwd_params* p) {
+  return round_up(4 * (size_t)p->B * p->H * (p->N / p->blk) * p->d);
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,8 +124,8 @@ const char* sagebwd_last_error(void) { return g_last_error; }
 
 size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p) {
   if (check_params(p) != SAGEBWD_OK) return 0;
-  if (!p->k_smooth || empty(p)) return 0;
-  return round_up(4 * (size_t)p->B * p->H * (p->N / p->blk) * p->d);
+  if (empty(p)) return 0;
+  return (p->k_smooth ? prologue_part_bytes(p) : 0) + (p->q_smooth ? prologue_part_bytes(p) : 0);
 }
 
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
@@ -132,13 +138,14 @@ size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
 
 sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
                                       int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
-                                      float* q_rstd, float* k_rstd, float* k_mean, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      float* q_rstd, float* k_rstd, float* k_mean, float* q_mean,
+                                      float* kbias, void* workspace, size_t workspace_bytes, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
   if (empty(p)) return SAGEBWD_OK;
   st = check_ptrs(Q, K, V, Qc, Kc, Vtc, Qs, Ks, Vs, q_rstd, k_rstd, k_mean);
   if (st != SAGEBWD_OK) return st;
+  if (p->q_smooth && (st = check_ptrs(q_mean, kbias)) != SAGEBWD_OK) return st;
   const size_t need = sagebwd_prologue_workspace_bytes(p);
   if (need > 0) {
     if (!workspace) return SAGEBWD_ERR_NULL;
@@ -152,22 +159,32 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
   a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc;
   a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
   a.q_rstd = q_rstd; a.k_rstd = k_rstd; a.k_mean = k_mean;
-  a.kpart = static_cast<float*>(workspace);
+  char* ws = static_cast<char*>(workspace);
+  a.kpart = p->k_smooth ? reinterpret_cast<float*>(ws) : nullptr;
+  if (p->q_smooth) {
+    a.q_mean = q_mean;
+    a.kbias = kbias;
+    a.qpart = reinterpret_cast<float*>(ws + (p->k_smooth ? prologue_part_bytes(p) : 0));
+  }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
-  a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.eps = p->eps;
+  a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.q_smooth = p->q_smooth != 0;
+  a.eps = p->eps;
   return hip_status(sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)), "sagebwd_quant_prologue");
 }
 
 sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
-                               const float* Qs, const float* Ks, const float* Vs, void* O, float* lse,
-                               void* stream) {
+                               const float* Qs, const float* Ks, const float* Vs, const float* kbias, void* O,
+                               float* lse, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
   if (empty(p)) return SAGEBWD_OK;
   st = check_ptrs(Qc, Kc, Vtc, Qs, Ks, Vs, O, lse);
   if (st != SAGEBWD_OK) return st;
+  if (p->q_smooth && (st = check_ptrs(kbias)) != SAGEBWD_OK) return st;
   ForwardArgs a{};
   a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc; a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
+  a.q_smooth = p->q_smooth != 0;
+  a.kbias = a.q_smooth ? kbias : nullptr;
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
@@ -176,7 +193,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
 
 static sagebwd_status backward_impl(const sagebwd_params* p, int part, const void* Q, const void* K,
                                     const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
-                                    const float* Ks, const float* q_rstd, const float* k_rstd, const void* O,
+                                    const float* Ks, const float* q_rstd, const float* k_rstd,
+                                    const float* q_mean, const float* kbias, const void* O,
                                     const float* lse, const void* dO, void* dQ, void* dK, void* dV,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   sagebwd_status st = check_params(p);
@@ -185,6 +203,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   if (empty(p)) return SAGEBWD_OK;
   st = check_ptrs(Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV);
   if (st != SAGEBWD_OK) return st;
+  if (p->q_smooth && (st = check_ptrs(q_mean, kbias)) != SAGEBWD_OK) return st;
   if (!workspace) return SAGEBWD_ERR_NULL;
   if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
   const BwdLayout L = bwd_layout(p);
@@ -199,6 +218,11 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   a.dO = static_cast<const unsigned short*>(dO);
   a.Qc = Qc; a.Kc = Kc; a.Qs = Qs; a.Ks = Ks;
   a.q_rstd = q_rstd; a.k_rstd = k_rstd; a.lse = lse;
+  a.q_smooth = p->q_smooth != 0;
+  if (a.q_smooth) {
+    a.q_mean = q_mean;
+    a.kbias = kbias;
+  }
   a.dQ = static_cast<unsigned short*>(dQ);
   a.dK = static_cast<unsigned short*>(dK);
   a.dV = static_cast<unsigned short*>(dV);
@@ -219,21 +243,22 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
 
 sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,
                                 const int8_t* Qc, const int8_t* Kc, const float* Qs, const float* Ks,
-                                const float* q_rstd, const float* k_rstd, const void* O, const float* lse,
-                                const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  return backward_impl(p, -1, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV, workspace,
-                       workspace_bytes, stream);
+                                const float* q_rstd, const float* k_rstd, const float* q_mean,
+                                const float* kbias, const void* O, const float* lse, const void* dO, void* dQ,
+                                void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(p, -1, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, O, lse, dO, dQ, dK, dV,
+                       workspace, workspace_bytes, stream);
 }
 
 sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part, const void* Q, const void* K,
                                      const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
-                                     const float* Ks, const float* q_rstd, const float* k_rstd, const void* O,
-                                     const float* lse, const void* dO, void* dQ, void* dK, void* dV,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     const float* Ks, const float* q_rstd, const float* k_rstd,
+                                     const float* q_mean, const float* kbias, const void* O, const float* lse,
+                                     const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   if (part < 0) return check_params(p) != SAGEBWD_OK ? check_params(p) : SAGEBWD_ERR_UNSUPPORTED;
-  return backward_impl(p, part, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV, workspace,
-                       workspace_bytes, stream);
+  return backward_impl(p, part, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, O, lse, dO, dQ, dK, dV,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -300,6 +300,10 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 //   before the next barrier, which publishes them.
 //   dS leaves as this lane's 16 codes per packet in 16-byte stores: the spilled tiles are
 //   dS^T, key-major, one per 64-row packet.
+//   With Q-smoothing (QS; SageBwd article, Q-smoothing paragraph) the lane's key bias enters
+//   every P exponent, and the lane sums its dS codes (v_dot4 against ones) times the tile
+//   scale; the epilogue adds sm_scale * (that sum over the four lane groups) * q_mean to dK^,
+//   the pages' dK_bias = (dS^T 1) mu_Q^T.
 template <int D, int BLK>
 struct BwdLds {
   using P = Packet<D>;
@@ -316,7 +320,7 @@ struct BwdLds {
   static constexpr int kCpSplit = kCopies - (kCpHi - 1) * NW;
 };
 
-template <int DT, int D, int BLK, bool SPILL>
+template <int DT, int D, int BLK, bool SPILL, bool QS>
 __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   using L = BwdLds<D, BLK>;
   using P = Packet<D>;
@@ -364,6 +368,9 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   }
   const float sK = a.Ks[(size_t)bh * nb + kb];
   const float smc = a.sm_scale;
+  // (QS) this lane's key bias in log2 units, and its running sum of dequantised dS codes
+  [[maybe_unused]] const float kb2 = QS ? a.kbias[hrow + key] * (smc * kLog2e) : 0.0f;
+  [[maybe_unused]] float dsum = 0.0f;
   float* redD = reinterpret_cast<float*>(lds + L::offRED);
 
   f32x4 dk[NCT], dv[NCT];
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         const f32x4 dvv = *reinterpret_cast<const f32x4*>(pb + P::bDV + 4 * (16 * (t % 4) + 4 * g));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, -lse2[r]));
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, QS ? kb2 - lse2[r] : -lse2[r]));
           if constexpr (decltype(masked)::value) {
             if (key > q0 + 16 * t + 4 * g + r) p = 0.0f;
           }
@@ -539,6 +546,14 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         dc[h][t] = (int)pack4_lo_bytes(quant_word_fma(v[0], dinv), quant_word_fma(v[1], dinv),
                                        quant_word_fma(v[2], dinv), quant_word_fma(v[3], dinv));
       }
+    if constexpr (QS) {
+      int isum = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) isum = __builtin_amdgcn_sdot4(dc[h][t], 0x01010101, isum, false);
+      dsum = __builtin_fmaf(sdS, (float)isum, dsum);
+    }
     {
       const float sk = smc * sdS * sQ;
 #pragma unroll
@@ -605,6 +620,18 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 
   // ---- epilogue: dV and dK (RMSNorm backward with K^ = K * rstd) for this lane's key;
   //      lane group g holds channels 16n + 4g + r
+  if constexpr (QS) {
+    // dK_bias: the key's dS sum over all its query rows (the four lane groups hold the rows)
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    const float* qm = a.q_mean + (size_t)bh * D;
+#pragma unroll
+    for (int n = 0; n < NCT; ++n) {
+      const f32x4 mq = *reinterpret_cast<const f32x4*>(qm + 16 * n + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(smc * dsum, mq[r], dk[n][r]);
+    }
+  }
   unsigned short* dvrow = a.dV + (hrow + key) * D;
 #pragma unroll
   for (int n = 0; n < NCT; ++n) {
@@ -875,8 +902,10 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
   }
   if (part < 0 || part == 1) {
     const hipError_t e =
-        a.spill ? launch_kernel(&bwd_main<DT, D, BLK, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
-                : launch_kernel(&bwd_main<DT, D, BLK, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a);
+        a.spill ? (a.q_smooth ? launch_kernel(&bwd_main<DT, D, BLK, true, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
+                              : launch_kernel(&bwd_main<DT, D, BLK, true, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a))
+                : (a.q_smooth ? launch_kernel(&bwd_main<DT, D, BLK, false, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
+                              : launch_kernel(&bwd_main<DT, D, BLK, false, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a));
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {

@@ -14,6 +14,9 @@
 //   l^32 (v_permlane32_swap). The quantised P~^T becomes the B operand of O^T = V^T P~^T
 //   after two v_permlane32_swap per subtile, which put keys 16g..16g+15 in lane group g,
 //   the order in which the V^T rows are stored.
+// With Q-smoothing (QS) each score also gets its key's bias b_k (SageBwd article, Q-smoothing
+// paragraph): t = S*sQ*sK + b_k in float per element, the row max is taken over t, and the
+// exponent is t * sm*log2e + (row terms); the tile's BLK biases ride in LDS after K and V^T.
 // Per key tile (the online-softmax step and the P~ quantisation tile, 32 rows x BLK keys):
 //   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); a = max P~ over the wave's tile;
 //   codes = rne(P~ * (127/a)); l = l*alpha + u*sum P~; O = O*alpha + u*(a/127)*sV*int(PV),
@@ -50,12 +53,13 @@ __device__ __forceinline__ int swz_f(int r, int j) {
   else return j ^ ((r >> 2) & 3);
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool QS = false>
 struct FwdLds {
   static constexpr int kBytesK = BLK * D;   // K codes [BLK][D], chunk j of row r at swz_f<D>(r, j)
   static constexpr int kBytesV = D * BLK;   // V^T codes [D][BLK], chunk j of row c at swz_f<BLK>(c, j)
-  static constexpr int kBytes = kBytesK + kBytesV;
-  static constexpr int kCopies = kBytes / 1024;              // 1 KB copies per tile
+  static constexpr int kBytesKV = kBytesK + kBytesV;
+  static constexpr int kBytes = kBytesKV + (QS ? 1024 : 0);   // (QS) key biases f32 [BLK], one 1 KB copy
+  static constexpr int kCopies = kBytesKV / 1024;            // 1 KB copies of K and V^T per tile
   static constexpr int kCopiesPerWave = kCopies / kWaves;
   static_assert(kCopies % kWaves == 0, "copies per wave");
 };
@@ -63,9 +67,9 @@ struct FwdLds {
 // Copies of key tile k0 into an LDS tile buffer: copy cp = w + kWaves*i moves LDS bytes
 // [1024 cp, 1024 cp + 1024); lane l fills the chunk at 1024 cp + 16 l and reads the logical
 // chunk that the swizzle puts there.
-template <int D, int BLK>
+template <int D, int BLK, bool QS>
 __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int k0, int8_t* dst, int w, int l) {
-  using L = FwdLds<D, BLK>;
+  using L = FwdLds<D, BLK, QS>;
   const int8_t* kh = a.Kc + (size_t)bh * a.N * D;     // this head's K codes
   const int8_t* vh = a.Vtc + (size_t)bh * D * a.N;    // this head's V^T codes
   const uint32_t hbytes = (uint32_t)a.N * D;
@@ -84,13 +88,18 @@ __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int 
       buffer_to_lds16(vh, hbytes, dst + cp * 1024, (uint32_t)(c * a.N + k0 + 16 * j), 0u);
     }
   }
+  if constexpr (QS) {
+    // the tile's key biases: 1 KB from key k0 on (lanes past the head's last key read zeros:
+    // the copy's range ends with the head's biases)
+    if (w == 0) buffer_to_lds16(a.kbias + bh * a.N, (uint32_t)a.N * 4, dst + L::kBytesKV, (uint32_t)(k0 * 4 + 16 * l), 0u);
+  }
 }
 
 }  // namespace
 
-template <int DT, int D, int BLK>
+template <int DT, int D, int BLK, bool QS>
 __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
-  using L = FwdLds<D, BLK>;
+  using L = FwdLds<D, BLK, QS>;
   constexpr int NSUB = BLK / 32;  // 32-key subtiles per key tile
   constexpr int DC = D / 32;      // 32-channel chunks
   __shared__ __attribute__((aligned(16))) int8_t lds[2][L::kBytes];
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
   for (int ct = 0; ct < DC; ++ct) o[ct] = f32x16{};
 
-  issue_tile<D, BLK>(a, bh, 0, lds[0], w, l);
+  issue_tile<D, BLK, QS>(a, bh, 0, lds[0], w, l);
   wait_vmcnt<0>();
   __syncthreads();
   // block scales of the current key tile, loaded one tile ahead
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) issue_tile<D, BLK>(a, bh, (kt + 1) * BLK, lds[(kt + 1) & 1], w, l);
+    if (has_next) issue_tile<D, BLK, QS>(a, bh, (kt + 1) * BLK, lds[(kt + 1) & 1], w, l);
     const float sK = sK_n, sV = sV_n;
     if (has_next) {
       sK_n = a.Ks[(size_t)bh * nb + kt + 1];
@@ -161,29 +170,54 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           s[t] = mfma_i8_32x32x32(ak, qreg[kk], s[t]);
         }
       }
-      if constexpr (DIAG) {
+      const float c2 = (sQ * sK) * (a.sm_scale * kLog2e);
+      [[maybe_unused]] const float c3 = a.sm_scale * kLog2e;
+      // row max over the visible keys (a row with none in this tile keeps its old max)
+      float rowmax;
+      [[maybe_unused]] float tf[QS ? NSUB : 1][16];   // (QS) S*sQ*sK + b_k per element
+      if constexpr (QS) {
+        const float* bl = reinterpret_cast<const float*>(lds[kt & 1] + L::kBytesKV);
+        const float cq = sQ * sK;
+        float fm = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qrow) s[t][r] = INT32_MIN;
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(bl + 32 * t + 8 * j + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float v = __builtin_fmaf((float)s[t][4 * j + i], cq, bq[i]);
+              if constexpr (DIAG) {
+                if (k0 + 32 * t + 8 * j + 4 * g + i > qrow) v = -INFINITY;
+              }
+              tf[t][4 * j + i] = v;
+              fm = fmaxf(fm, v);
+            }
           }
-      }
-      int rmax = INT32_MIN;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(fm), __float_as_int(fm), false, false);
+        rowmax = fmaxf(__int_as_float((int)sw[0]), __int_as_float((int)sw[1])) * c3;
+      } else {
+        if constexpr (DIAG) {
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t)
+          for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) rmax = max(rmax, s[t][r]);
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(rmax, rmax, false, false);
-        rmax = max((int)sw[0], (int)sw[1]);   // lanes l and l^32 hold the same query row (signed)
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+              if (key > qrow) s[t][r] = INT32_MIN;
+            }
+        }
+        int rmax = INT32_MIN;
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rmax = max(rmax, s[t][r]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(rmax, rmax, false, false);
+          rmax = max((int)sw[0], (int)sw[1]);   // lanes l and l^32 hold the same query row (signed)
+        }
+        rowmax = (float)rmax * c2;
+        if constexpr (DIAG) rowmax = rmax == INT32_MIN ? -INFINITY : rowmax;
       }
-
-      const float c2 = (sQ * sK) * (a.sm_scale * kLog2e);
-      // row max over the visible keys (a row with none in this tile keeps its old max)
-      float rowmax = (float)rmax * c2;
-      if constexpr (DIAG) rowmax = rmax == INT32_MIN ? -INFINITY : rowmax;
       const float m_new = fmaxf(m, rowmax);
       const bool moved = __builtin_amdgcn_ballot_w64(m_new > mo + kLazy) != 0;
       const float mo_new = moved ? m_new : mo;
@@ -205,8 +239,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           float u[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = __builtin_fmaf((float)s[t][4 * j + i], c2, bias);
-            if constexpr (DIAG) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
+            float x;
+            if constexpr (QS) {
+              x = __builtin_fmaf(tf[t][4 * j + i], c3, bias);   // -inf stays -inf (masked)
+            } else {
+              x = __builtin_fmaf((float)s[t][4 * j + i], c2, bias);
+              if constexpr (DIAG) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
+            }
             u[i] = __builtin_amdgcn_exp2f(x);
             tsum += u[i];
           }
@@ -278,7 +317,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 template <int DT, int D, int BLK>
 static hipError_t launch_forward_t(const ForwardArgs& a, hipStream_t st) {
   const long long nq = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
-  return launch_kernel(&fwd_kernel<DT, D, BLK>, dim3((unsigned)(nq * a.BH)), dim3(kWaves * 64), st, a);
+  const dim3 grid((unsigned)(nq * a.BH)), block(kWaves * 64);
+  return a.q_smooth ? launch_kernel(&fwd_kernel<DT, D, BLK, true>, grid, block, st, a)
+                    : launch_kernel(&fwd_kernel<DT, D, BLK, false>, grid, block, st, a);
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st) {

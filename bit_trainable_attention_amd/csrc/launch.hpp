@@ -15,19 +15,23 @@ struct PrologueArgs {
   float *Qs, *Ks, *Vs;               // [BH, N/BLK]
   float *q_rstd, *k_rstd;            // [BH, N]
   float* k_mean;                     // [BH, D]
-  float* kpart;                      // [BH, N/BLK, D] (smoothing only)
+  float* kpart;                      // [BH, N/BLK, D] (K-smoothing only)
+  float* q_mean;                     // [BH, D] (Q-smoothing only)
+  float* kbias;                      // [BH, N] (Q-smoothing only)
+  float* qpart;                      // [BH, N/BLK, D] (Q-smoothing only)
   int BH, N, D, BLK, dtype;
-  int qk_norm, k_smooth;
+  int qk_norm, k_smooth, q_smooth;
   float eps;
 };
 
 struct ForwardArgs {
   const int8_t *Qc, *Kc, *Vtc;
   const float *Qs, *Ks, *Vs;
+  const float* kbias;                // [BH, N] (Q-smoothing only)
   unsigned short* O;                 // [BH, N, D]
   float* lse;                        // [BH, N]
   int BH, N, D, BLK, dtype;
-  int causal;
+  int causal, q_smooth;
   float sm_scale;
 };
 
@@ -36,6 +40,7 @@ struct BackwardArgs {
   const int8_t *Qc, *Kc;                     // [BH, N, D]
   const float *Qs, *Ks;                      // [BH, N/BLK]
   const float *q_rstd, *k_rstd, *lse;        // [BH, N]
+  const float *q_mean, *kbias;               // [BH, D], [BH, N] (Q-smoothing only)
   unsigned short *dQ, *dK, *dV;              // [BH, N, D]
   // workspace regions
   int8_t* pk;                                // [BH, N/64] tile packets
@@ -46,7 +51,7 @@ struct BackwardArgs {
   long long spill_tiles;                     // dS tiles per head
   int spill;
   int BH, N, D, BLK, dtype;
-  int causal, qk_norm;
+  int causal, qk_norm, q_smooth;
   float sm_scale;
 };
 

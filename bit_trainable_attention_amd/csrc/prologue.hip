@@ -17,13 +17,19 @@
 // and every lane ends with the tree's result.
 //
 // pass1  one workgroup per (head, block, tensor):
-//          Q: rstd, Q^ = Q*rstd, block absmax, codes (token-major);
-//          K: rstd; with smoothing, the block's per-channel sums of K^ (group t mod 16 in
-//             ascending order, then the pairwise tree over the 16 groups); without, codes;
+//          Q: rstd, Q^ = Q*rstd; with Q-smoothing, the block's per-channel sums of Q^ (as
+//             for K); without, block absmax and codes (token-major);
+//          K: rstd; with K-smoothing, the block's per-channel sums of K^ (group t mod 16 in
+//             ascending order, then the pairwise tree over the 16 groups); with neither
+//             smoothing, codes;
 //          V: block absmax, codes written channel-major (V^T) through an LDS byte tile.
-// pass2  (smoothing only) one workgroup per (head, block): the head's K mean (block sums in
-//          ascending block order, / N; every workgroup of the head computes it, block 0's
-//          stores it), K~ = K^ - mean, absmax, codes.
+// pass2  (either smoothing) one workgroup per (head, block) for K, and with Q-smoothing one
+//          more per (head, block) for Q: the head's mean (block sums in ascending block
+//          order, / N; every workgroup of the head computes it, block 0's stores it),
+//          x~ = x^ - mean, absmax, codes. With Q-smoothing the K workgroups also compute the
+//          query mean and each key's bias b = Ks * (codes . q_mean) (SageBwd article,
+//          Q-smoothing paragraph): per token, each lane's chunk in ascending channel order,
+//          then the 16-lane tree.
 #pragma clang fp contract(off)
 
 #include "common.hpp"
@@ -190,8 +196,9 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
     for (int p = 0; p < S::P; ++p) rstd_out[16 * p + j] = 1.0f;
   }
 
-  if (tensor == 1 && a.k_smooth) {
-    // Per-channel block sums of K^: group j (tokens t = j mod 16) in ascending order ...
+  if ((tensor == 1 && a.k_smooth) || (tensor == 0 && a.q_smooth)) {
+    float* part_out = tensor == 1 ? a.kpart : a.qpart;
+    // Per-channel block sums of K^ (or Q^): group j (tokens t = j mod 16) in ascending order ...
 #pragma unroll
     for (int i = 0; i < S::CW; ++i) {
       float g = 0.0f;
@@ -209,37 +216,25 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
       for (int u = 0; u < 4; ++u) t4[u] = t8[2 * u] + t8[2 * u + 1];
 #pragma unroll
       for (int u = 0; u < 2; ++u) t2[u] = t4[2 * u] + t4[2 * u + 1];
-      a.kpart[sidx * D + c] = t2[0] + t2[1];
+      part_out[sidx * D + c] = t2[0] + t2[1];
     }
     return;
   }
   if (tensor == 1 && blk_id == 0) {
     for (int c = threadIdx.x; c < D; c += kThreads) a.k_mean[(size_t)bh * D + c] = 0.0f;
   }
+  if (tensor == 1 && a.q_smooth) return;   // the keys' codes and biases come from pass2
   const float amax = slice_absmax<D, BLK>(s, lds.red);
   quant_slice_token_major<D, BLK>(s, amax, (tensor == 0 ? a.Qc : a.Kc) + tok0 * D,
                                   (tensor == 0 ? a.Qs : a.Ks) + sidx, j, ch);
 }
 
-template <int DT, int D, int BLK>
-__global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
-  using S = Slice<D, BLK>;
-  __shared__ float red[kThreads / 64];
-  const int nb = a.N / BLK;
-  const int blk_id = blockIdx.x % nb;
-  const int bh = blockIdx.x / nb;
-  const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;
-  const size_t sidx = (size_t)bh * nb + blk_id;
-  const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
-
-  S s;
-  load_slice<DT, D, BLK>(a.K + tok0 * D, s, j, ch);
-  // mean of the head's keys per channel: its blocks' channel sums in ascending block order,
-  // then one division by N (every workgroup of the head computes the same value; the one of
-  // block 0 also stores it)
-  __shared__ float mean[D];
+// The head's per-channel mean from its blocks' channel sums (ascending block order, then one
+// division by N) into mean[0..D); threads < D each own a channel.
+template <int D>
+__device__ __forceinline__ void head_mean(const float* __restrict__ part_head, int nb, int N, float* mean) {
   if (threadIdx.x < D) {
-    const float* part = a.kpart + (size_t)bh * nb * D + threadIdx.x;
+    const float* part = part_head + threadIdx.x;
     float tot = 0.0f;
     int b = 0;
     for (; b + 16 <= nb; b += 16) {   // 16 loads in flight, then the additions in block order
@@ -250,25 +245,70 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
       for (int i = 0; i < 16; ++i) tot = tot + v[i];
     }
     for (; b < nb; ++b) tot = tot + part[(size_t)b * D];
-    const float m = tot / (float)a.N;
-    mean[threadIdx.x] = m;
-    if (blk_id == 0) a.k_mean[(size_t)bh * D + threadIdx.x] = m;
+    mean[threadIdx.x] = tot / (float)N;
   }
+}
+
+template <int DT, int D, int BLK>
+__global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
+  using S = Slice<D, BLK>;
+  __shared__ float red[kThreads / 64];
+  __shared__ float mean[D];
+  __shared__ float qmean[D];
+  const int nb = a.N / BLK;
+  const long long nblocks = (long long)a.BH * nb;
+  const bool is_q = (long long)blockIdx.x >= nblocks;           // Q-smoothing workgroups follow
+  const long long wg = is_q ? (long long)blockIdx.x - nblocks : (long long)blockIdx.x;
+  const int blk_id = (int)(wg % nb);
+  const int bh = (int)(wg / nb);
+  const size_t tok0 = (size_t)bh * a.N + (size_t)blk_id * BLK;
+  const size_t sidx = (size_t)bh * nb + blk_id;
+  const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
+
+  S s;
+  load_slice<DT, D, BLK>((is_q ? a.Q : a.K) + tok0 * D, s, j, ch);
+  // mean of the head's keys (or queries) per channel; every workgroup of the head computes the
+  // same value, the one of block 0 stores it
+  const bool smooth = is_q || a.k_smooth;
+  if (smooth) {
+    head_mean<D>((is_q ? a.qpart : a.kpart) + (size_t)bh * nb * D, nb, a.N, mean);
+    if (blk_id == 0 && threadIdx.x < D) (is_q ? a.q_mean : a.k_mean)[(size_t)bh * D + threadIdx.x] = mean[threadIdx.x];
+  }
+  if (!is_q && a.q_smooth) head_mean<D>(a.qpart + (size_t)bh * nb * D, nb, a.N, qmean);
   __syncthreads();
   float mu[S::CW];
 #pragma unroll
-  for (int i = 0; i < S::CW; ++i) mu[i] = mean[ch * S::CW + i];
+  for (int i = 0; i < S::CW; ++i) mu[i] = smooth ? mean[ch * S::CW + i] : 0.0f;
+  const float* rstd = is_q ? a.q_rstd : a.k_rstd;
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
-    const float r = a.qk_norm ? a.k_rstd[tok0 + 16 * p + j] : 1.0f;
+    const float r = a.qk_norm ? rstd[tok0 + 16 * p + j] : 1.0f;
 #pragma unroll
     for (int i = 0; i < S::CW; ++i) {
-      const float kh = s.x[p][i] * r;
-      s.x[p][i] = kh - mu[i];
+      const float xh = s.x[p][i] * r;
+      s.x[p][i] = xh - mu[i];
     }
   }
   const float amax = slice_absmax<D, BLK>(s, red);
-  quant_slice_token_major<D, BLK>(s, amax, a.Kc + tok0 * D, a.Ks + sidx, j, ch);
+  quant_slice_token_major<D, BLK>(s, amax, (is_q ? a.Qc : a.Kc) + tok0 * D, (is_q ? a.Qs : a.Ks) + sidx, j, ch);
+  if (is_q || !a.q_smooth) return;
+  // key bias b = Ks * (codes . q_mean): the codes as quant_slice_token_major made them
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float scale = amax > 0.0f ? amax / 127.0f : 0.0f;
+  float qm[S::CW];
+#pragma unroll
+  for (int i = 0; i < S::CW; ++i) qm[i] = qmean[ch * S::CW + i];
+#pragma unroll
+  for (int p = 0; p < S::P; ++p) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) {
+      const float code = (float)(int8_t)quant_word(s.x[p][i], inv);
+      dot = dot + code * qm[i];
+    }
+    dot = row_tree_sum(dot);
+    if (ch == 0) a.kbias[tok0 + 16 * p + j] = scale * dot;
+  }
 }
 
 template <int DT, int D, int BLK>
@@ -276,8 +316,9 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st) {
   const int nb = a.N / BLK;
   const long long nblocks = (long long)a.BH * nb;
   hipError_t e = launch_kernel(&prologue_pass1<DT, D, BLK>, dim3((unsigned)(nblocks * 3)), dim3(kThreads), st, a);
-  if (e != hipSuccess || !a.k_smooth) return e;
-  return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)nblocks), dim3(kThreads), st, a);
+  if (e != hipSuccess || !(a.k_smooth || a.q_smooth)) return e;
+  return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)(nblocks * (a.q_smooth ? 2 : 1))),
+                       dim3(kThreads), st, a);
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st) {

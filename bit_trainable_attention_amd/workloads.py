@@ -19,8 +19,10 @@ quantisation and the 325M Llama pretraining run):
 
 Draw recipe: numpy PCG64 with seed 1000 + k (k = 1..5 in the order above); draws
 in order Q, K, V, dO (float32 standard normals times the stated std), then the
-extras (bias, outlier channels); rounding float32 -> fp16/bf16 is round to nearest
-even. The same host arrays feed the GPU and the oracle.
+extras (K bias, outlier channels, and last a per-(head, channel) Q bias for the
+Q-smoothing cases, which give any workload q_smooth=True and a q_bias_var); rounding
+float32 -> fp16/bf16 is round to nearest even. The same host arrays feed the GPU and
+the oracle.
 """
 from __future__ import annotations
 
@@ -48,6 +50,8 @@ class Workload:
     k_bias_var: float = 0.0      # variance of the per-(head, channel) bias added to K
     k_outlier_channels: int = 0  # number of K channels scaled by k_outlier_scale
     k_outlier_scale: float = 1.0
+    q_smooth: bool = False       # the optional Q-smoothing variant
+    q_bias_var: float = 0.0      # variance of the per-(head, channel) bias added to Q (drawn last)
 
     @property
     def seed(self) -> int:
@@ -143,6 +147,10 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray
         idx = np.sort(rng.choice(w.d, size=w.k_outlier_channels, replace=False))
         k[..., idx] *= np.float32(w.k_outlier_scale)
         out["k_outlier_idx"] = idx
+    if w.q_bias_var > 0.0:
+        qb = rng.standard_normal((w.H, w.d), dtype=np.float32) * np.float32(np.sqrt(w.q_bias_var))
+        q += qb[None, :, None, :]
+        out["q_bias"] = qb
     out["Q"] = f32_to_bits(q, w.dtype)
     out["K"] = f32_to_bits(k, w.dtype)
     out["V"] = f32_to_bits(v, w.dtype)

@@ -15,7 +15,13 @@
  *     backward recomputed QK^T, dV = P^T dO, dK = dS^T Q, dQ = dS K) and dP = dO V^T in the
  *     16-bit input type with float32 accumulation (article, precision-split paragraph);
  *   - a flash-style forward and backward that never writes the N x N scores to memory
- *     (TurboQuant blog, FlashAttention section).
+ *     (TurboQuant blog, FlashAttention section);
+ *   - optionally Q-smoothing (article, Q-smoothing paragraph, which names the bias term
+ *     (dS^T 1) mu_Q^T): the queries' per-channel mean mu_Q over the N tokens of a head is
+ *     subtracted before quantising Q; every score then gets back the per-key bias
+ *     b_k = (K~ mu_Q)_k, taken from the dequantised K codes, b_k = Ks * (Kc_k . mu_Q); and dK
+ *     gets dK_bias = (dS^T 1) mu_Q^T, with dS the dequantised dS codes of each tile summed
+ *     over its queries. dQ is unchanged.
  *
  * In-kernel quantisation tiles (P~ in the forward, P and dS in the backward) use the same
  * absmax/127 rule in float32, except that the kernels take 127/absmax from the hardware
@@ -80,6 +86,8 @@ typedef struct {
   float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(d)                            */
   int32_t dtype;        /* sagebwd_dtype of Q, K, V, dO, O, dQ, dK, dV                       */
   int32_t dq_mode;      /* how the backward reduces dQ over key blocks (sagebwd_dq_mode)     */
+  int32_t q_smooth;     /* nonzero: subtract Q's per-channel mean before quantising and add
+                           the key bias / dK_bias terms back (see above)                    */
 } sagebwd_params;
 
 /* dQ = dS K sums over every key block. SAGEBWD_DQ_SPILL writes each (64-query, blk-key) tile
@@ -95,19 +103,25 @@ typedef enum { SAGEBWD_DQ_AUTO = 0, SAGEBWD_DQ_SPILL = 1, SAGEBWD_DQ_ATOMIC = 2 
 #define SAGEBWD_DQ_AUTO_SPILL_LIMIT (16ull << 30)
 
 /* Bytes of scratch sagebwd_quant_prologue needs: the per-block channel sums of the
- * normalised keys, float32 [B,H,N/blk,d] (0 when k_smooth is off). Returns 0 for
+ * normalised keys, float32 [B,H,N/blk,d], when k_smooth is on, then (256-byte aligned) those
+ * of the normalised queries when q_smooth is on (0 when both are off). Returns 0 for
  * invalid params. */
 size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
 
-/* Quantisation prologue: QK-norm -> K-smoothing -> per-block INT8 codes and scales.
- * The codes, scales and statistics are the "quantised views" both passes reuse (the
- * Full-Stack FP4 page, section 2.4, reuses quantised Q, K, V between the passes).
+/* Quantisation prologue: QK-norm -> K-smoothing (and Q-smoothing) -> per-block INT8 codes
+ * and scales. The codes, scales and statistics are the "quantised views" both passes reuse
+ * (the Full-Stack FP4 page, section 2.4, reuses quantised Q, K, V between the passes).
  *   Q, K, V  in : dtype [B,H,N,d]
- *   Qc, Kc   out: int8 [B,H,N,d]   codes of Q^ and of K~ = K^ - mean (smoothed keys)
+ *   Qc, Kc   out: int8 [B,H,N,d]   codes of Q^ (of Q~ = Q^ - q_mean with q_smooth) and of
+ *                                  K~ = K^ - mean (smoothed keys)
  *   Vtc      out: int8 [B,H,d,N]   codes of V, stored TRANSPOSED (channel-major)
  *   Qs,Ks,Vs out: float32 [B,H,N/blk]  block scales
  *   q_rstd, k_rstd out: float32 [B,H,N]  1/sqrt(mean(x^2)+eps) per token (1 if !qk_norm)
  *   k_mean   out: float32 [B,H,d]  the subtracted mean (0 if !k_smooth)
+ *   q_mean   out: float32 [B,H,d]  the subtracted query mean (q_smooth only; else ignored,
+ *                                  may be NULL)
+ *   kbias    out: float32 [B,H,N]  b_k = Ks * (Kc_k . q_mean), float32 sum over channels
+ *                                  (q_smooth only; else ignored, may be NULL)
  *   workspace   : >= sagebwd_prologue_workspace_bytes(p) bytes (may be NULL if that is 0)
  * Bit-exact contract: per token, the d channels form 16 chunks of d/16 consecutive
  * channels; each chunk sums x*x in ascending channel order in float32, and ss is the
@@ -116,23 +130,26 @@ size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
  * root; x^ = x*rstd; the mean: inside each block, token t joins group t mod 16, each group
  * sums its tokens in ascending order and the block sum is the same pairwise tree of the 16
  * group sums; the block sums are then added in ascending block order and divided by N;
- * K~ = K^ - mean; then the INT8 rule above. */
+ * K~ = K^ - mean; then the INT8 rule above. q_mean is taken the same way from Q^ (and
+ * Q~ = Q^ - q_mean). kbias is not bit-specified (float32, any summation order). */
 sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
                                       const void* Q, const void* K, const void* V,
                                       int8_t* Qc, int8_t* Kc, int8_t* Vtc,
                                       float* Qs, float* Ks, float* Vs,
                                       float* q_rstd, float* k_rstd, float* k_mean,
+                                      float* q_mean, float* kbias,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
 /* Forward: O = softmax(sm_scale * Q^ K~^T [causal mask]) V with INT8 QK^T and PV.
- *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs
+ *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs, and its kbias with q_smooth (each
+ *            score is then sm_scale * (Q~ K~^T + b_k); kbias ignored, may be NULL, without)
  *   O   out: dtype [B,H,N,d]
  *   lse out: float32 [B,H,N], natural-log logsumexp of each row of the scaled scores */
 sagebwd_status sagebwd_forward(const sagebwd_params* p,
                                const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
                                const float* Qs, const float* Ks, const float* Vs,
-                               void* O, float* lse, void* stream);
+                               const float* kbias, void* O, float* lse, void* stream);
 
 /* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
  * boundary, in this order; "chunk" = 16 bytes):
@@ -170,6 +187,7 @@ size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
  * RMSNorm backward is applied; K-smoothing adds no term because every row of dS sums to 0).
  *   Q, K, V       in : dtype [B,H,N,d], the prologue's inputs
  *   Qc, Kc, Qs, Ks, q_rstd, k_rstd in: the prologue's outputs
+ *   q_mean, kbias in : the prologue's outputs with q_smooth (ignored, may be NULL, without)
  *   O, lse        in : the forward's outputs
  *   dO            in : dtype [B,H,N,d]
  *   dQ, dK, dV    out: dtype [B,H,N,d]
@@ -179,6 +197,7 @@ sagebwd_status sagebwd_backward(const sagebwd_params* p,
                                 const int8_t* Qc, const int8_t* Kc,
                                 const float* Qs, const float* Ks,
                                 const float* q_rstd, const float* k_rstd,
+                                const float* q_mean, const float* kbias,
                                 const void* O, const float* lse, const void* dO,
                                 void* dQ, void* dK, void* dV,
                                 void* workspace, size_t workspace_bytes, void* stream);
@@ -196,6 +215,7 @@ sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part,
                                      const int8_t* Qc, const int8_t* Kc,
                                      const float* Qs, const float* Ks,
                                      const float* q_rstd, const float* k_rstd,
+                                     const float* q_mean, const float* kbias,
                                      const void* O, const float* lse, const void* dO,
                                      void* dQ, void* dK, void* dV,
                                      void* workspace, size_t workspace_bytes, void* stream);

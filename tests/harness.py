@@ -31,7 +31,7 @@ def spec_for(w: wl.Workload, dtype: Optional[str] = None) -> oq.Spec:
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
                    fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
-                   bwd_sk=w.blk)
+                   bwd_sk=w.blk, q_smooth=w.q_smooth)
 
 
 def rel_l2(a, b) -> float:
@@ -59,7 +59,7 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 def params_for(w: wl.Workload, dq_mode: int = 0):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                           dq_mode=dq_mode)
+                           dq_mode=dq_mode, q_smooth=w.q_smooth)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -128,8 +128,17 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
 
 
 def check_prologue(g: Dict[str, np.ndarray], o: Dict[str, np.ndarray]) -> None:
-    """The GPU prologue's codes, scales, rstd and K mean equal the oracle's bit for bit."""
-    for k in ("Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"):
+    """The GPU prologue's codes, scales, rstd and K mean (and query mean with Q-smoothing)
+    equal the oracle's bit for bit; the key bias (float32 on the GPU, any summation order)
+    is within float32 rounding of the oracle's float64 value."""
+    keys = ["Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"]
+    if "kbias" in g:
+        keys.append("q_mean")
+        kb = np.asarray(o["kbias"], np.float64)
+        err = np.max(np.abs(g["kbias"].astype(np.float64) - kb))
+        # a float32 dot product over d terms: a few ulps of the largest term's magnitude
+        assert err <= 1e-5 * max(1.0, float(np.max(np.abs(kb)))), err
+    for k in keys:
         assert g[k].dtype == o[k].dtype, k
         assert np.array_equal(g[k], o[k]), (k, int(np.sum(g[k] != o[k])))
     assert np.array_equal(g["Vtc"], np.swapaxes(o["Vc"], -1, -2)), int(np.sum(g["Vtc"] != np.swapaxes(o["Vc"], -1, -2)))
@@ -141,6 +150,9 @@ def pro_to_device(pro: Dict[str, np.ndarray]):
     out = {}
     for k in ("Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"):
         out[k] = torch.from_numpy(np.ascontiguousarray(pro[k])).to("cuda:0")
+    if np.any(pro.get("q_mean", 0)):
+        out["q_mean"] = torch.from_numpy(np.ascontiguousarray(pro["q_mean"])).to("cuda:0")
+        out["kbias"] = torch.from_numpy(np.ascontiguousarray(pro["kbias"], dtype=np.float32)).to("cuda:0")
     out["Vtc"] = torch.from_numpy(np.ascontiguousarray(np.swapaxes(pro["Vc"], -1, -2))).to("cuda:0")
     return out
 

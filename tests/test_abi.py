@@ -13,7 +13,7 @@ lib = _lib.load()  # fails loudly if the library was not built
 
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
-                dtype=_lib.SAGEBWD_FP16, dq_mode=0)
+                dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -48,15 +48,15 @@ def test_last_error_empty_without_failures():
 
 
 def _prologue(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 12), ws, ws_bytes, None)
+    return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 14), ws, ws_bytes, None)
 
 
 def _forward(p, ptr=FAKE):
-    return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 8), None)
+    return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 9), None)
 
 
 def _backward(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 15), ws, ws_bytes, None)
+    return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 17), ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("call", [_prologue, _forward, _backward])
@@ -77,7 +77,7 @@ def test_invalid_params_rejected(call):
 
 
 def test_null_params_rejected():
-    assert lib.sagebwd_forward(None, *([FAKE] * 8), None) == -1
+    assert lib.sagebwd_forward(None, *([FAKE] * 9), None) == -1
     assert lib.sagebwd_backward_workspace_bytes(None) == 0
     assert lib.sagebwd_prologue_workspace_bytes(None) == 0
 
@@ -127,9 +127,9 @@ def test_empty_is_a_noop():
 def test_backward_part_rejects_bad_part():
     p = P()
     for part in (-1, 3, 99):
-        assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
-    assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 15), FAKE, 1 << 40, None) == -3
-    assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 15), FAKE, 0, None) == -5
+        assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 17), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 17), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 17), FAKE, 0, None) == -5
 
 
 def test_binding_rejects_host_tensors():
@@ -146,3 +146,27 @@ def test_binding_rejects_host_tensors():
         sagebwd_attention(q, q, q, blk=64)
     with pytest.raises(ValueError, match="layout"):
         sagebwd_attention(q, q, q, blk=64, layout="nhd")
+
+
+def test_q_smooth_arguments():
+    # the query mean / key bias pointers are required with q_smooth and ignored (NULL is
+    # fine) without; the prologue scratch grows by the queries' block sums
+    def pro_with(p, qm, kb):
+        ptrs = [FAKE] * 12 + [qm, kb]
+        return lib.sagebwd_quant_prologue(ctypes.byref(p), *ptrs, FAKE, 1 << 40, None)
+    assert pro_with(P(q_smooth=1), 0, FAKE) == -1
+    assert pro_with(P(q_smooth=1), FAKE, 0) == -1
+    assert pro_with(P(q_smooth=1), MIS, FAKE) == -4
+    fw = lambda p, kb: lib.sagebwd_forward(ctypes.byref(p), *([FAKE] * 6), kb, FAKE, FAKE, None)
+    assert fw(P(q_smooth=1), 0) == -1
+    bw = lambda p, qm, kb: lib.sagebwd_backward(ctypes.byref(p), *([FAKE] * 9), qm, kb, *([FAKE] * 6),
+                                                FAKE, 1 << 40, None)
+    assert bw(P(q_smooth=1), 0, FAKE) == -1
+    assert bw(P(q_smooth=1), FAKE, 0) == -1
+    up = lambda x: (x + 255) // 256 * 256
+    part = up(4 * 2 * 4 * 64)
+    assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(q_smooth=1))) == 2 * part
+    assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(q_smooth=1, k_smooth=0))) == part
+    # the q_smooth-only scratch must still be passed
+    assert lib.sagebwd_quant_prologue(ctypes.byref(P(q_smooth=1, k_smooth=0)), *([FAKE] * 14), FAKE,
+                                      part - 1, None) == -5
