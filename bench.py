@@ -97,6 +97,8 @@ def main():
                     help="before warm-up, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--q-smooth", action="store_true",
+                    help="time the Q-smoothing variant on the same inputs (default: off, as the metric)")
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
@@ -109,6 +111,8 @@ def main():
     from bit_trainable_attention_amd import api
     from bit_trainable_attention_amd import workloads as wl
     w = wl.WORKLOADS[args.workload]
+    if args.q_smooth:
+        w = w.with_shape(q_smooth=True)
 
     def to_device(bits):
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
@@ -117,7 +121,8 @@ def main():
     log(f"[bench] workload {w.name}: B{w.B} H{w.H} N{w.N} d{w.d} {w.dtype} causal={w.causal} "
         f"qk_norm={w.qk_norm} k_smooth={w.k_smooth} blk={w.blk}")
     x = wl.make_inputs(w)
-    p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+    p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
+                        q_smooth=w.q_smooth)
     dev = torch.device("cuda:0")
     Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
     pro = api.sagebwd_quant_prologue(p, Q, K, V)
@@ -202,7 +207,7 @@ def main():
             for t in (qg, kg, vg):
                 t.grad = None
             o = sagebwd_attention(qg, kg, vg, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
-                                  blk=w.blk, eps=w.eps)
+                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth)
             o.backward(dO)
 
         for _ in range(2):
@@ -233,9 +238,9 @@ def main():
         "dtype": "int8+fp16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} H{w.H} N{w.N} d{w.d} causal {w.dtype} QK-norm "
-                               f"K-smoothing blk{w.blk} (prologue+fwd+bwd)",
+                               f"K-smoothing blk{w.blk}{' Q-smoothing' if w.q_smooth else ''} (prologue+fwd+bwd)",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "blk": w.blk,
-                   "dtype": w.dtype, "parallelism": "single GPU"},
+                   "dtype": w.dtype, "q_smooth": w.q_smooth, "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak_step, 4),
         "step_ms": {k: round(v, 4) for k, v in step_stats.items()},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
