@@ -14,9 +14,10 @@ SAGEBWD_BF16 = 1
 DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 
 # Quantisation tile shapes of the kernels (include/sagebwd.h); the backward's P and dS tiles
-# span one query block (blk rows).
+# span one query block (blk rows) by BWD_P_TILE_K and min(blk, BWD_DS_TILE_K) keys.
 FWD_TILE_Q = 32
 BWD_P_TILE_K = 16
+BWD_DS_TILE_K = 64
 
 STATUS = {
     0: "SAGEBWD_OK", -1: "SAGEBWD_ERR_NULL", -2: "SAGEBWD_ERR_SHAPE", -3: "SAGEBWD_ERR_UNSUPPORTED",

@@ -89,7 +89,7 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     tiles = nb * nt - r * nb * (nb - 1) // 2 if p.causal else nb * nt
     off = {"packet_bytes": PACKET_BYTES[p.d], "packets": 0, "tiles_per_head": tiles}
     after = up(bh * nt * PACKET_BYTES[p.d])
-    ktp, dsp, dsm = up(bh * nb * p.d * p.blk), up(bh * tiles * 64 * p.blk), up(bh * tiles * 4)
+    ktp, dsp, dsm = up(bh * nb * p.d * p.blk), up(bh * tiles * 64 * p.blk), up(bh * tiles * (p.blk // 64) * 4)
     spill = p.dq_mode == 1 or (p.dq_mode == 0 and ktp + dsp + dsm <= SPILL_LIMIT)
     off["spill"] = int(spill)
     if spill:

@@ -70,7 +70,7 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
   L.tiles = sagebwd::spill_tiles_per_head(p->N, p->blk, p->causal != 0);
   const size_t ktp_bytes = round_up(bh * (p->N / p->blk) * (size_t)p->d * p->blk);
   const size_t dsp_bytes = round_up(bh * (size_t)L.tiles * 64 * p->blk);
-  const size_t dsm_bytes = round_up(bh * (size_t)L.tiles * 4);
+  const size_t dsm_bytes = round_up(bh * (size_t)L.tiles * (p->blk / 64) * 4);
   const size_t spill_bytes = ktp_bytes + dsp_bytes + dsm_bytes;
   // the dQ pass addresses one head's dS tiles with 32-bit buffer offsets
   L.spill_fits = (size_t)L.tiles * 64 * p->blk < (1ull << 32);

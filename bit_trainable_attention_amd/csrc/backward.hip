@@ -50,6 +50,11 @@ __device__ __forceinline__ int tile_token_pos(int u) { return 16 * ((u >> 2) & 3
 // the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// A wave-uniform float held in a scalar register.
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Sum over each 16-lane row, returned to every lane of the row (DPP butterfly).
 template <int CTRL>
 __device__ __forceinline__ float add_dpp_row(float v) {
@@ -294,35 +299,33 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 // that order; the Q^T operands come from the row-major Q codes through transposing reads.
 //   P is quantised on the wave's own TQ x 16 tile (no cross-wave step), so dV runs before
 //   the one workgroup barrier of the tile, which publishes the waves' |dS| maxima (dS is
-//   quantised on the TQ x BLK tile, one block). Everything the tile needs from LDS is in
-//   registers before that barrier, so right after it the tile buffer takes the copies of
-//   the tile two steps ahead (two tile buffers); each wave waits for its own copies just
-//   before the next barrier, which publishes them.
+//   quantised on TQ x 64 tiles: one query block by the 64 keys of four waves). Everything
+//   the tile needs from LDS is in registers before that barrier, so right after it the tile
+//   buffer takes the copies of the tile two steps ahead (two tile buffers); each wave waits
+//   for its own copies just before the next barrier, which publishes them.
 //   dS leaves as this lane's 16 codes per packet in 16-byte stores: the spilled tiles are
-//   dS^T, key-major, one per 64-row packet.
+//   dS^T, key-major, one per 64-row packet, with one dQ multiplier per 64 keys.
 //   With Q-smoothing (QS; SageBwd article, Q-smoothing paragraph) the lane's key bias enters
 //   every P exponent, and the lane sums its dS codes (v_dot4 against ones) times the tile
 //   scale; the epilogue adds sm_scale * (that sum over the four lane groups) * q_mean to dK^,
 //   the pages' dK_bias = (dS^T 1) mu_Q^T.
-template <int D, int BLK>
+template <int D, int BLK, bool SPILL>
 struct BwdLds {
   using P = Packet<D>;
   static constexpr int NW = BLK / 16;             // waves
   static constexpr int NH = BLK / kPq;            // packets per query tile
   static constexpr int kBuf = NH * P::kBytes;     // one tile buffer (two of them)
-  static constexpr int offRED = 2 * kBuf;         // |dS| maxima [2][NW] (by tile parity)
-  static constexpr int offKT = offRED + 2 * NW * 4;  // atomic mode: K^T codes [D][BLK]
-  static constexpr int kBytesSpill = offKT;
-  static constexpr int kBytesAtomic = offKT + D * BLK;
-  // 1 KB copies of one tile: kCpHi for waves w < kCpSplit, one fewer for the rest
-  static constexpr int kCopies = NH * P::kCopies;
-  static constexpr int kCpHi = (kCopies + NW - 1) / NW;
-  static constexpr int kCpSplit = kCopies - (kCpHi - 1) * NW;
+  static constexpr int kTiles = 2 * kBuf;
+  static constexpr int offKT = kTiles;            // atomic mode: K^T codes [D][BLK]
+  static constexpr int kBytes = SPILL ? kTiles : kTiles + D * BLK;
+  static constexpr int kCopies = NH * P::kCopies; // 1 KB copies of one tile
+  static constexpr int kMinBlocks = BLK == 64 ? 2 : 1;   // workgroups per CU
 };
 
 template <int DT, int D, int BLK, bool SPILL, bool QS>
-__global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
-  using L = BwdLds<D, BLK>;
+__global__ __launch_bounds__((BwdLds<D, BLK, SPILL>::NW * 64), (BwdLds<D, BLK, SPILL>::kMinBlocks))
+void bwd_main(BackwardArgs a) {
+  using L = BwdLds<D, BLK, SPILL>;
   using P = Packet<D>;
   constexpr int NW = L::NW;        // waves per workgroup
   constexpr int NH = L::NH;        // packets per query tile
@@ -332,16 +335,22 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   constexpr int KCH = D / 64;      // 64-channel chunks (INT8 contraction of S)
   constexpr int HCH = D / 32;      // 32-channel chunks (16-bit contraction of dP)
   constexpr int NCT = D / 16;      // 16-channel output tiles of dV^T, dK^T and dQ
-  __shared__ __attribute__((aligned(1024))) int8_t lds[SPILL ? L::kBytesSpill : L::kBytesAtomic];
+  constexpr int KD = BLK / 64;     // 64-key dS tiles of a key block
+  __shared__ __attribute__((aligned(1024))) int8_t lds[L::kBytes];
+  // |dS| maxima of the waves [tile parity][wave], apart from the tile buffers so that reading
+  // them never waits for copies in flight into the buffers
+  __shared__ float redD[2 * NW];
 
   const int nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
   const int kb = blockIdx.x / a.BH;            // key block; 0 first (most work when causal)
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g = l >> 4, lr = l & 15;
   const int tid = threadIdx.x;
-  const int k0 = kb * BLK;
+  const int k0 = kb * BLK;                     // first key of the block
   const int kl = 16 * w + lr;                  // this lane's key inside the block
   const int key = k0 + kl;
+  const int wg0 = 4 * (w / 4);                 // first wave of this wave's 64-key dS tile
+  const int dg = kl >> 6;                      // that dS tile inside the key block
   const size_t hrow = (size_t)bh * a.N;
   const int ntq = a.N / TQ;                    // query tiles
   const int8_t* pkh = a.pk + (size_t)bh * ntq * L::kBuf;    // this head's packets
@@ -371,7 +380,6 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   // (QS) this lane's key bias in log2 units, and its running sum of dequantised dS codes
   [[maybe_unused]] const float kb2 = QS ? a.kbias[hrow + key] * (smc * kLog2e) : 0.0f;
   [[maybe_unused]] float dsum = 0.0f;
-  float* redD = reinterpret_cast<float*>(lds + L::offRED);
 
   f32x4 dk[NCT], dv[NCT];
 #pragma unroll
@@ -380,12 +388,13 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   // per-lane byte offsets of the operands inside a packet. Rows 16t + lr share their
   // swizzle for every t, except that at d = 128 the Q rows of odd t have bit 2 of the slot
   // flipped, i.e. their 64-channel chunks swapped (swz_q); so each operand address is
-  // buffer + one of these offsets + a compile-time constant.
-  int oQ[KCH], oDO[HCH];
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) oQ[c] = P::bQ + lr * D + 16 * swz_q<D>(lr, 4 * c + g);
-#pragma unroll
-  for (int c = 0; c < HCH; ++c) oDO[c] = P::bDO + lr * 2 * D + 16 * swz_do<D>(lr, 4 * c + g);
+  // buffer + one of these offsets + a compile-time constant. Channel chunk c of a row (16
+  // bytes at slot 4c + g, swizzled) sits at the chunk-0 offset XOR 64c: the swizzles XOR the
+  // slot with a function of the row alone. Buffer offsets are multiples of 1 KB, so the XOR
+  // may be applied after adding them; the kernels do so in the tile loop, which keeps one
+  // register per operand stream instead of one per chunk.
+  const int oQ0 = P::bQ + lr * D + 16 * swz_q<D>(lr, g);
+  const int oDO0 = P::bDO + lr * 2 * D + 16 * swz_do<D>(lr, g);
   const int oT = P::bDOT + lr * kPq + 16 * swz<kPq>(lr, g);   // dO^T codes, channel 16n + lr
   // Q^T operands by transposing reads of the row-major Q codes: for channel tile n, lane
   // 16g + 2i + h names 8 bytes (channels 16n + 8h ..) of packet row 16(i/4) + 4g + i%4 (and
@@ -400,10 +409,15 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 
   // copies of query tile qt into a tile buffer: wave w moves KB cp = w, w + NW, ...
   auto issue = [&](int qt, int8_t* dst) {
+    constexpr int kFull = L::kCopies / NW, kRest = L::kCopies % NW;
 #pragma unroll
-    for (int j = 0; j < L::kCpHi; ++j) {
+    for (int j = 0; j < kFull; ++j) {
       const int cp = w + NW * j;
-      if (cp < L::kCopies) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * L::kBuf + cp * 1024);
+      buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * L::kBuf + cp * 1024);
+    }
+    if constexpr (kRest > 0) {
+      const int cp = w + NW * kFull;
+      if (w < kRest) buffer_to_lds16(pkh, pkh_bytes, dst + cp * 1024, 16 * l, qt * L::kBuf + cp * 1024);
     }
   };
   // vector-memory operations a wave issues per step after the step's copies: the dS^T
@@ -411,65 +425,65 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
   constexpr int kStores = SPILL ? 2 * NH : NCT * 4;
 
   const int qt0 = a.causal ? kb : 0;           // first query tile at or below the diagonal
-  issue(qt0, lds);
-  if (qt0 + 1 < ntq) issue(qt0 + 1, lds + L::kBuf);
-  wait_vmcnt<0>();
-  __syncthreads();
 
-  for (int qt = qt0; qt < ntq; ++qt) {
-    const int q0 = qt * TQ;
-    const int step = qt - qt0;
-    const int bofs = (step & 1) * L::kBuf;       // byte offset of this tile's buffer
-    const int8_t* buf = lds + bofs;
+  // ---- the phases of one query tile; state carried between them (registers)
+  float sQ = 0.0f, sdO = 0.0f, c2 = 0.0f;
+  i32x4 s[NS];
+  f32x4 dp[NS];
+  float dsf[NS][4];
+  i32x4 qtr[NH][NCT];
+  i32x4 dc[NH];
 
-    const float sQ = *reinterpret_cast<const float*>(buf + P::bSQ);
-    const float sdO = *reinterpret_cast<const float*>(buf + P::bSDO);
-    const float c2 = (sQ * sK) * (smc * kLog2e);
-
-    // ---- S = Q K~^T and dP = dO V^T for the 16-row sub-tiles (LLVM's interleaving strategy
-    //      1 for this block: measured 1.7-2.6% faster than the default schedule)
+  // S = Q K~^T and dP = dO V^T for the 16-row sub-tiles of the tile at byte offset bofs
+  // (LLVM's interleaving strategy 1 for this block: measured 1.7-2.6% faster than the
+  // default schedule)
+  auto phase_sdp = [&](int bofs) {
+    // uniform values, kept in scalar registers
+    sQ = uniform_f(*reinterpret_cast<const float*>(lds + bofs + P::bSQ));
+    sdO = uniform_f(*reinterpret_cast<const float*>(lds + bofs + P::bSDO));
+    c2 = uniform_f((sQ * sK) * (smc * kLog2e));
+    const int qb = bofs + oQ0, db = bofs + oDO0;
     __builtin_amdgcn_iglp_opt(1);
-    i32x4 s[NS];
-    f32x4 dp[NS];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
-      const int8_t* pb = buf + (t / 4) * P::kBytes;
+      const int8_t* pb = lds + (t / 4) * P::kBytes;
       s[t] = i32x4{};
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
         const int cq = D == 128 ? c ^ (t & 1) : c;   // (t % 4) & 1 == t & 1
-        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + oQ[cq] + 16 * (t % 4) * D);
+        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + (qb ^ (64 * cq)) + 16 * (t % 4) * D);
         s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
       }
       dp[t] = f32x4{};
 #pragma unroll
       for (int c = 0; c < HCH; ++c) {
-        const u16x8 ad = *reinterpret_cast<const u16x8*>(pb + oDO[c] + 32 * (t % 4) * D);
+        const u16x8 ad = *reinterpret_cast<const u16x8*>(pb + (db ^ (64 * c)) + 32 * (t % 4) * D);
         dp[t] = mfma_16b_16x16x32<DT>(ad, vreg[c], dp[t]);
       }
     }
-    // ---- P = 2^(S c - lse2), dS = P (dP - D): register r of sub-tile t is row 16t + 4g + r
-    float pf[NS][4], dsf[NS][4];
-    auto elems = [&](auto masked) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int8_t* pb = buf + (t / 4) * P::kBytes;
-        const f32x4 lse2 = *reinterpret_cast<const f32x4*>(pb + P::bLSE + 4 * (16 * (t % 4) + 4 * g));
-        const f32x4 dvv = *reinterpret_cast<const f32x4*>(pb + P::bDV + 4 * (16 * (t % 4) + 4 * g));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, QS ? kb2 - lse2[r] : -lse2[r]));
-          if constexpr (decltype(masked)::value) {
-            if (key > q0 + 16 * t + 4 * g + r) p = 0.0f;
-          }
-          pf[t][r] = p;
-          dsf[t][r] = p * (dp[t][r] - dvv[r]);
-        }
-      }
-    };
-    if (a.causal && k0 + BLK - 1 > q0) elems(std::true_type{});
-    else elems(std::false_type{});
+  };
 
+  // P = 2^(S c - lse2), dS = P (dP - D) of sub-tile t: register r is row 16t + 4g + r
+  float pf[NS][4];
+  auto elem_tile = [&](const int8_t* buf, int t, int q0, auto masked) {
+    const int8_t* pb = buf + (t / 4) * P::kBytes;
+    const f32x4 lse2 = *reinterpret_cast<const f32x4*>(pb + P::bLSE + 4 * (16 * (t % 4) + 4 * g));
+    const f32x4 dvv = *reinterpret_cast<const f32x4*>(pb + P::bDV + 4 * (16 * (t % 4) + 4 * g));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, QS ? kb2 - lse2[r] : -lse2[r]));
+      if constexpr (decltype(masked)::value) {
+        if (key > q0 + 16 * t + 4 * g + r) p = 0.0f;
+      }
+      pf[t][r] = p;
+      dsf[t][r] = p * (dp[t][r] - dvv[r]);
+    }
+  };
+
+  // the tile maxima (|dS| maximum to the workgroup), P codes and dV, and the Q^T operands of
+  // dK: every remaining read of the tile's buffer
+  auto phase_post = [&](int bofs, int step) {
+    const int8_t* buf = lds + bofs;
     // ---- tile maxima (chains of three-input maxima; the |dS| maximum goes to the workgroup)
     float pm = pf[0][0], dm = fabsf(dsf[0][0]);
 #pragma unroll
@@ -507,37 +521,29 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
       }
     }
-    // Q^T operands of dK, read before the barrier (after it the buffer is refilled)
-    i32x4 qtr[NH][NCT];
-    {
-      const int qa = bofs + oQT;
+    // ---- Q^T operands of dK (after the next barrier the buffer is refilled)
+    const int qa = bofs + oQT;
 #pragma unroll
-      for (int n = 0; n < NCT; ++n) {
-        const int8_t* pn = lds + (qa ^ (16 * n));
+    for (int n = 0; n < NCT; ++n) {
+      const int8_t* pn = lds + (qa ^ (16 * n));
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const i32x2 x0 = lds_read_tr8(pn + h * P::kBytes);
-          const i32x2 x1 = lds_read_tr8(pn + h * P::kBytes + 32 * D);
-          qtr[h][n] = i32x4{x0[0], x0[1], x1[0], x1[1]};
-        }
+      for (int h = 0; h < NH; ++h) {
+        const i32x2 x0 = lds_read_tr8(pn + h * P::kBytes);
+        const i32x2 x1 = lds_read_tr8(pn + h * P::kBytes + 32 * D);
+        qtr[h][n] = i32x4{x0[0], x0[1], x1[0], x1[1]};
       }
     }
-    // the copies of tile qt+1 (issued one step ago) must have landed before the barrier that
-    // publishes them; issued after them: last step's stores or atomics
-    wait_vmcnt<kStores>();
-    lds_barrier();
-    if constexpr (SPILL) {
-      if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
-    }
+  };
 
-    // ---- dS codes on the TQ x BLK tile (one block), dK^T += Q^T dS
-    float da = redD[(step & 1) * NW];
+  // dS codes on the TQ x 64 tile of this wave's four-wave group (its |dS| maxima published
+  // by the barrier after phase_post), dK^T += Q^T dS, and the spilled dS^T tile
+  auto phase_dk = [&](int step, int qt) {
+    float da = redD[(step & 1) * NW + wg0];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) da = fmaxf(da, redD[(step & 1) * NW + i]);
+    for (int i = 1; i < 4; ++i) da = fmaxf(da, redD[(step & 1) * NW + wg0 + i]);
     da = fmaxf(da, FLT_MIN);
     const float dinv = 127.0f * __builtin_amdgcn_rcpf(da);
     const float sdS = da * (1.0f / 127.0f);
-    i32x4 dc[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -565,56 +571,96 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
         for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(sk, (float)acc[r], dk[n][r]);
       }
     }
-
     if constexpr (SPILL) {
-      // ---- the dS^T tile of each packet [BLK][64] for the query-major dQ pass: key row kl,
-      //      chunk g (rows in the contraction order above) at slot swz_ds(kl, g); and its
-      //      dQ multiplier (the same for the tile's packets)
+      // the dS^T tile of each packet [BLK][64] for the query-major dQ pass: key row kl,
+      // chunk g (rows in the contraction order above) at slot swz_ds(kl, g); and the dQ
+      // multiplier of its 64 keys (the same for the tile's packets)
       const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt * NH);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         *reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq + 16 * swz_ds(kl, g)) = dc[h];
-        if (l == 0) a.dsm[ti + h] = smc * sdS * sK;   // every wave stores the same value
+        if (l == 0) a.dsm[(ti + h) * KD + dg] = smc * sdS * sK;   // every wave of the group stores the same value
       }
-    } else {
-      // ---- dQ = dS K on the TQ x BLK tile, added to the float32 accumulator with atomics.
-      //      The dS^T tile [BLK][TQ] goes through the released tile buffer once (chunk
-      //      4h + g of key row kl at slot swz<TQ>(kl, 4h + g)) and is read back query by
-      //      query (transposing reads); wave w computes query chunk w against all channels.
-      int8_t* dst = lds + bofs;
+    }
+  };
+
+  {
+    issue(qt0, lds);
+    if (qt0 + 1 < ntq) issue(qt0 + 1, lds + L::kBuf);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int qt = qt0; qt < ntq; ++qt) {
+      const int q0 = qt * TQ;
+      const int step = qt - qt0;
+      const int bofs = (step & 1) * L::kBuf;   // byte offset of this tile's buffer
+      phase_sdp(bofs);
+      if (a.causal && k0 + 16 * w + 15 > q0) {   // diagonal tiles: mask keys above the queries
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
-        *reinterpret_cast<i32x4*>(dst + kl * TQ + 16 * swz<TQ>(kl, 4 * h + g)) = dc[h];
+        for (int t = 0; t < NS; ++t) elem_tile(lds + bofs, t, q0, std::true_type{});
+      } else {
+#pragma unroll
+        for (int t = 0; t < NS; ++t) elem_tile(lds + bofs, t, q0, std::false_type{});
+      }
+      phase_post(bofs, step);
+      // the copies of tile qt+1 (issued one step ago) must have landed before the barrier
+      // that publishes them; issued after them: last step's stores or atomics
+      wait_vmcnt<kStores>();
       lds_barrier();
-      i32x4 acc[NCT];
+      if constexpr (SPILL) {
+        if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
+      }
+      phase_dk(step, qt);
+      if constexpr (!SPILL) {
+        // ---- dQ = dS K on the TQ x BLK tile, added to the float32 accumulator with atomics.
+        //      The dS^T tile [BLK][TQ] goes through the released tile buffer once (chunk
+        //      4h + g of key row kl at slot swz<TQ>(kl, 4h + g)) and is read back query by
+        //      query (transposing reads); wave w computes query chunk w against all
+        //      channels, one 64-key dS tile (one scale) at a time.
+        int8_t* dst = lds + bofs;
 #pragma unroll
-      for (int n = 0; n < NCT; ++n) acc[n] = i32x4{};
+        for (int h = 0; h < NH; ++h)
+          *reinterpret_cast<i32x4*>(dst + kl * TQ + 16 * swz<TQ>(kl, 4 * h + g)) = dc[h];
+        // the scale of every 64-key dS tile of the block
+        float sc[KD];
 #pragma unroll
-      for (int kc = 0; kc < BLK / 64; ++kc) {
-        const int i = lr >> 1, hh = l & 1;
-        const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
-        const i32x2 x0 = lds_read_tr8(dst + r0 * TQ + 16 * swz<TQ>(r0, w) + 8 * hh);
-        const i32x2 x1 = lds_read_tr8(dst + r1 * TQ + 16 * swz<TQ>(r1, w) + 8 * hh);
-        const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
+        for (int kc = 0; kc < KD; ++kc) {
+          float m = redD[(step & 1) * NW + 4 * kc];
 #pragma unroll
-        for (int n = 0; n < NCT; ++n) {
-          const int c = 16 * n + lr;
-          const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
-          acc[n] = mfma_i8_16x16x64(as, bk, acc[n]);
+          for (int i = 1; i < 4; ++i) m = fmaxf(m, redD[(step & 1) * NW + 4 * kc + i]);
+          sc[kc] = smc * (fmaxf(m, FLT_MIN) * (1.0f / 127.0f)) * sK;
         }
+        lds_barrier();
+        f32x4 accf[NCT];
+#pragma unroll
+        for (int n = 0; n < NCT; ++n) accf[n] = f32x4{};
+#pragma unroll
+        for (int kc = 0; kc < KD; ++kc) {
+          const int i = lr >> 1, hh = l & 1;
+          const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
+          const i32x2 x0 = lds_read_tr8(dst + r0 * TQ + 16 * swz<TQ>(r0, w) + 8 * hh);
+          const i32x2 x1 = lds_read_tr8(dst + r1 * TQ + 16 * swz<TQ>(r1, w) + 8 * hh);
+          const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+          for (int n = 0; n < NCT; ++n) {
+            const int c = 16 * n + lr;
+            const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
+            const i32x4 acc = mfma_i8_16x16x64(as, bk, i32x4{});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accf[n][r] = __builtin_fmaf(sc[kc], (float)acc[r], accf[n][r]);
+          }
+        }
+        // every wave has read the staged tile: the buffer takes the tile two steps ahead
+        lds_barrier();
+        if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
+        // result: query chunk w = 4h' + u of the tile, position 4g + r = row 16g + 4u + r of
+        // packet h'
+        const int qrow = q0 + kPq * (w / 4) + 16 * g + 4 * (w % 4);
+#pragma unroll
+        for (int n = 0; n < NCT; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            unsafeAtomicAdd(a.dq_acc + (hrow + qrow + r) * D + 16 * n + lr, accf[n][r]);
       }
-      // every wave has read the staged tile: the buffer takes the tile two steps ahead
-      lds_barrier();
-      if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
-      // result: query chunk w = 4h' + u of the tile, position 4g + r = row 16g + 4u + r of
-      // packet h'
-      const float sc = smc * sdS * sK;
-      const int qrow = q0 + kPq * (w / 4) + 16 * g + 4 * (w % 4);
-#pragma unroll
-      for (int n = 0; n < NCT; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          unsafeAtomicAdd(a.dq_acc + (hrow + qrow + r) * D + 16 * n + lr, sc * (float)acc[n][r]);
     }
   }
 
@@ -674,9 +720,9 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 
 // ------------------------------------------------------------------------------ bwd_dq
 // Query-major dQ pass over the spilled dS^T tiles: one workgroup (4 waves) per (head, 64-query
-// tile). For every key block up to the diagonal, dQ^ += m(kb) * (dS_codes . K_codes) runs on
-// v_mfma_i32_16x16x64_i8 with float32 accumulation in registers (m = sm_scale * s_dS * s_K of
-// the tile). The tile's dS^T codes [BLK][64] stream through a ring of three LDS buffers
+// tile). For every key block up to the diagonal and each of its 64-key dS tiles,
+// dQ^ += m * (dS_codes . K_codes) runs on v_mfma_i32_16x16x64_i8 with float32 accumulation in
+// registers (m = sm_scale * s_dS * s_K of that 64-key tile). The tile's dS^T codes [BLK][64] stream through a ring of three LDS buffers
 // (buffer->LDS copies issued two key blocks ahead) and are read back query-major with
 // transposing reads: the A operand (rows = queries, contraction = keys). Wave w computes all
 // 64 queries against its own NPW 16-channel tiles, so it needs only those channels of the
@@ -687,7 +733,7 @@ __global__ __launch_bounds__(BLK * 4, 1) void bwd_main(BackwardArgs a) {
 template <int D, int BLK>
 struct DqLds {
   static constexpr int kTile = kPq * BLK;           // one dS^T tile [BLK][64]
-  static constexpr int bM = kTile;                  // then its dQ multiplier (first word)
+  static constexpr int bM = kTile;                  // then its dQ multipliers (one per 64 keys)
   static constexpr int kBuf = kTile + 1024;         // one ring slot
   static constexpr int kCopiesPerWave = kTile / 1024 / 4;
   // slot 0 also holds the epilogue's dQ^ tile [64][D] f32
@@ -714,7 +760,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   const int kb_last = a.causal ? (q0 + kPq - 1) / BLK : nb - 1;
   const int8_t* dsh = a.dsp + (size_t)bh * a.spill_tiles * (kPq * BLK);
   const uint32_t dsh_bytes = (uint32_t)(a.spill_tiles * (kPq * BLK));
-  const float* dmh = a.dsm + (size_t)bh * a.spill_tiles;
+  const float* dmh = a.dsm + (size_t)bh * a.spill_tiles * KC;
   const int8_t* kth = a.ktp + (size_t)bh * nb * (D * BLK);
   auto slot = [&](auto s_c) -> int8_t* {
     constexpr int S = decltype(s_c)::value;
@@ -724,7 +770,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   };
 
   // this wave's share of the copies of key block kb's dS^T tile (and, by wave 3, of its
-  // multiplier) into ring slot S
+  // multipliers) into ring slot S
   auto issue_ds = [&](int kb, auto s_c) {
     const long long ti = spill_tile_index(a.N, BLK, a.causal, kb, qt);
     int8_t* dst = slot(s_c);
@@ -733,7 +779,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
       const int cp = w + 4 * j;
       buffer_to_lds16(dsh, dsh_bytes, dst + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
     }
-    if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4), dst + L::bM, 4 * l, (uint32_t)(ti * 4));
+    if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4 * KC), dst + L::bM, 4 * l, (uint32_t)(ti * 4 * KC));
   };
   // K^T operands of key block kb: channel c = 16(NPW w + n) + lr, keys 64kc + 16g .. +15
   // (chunk 4kc + g of row c, at slot swz<BLK>(c, 4kc + g))
@@ -774,14 +820,9 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
     load_kt(min(kb + 1, kb_last));
     issue_ds(min(kb + 2, kb_last), std::integral_constant<int, (S + 2) % 3>{});
     const int8_t* buf = slot(s_c);
-    const float m = *reinterpret_cast<const float*>(buf + L::bM);
-    i32x4 acc[4][NPW];
-#pragma unroll
-    for (int qs = 0; qs < 4; ++qs)
-#pragma unroll
-      for (int n = 0; n < NPW; ++n) acc[qs][n] = i32x4{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
+      const float m = reinterpret_cast<const float*>(buf + L::bM)[kc];
       // A: keys 64kc + 16g .. +15 of query position 16qs + lr, two transposing reads of 8 keys
       const int i = lr >> 1, hh = l & 1;
       const int r0 = 64 * kc + 16 * g + i, r1 = r0 + 8;
@@ -791,15 +832,13 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
         const i32x2 x1 = lds_read_tr8(buf + r1 * kPq + 16 * swz_ds(r1, qs) + 8 * hh);
         const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
-        for (int n = 0; n < NPW; ++n) acc[qs][n] = mfma_i8_16x16x64(as, kt[n][kc], acc[qs][n]);
+        for (int n = 0; n < NPW; ++n) {
+          const i32x4 acc = mfma_i8_16x16x64(as, kt[n][kc], i32x4{});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dq[qs][n][r] = __builtin_fmaf(m, (float)acc[r], dq[qs][n][r]);
+        }
       }
     }
-#pragma unroll
-    for (int qs = 0; qs < 4; ++qs)
-#pragma unroll
-      for (int n = 0; n < NPW; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dq[qs][n][r] = __builtin_fmaf(m, (float)acc[qs][n][r], dq[qs][n][r]);
   };
 
   using S0 = std::integral_constant<int, 0>;
@@ -901,11 +940,14 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 1) {
-    const hipError_t e =
-        a.spill ? (a.q_smooth ? launch_kernel(&bwd_main<DT, D, BLK, true, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
-                              : launch_kernel(&bwd_main<DT, D, BLK, true, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a))
-                : (a.q_smooth ? launch_kernel(&bwd_main<DT, D, BLK, false, true>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a)
-                              : launch_kernel(&bwd_main<DT, D, BLK, false, false>, dim3((unsigned)(nb * a.BH)), dim3(BLK * 4), st, a));
+    auto go = [&](auto spill_c, auto qs_c) {
+      constexpr bool SP = decltype(spill_c)::value, QSV = decltype(qs_c)::value;
+      using L = BwdLds<D, BLK, SP>;
+      return launch_kernel(&bwd_main<DT, D, BLK, SP, QSV>, dim3((unsigned)(nb * a.BH)), dim3(L::NW * 64), st, a);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    const hipError_t e = a.spill ? (a.q_smooth ? go(T{}, T{}) : go(T{}, F{})) : (a.q_smooth ? go(F{}, T{}) : go(F{}, F{}));
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {

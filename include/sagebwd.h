@@ -31,7 +31,7 @@
  *                    max moves once per such tile and P~ = exp(s - running max); the row
  *                    sum l accumulates P~ before quantisation.
  *   P  (backward)  : blk query rows (one query block) x SAGEBWD_BWD_P_TILE_K keys.
- *   dS (backward)  : blk query rows x blk keys (one block of dS).
+ *   dS (backward)  : blk query rows x SAGEBWD_BWD_DS_TILE_K keys.
  * Every tile lies inside one blk x blk block, so the block scales factor out of each
  * integer product.
  *
@@ -61,6 +61,7 @@ extern "C" {
 
 #define SAGEBWD_FWD_TILE_Q 32
 #define SAGEBWD_BWD_P_TILE_K 16
+#define SAGEBWD_BWD_DS_TILE_K 64
 
 typedef enum {
   SAGEBWD_OK = 0,
@@ -179,7 +180,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *                                    16*((u>>2)&3) + 4*(u>>4) + (u&3) of the key's row,
  *                                    then chunk j of row k stored at chunk
  *                                    j^(((k>>1)^(k>>4))&3)
- *   dsm     float32 [B,H,T]          sm_scale * (dS tile scale) * (K block scale)
+ *   dsm     float32 [B,H,T,blk/64]   per 64 keys of the tile (one dS scale tile):
+ *                                    sm_scale * (dS tile scale) * (K block scale)
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 

@@ -31,7 +31,7 @@ def spec_for(w: wl.Workload, dtype: Optional[str] = None) -> oq.Spec:
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
                    fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
-                   bwd_sk=w.blk, q_smooth=w.q_smooth)
+                   bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth)
 
 
 def rel_l2(a, b) -> float:

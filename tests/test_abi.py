@@ -31,7 +31,8 @@ def test_exports_every_header_symbol():
 
 def test_header_tile_constants_match_binding():
     c = header_constants()
-    assert (c["FWD_TILE_Q"], c["BWD_P_TILE_K"]) == (_lib.FWD_TILE_Q, _lib.BWD_P_TILE_K)
+    assert (c["FWD_TILE_Q"], c["BWD_P_TILE_K"], c["BWD_DS_TILE_K"]) == \
+        (_lib.FWD_TILE_Q, _lib.BWD_P_TILE_K, _lib.BWD_DS_TILE_K)
 
 
 def test_status_strings():
