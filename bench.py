@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--q-smooth", action="store_true",
                     help="time the Q-smoothing variant on the same inputs (default: off, as the metric)")
+    ap.add_argument("--layout", default="bhnd", choices=("bhnd", "bnhd"),
+                    help="memory layout of the 16-bit tensors handed to the library (default [B,H,N,d])")
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
@@ -122,9 +124,11 @@ def main():
         f"qk_norm={w.qk_norm} k_smooth={w.k_smooth} blk={w.blk}")
     x = wl.make_inputs(w)
     p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                        q_smooth=w.q_smooth)
+                        q_smooth=w.q_smooth, layout=args.layout)
     dev = torch.device("cuda:0")
     Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
+    if args.layout == "bnhd":
+        Q, K, V, dO = (t.transpose(1, 2).contiguous() for t in (Q, K, V, dO))
     pro = api.sagebwd_quant_prologue(p, Q, K, V)
     pro_ws = torch.empty(max(api.sagebwd_prologue_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
     O, lse = api.sagebwd_forward(p, pro)
@@ -207,7 +211,7 @@ def main():
             for t in (qg, kg, vg):
                 t.grad = None
             o = sagebwd_attention(qg, kg, vg, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
-                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth)
+                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth, layout=args.layout)
             o.backward(dO)
 
         for _ in range(2):
@@ -240,7 +244,7 @@ def main():
         "config": {"workload": f"{w.name}: B{w.B} H{w.H} N{w.N} d{w.d} causal {w.dtype} QK-norm "
                                f"K-smoothing blk{w.blk}{' Q-smoothing' if w.q_smooth else ''} (prologue+fwd+bwd)",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "blk": w.blk,
-                   "dtype": w.dtype, "q_smooth": w.q_smooth, "parallelism": "single GPU"},
+                   "dtype": w.dtype, "q_smooth": w.q_smooth, "layout": args.layout, "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak_step, 4),
         "step_ms": {k: round(v, 4) for k, v in step_stats.items()},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsagebwd.
 SAGEBWD_FP16 = 0
 SAGEBWD_BF16 = 1
 DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
+LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 
 # Quantisation tile shapes of the kernels (include/sagebwd.h); the backward's P and dS tiles
 # span one query block (blk rows) by BWD_P_TILE_K and min(blk, BWD_DS_TILE_K) keys.
@@ -32,6 +33,7 @@ class Params(ctypes.Structure):
         ("blk", ctypes.c_int32), ("causal", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
     ]
 
 

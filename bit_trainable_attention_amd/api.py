@@ -19,11 +19,13 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
                 dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0,
-                q_smooth: bool = False) -> _lib.Params:
-    """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics (include/sagebwd.h)."""
+                q_smooth: bool = False, layout: str = "bhnd") -> _lib.Params:
+    """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics; layout of the 16-bit tensors:
+    "bhnd" [B,H,N,d] or "bnhd" [B,N,H,d] (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
+    lay = {"bhnd": _lib.LAYOUT_BHND, "bnhd": _lib.LAYOUT_BNHD}[layout]
     return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode,
-                       int(q_smooth))
+                       int(q_smooth), lay)
 
 
 def sagebwd_status_string(status: int) -> str:
@@ -62,7 +64,8 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
 
 def _shapes(p: _lib.Params):
     bhnd = (p.B, p.H, p.N, p.d)
-    return dict(x=bhnd, xt=(p.B, p.H, p.d, p.N), s=(p.B, p.H, p.N // p.blk), r=(p.B, p.H, p.N),
+    x16 = (p.B, p.N, p.H, p.d) if p.layout == _lib.LAYOUT_BNHD else bhnd
+    return dict(x=bhnd, x16=x16, xt=(p.B, p.H, p.d, p.N), s=(p.B, p.H, p.N // p.blk), r=(p.B, p.H, p.N),
                 m=(p.B, p.H, p.d))
 
 
@@ -113,7 +116,7 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
     for name, t in (("Q", Q), ("K", K), ("V", V)):
-        _want(t, name, sh["x"], dt, dev)
+        _want(t, name, sh["x16"], dt, dev)
     if out is None:
         out = dict(
             Qc=torch.empty(sh["x"], dtype=torch.int8, device=dev),
@@ -163,10 +166,10 @@ def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[to
     for name, key, tdt in wanted:
         _want(pro[name], name, sh[key], tdt, dev)
     if O is None:
-        O = torch.empty(sh["x"], dtype=_TORCH_DTYPE[p.dtype], device=dev)
+        O = torch.empty(sh["x16"], dtype=_TORCH_DTYPE[p.dtype], device=dev)
     if lse is None:
         lse = torch.empty(sh["r"], dtype=torch.float32, device=dev)
-    _want(O, "O", sh["x"], _TORCH_DTYPE[p.dtype], dev)
+    _want(O, "O", sh["x16"], _TORCH_DTYPE[p.dtype], dev)
     _want(lse, "lse", sh["r"], torch.float32, dev)
     st = _lib.load().sagebwd_forward(
         ctypes.byref(p), _ptr(pro["Qc"]), _ptr(pro["Kc"]), _ptr(pro["Vtc"]),
@@ -181,7 +184,7 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
     for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
-        _want(t, name, sh["x"], dt, dev)
+        _want(t, name, sh["x16"], dt, dev)
     wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Qs", "s", torch.float32),
               ("Ks", "s", torch.float32), ("q_rstd", "r", torch.float32), ("k_rstd", "r", torch.float32)]
     if p.q_smooth:
@@ -190,9 +193,9 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
         _want(pro[name], name, sh[key], tdt, dev)
     _want(lse, "lse", sh["r"], torch.float32, dev)
     if grads is None:
-        grads = {n: torch.empty(sh["x"], dtype=dt, device=dev) for n in ("dQ", "dK", "dV")}
+        grads = {n: torch.empty(sh["x16"], dtype=dt, device=dev) for n in ("dQ", "dK", "dV")}
     for n in ("dQ", "dK", "dV"):
-        _want(grads[n], n, sh["x"], dt, dev)
+        _want(grads[n], n, sh["x16"], dt, dev)
     need = sagebwd_backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

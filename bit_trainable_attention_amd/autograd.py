@@ -6,9 +6,10 @@ and delivers dQ, dK, dV with respect to the raw q, k, v handed in (the RMSNorm b
 QK-norm included; K-smoothing contributes nothing, SageBwd article, K-smoothing paragraph).
 Every step runs in libsagebwd.so; there is no CPU path.
 
-Layouts: "bhnd" takes [B, H, N, d] tensors as they are (contiguous); "bnhd" takes the
-[B, N, H, d] layout of a fused projection output and hands the library a contiguous
-[B, H, N, d] copy (the kernels read head-major rows), returning gradients in [B, N, H, d].
+Layouts: "bhnd" takes [B, H, N, d] tensors, "bnhd" the [B, N, H, d] layout of a fused
+projection output; the kernels read and write either layout in place (sagebwd_params.layout),
+so neither costs a copy of a contiguous input. O and the gradients come back in the layout of
+the inputs.
 """
 from __future__ import annotations
 
@@ -29,14 +30,17 @@ class SageBwdAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal: bool, qk_norm: bool, k_smooth: bool, blk: int, eps: float,
-                sm_scale: float, dq_mode: int, q_smooth: bool):
+                sm_scale: float, dq_mode: int, q_smooth: bool, layout: str):
         if q.dtype not in _DTYPES:
             raise TypeError(f"q, k, v must be float16 or bfloat16, got {q.dtype}")
         if q.dim() != 4:
-            raise ValueError(f"expected [B, H, N, d] tensors, got shape {tuple(q.shape)}")
-        B, H, N, d = q.shape
+            raise ValueError(f"expected 4-d {layout} tensors, got shape {tuple(q.shape)}")
+        if layout == "bnhd":
+            B, N, H, d = q.shape
+        else:
+            B, H, N, d = q.shape
         p = api.make_params(B, H, N, d, blk, causal, qk_norm, k_smooth, _DTYPES[q.dtype], eps=eps,
-                            sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth)
+                            sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth, layout=layout)
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         pro = api.sagebwd_quant_prologue(p, q, k, v)
         O, lse = api.sagebwd_forward(p, pro)
@@ -51,7 +55,7 @@ class SageBwdAttention(torch.autograd.Function):
         q, k, v, O, lse, *saved = ctx.saved_tensors
         pro = dict(zip(ctx.saved_names, saved))
         g = api.sagebwd_backward(ctx.params, q, k, v, pro, O, lse, dO.contiguous())
-        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None, None
+        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None, None, None
 
 
 def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
@@ -64,12 +68,8 @@ def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     mean is subtracted before quantising and added back through the key bias and dK_bias). The lse returned with return_lse is float32 [B, H, N]
     (natural log) and carries no gradient.
     """
-    if layout == "bnhd":
-        q, k, v = (t.transpose(1, 2) for t in (q, k, v))
-    elif layout != "bhnd":
+    if layout not in ("bhnd", "bnhd"):
         raise ValueError(f"layout must be 'bhnd' or 'bnhd', got {layout!r}")
     O, lse = SageBwdAttention.apply(q, k, v, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
-                                    float(eps), float(sm_scale), int(dq_mode), bool(q_smooth))
-    if layout == "bnhd":
-        O = O.transpose(1, 2)
+                                    float(eps), float(sm_scale), int(dq_mode), bool(q_smooth), layout)
     return (O, lse) if return_lse else O

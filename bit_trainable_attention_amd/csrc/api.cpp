@@ -29,6 +29,7 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->dtype != SAGEBWD_FP16 && p->dtype != SAGEBWD_BF16) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->dq_mode < SAGEBWD_DQ_AUTO || p->dq_mode > SAGEBWD_DQ_ATOMIC) return SAGEBWD_ERR_UNSUPPORTED;
   if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->layout != SAGEBWD_LAYOUT_BHND && p->layout != SAGEBWD_LAYOUT_BNHD) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
   // (N * d * 4 < 2^31), grids in 2^31 workgroups
@@ -38,6 +39,12 @@ sagebwd_status check_params(const sagebwd_params* p) {
 }
 
 bool empty(const sagebwd_params* p) { return p->B == 0 || p->H == 0 || p->N == 0; }
+
+sagebwd::Strides16 strides16(const sagebwd_params* p) {
+  const long long d = p->d, N = p->N, H = p->H;
+  if (p->layout == SAGEBWD_LAYOUT_BNHD) return {N * H * d, d, (int)(H * d), p->H};
+  return {H * N * d, N * d, (int)d, p->H};
+}
 
 size_t elems(const sagebwd_params* p) { return (size_t)p->B * p->H * p->N * p->d; }
 
@@ -167,6 +174,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
     a.qpart = reinterpret_cast<float*>(ws + (p->k_smooth ? prologue_part_bytes(p) : 0));
   }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.x16 = strides16(p);
   a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.q_smooth = p->q_smooth != 0;
   a.eps = p->eps;
   return hip_status(sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)), "sagebwd_quant_prologue");
@@ -187,6 +195,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
   a.kbias = a.q_smooth ? kbias : nullptr;
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.x16 = strides16(p);
   a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
   return hip_status(sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)), "sagebwd_forward");
 }
@@ -237,6 +246,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
     a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
   }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.x16 = strides16(p);
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
   return hip_status(sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)), "sagebwd_backward");
 }

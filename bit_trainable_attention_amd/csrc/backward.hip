@@ -156,8 +156,9 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * j + k;                       // token inside the tile
       const size_t tok = tok0 + kPq * q + r;
-      const unsigned short* dsrc = a.dO + tok * D + c0;
-      const unsigned short* osrc = a.O + tok * D + c0;
+      const size_t row16 = a.x16.row(bh, blk_id * BLK + kPq * q + r);
+      const unsigned short* dsrc = a.dO + row16 + c0;
+      const unsigned short* osrc = a.O + row16 + c0;
       float part = 0.0f;
       if constexpr (CW == 8) {
         const u16x8 dv = *reinterpret_cast<const u16x8*>(dsrc);
@@ -361,8 +362,9 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int c = 0; c < KCH; ++c) kreg[c] = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + key) * D + 64 * c + 16 * g);
   u16x8 vreg[HCH];
+  const size_t krow16 = a.x16.row(bh, key);   // this lane's key row of the 16-bit tensors
 #pragma unroll
-  for (int c = 0; c < HCH; ++c) vreg[c] = *reinterpret_cast<const u16x8*>(a.V + (hrow + key) * D + 32 * c + 8 * g);
+  for (int c = 0; c < HCH; ++c) vreg[c] = *reinterpret_cast<const u16x8*>(a.V + krow16 + 32 * c + 8 * g);
   if constexpr (!SPILL) {
     // K^T codes of the block for dQ = dS K: [D][BLK], chunk j of row c at slot swz<BLK>(c, j)
     for (int ch = tid; ch < BLK * D / 16; ch += NT) {
@@ -678,7 +680,7 @@ void bwd_main(BackwardArgs a) {
       for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(smc * dsum, mq[r], dk[n][r]);
     }
   }
-  unsigned short* dvrow = a.dV + (hrow + key) * D;
+  unsigned short* dvrow = a.dV + krow16;
 #pragma unroll
   for (int n = 0; n < NCT; ++n) {
     u16x4 v;
@@ -686,10 +688,10 @@ void bwd_main(BackwardArgs a) {
     for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dv[n][r]);
     *reinterpret_cast<u16x4*>(dvrow + 16 * n + 4 * g) = v;
   }
-  unsigned short* dkrow = a.dK + (hrow + key) * D;
+  unsigned short* dkrow = a.dK + krow16;
   if (a.qk_norm) {
     const float rs = a.k_rstd[hrow + key];
-    const unsigned short* krow = a.K + (hrow + key) * D;
+    const unsigned short* krow = a.K + krow16;
     float kh[NCT][4];
     float dot = 0.0f;
 #pragma unroll
@@ -870,13 +872,14 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   for (int e = threadIdx.x; e < kPq * CPR; e += 256) {
     const int r = e / CPR, c = (e % CPR) * 8;
     const size_t tok = hrow + q0 + r;
+    const size_t row16 = a.x16.row(bh, q0 + r);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = t[r * D + c + i];
     u16x8 out;
     if (a.qk_norm) {
       const float rs = a.q_rstd[tok];
-      const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + tok * D + c);
+      const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + row16 + c);
       float qh[8], dot = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -892,7 +895,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(v[i]);
     }
-    *reinterpret_cast<u16x8*>(a.dQ + tok * D + c) = out;
+    *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
   }
 }
 
@@ -906,6 +909,7 @@ __global__ __launch_bounds__(256) void dq_finalize(BackwardArgs a) {
   const size_t tok = gidx / CPR;
   const int c = (int)(gidx % CPR) * 8;
   if (tok >= tokens) return;  // whole rows only: CPR divides 256, so a row never straddles this
+  const size_t row16 = a.x16.row((int)(tok / a.N), (int)(tok % a.N));
   const float* src = a.dq_acc + tok * D + c;
   float dq[8];
   *reinterpret_cast<float4*>(dq) = *reinterpret_cast<const float4*>(src);
@@ -913,7 +917,7 @@ __global__ __launch_bounds__(256) void dq_finalize(BackwardArgs a) {
   u16x8 out;
   if (a.qk_norm) {
     const float rs = a.q_rstd[tok];
-    const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + tok * D + c);
+    const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + row16 + c);
     float qh[8], dot = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -929,7 +933,7 @@ __global__ __launch_bounds__(256) void dq_finalize(BackwardArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(dq[i]);
   }
-  *reinterpret_cast<u16x8*>(a.dQ + tok * D + c) = out;
+  *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
 }
 
 template <int DT, int D, int BLK>

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
   if (!active) return;
   const float ltot = lsum_run + __shfl_xor(lsum_run, 32);
   const float linv = 1.0f / ltot;
-  unsigned short* orow = a.O + ((size_t)bh * a.N + qrow) * D;
+  unsigned short* orow = a.O + a.x16.row(bh, qrow);
 #pragma unroll
   for (int ct = 0; ct < DC; ++ct)
 #pragma unroll

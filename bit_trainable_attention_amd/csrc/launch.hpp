@@ -9,6 +9,16 @@
 
 namespace sagebwd {
 
+// Element strides of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV): element (b, h, n, c)
+// sits at b*sb + h*sh + n*sn + c (channels contiguous). [B,H,N,d]: sb = H*N*d, sh = N*d,
+// sn = d; [B,N,H,d]: sb = N*H*d, sh = d, sn = H*d.
+struct Strides16 {
+  long long sb, sh;
+  int sn, H;
+  __host__ __device__ size_t head(int bh) const { return (size_t)(bh / H) * sb + (size_t)(bh % H) * sh; }
+  __host__ __device__ size_t row(int bh, int n) const { return head(bh) + (size_t)n * sn; }
+};
+
 struct PrologueArgs {
   const unsigned short *Q, *K, *V;   // 16-bit [BH, N, D]
   int8_t *Qc, *Kc, *Vtc;             // [BH, N, D], [BH, N, D], [BH, D, N]
@@ -22,6 +32,7 @@ struct PrologueArgs {
   int BH, N, D, BLK, dtype;
   int qk_norm, k_smooth, q_smooth;
   float eps;
+  Strides16 x16;                     // layout of the 16-bit tensors
 };
 
 struct ForwardArgs {
@@ -33,6 +44,7 @@ struct ForwardArgs {
   int BH, N, D, BLK, dtype;
   int causal, q_smooth;
   float sm_scale;
+  Strides16 x16;                     // layout of the 16-bit tensors
 };
 
 struct BackwardArgs {
@@ -53,6 +65,7 @@ struct BackwardArgs {
   int BH, N, D, BLK, dtype;
   int causal, qk_norm, q_smooth;
   float sm_scale;
+  Strides16 x16;                     // layout of the 16-bit tensors
 };
 
 // Enqueue one kernel and return the status of this launch itself (hipLaunchKernel reports

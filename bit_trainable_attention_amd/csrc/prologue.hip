@@ -63,12 +63,13 @@ __device__ __forceinline__ void load_chunk(const unsigned short* __restrict__ sr
   }
 }
 
+// blk_src: the block's first token row; rows are sn elements apart
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void load_slice(const unsigned short* __restrict__ blk_src, Slice<D, BLK>& s, int j,
-                                           int ch) {
+__device__ __forceinline__ void load_slice(const unsigned short* __restrict__ blk_src, int sn, Slice<D, BLK>& s,
+                                           int j, int ch) {
 #pragma unroll
   for (int p = 0; p < Slice<D, BLK>::P; ++p)
-    load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * D + ch * Slice<D, BLK>::CW, s.x[p]);
+    load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * sn + ch * Slice<D, BLK>::CW, s.x[p]);
 }
 
 // Sum of the 16 lanes of each row by the pairwise tree (xor 1, xor 2, half mirror, mirror).
@@ -166,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
   S s;
-  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + tok0 * D, s, j, ch);
+  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + a.x16.row(bh, blk_id * BLK), a.x16.sn, s,
+                         j, ch);
 
   if (tensor == 2) {
     // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token].
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
   const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
   S s;
-  load_slice<DT, D, BLK>((is_q ? a.Q : a.K) + tok0 * D, s, j, ch);
+  load_slice<DT, D, BLK>((is_q ? a.Q : a.K) + a.x16.row(bh, blk_id * BLK), a.x16.sn, s, j, ch);
   // mean of the head's keys (or queries) per channel; every workgroup of the head computes the
   // same value, the one of block 0 stores it
   const bool smooth = is_q || a.k_smooth;

@@ -37,7 +37,8 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors), contiguous,
- *     16-byte aligned. Shapes are given in [B,H,N,d] order, last index fastest.
+ *     16-byte aligned. Shapes are given in [B,H,N,d] order, last index fastest, except that
+ *     the 16-bit tensors follow sagebwd_params.layout ([B,N,H,d] with SAGEBWD_LAYOUT_BNHD).
  *   - The caller owns every buffer. The library allocates nothing, keeps no state between
  *     calls, never synchronises, and is re-entrant; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream). Calls sharing a workspace must be
@@ -68,8 +69,8 @@ typedef enum {
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
                                    B*H > 2^24                                               */
-  SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype or dq_mode,
-                                   eps < 0                                                  */
+  SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
+                                   layout, eps < 0                                          */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
@@ -89,7 +90,14 @@ typedef struct {
   int32_t dq_mode;      /* how the backward reduces dQ over key blocks (sagebwd_dq_mode)     */
   int32_t q_smooth;     /* nonzero: subtract Q's per-channel mean before quantising and add
                            the key bias / dK_bias terms back (see above)                    */
+  int32_t layout;       /* sagebwd_layout of the 16-bit tensors Q, K, V, O, dO, dQ, dK, dV   */
 } sagebwd_params;
+
+/* Memory layout of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV; contiguous either way).
+ * BHND is [B,H,N,d]; BNHD is [B,N,H,d], the layout a fused QKV projection produces, read and
+ * written in place (no transposing copies). Every other tensor (codes, scales, statistics,
+ * lse) keeps its documented [B,H,...] layout. */
+typedef enum { SAGEBWD_LAYOUT_BHND = 0, SAGEBWD_LAYOUT_BNHD = 1 } sagebwd_layout;
 
 /* dQ = dS K sums over every key block. SAGEBWD_DQ_SPILL writes each (64-query, blk-key) tile
  * of INT8 dS codes once to the workspace and contracts them with K in a query-major pass

@@ -56,10 +56,10 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 
 # ------------------------------------------------------------------------------- GPU side
 
-def params_for(w: wl.Workload, dq_mode: int = 0):
+def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd"):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                           dq_mode=dq_mode, q_smooth=w.q_smooth)
+                           dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -75,12 +75,18 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
-            pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0) -> Dict[str, np.ndarray]:
-    """Run the HIP path and return host copies (numpy) of everything it produced."""
+            pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd") -> Dict[str, np.ndarray]:
+    """Run the HIP path and return host copies (numpy) of everything it produced. With
+    layout "bnhd" the 16-bit tensors are handed to the library as [B,N,H,d] (a transposed
+    copy of the same values) and its O, dQ, dK, dV are returned transposed back."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w, dq_mode)
-    Q, K, V, dO = (to_device(x[k], w.dtype) for k in ("Q", "K", "V", "dO"))
+    p = params_for(w, dq_mode, layout)
+    tr = (lambda t: t.transpose(1, 2).contiguous()) if layout == "bnhd" else (lambda t: t)
+    back = (lambda t: t.transpose(1, 2)) if layout == "bnhd" else (lambda t: t)
+    Q, K, V, dO = (tr(to_device(x[k], w.dtype)) for k in ("Q", "K", "V", "dO"))
+    if O_in is not None:
+        O_in = tr(O_in)
     res: Dict[str, np.ndarray] = {}
     pro = pro_in
     if "prologue" in stages:
@@ -95,11 +101,11 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
         for k, v in pro.items():
             res[k] = v.cpu().numpy()
     if "forward" in stages:
-        res["O"] = O.float().cpu().numpy().astype(np.float64)
+        res["O"] = back(O).float().cpu().numpy().astype(np.float64)
         res["LSE"] = lse.cpu().numpy()
     if "backward" in stages:
         for k in ("dQ", "dK", "dV"):
-            res[k] = g[k].float().cpu().numpy().astype(np.float64)
+            res[k] = back(g[k]).float().cpu().numpy().astype(np.float64)
         lay = api.backward_workspace_layout(p)
         npk = w.B * w.H * (w.N // 64) * lay["packet_bytes"]   # only the packet region is decoded
         ws = g["workspace"][:npk].cpu().numpy()
