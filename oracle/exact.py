@@ -2,12 +2,14 @@
 
 Test infrastructure only (see oracle/__init__.py). No quantisation anywhere.
 
-Forward:  Q^ = RMSNorm(Q), K^ = RMSNorm(K) per token over d (gain 1, when QK-norm is on;
-          SageBwd article, QK-norm paragraph); S = sm * Q^ K^T, masked above the
+Forward:  Q^ = g_Q o RMSNorm(Q), K^ = g_K o RMSNorm(K) per token over d (when QK-norm is on;
+          SageBwd article, QK-norm paragraph; the gains g [H, d] default to 1 and are
+          learnable, their gradients dg = sum over batch and tokens of dX^ o RMSNorm(X));
+          S = sm * Q^ K^T, masked above the
           diagonal when causal; P = softmax_rows(S); O = P V; LSE = ln sum_j exp(S_ij).
 Backward: dV = P^T dO; dP = dO V^T; D = rowsum(dO o O); dS = P o (dP - D);
           dQ^ = sm * dS K^; dK^ = sm * dS^T Q^ (SageBwd article, gradient paragraph);
-          dQ, dK = RMSNorm backward of dQ^, dK^.
+          dQ, dK = RMSNorm backward of g o dQ^, g o dK^.
 K-smoothing is left out: subtracting any fixed vector from every key adds a per-row
 constant to S, which softmax ignores (pinned by test_oracle_exact.py).
 
@@ -37,10 +39,22 @@ def rms_norm_backward(dy: np.ndarray, y: np.ndarray, rstd: np.ndarray) -> np.nda
     return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
 
 
+def _gain_rows(g, lead, BH: int, d: int) -> np.ndarray:
+    """A gain [H, d] (or None -> ones) as [BH, 1, d] for inputs with leading dims (.., H)."""
+    if g is None:
+        return np.ones((BH, 1, d))
+    g = np.asarray(g, dtype=np.float64)
+    return np.broadcast_to(g, tuple(lead[:-1]) + g.shape).reshape(BH, 1, d)
+
+
 def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-6,
               sm_scale: Optional[float] = None, k_shift: Optional[np.ndarray] = None,
-              row_block: int = 512, want_ds_stats: bool = False) -> Dict[str, np.ndarray]:
+              row_block: int = 512, want_ds_stats: bool = False,
+              q_gain: Optional[np.ndarray] = None, k_gain: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Exact attention on [..., N, d] float64 inputs; the backward runs when dO is given.
+
+    q_gain, k_gain: optional QK-norm gains [H, d] (the last leading axis of the inputs is H);
+    with them the backward also returns dq_gain, dk_gain [H, d].
 
     k_shift: optional vector (broadcast to [..., d]) subtracted from every normalised key
     before the scores (used only to check that K-smoothing leaves the output unchanged).
@@ -58,9 +72,12 @@ def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-
     v = V.reshape((-1, N, d))
     BH = q.shape[0]
     sm = sm_scale if sm_scale is not None else 1.0 / np.sqrt(d)
+    gq = _gain_rows(q_gain, lead, BH, d)
+    gk = _gain_rows(k_gain, lead, BH, d)
     if qk_norm:
-        qh, rq = rms_norm(q, eps)
-        kh, rk = rms_norm(k, eps)
+        qn, rq = rms_norm(q, eps)
+        kn, rk = rms_norm(k, eps)
+        qh, kh = qn * gq, kn * gk
     else:
         qh, rq = q, np.ones((BH, N))
         kh, rk = k, np.ones((BH, N))
@@ -109,8 +126,12 @@ def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-
     out = dict(O=O.reshape(lead + (N, d)), LSE=LSE.reshape(lead + (N,)))
     if have_bwd:
         if qk_norm:
-            dq = rms_norm_backward(dqh, qh, rq)
-            dk = rms_norm_backward(dkh, kh, rk)
+            dq = rms_norm_backward(dqh * gq, qn, rq)
+            dk = rms_norm_backward(dkh * gk, kn, rk)
+            if q_gain is not None or k_gain is not None:
+                H = lead[-1]
+                out.update(dq_gain=(dqh * qn).reshape((-1, H, N, d)).sum(axis=(0, 2)),
+                           dk_gain=(dkh * kn).reshape((-1, H, N, d)).sum(axis=(0, 2)))
         else:
             dq, dk = dqh, dkh
         out.update(dQ=dq.reshape(lead + (N, d)), dK=dk.reshape(lead + (N, d)),

@@ -4,7 +4,8 @@ Test infrastructure only (see oracle/__init__.py).
 
 What is computed, in the order of the SageBwd article:
   1. QK-norm: RMSNorm of every token vector of Q and of K over the head dimension,
-     gain 1 (SageBwd article, QK-norm paragraph).
+     times an optional learnable gain g [H, d] per head and channel (1 when absent;
+     SageBwd article, QK-norm paragraph); the backward also returns the gains' gradients.
   2. K-smoothing: subtract from every key the mean key of its head, i.e. the
      per-channel mean over all N tokens, right before quantising (SageBwd article,
      K-smoothing paragraph; the axis follows from the Q-smoothing paragraph, whose
@@ -240,25 +241,40 @@ def identity_block_quant(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarra
     return x, np.ones(x.shape[:-2] + (x.shape[-2] // blk,), dtype=np.float64)
 
 
+def apply_gain_f32(xn: np.ndarray, g: Optional[np.ndarray]) -> np.ndarray:
+    """The QK-norm gain: x^ = fl(n * g[h, c]) for n [B,H,N,d] (the normalised tokens) and
+    g [H, d] float32 (one IEEE product per element); g None leaves n unchanged (gain 1)."""
+    if g is None:
+        return xn
+    return (xn * np.asarray(g, dtype=F32)[None, :, None, :]).astype(F32)
+
+
 def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
-             block_quant: BlockQuant = quant_blocks_f32) -> Dict[str, np.ndarray]:
-    """QK-norm -> K-smoothing -> per-block INT8 quantisation of Q^, K~, V.
+             block_quant: BlockQuant = quant_blocks_f32, q_gain: Optional[np.ndarray] = None,
+             k_gain: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """QK-norm (with optional gains [H, d]) -> K-smoothing -> per-block INT8 quantisation
+    of Q^, K~, V.
 
     Inputs: float32 arrays [B,H,N,d] holding the exact values of the 16-bit inputs.
     Returns codes Qc, Kc, Vc (int8 [B,H,N,d], V in natural token-major layout),
     scales Qs, Ks, Vs (float32 [B,H,N/blk]), q_rstd, k_rstd (float32 [B,H,N], 1 when
-    QK-norm is off), k_mean (float32 [B,H,d], 0 when smoothing is off), and the
-    normalised Qhat, Khat (float32) that the RMSNorm backward needs.
+    QK-norm is off), k_mean (float32 [B,H,d], 0 when smoothing is off), the normalised
+    tokens before the gain Qn, Kn and after it Qhat, Khat (float32), which the RMSNorm
+    backward and the gains' gradients need, and the gains (q_gain, k_gain; None = 1).
     """
     Q = np.asarray(Q, dtype=F32)
     K = np.asarray(K, dtype=F32)
     V = np.asarray(V, dtype=F32)
     if spec.qk_norm:
-        Qh, q_rstd = rms_norm_f32(Q, spec.eps)
-        Kh, k_rstd = rms_norm_f32(K, spec.eps)
+        Qn, q_rstd = rms_norm_f32(Q, spec.eps)
+        Kn, k_rstd = rms_norm_f32(K, spec.eps)
+        Qh, Kh = apply_gain_f32(Qn, q_gain), apply_gain_f32(Kn, k_gain)
     else:
+        if q_gain is not None or k_gain is not None:
+            raise ValueError("QK-norm gains need qk_norm")
         Qh, q_rstd = Q, np.ones(Q.shape[:-1], dtype=F32)
         Kh, k_rstd = K, np.ones(K.shape[:-1], dtype=F32)
+        Qn, Kn = Qh, Kh
     if spec.k_smooth:
         Kt, mu = k_smooth_f32(Kh, spec.blk)
     else:
@@ -273,7 +289,7 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
     Kc, Ks = block_quant(Kt, spec.blk)
     Vc, Vs = block_quant(V, spec.blk)
     out = dict(Qc=Qc, Kc=Kc, Vc=Vc, Qs=Qs, Ks=Ks, Vs=Vs, q_rstd=q_rstd, k_rstd=k_rstd,
-               k_mean=mu, q_mean=mu_q, Qhat=Qh, Khat=Kh)
+               k_mean=mu, q_mean=mu_q, Qhat=Qh, Khat=Kh, Qn=Qn, Kn=Kn, q_gain=q_gain, k_gain=k_gain)
     out["kbias"] = key_bias(Kc, Ks, mu_q, spec.blk) if spec.q_smooth else np.zeros(K.shape[:-1])
     return out
 
@@ -436,9 +452,11 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
               (+ sm * sdS * (qdS^T 1) mu_Q^T with Q-smoothing: Q^ = Q~ + mu_Q, so
                dS^T Q^ = dS^T Q~ + (dS^T 1) mu_Q^T, the pages' dK_bias term)
       dQ_I += sm * sdS * sK(J) * (qdS . Kc_J)          (Kc: the smoothed K codes)
-    Epilogue: dQ = RMSNorm-backward(dQ^, Q^, q_rstd), dK = RMSNorm-backward(dK^, K^,
-    k_rstd) when QK-norm is on (K^ before smoothing; smoothing adds no term because
-    every dS row sums to zero), then all three are rounded to the dtype.
+    Epilogue: dQ = RMSNorm-backward(g_Q o dQ^, Qn, q_rstd), dK = RMSNorm-backward(g_K o dK^,
+    Kn, k_rstd) when QK-norm is on (Qn, Kn: the normalised tokens before the gains, K before
+    smoothing; smoothing adds no term because every dS row sums to zero), then all three are
+    rounded to the dtype. With gains, dq_gain = sum over batch and tokens of dQ^ o Qn (and
+    likewise dk_gain), float64 [H, d].
     With q_tiles / k_tiles only pairs whose I is in q_tiles (bwd_tq units) or whose J
     is in k_tiles (bwd_sk units) are visited: dQ is then exact for those query tiles,
     dK and dV for those key tiles, and NaN elsewhere.
@@ -498,9 +516,20 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
                 dKh[:, j0:j0 + sk, :] += q_smooth_dk_bias(qdS, sdS, muq, sm)
             dQh[:, i0:i0 + tq, :] += (sm * sdS * ks[:, j0 // blk])[:, None, None] * (
                 qdS @ kc[:, j0:j0 + sk, :])
+    gains = {}
     if spec.qk_norm:
-        dQ = rms_norm_backward(dQh, _flat(pro["Qhat"]), _flat(pro["q_rstd"]))
-        dK = rms_norm_backward(dKh, _flat(pro["Khat"]), _flat(pro["k_rstd"]))
+        # with gains g: X^ = g o n, so dn = g o dX^ and dg = sum over batch and tokens of dX^ o n
+        qg, kg = pro.get("q_gain"), pro.get("k_gain")
+        Qn, Kn = _flat(pro.get("Qn", pro["Qhat"])), _flat(pro.get("Kn", pro["Khat"]))
+        gq = np.ones((1, 1, d)) if qg is None else np.broadcast_to(
+            np.asarray(qg, np.float64), (B, H, d)).reshape(B * H, 1, d)
+        gk = np.ones((1, 1, d)) if kg is None else np.broadcast_to(
+            np.asarray(kg, np.float64), (B, H, d)).reshape(B * H, 1, d)
+        dQ = rms_norm_backward(dQh * gq, Qn, _flat(pro["q_rstd"]))
+        dK = rms_norm_backward(dKh * gk, Kn, _flat(pro["k_rstd"]))
+        if qg is not None or kg is not None:
+            gains = dict(dq_gain=(dQh * Qn).reshape(B, H, N, d).sum(axis=(0, 2)),
+                         dk_gain=(dKh * Kn).reshape(B, H, N, d).sum(axis=(0, 2)))
     else:
         dQ, dK = dQh, dKh
     if qsel is not None or ksel is not None:
@@ -519,6 +548,7 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
         dV=round_to_dtype(dV, spec.dtype).reshape(B, H, N, d),
         D=D, dOc=dOc, dOs=dOs,
     )
+    out.update(gains)
     return out
 
 
@@ -535,9 +565,11 @@ def q_smooth_dk_bias(qdS, sdS, mu_q, sm: float) -> np.ndarray:
 
 
 def run(Q, K, V, dO, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
-        block_quant: BlockQuant = quant_blocks_f32):
-    """Prologue -> forward -> backward on whole tensors. Returns one dict of everything."""
-    pro = prologue(Q, K, V, spec, block_quant=block_quant)
+        block_quant: BlockQuant = quant_blocks_f32, q_gain: Optional[np.ndarray] = None,
+        k_gain: Optional[np.ndarray] = None):
+    """Prologue -> forward -> backward on whole tensors. Returns one dict of everything
+    (with gains [H, d] also their gradients dq_gain, dk_gain)."""
+    pro = prologue(Q, K, V, spec, block_quant=block_quant, q_gain=q_gain, k_gain=k_gain)
     O, LSE = forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec,
                      tile_quant=tile_quant, kbias=pro["kbias"] if spec.q_smooth else None)
     g = backward(pro, Q, K, V, O, LSE, dO, spec, tile_quant=tile_quant, block_quant=block_quant)

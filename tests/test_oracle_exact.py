@@ -142,3 +142,66 @@ def test_ds_rms_falls_with_sqrt_n(causal):
         rms.append(np.sqrt(np.mean(out["ds_rms"][..., rows] ** 2)))
     slope = np.polyfit(np.log(Ns), np.log(rms), 1)[0]
     assert slope <= -0.5 + 0.1, slope
+
+
+# ---------------------------------------------------------------- learnable QK-norm gains
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gain_grad_fd(causal):
+    """Gradients with respect to Q, K, V and the two gains [H, d] against central finite
+    differences of L = sum(dO o O)."""
+    rng = np.random.default_rng(51 + causal)
+    B, H, N, d = 1, 2, 5, 4
+    Q, K, V, dO = (_rand(rng, B, H, N, d) for _ in range(4))
+    gq = 1.0 + 0.3 * _rand(rng, H, d)
+    gk = 1.0 + 0.3 * _rand(rng, H, d)
+    kw = dict(causal=causal, qk_norm=True, eps=1e-6)
+    out = exact.attention(Q, K, V, dO, q_gain=gq, k_gain=gk, **kw)
+    h = 1e-6
+    args = {"Q": Q, "K": K, "V": V, "gq": gq, "gk": gk}
+
+    def L(a):
+        return exact.loss(a["Q"], a["K"], a["V"], dO, q_gain=a["gq"], k_gain=a["gk"], **kw)
+
+    for name, G in (("Q", out["dQ"]), ("K", out["dK"]), ("V", out["dV"]), ("gq", out["dq_gain"]),
+                    ("gk", out["dk_gain"])):
+        X = args[name]
+        fd = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            ap, am = dict(args), dict(args)
+            ap[name] = X.copy(); ap[name][idx] += h
+            am[name] = X.copy(); am[name][idx] -= h
+            fd[idx] = (L(ap) - L(am)) / (2 * h)
+        err = np.linalg.norm(G - fd) / max(np.linalg.norm(fd), 1e-30)
+        assert err < 1e-6, (name, err)
+
+
+def test_gain_matches_torch_autograd():
+    """torch's RMSNorm with a weight and its attention routine, autograd in float64."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(61)
+    B, H, N, d = 2, 3, 23, 8
+    Q, K, V, dO = (_rand(rng, B, H, N, d) for _ in range(4))
+    gq = 1.0 + 0.5 * _rand(rng, H, d)
+    gk = 1.0 + 0.5 * _rand(rng, H, d)
+    eps = 1e-6
+    out = exact.attention(Q, K, V, dO, causal=True, qk_norm=True, eps=eps, row_block=8, q_gain=gq, k_gain=gk)
+    tq, tk, tv, tgq, tgk = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V, gq, gk))
+    a = F.rms_norm(tq, (d,), eps=eps) * tgq[None, :, None, :]
+    b = F.rms_norm(tk, (d,), eps=eps) * tgk[None, :, None, :]
+    o = F.scaled_dot_product_attention(a, b, tv, is_causal=True)
+    o.backward(torch.tensor(dO))
+    assert np.allclose(out["O"], o.detach().numpy(), rtol=1e-10, atol=1e-12)
+    for mine, ref in ((out["dQ"], tq), (out["dK"], tk), (out["dV"], tv), (out["dq_gain"], tgq),
+                      (out["dk_gain"], tgk)):
+        assert np.allclose(mine, ref.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_unit_gain_is_no_gain():
+    rng = np.random.default_rng(71)
+    Q, K, V, dO = (_rand(rng, 1, 2, 9, 8) for _ in range(4))
+    a = exact.attention(Q, K, V, dO, causal=True, qk_norm=True)
+    b = exact.attention(Q, K, V, dO, causal=True, qk_norm=True, q_gain=np.ones((2, 8)), k_gain=np.ones((2, 8)))
+    for k in ("O", "dQ", "dK", "dV"):
+        assert np.array_equal(a[k], b[k]), k

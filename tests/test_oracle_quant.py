@@ -389,3 +389,76 @@ def test_q_smoothing_planted_mistake_is_caught(monkeypatch, mistake):
     got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
     ref = _exact_all(Q, K, V, dO, spec)
     assert not all(_rel(got[n], ref[n]) < 3e-6 for n in ("O", "dQ", "dK", "dV"))
+
+
+# ----------------------------------------------------------------- learnable QK-norm gains
+
+def _gain_case(seed, causal=True, N=128, d=32):
+    rng = np.random.default_rng(seed)
+    B, H = 2, 2
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    gq = (1.0 + 0.4 * rng.standard_normal((H, d))).astype(F32)
+    gk = (1.0 + 0.4 * rng.standard_normal((H, d))).astype(F32)
+    spec = oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64")
+    return Q, K, V, dO, gq, gk, spec
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_quant_with_gains(causal):
+    """Identity quantisers with learnable QK-norm gains: equal to exact attention with the same
+    gains (O, dQ, dK, dV and both gain gradients), up to the float32 prologue."""
+    Q, K, V, dO, gq, gk, spec = _gain_case(81 + causal, causal)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant,
+                 q_gain=gq, k_gain=gk)
+    ref = exact.attention(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64),
+                          dO.astype(np.float64), causal=causal, qk_norm=True, eps=spec.eps,
+                          q_gain=gq.astype(np.float64), k_gain=gk.astype(np.float64))
+    for name in ("O", "dQ", "dK", "dV", "dq_gain", "dk_gain"):
+        assert _rel(got[name], ref[name]) < 3e-6, name
+
+
+def test_gain_prologue_power_of_two_exact():
+    """A power-of-two gain scales the normalised values exactly, so every code is unchanged
+    and every block scale of Q and K is multiplied by exactly that power (K-smoothing
+    commutes with it: the mean scales by the same power)."""
+    Q, K, V, dO, _, _, spec = _gain_case(91)
+    H, d = Q.shape[1], Q.shape[3]
+    rng = np.random.default_rng(92)
+    e = rng.integers(-3, 4, size=H)                     # one power per head, all channels
+    g = np.repeat(np.exp2(e.astype(np.float64))[:, None], d, axis=1).astype(F32)
+    a = oq.prologue(Q, K, V, spec)
+    b = oq.prologue(Q, K, V, spec, q_gain=g, k_gain=g)
+    for k in ("Qc", "Kc", "Vc", "Vs", "q_rstd", "k_rstd"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    f = np.exp2(e.astype(np.float64))[None, :, None]
+    np.testing.assert_array_equal(b["Qs"], (a["Qs"] * f).astype(F32))
+    np.testing.assert_array_equal(b["Ks"], (a["Ks"] * f).astype(F32))
+
+
+def test_unit_gain_equals_no_gain():
+    Q, K, V, dO, gq, gk, spec = _gain_case(93)
+    ones = np.ones_like(gq)
+    a = oq.run(Q, K, V, dO, spec)
+    b = oq.run(Q, K, V, dO, spec, q_gain=ones, k_gain=ones)
+    for k in ("Qc", "Kc", "Qs", "Ks", "O", "dQ", "dK", "dV"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_gain_planted_mistake_is_caught(monkeypatch):
+    """Dropping the gain from the RMSNorm backward (dn = dX^ instead of g o dX^) breaks the
+    identity-quantiser pin."""
+    Q, K, V, dO, gq, gk, spec = _gain_case(94)
+    real = oq.rms_norm_backward
+    calls = []
+
+    def no_gain(dy, y, r):
+        calls.append(1)
+        return real(dy / np.broadcast_to(np.asarray(gq, np.float64), (Q.shape[0],) + gq.shape).reshape(-1, 1, gq.shape[-1])
+                    if len(calls) == 1 else dy, y, r)
+    monkeypatch.setattr(oq, "rms_norm_backward", no_gain)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant,
+                 q_gain=gq, k_gain=gk)
+    ref = exact.attention(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64),
+                          dO.astype(np.float64), causal=True, qk_norm=True, eps=spec.eps,
+                          q_gain=gq.astype(np.float64), k_gain=gk.astype(np.float64))
+    assert _rel(got["dQ"], ref["dQ"]) > 1e-2
