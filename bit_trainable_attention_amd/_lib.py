@@ -33,7 +33,7 @@ class Params(ctypes.Structure):
         ("blk", ctypes.c_int32), ("causal", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
-        ("layout", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("qk_gain", ctypes.c_int32),
     ]
 
 
@@ -43,11 +43,11 @@ _ST = ctypes.c_int
 
 SIGNATURES = {
     "sagebwd_prologue_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
-    "sagebwd_quant_prologue": (_ST, [ctypes.POINTER(Params)] + [_P] * 14 + [_P, _SIZE, _P]),
+    "sagebwd_quant_prologue": (_ST, [ctypes.POINTER(Params)] + [_P] * 16 + [_P, _SIZE, _P]),
     "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 9 + [_P]),
     "sagebwd_backward_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
-    "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 17 + [_P, _SIZE, _P]),
-    "sagebwd_backward_part": (_ST, [ctypes.POINTER(Params), ctypes.c_int32] + [_P] * 17 + [_P, _SIZE, _P]),
+    "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 21 + [_P, _SIZE, _P]),
+    "sagebwd_backward_part": (_ST, [ctypes.POINTER(Params), ctypes.c_int32] + [_P] * 21 + [_P, _SIZE, _P]),
     "sagebwd_status_string": (ctypes.c_char_p, [_ST]),
     "sagebwd_last_error": (ctypes.c_char_p, []),
 }

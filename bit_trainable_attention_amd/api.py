@@ -19,13 +19,14 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
                 dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0,
-                q_smooth: bool = False, layout: str = "bhnd") -> _lib.Params:
+                q_smooth: bool = False, layout: str = "bhnd", qk_gain: bool = False) -> _lib.Params:
     """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics; layout of the 16-bit tensors:
-    "bhnd" [B,H,N,d] or "bnhd" [B,N,H,d] (include/sagebwd.h)."""
+    "bhnd" [B,H,N,d] or "bnhd" [B,N,H,d]; qk_gain: learnable QK-norm gains [H,d]
+    (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
     lay = {"bhnd": _lib.LAYOUT_BHND, "bnhd": _lib.LAYOUT_BNHD}[layout]
     return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode,
-                       int(q_smooth), lay)
+                       int(q_smooth), lay, int(qk_gain))
 
 
 def sagebwd_status_string(status: int) -> str:
@@ -103,20 +104,38 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     else:
         off["dq_acc"] = after
         off["total"] = after + up(4 * bh * p.N * p.d)
+    if p.qk_gain:
+        off["gq"] = off["total"]
+        off["gk"] = off["gq"] + up(4 * bh * nt * p.d)
+        off["total"] = off["gk"] + up(4 * bh * nb * p.d)
     return off
+
+
+def _gains(p: _lib.Params, q_gain, k_gain, dev):
+    if not p.qk_gain:
+        return None, None
+    for name, g in (("q_gain", q_gain), ("k_gain", k_gain)):
+        if g is None:
+            raise ValueError(f"{name} is required with qk_gain")
+        _want(g, name, (p.H, p.d), torch.float32, dev)
+    return q_gain, k_gain
 
 
 def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                            out: Optional[Dict[str, torch.Tensor]] = None,
                            workspace: Optional[torch.Tensor] = None,
-                           stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
-    """QK-norm -> K-smoothing (and Q-smoothing) -> per-block INT8 codes/scales. Returns the
-    prologue tensors; with q_smooth also q_mean [B,H,d] and kbias [B,H,N]."""
+                           stream: Optional[torch.cuda.Stream] = None,
+                           q_gain: Optional[torch.Tensor] = None,
+                           k_gain: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """QK-norm (with the gains [H,d] when p.qk_gain) -> K-smoothing (and Q-smoothing) ->
+    per-block INT8 codes/scales. Returns the prologue tensors; with q_smooth also q_mean
+    [B,H,d] and kbias [B,H,N]."""
     dev = Q.device
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
     for name, t in (("Q", Q), ("K", K), ("V", V)):
         _want(t, name, sh["x16"], dt, dev)
+    q_gain, k_gain = _gains(p, q_gain, k_gain, dev)
     if out is None:
         out = dict(
             Qc=torch.empty(sh["x"], dtype=torch.int8, device=dev),
@@ -148,7 +167,7 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
         _ptr(out["Qc"]), _ptr(out["Kc"]), _ptr(out["Vtc"]), _ptr(out["Qs"]), _ptr(out["Ks"]), _ptr(out["Vs"]),
         _ptr(out["q_rstd"]), _ptr(out["k_rstd"]), _ptr(out["k_mean"]),
         _ptr(out.get("q_mean") if p.q_smooth else None), _ptr(out.get("kbias") if p.q_smooth else None),
-        _ptr(workspace), ws_bytes, _stream(dev, stream))
+        _ptr(q_gain), _ptr(k_gain), _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(st, "sagebwd_quant_prologue")
     return out
 
@@ -179,8 +198,9 @@ def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[to
     return O, lse
 
 
-def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
+def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace, q_gain=None, k_gain=None):
     dev = Q.device
+    q_gain, k_gain = _gains(p, q_gain, k_gain, dev)
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
     for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
@@ -196,6 +216,11 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
         grads = {n: torch.empty(sh["x16"], dtype=dt, device=dev) for n in ("dQ", "dK", "dV")}
     for n in ("dQ", "dK", "dV"):
         _want(grads[n], n, sh["x16"], dt, dev)
+    if p.qk_gain:
+        for n in ("dq_gain", "dk_gain"):
+            if n not in grads:
+                grads[n] = torch.empty((p.H, p.d), dtype=torch.float32, device=dev)
+            _want(grads[n], n, (p.H, p.d), torch.float32, dev)
     need = sagebwd_backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -203,7 +228,9 @@ def _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace):
     args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(pro["Qc"]), _ptr(pro["Kc"]),
             _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["q_rstd"]), _ptr(pro["k_rstd"]),
             _ptr(pro["q_mean"] if p.q_smooth else None), _ptr(pro["kbias"] if p.q_smooth else None),
+            _ptr(q_gain), _ptr(k_gain),
             _ptr(O), _ptr(lse), _ptr(dO), _ptr(grads["dQ"]), _ptr(grads["dK"]), _ptr(grads["dV"]),
+            _ptr(grads.get("dq_gain")), _ptr(grads.get("dk_gain")),
             _ptr(workspace), ws_bytes]
     return args, grads, workspace
 
@@ -212,9 +239,11 @@ def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.
                      pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
                      grads: Optional[Dict[str, torch.Tensor]] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     stream: Optional[torch.cuda.Stream] = None) -> Dict[str, torch.Tensor]:
-    """Backward. Returns dict(dQ, dK, dV, workspace)."""
-    args, grads, workspace = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace)
+                     stream: Optional[torch.cuda.Stream] = None,
+                     q_gain: Optional[torch.Tensor] = None,
+                     k_gain: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Backward. Returns dict(dQ, dK, dV, workspace) and, with p.qk_gain, dq_gain, dk_gain."""
+    args, grads, workspace = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace, q_gain, k_gain)
     st = _lib.load().sagebwd_backward(ctypes.byref(p), *args, _stream(Q.device, stream))
     _check(st, "sagebwd_backward")
     out = dict(grads)
@@ -225,8 +254,9 @@ def sagebwd_backward(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.
 def sagebwd_backward_part(p: _lib.Params, part: int, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                           pro: Dict[str, torch.Tensor], O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
                           grads: Dict[str, torch.Tensor], workspace: torch.Tensor,
-                          stream: Optional[torch.cuda.Stream] = None) -> None:
-    """One stage (0: pre, 1: main, 2: finalize) of the backward; see include/sagebwd.h."""
-    args, _, _ = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace)
+                          stream: Optional[torch.cuda.Stream] = None,
+                          q_gain: Optional[torch.Tensor] = None, k_gain: Optional[torch.Tensor] = None) -> None:
+    """One stage (0: pre, 1: main, 2: the dQ pass) of the backward; see include/sagebwd.h."""
+    args, _, _ = _backward_args(p, Q, K, V, pro, O, lse, dO, grads, workspace, q_gain, k_gain)
     st = _lib.load().sagebwd_backward_part(ctypes.byref(p), int(part), *args, _stream(Q.device, stream))
     _check(st, f"sagebwd_backward_part({part})")

@@ -13,7 +13,7 @@ the inputs.
 """
 from __future__ import annotations
 
-from typing import Tuple, Union
+from typing import Optional, Tuple, Union
 
 import torch
 
@@ -29,8 +29,8 @@ class SageBwdAttention(torch.autograd.Function):
     """Autograd node: forward = prologue + INT8 forward, backward = the library's backward."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal: bool, qk_norm: bool, k_smooth: bool, blk: int, eps: float,
-                sm_scale: float, dq_mode: int, q_smooth: bool, layout: str):
+    def forward(ctx, q, k, v, q_gain, k_gain, causal: bool, qk_norm: bool, k_smooth: bool, blk: int,
+                eps: float, sm_scale: float, dq_mode: int, q_smooth: bool, layout: str):
         if q.dtype not in _DTYPES:
             raise TypeError(f"q, k, v must be float16 or bfloat16, got {q.dtype}")
         if q.dim() != 4:
@@ -39,37 +39,51 @@ class SageBwdAttention(torch.autograd.Function):
             B, N, H, d = q.shape
         else:
             B, H, N, d = q.shape
+        gained = q_gain is not None
+        if gained != (k_gain is not None):
+            raise ValueError("q_gain and k_gain go together")
         p = api.make_params(B, H, N, d, blk, causal, qk_norm, k_smooth, _DTYPES[q.dtype], eps=eps,
-                            sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth, layout=layout)
+                            sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth, layout=layout,
+                            qk_gain=gained)
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        pro = api.sagebwd_quant_prologue(p, q, k, v)
+        gains = (q_gain.detach().float().contiguous(), k_gain.detach().float().contiguous()) if gained else (None, None)
+        pro = api.sagebwd_quant_prologue(p, q, k, v, q_gain=gains[0], k_gain=gains[1])
         O, lse = api.sagebwd_forward(p, pro)
         ctx.params = p
         ctx.saved_names = _SAVED_QS if q_smooth else _SAVED
-        ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in ctx.saved_names))
+        ctx.gain_dtypes = (q_gain.dtype, k_gain.dtype) if gained else None
+        ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in ctx.saved_names), *(gains if gained else ()))
         ctx.mark_non_differentiable(lse)
         return O, lse
 
     @staticmethod
     def backward(ctx, dO, _dlse):
         q, k, v, O, lse, *saved = ctx.saved_tensors
-        pro = dict(zip(ctx.saved_names, saved))
-        g = api.sagebwd_backward(ctx.params, q, k, v, pro, O, lse, dO.contiguous())
-        return g["dQ"], g["dK"], g["dV"], None, None, None, None, None, None, None, None, None
+        pro = dict(zip(ctx.saved_names, saved[:len(ctx.saved_names)]))
+        gains = saved[len(ctx.saved_names):] if ctx.gain_dtypes else (None, None)
+        g = api.sagebwd_backward(ctx.params, q, k, v, pro, O, lse, dO.contiguous(), q_gain=gains[0],
+                                 k_gain=gains[1])
+        dgq = dgk = None
+        if ctx.gain_dtypes:
+            dgq, dgk = g["dq_gain"].to(ctx.gain_dtypes[0]), g["dk_gain"].to(ctx.gain_dtypes[1])
+        return (g["dQ"], g["dK"], g["dV"], dgq, dgk) + (None,) * 10
 
 
 def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                       qk_norm: bool = True, k_smooth: bool = True, blk: int = 128, eps: float = 1e-6,
                       sm_scale: float = 0.0, layout: str = "bhnd", return_lse: bool = False,
-                      dq_mode: int = 0, q_smooth: bool = False) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+                      dq_mode: int = 0, q_smooth: bool = False, q_gain: Optional[torch.Tensor] = None,
+                      k_gain: Optional[torch.Tensor] = None) -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
     """SageBwd-style INT8 attention with gradients (see the module docstring).
 
     sm_scale <= 0 selects 1/sqrt(d); q_smooth selects the Q-smoothing variant (the query
-    mean is subtracted before quantising and added back through the key bias and dK_bias). The lse returned with return_lse is float32 [B, H, N]
-    (natural log) and carries no gradient.
+    mean is subtracted before quantising and added back through the key bias and dK_bias).
+    q_gain, k_gain: optional learnable QK-norm gains [H, d] (both or neither; they receive
+    gradients). The lse returned with return_lse is float32 [B, H, N] (natural log) and
+    carries no gradient.
     """
     if layout not in ("bhnd", "bnhd"):
         raise ValueError(f"layout must be 'bhnd' or 'bnhd', got {layout!r}")
-    O, lse = SageBwdAttention.apply(q, k, v, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
+    O, lse = SageBwdAttention.apply(q, k, v, q_gain, k_gain, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
                                     float(eps), float(sm_scale), int(dq_mode), bool(q_smooth), layout)
     return (O, lse) if return_lse else O

@@ -30,6 +30,7 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->dq_mode < SAGEBWD_DQ_AUTO || p->dq_mode > SAGEBWD_DQ_ATOMIC) return SAGEBWD_ERR_UNSUPPORTED;
   if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->layout != SAGEBWD_LAYOUT_BHND && p->layout != SAGEBWD_LAYOUT_BNHD) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->qk_gain && !p->qk_norm) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
   // (N * d * 4 < 2^31), grids in 2^31 workgroups
@@ -66,7 +67,7 @@ struct BwdLayout {
   bool spill;
   bool spill_fits;  // one head's dS tiles stay below 4 GiB
   long long tiles;  // dS tiles per head (spill mode)
-  size_t pk, dq, ktp, dsp, dsm, total;
+  size_t pk, dq, ktp, dsp, dsm, gq, gk, total;
 };
 
 BwdLayout bwd_layout(const sagebwd_params* p) {
@@ -92,6 +93,12 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
     L.dq = after_pk;
     L.total = L.dq + round_up(4 * elems(p));
   }
+  if (p->qk_gain) {
+    // partial sums of the gains' gradients: per (head, 64-query tile) and per (head, key block)
+    L.gq = L.total;
+    L.gk = L.gq + round_up(4 * bh * (p->N / 64) * (size_t)p->d);
+    L.total = L.gk + round_up(4 * bh * (p->N / p->blk) * (size_t)p->d);
+  }
   return L;
 }
 
@@ -110,7 +117,7 @@ const char* sagebwd_status_string(sagebwd_status s) {
     case SAGEBWD_OK: return "ok";
     case SAGEBWD_ERR_NULL: return "null pointer argument";
     case SAGEBWD_ERR_SHAPE: return "invalid shape (negative size, or N not a multiple of blk)";
-    case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype or eps)";
+    case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype, dq_mode, layout, eps or gains)";
     case SAGEBWD_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
     case SAGEBWD_ERR_HIP: return "HIP kernel launch failed";
@@ -146,13 +153,15 @@ size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
 sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
                                       int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
                                       float* q_rstd, float* k_rstd, float* k_mean, float* q_mean,
-                                      float* kbias, void* workspace, size_t workspace_bytes, void* stream) {
+                                      float* kbias, const float* q_gain, const float* k_gain, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
   if (empty(p)) return SAGEBWD_OK;
   st = check_ptrs(Q, K, V, Qc, Kc, Vtc, Qs, Ks, Vs, q_rstd, k_rstd, k_mean);
   if (st != SAGEBWD_OK) return st;
   if (p->q_smooth && (st = check_ptrs(q_mean, kbias)) != SAGEBWD_OK) return st;
+  if (p->qk_gain && (st = check_ptrs(q_gain, k_gain)) != SAGEBWD_OK) return st;
   const size_t need = sagebwd_prologue_workspace_bytes(p);
   if (need > 0) {
     if (!workspace) return SAGEBWD_ERR_NULL;
@@ -166,6 +175,10 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
   a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc;
   a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
   a.q_rstd = q_rstd; a.k_rstd = k_rstd; a.k_mean = k_mean;
+  if (p->qk_gain) {
+    a.q_gain = q_gain;
+    a.k_gain = k_gain;
+  }
   char* ws = static_cast<char*>(workspace);
   a.kpart = p->k_smooth ? reinterpret_cast<float*>(ws) : nullptr;
   if (p->q_smooth) {
@@ -203,8 +216,9 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
 static sagebwd_status backward_impl(const sagebwd_params* p, int part, const void* Q, const void* K,
                                     const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
                                     const float* Ks, const float* q_rstd, const float* k_rstd,
-                                    const float* q_mean, const float* kbias, const void* O,
-                                    const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                    const float* q_mean, const float* kbias, const float* q_gain,
+                                    const float* k_gain, const void* O, const float* lse, const void* dO,
+                                    void* dQ, void* dK, void* dV, float* dq_gain, float* dk_gain,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
@@ -213,6 +227,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   st = check_ptrs(Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, O, lse, dO, dQ, dK, dV);
   if (st != SAGEBWD_OK) return st;
   if (p->q_smooth && (st = check_ptrs(q_mean, kbias)) != SAGEBWD_OK) return st;
+  if (p->qk_gain && (st = check_ptrs(q_gain, k_gain, dq_gain, dk_gain)) != SAGEBWD_OK) return st;
   if (!workspace) return SAGEBWD_ERR_NULL;
   if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
   const BwdLayout L = bwd_layout(p);
@@ -235,6 +250,14 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   a.dQ = static_cast<unsigned short*>(dQ);
   a.dK = static_cast<unsigned short*>(dK);
   a.dV = static_cast<unsigned short*>(dV);
+  if (p->qk_gain) {
+    a.q_gain = q_gain;
+    a.k_gain = k_gain;
+    a.dq_gain = dq_gain;
+    a.dk_gain = dk_gain;
+    a.gq_part = reinterpret_cast<float*>(ws + L.gq);
+    a.gk_part = reinterpret_cast<float*>(ws + L.gk);
+  }
   a.pk = reinterpret_cast<int8_t*>(ws + L.pk);
   a.spill = L.spill;
   if (L.spill) {
@@ -254,21 +277,23 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
 sagebwd_status sagebwd_backward(const sagebwd_params* p, const void* Q, const void* K, const void* V,
                                 const int8_t* Qc, const int8_t* Kc, const float* Qs, const float* Ks,
                                 const float* q_rstd, const float* k_rstd, const float* q_mean,
-                                const float* kbias, const void* O, const float* lse, const void* dO, void* dQ,
-                                void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
-  return backward_impl(p, -1, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, O, lse, dO, dQ, dK, dV,
-                       workspace, workspace_bytes, stream);
+                                const float* kbias, const float* q_gain, const float* k_gain, const void* O,
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV, float* dq_gain,
+                                float* dk_gain, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(p, -1, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, q_gain, k_gain, O, lse, dO,
+                       dQ, dK, dV, dq_gain, dk_gain, workspace, workspace_bytes, stream);
 }
 
 sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part, const void* Q, const void* K,
                                      const void* V, const int8_t* Qc, const int8_t* Kc, const float* Qs,
                                      const float* Ks, const float* q_rstd, const float* k_rstd,
-                                     const float* q_mean, const float* kbias, const void* O, const float* lse,
-                                     const void* dO, void* dQ, void* dK, void* dV, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     const float* q_mean, const float* kbias, const float* q_gain,
+                                     const float* k_gain, const void* O, const float* lse, const void* dO,
+                                     void* dQ, void* dK, void* dV, float* dq_gain, float* dk_gain,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   if (part < 0) return check_params(p) != SAGEBWD_OK ? check_params(p) : SAGEBWD_ERR_UNSUPPORTED;
-  return backward_impl(p, part, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, O, lse, dO, dQ, dK, dV,
-                       workspace, workspace_bytes, stream);
+  return backward_impl(p, part, Q, K, V, Qc, Kc, Qs, Ks, q_rstd, k_rstd, q_mean, kbias, q_gain, k_gain, O, lse,
+                       dO, dQ, dK, dV, dq_gain, dk_gain, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

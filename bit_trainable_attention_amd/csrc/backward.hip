@@ -341,6 +341,7 @@ void bwd_main(BackwardArgs a) {
   // |dS| maxima of the waves [tile parity][wave], apart from the tile buffers so that reading
   // them never waits for copies in flight into the buffers
   __shared__ float redD[2 * NW];
+  __shared__ float gred[NW][D];   // (gains) the waves' partial sums of dk_gain
 
   const int nb = a.N / BLK;
   const int bh = blockIdx.x % a.BH;
@@ -690,16 +691,26 @@ void bwd_main(BackwardArgs a) {
   }
   unsigned short* dkrow = a.dK + krow16;
   if (a.qk_norm) {
+    // K^ = g o n with n = K * rstd: dn = g o dK^, dK = rstd * (dn - n * mean_c(dn o n)), and
+    // the gain's gradient collects dK^ o n over the keys (g = 1 without gains)
     const float rs = a.k_rstd[hrow + key];
     const unsigned short* krow = a.K + krow16;
+    const float* gain = a.k_gain ? a.k_gain + (size_t)(bh % a.x16.H) * D : nullptr;
     float kh[NCT][4];
     float dot = 0.0f;
 #pragma unroll
     for (int n = 0; n < NCT; ++n) {
       const u16x4 kv = *reinterpret_cast<const u16x4*>(krow + 16 * n + 4 * g);
+      f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (gain) gv = *reinterpret_cast<const f32x4*>(gain + 16 * n + 4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         kh[n][r] = to_f32<DT>(kv[r]) * rs;
+        if (gain) {
+          const float u = dk[n][r];
+          dk[n][r] = u * gv[r];
+          dv[n][r] = u * kh[n][r];   // dv is stored: its registers carry the gain products
+        }
         dot = __builtin_fmaf(dk[n][r], kh[n][r], dot);
       }
     }
@@ -710,6 +721,24 @@ void bwd_main(BackwardArgs a) {
     for (int n = 0; n < NCT; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dk[n][r] = rs * (dk[n][r] - kh[n][r] * mean);
+    if (gain) {
+      // this key block's partial of dk_gain: over the wave's 16 keys (a DPP row sum), then over
+      // the waves in order
+#pragma unroll
+      for (int n = 0; n < NCT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = row_sum16(dv[n][r]);
+          if (lr == 0) gred[w][16 * n + 4 * g + r] = t;
+        }
+      __syncthreads();
+      if (tid < D) {
+        float t = gred[0][tid];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) t += gred[i][tid];
+        a.gk_part[((size_t)bh * nb + kb) * D + tid] = t;
+      }
+    }
   }
 #pragma unroll
   for (int n = 0; n < NCT; ++n) {
@@ -717,6 +746,71 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dk[n][r]);
     *reinterpret_cast<u16x4*>(dkrow + 16 * n + 4 * g) = v;
+  }
+}
+
+// ------------------------------------------------------------------------------ dQ epilogue
+// One 64-query tile of dQ^ (query rows q0 .. q0 + 63 of head bh, q0 = 64 qt): RMSNorm backward
+// with the gain (Q^ = g o n, n = Q * rstd: dn = g o dQ^, dQ = rstd * (dn - n * mean_c(dn o n)),
+// g = 1 without gains), rounding to the dtype, and with gains the tile's partial of dq_gain
+// (dQ^ o n summed over the rows in a fixed order). 256 threads; D/8 lanes per row, 8
+// channels each; row(r, c, v) fills v[0..7] with dQ^ of tile row r, channels c .. c + 7.
+// gred: 8 KB of LDS the caller no longer needs once every row has been read.
+template <int DT, int D, typename RowF>
+__device__ __forceinline__ void dq_tile_epilogue(const BackwardArgs& a, int bh, int qt, RowF&& row, float* gred) {
+  constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
+  constexpr int RPP = 256 / CPR;                    // rows per pass
+  static_assert(RPP * D * 4 == 8192, "gain partials take 8 KB");
+  const size_t hrow = (size_t)bh * a.N;
+  const int q0 = qt * kPq;
+  const int c = (threadIdx.x % CPR) * 8;
+  const float* gain = (a.qk_norm && a.q_gain) ? a.q_gain + (size_t)(bh % a.x16.H) * D + c : nullptr;
+  float gv[8], gp[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gv[i] = gain ? gain[i] : 1.0f;
+    gp[i] = 0.0f;
+  }
+  for (int r = threadIdx.x / CPR; r < kPq; r += RPP) {
+    const size_t tok = hrow + q0 + r;
+    const size_t row16 = a.x16.row(bh, q0 + r);
+    float v[8];
+    row(r, c, v);
+    u16x8 out;
+    if (a.qk_norm) {
+      const float rs = a.q_rstd[tok];
+      const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + row16 + c);
+      float qh[8], dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qh[i] = to_f32<DT>(qv[i]) * rs;
+        if (gain) {
+          gp[i] = __builtin_fmaf(v[i], qh[i], gp[i]);
+          v[i] = v[i] * gv[i];
+        }
+        dot = __builtin_fmaf(v[i], qh[i], dot);
+      }
+#pragma unroll
+      for (int o = CPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+      const float mean = dot / (float)D;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(rs * (v[i] - qh[i] * mean));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(v[i]);
+    }
+    *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
+  }
+  if (gain) {
+    __syncthreads();   // every row has been read: gred may overlap the rows' source
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gred[(threadIdx.x / CPR) * D + c + i] = gp[i];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      float t = gred[threadIdx.x];
+      for (int i = 1; i < RPP; ++i) t += gred[i * D + threadIdx.x];
+      a.gq_part[((size_t)bh * (a.N / kPq) + qt) * D + threadIdx.x] = t;
+    }
   }
 }
 
@@ -867,73 +961,45 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) t[(16 * g + 4 * qs + r) * D + 16 * (NPW * w + n) + lr] = dq[qs][n][r];
   __syncthreads();
-  constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
-  const size_t hrow = (size_t)bh * a.N;
-  for (int e = threadIdx.x; e < kPq * CPR; e += 256) {
-    const int r = e / CPR, c = (e % CPR) * 8;
-    const size_t tok = hrow + q0 + r;
-    const size_t row16 = a.x16.row(bh, q0 + r);
-    float v[8];
+  dq_tile_epilogue<DT, D>(a, bh, qt, [&](int r, int c, float* v) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = t[r * D + c + i];
-    u16x8 out;
-    if (a.qk_norm) {
-      const float rs = a.q_rstd[tok];
-      const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + row16 + c);
-      float qh[8], dot = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        qh[i] = to_f32<DT>(qv[i]) * rs;
-        dot = __builtin_fmaf(v[i], qh[i], dot);
-      }
-#pragma unroll
-      for (int o = CPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-      const float mean = dot / (float)D;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(rs * (v[i] - qh[i] * mean));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(v[i]);
-    }
-    *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
-  }
+  }, t);
 }
 
 // ------------------------------------------------------------------------------ dq_finalize
-// One group of D/8 lanes per token: dQ = rstd * (dQ^ - Q^ * mean_c(dQ^ o Q^)), Q^ = Q * rstd.
+// (atomic mode) One workgroup per (head, 64-query tile): the tile epilogue over the float32
+// dQ^ accumulator rows.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void dq_finalize(BackwardArgs a) {
-  constexpr int CPR = D / 8;
-  const size_t tokens = (size_t)a.BH * a.N;
-  const size_t gidx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t tok = gidx / CPR;
-  const int c = (int)(gidx % CPR) * 8;
-  if (tok >= tokens) return;  // whole rows only: CPR divides 256, so a row never straddles this
-  const size_t row16 = a.x16.row((int)(tok / a.N), (int)(tok % a.N));
-  const float* src = a.dq_acc + tok * D + c;
-  float dq[8];
-  *reinterpret_cast<float4*>(dq) = *reinterpret_cast<const float4*>(src);
-  *reinterpret_cast<float4*>(dq + 4) = *reinterpret_cast<const float4*>(src + 4);
-  u16x8 out;
-  if (a.qk_norm) {
-    const float rs = a.q_rstd[tok];
-    const u16x8 qv = *reinterpret_cast<const u16x8*>(a.Q + row16 + c);
-    float qh[8], dot = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qh[i] = to_f32<DT>(qv[i]) * rs;
-      dot = __builtin_fmaf(dq[i], qh[i], dot);
+  const int ntile = a.N / kPq;
+  const int bh = blockIdx.x / ntile, qt = blockIdx.x % ntile;
+  __shared__ float gred[2048];
+  const float* src = a.dq_acc + ((size_t)bh * a.N + (size_t)qt * kPq) * D;
+  dq_tile_epilogue<DT, D>(a, bh, qt, [&](int r, int c, float* v) {
+    *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src + (size_t)r * D + c);
+    *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + (size_t)r * D + c + 4);
+  }, gred);
+}
+
+// ------------------------------------------------------------------------------ gain_reduce
+// (gains) dq_gain[h] and dk_gain[h] (blockIdx.y = 0, 1): the per-tile partials of every batch
+// entry of head h summed in a fixed order (batch, then tile).
+template <int D>
+__global__ __launch_bounds__(128) void gain_reduce(BackwardArgs a) {
+  const int h = blockIdx.x, H = a.x16.H, B = a.BH / H;
+  const bool is_q = blockIdx.y == 0;
+  const int T = is_q ? a.N / kPq : a.N / a.BLK;
+  const float* part = is_q ? a.gq_part : a.gk_part;
+  float* out = is_q ? a.dq_gain : a.dk_gain;
+  for (int c = threadIdx.x; c < D; c += 128) {
+    float acc = 0.0f;
+    for (int b = 0; b < B; ++b) {
+      const float* pb = part + (size_t)(b * H + h) * T * D + c;
+      for (int t = 0; t < T; ++t) acc += pb[(size_t)t * D];
     }
-#pragma unroll
-    for (int o = CPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-    const float mean = dot / (float)D;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(rs * (dq[i] - qh[i] * mean));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = from_f32<DT>(dq[i]);
+    out[(size_t)h * D + c] = acc;
   }
-  *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
 }
 
 template <int DT, int D, int BLK>
@@ -955,10 +1021,11 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {
-    if (a.spill)
-      return launch_kernel(&bwd_dq<DT, D, BLK>, dim3((unsigned)((long long)(a.N / kPq) * a.BH)), dim3(256), st, a);
-    const long long threads = (long long)a.BH * a.N * (D / 8);
-    return launch_kernel(&dq_finalize<DT, D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), st, a);
+    const dim3 tiles((unsigned)((long long)(a.N / kPq) * a.BH));
+    const hipError_t e = a.spill ? launch_kernel(&bwd_dq<DT, D, BLK>, tiles, dim3(256), st, a)
+                                 : launch_kernel(&dq_finalize<DT, D>, tiles, dim3(256), st, a);
+    if (e != hipSuccess) return e;
+    if (a.q_gain) return launch_kernel(&gain_reduce<D>, dim3((unsigned)a.x16.H, 2), dim3(128), st, a);
   }
   return hipSuccess;
 }

@@ -29,6 +29,7 @@ struct PrologueArgs {
   float* q_mean;                     // [BH, D] (Q-smoothing only)
   float* kbias;                      // [BH, N] (Q-smoothing only)
   float* qpart;                      // [BH, N/BLK, D] (Q-smoothing only)
+  const float *q_gain, *k_gain;      // QK-norm gains [H, D] (NULL: gain 1)
   int BH, N, D, BLK, dtype;
   int qk_norm, k_smooth, q_smooth;
   float eps;
@@ -53,6 +54,9 @@ struct BackwardArgs {
   const float *Qs, *Ks;                      // [BH, N/BLK]
   const float *q_rstd, *k_rstd, *lse;        // [BH, N]
   const float *q_mean, *kbias;               // [BH, D], [BH, N] (Q-smoothing only)
+  const float *q_gain, *k_gain;              // QK-norm gains [H, D] (NULL: gain 1)
+  float *dq_gain, *dk_gain;                  // their gradients [H, D] (with the gains)
+  float *gq_part, *gk_part;                  // gain-gradient partials [BH, N/64, D], [BH, N/BLK, D]
   unsigned short *dQ, *dK, *dV;              // [BH, N, D]
   // workspace regions
   int8_t* pk;                                // [BH, N/64] tile packets

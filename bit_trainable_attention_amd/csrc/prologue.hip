@@ -107,6 +107,21 @@ __device__ __forceinline__ void qk_norm_slice(Slice<D, BLK>& s, float eps, float
   }
 }
 
+// The learnable QK-norm gain of head h (NULL: gain 1): x^ = fl(x^ * g[h][c]) for the thread's
+// channels (SageBwd article, QK-norm paragraph: RMSNorm per token, here with its weight).
+template <int D, int BLK>
+__device__ __forceinline__ void apply_gain_slice(Slice<D, BLK>& s, const float* __restrict__ gain, int h, int ch) {
+  using S = Slice<D, BLK>;
+  if (!gain) return;
+  float g[S::CW];
+#pragma unroll
+  for (int i = 0; i < S::CW; ++i) g[i] = gain[(size_t)h * D + ch * S::CW + i];
+#pragma unroll
+  for (int p = 0; p < S::P; ++p)
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) s.x[p][i] = s.x[p][i] * g[i];
+}
+
 // Block absmax over the workgroup (exact: max is order independent).
 template <int D, int BLK>
 __device__ __forceinline__ float slice_absmax(const Slice<D, BLK>& s, float* red) {
@@ -193,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   float* rstd_out = (tensor == 0 ? a.q_rstd : a.k_rstd) + tok0;
   if (a.qk_norm) {
     qk_norm_slice<D, BLK>(s, a.eps, rstd_out, j, ch);
+    apply_gain_slice<D, BLK>(s, tensor == 0 ? a.q_gain : a.k_gain, bh % a.x16.H, ch);
   } else if (ch == 0) {
 #pragma unroll
     for (int p = 0; p < S::P; ++p) rstd_out[16 * p + j] = 1.0f;
@@ -278,16 +294,20 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
   }
   if (!is_q && a.q_smooth) head_mean<D>(a.qpart + (size_t)bh * nb * D, nb, a.N, qmean);
   __syncthreads();
-  float mu[S::CW];
+  float mu[S::CW], gn[S::CW];
+  const float* gain = a.qk_norm ? (is_q ? a.q_gain : a.k_gain) : nullptr;
 #pragma unroll
-  for (int i = 0; i < S::CW; ++i) mu[i] = smooth ? mean[ch * S::CW + i] : 0.0f;
+  for (int i = 0; i < S::CW; ++i) {
+    mu[i] = smooth ? mean[ch * S::CW + i] : 0.0f;
+    gn[i] = gain ? gain[(size_t)(bh % a.x16.H) * D + ch * S::CW + i] : 1.0f;
+  }
   const float* rstd = is_q ? a.q_rstd : a.k_rstd;
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
     const float r = a.qk_norm ? rstd[tok0 + 16 * p + j] : 1.0f;
 #pragma unroll
     for (int i = 0; i < S::CW; ++i) {
-      const float xh = s.x[p][i] * r;
+      const float xh = (s.x[p][i] * r) * gn[i];   // gn = 1 without gains: exact
       s.x[p][i] = xh - mu[i];
     }
   }

@@ -70,7 +70,7 @@ typedef enum {
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
                                    B*H > 2^24                                               */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
-                                   layout, eps < 0                                          */
+                                   layout, eps < 0, qk_gain without qk_norm                 */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
@@ -82,7 +82,7 @@ typedef struct {
   int32_t B, H, N, d;   /* batch, heads, tokens, head dim (d in {64, 128})                  */
   int32_t blk;          /* quantisation block, tokens (64 or 128); N % blk == 0             */
   int32_t causal;       /* nonzero: key j is visible to query i iff j <= i                  */
-  int32_t qk_norm;      /* nonzero: RMSNorm Q and K per token (gain 1)                      */
+  int32_t qk_norm;      /* nonzero: RMSNorm Q and K per token (gain 1 unless qk_gain)       */
   int32_t k_smooth;     /* nonzero: subtract K's per-channel mean before quantising         */
   float eps;            /* RMSNorm epsilon (>= 0), e.g. 1e-6                                */
   float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(d)                            */
@@ -91,6 +91,11 @@ typedef struct {
   int32_t q_smooth;     /* nonzero: subtract Q's per-channel mean before quantising and add
                            the key bias / dK_bias terms back (see above)                    */
   int32_t layout;       /* sagebwd_layout of the 16-bit tensors Q, K, V, O, dO, dQ, dK, dV   */
+  int32_t qk_gain;      /* nonzero (needs qk_norm): learnable QK-norm gains q_gain, k_gain
+                           [H,d] float32, Q^ = g_Q o RMSNorm(Q) and K^ = g_K o RMSNorm(K) per
+                           head and channel (SageBwd article, QK-norm paragraph: RMSNorm per
+                           token, here with its weight); the backward also returns their
+                           gradients dq_gain, dk_gain [H,d] (sums over batch and tokens)     */
 } sagebwd_params;
 
 /* Memory layout of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV; contiguous either way).
@@ -131,12 +136,14 @@ size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
  *                                  may be NULL)
  *   kbias    out: float32 [B,H,N]  b_k = Ks * (Kc_k . q_mean), float32 sum over channels
  *                                  (q_smooth only; else ignored, may be NULL)
+ *   q_gain, k_gain in: float32 [H,d]  QK-norm gains (qk_gain only; else ignored, may be NULL)
  *   workspace   : >= sagebwd_prologue_workspace_bytes(p) bytes (may be NULL if that is 0)
  * Bit-exact contract: per token, the d channels form 16 chunks of d/16 consecutive
  * channels; each chunk sums x*x in ascending channel order in float32, and ss is the
  * pairwise tree of the 16 chunk sums ((c0+c1), (c2+c3), ..., then pairs of those, down to
  * one); rstd = 1/sqrt(ss/d + eps) with correctly rounded float32 division and square
- * root; x^ = x*rstd; the mean: inside each block, token t joins group t mod 16, each group
+ * root; x^ = x*rstd (then x^ = x^*g[h][c] with qk_gain, one float32 product); the mean:
+ * inside each block, token t joins group t mod 16, each group
  * sums its tokens in ascending order and the block sum is the same pairwise tree of the 16
  * group sums; the block sums are then added in ascending block order and divided by N;
  * K~ = K^ - mean; then the INT8 rule above. q_mean is taken the same way from Q^ (and
@@ -147,6 +154,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
                                       float* Qs, float* Ks, float* Vs,
                                       float* q_rstd, float* k_rstd, float* k_mean,
                                       float* q_mean, float* kbias,
+                                      const float* q_gain, const float* k_gain,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
 
@@ -190,6 +198,9 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *                                    j^(((k>>1)^(k>>4))&3)
  *   dsm     float32 [B,H,T,blk/64]   per 64 keys of the tile (one dS scale tile):
  *                                    sm_scale * (dS tile scale) * (K block scale)
+ * then, with qk_gain:
+ *   gq      float32 [B,H,N/64,d]     partial dq_gain of each 64-query tile
+ *   gk      float32 [B,H,N/blk,d]    partial dk_gain of each key block
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 
@@ -198,9 +209,12 @@ size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
  *   Q, K, V       in : dtype [B,H,N,d], the prologue's inputs
  *   Qc, Kc, Qs, Ks, q_rstd, k_rstd in: the prologue's outputs
  *   q_mean, kbias in : the prologue's outputs with q_smooth (ignored, may be NULL, without)
+ *   q_gain, k_gain in : float32 [H,d], the prologue's gains with qk_gain (else ignored)
  *   O, lse        in : the forward's outputs
  *   dO            in : dtype [B,H,N,d]
  *   dQ, dK, dV    out: dtype [B,H,N,d]
+ *   dq_gain, dk_gain out: float32 [H,d], the gains' gradients with qk_gain (else ignored,
+ *                    may be NULL); float32 sums over tiles in a fixed order (deterministic)
  *   workspace        : >= sagebwd_backward_workspace_bytes(p) bytes, layout above */
 sagebwd_status sagebwd_backward(const sagebwd_params* p,
                                 const void* Q, const void* K, const void* V,
@@ -208,15 +222,18 @@ sagebwd_status sagebwd_backward(const sagebwd_params* p,
                                 const float* Qs, const float* Ks,
                                 const float* q_rstd, const float* k_rstd,
                                 const float* q_mean, const float* kbias,
+                                const float* q_gain, const float* k_gain,
                                 const void* O, const float* lse, const void* dO,
                                 void* dQ, void* dK, void* dV,
+                                float* dq_gain, float* dk_gain,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* One stage of sagebwd_backward, for callers that schedule or time the stages apart:
  *   part 0: D = rowsum(dO o O), dO codes/scales, the packets (and K^T codes or a zeroed
  *           dq_acc)
  *   part 1: the fused key-block kernel (S, P, dP, dS; dV, dK final; dQ^ accumulated)
- *   part 2: dQ = RMSNorm backward of dq_acc, rounded to the dtype
+ *   part 2: the dQ pass (dQ = dS K from the spilled tiles, or from dq_acc), RMSNorm
+ *           backward, rounding to the dtype; with qk_gain also the gains' gradients
  * Arguments as for sagebwd_backward. Running parts 0, 1, 2 in order on one stream with the
  * same workspace is exactly sagebwd_backward; any other order gives undefined results.
  * part outside 0..2 -> SAGEBWD_ERR_UNSUPPORTED. */
@@ -226,8 +243,10 @@ sagebwd_status sagebwd_backward_part(const sagebwd_params* p, int32_t part,
                                      const float* Qs, const float* Ks,
                                      const float* q_rstd, const float* k_rstd,
                                      const float* q_mean, const float* kbias,
+                                     const float* q_gain, const float* k_gain,
                                      const void* O, const float* lse, const void* dO,
                                      void* dQ, void* dK, void* dV,
+                                     float* dq_gain, float* dk_gain,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */

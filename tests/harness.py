@@ -56,10 +56,10 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 
 # ------------------------------------------------------------------------------- GPU side
 
-def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd"):
+def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd", qk_gain: bool = False):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                           dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout)
+                           dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout, qk_gain=qk_gain)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -75,13 +75,19 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
-            pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd") -> Dict[str, np.ndarray]:
+            pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd",
+            gains=None) -> Dict[str, np.ndarray]:
     """Run the HIP path and return host copies (numpy) of everything it produced. With
     layout "bnhd" the 16-bit tensors are handed to the library as [B,N,H,d] (a transposed
-    copy of the same values) and its O, dQ, dK, dV are returned transposed back."""
+    copy of the same values) and its O, dQ, dK, dV are returned transposed back. gains:
+    optional (q_gain, k_gain) float32 [H, d] arrays (learnable QK-norm gains); their
+    gradients come back as dq_gain, dk_gain."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w, dq_mode, layout)
+    p = params_for(w, dq_mode, layout, qk_gain=gains is not None)
+    gq = gk = None
+    if gains is not None:
+        gq, gk = (torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda:0") for g in gains)
     tr = (lambda t: t.transpose(1, 2).contiguous()) if layout == "bnhd" else (lambda t: t)
     back = (lambda t: t.transpose(1, 2)) if layout == "bnhd" else (lambda t: t)
     Q, K, V, dO = (tr(to_device(x[k], w.dtype)) for k in ("Q", "K", "V", "dO"))
@@ -90,12 +96,12 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
     res: Dict[str, np.ndarray] = {}
     pro = pro_in
     if "prologue" in stages:
-        pro = api.sagebwd_quant_prologue(p, Q, K, V)
+        pro = api.sagebwd_quant_prologue(p, Q, K, V, q_gain=gq, k_gain=gk)
     O, lse = O_in, lse_in
     if "forward" in stages:
         O, lse = api.sagebwd_forward(p, pro)
     if "backward" in stages:
-        g = api.sagebwd_backward(p, Q, K, V, pro, O, lse, dO)
+        g = api.sagebwd_backward(p, Q, K, V, pro, O, lse, dO, q_gain=gq, k_gain=gk)
     torch.cuda.synchronize()
     if "prologue" in stages:
         for k, v in pro.items():
@@ -106,6 +112,9 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
     if "backward" in stages:
         for k in ("dQ", "dK", "dV"):
             res[k] = back(g[k]).float().cpu().numpy().astype(np.float64)
+        if gains is not None:
+            res["dq_gain"] = g["dq_gain"].cpu().numpy().astype(np.float64)
+            res["dk_gain"] = g["dk_gain"].cpu().numpy().astype(np.float64)
         lay = api.backward_workspace_layout(p)
         npk = w.B * w.H * (w.N // 64) * lay["packet_bytes"]   # only the packet region is decoded
         ws = g["workspace"][:npk].cpu().numpy()

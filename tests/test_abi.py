@@ -13,7 +13,7 @@ lib = _lib.load()  # fails loudly if the library was not built
 
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
-                dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND)
+                dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND, qk_gain=0)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -49,7 +49,7 @@ def test_last_error_empty_without_failures():
 
 
 def _prologue(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 14), ws, ws_bytes, None)
+    return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 16), ws, ws_bytes, None)
 
 
 def _forward(p, ptr=FAKE):
@@ -57,7 +57,7 @@ def _forward(p, ptr=FAKE):
 
 
 def _backward(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
-    return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 17), ws, ws_bytes, None)
+    return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 21), ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("call", [_prologue, _forward, _backward])
@@ -70,6 +70,7 @@ def test_invalid_params_rejected(call):
     assert call(P(dq_mode=3)) == -3
     assert call(P(layout=2)) == -3
     assert call(P(layout=-1)) == -3
+    assert call(P(qk_gain=1, qk_norm=0)) == -3   # gains need QK-norm
     assert call(P(N=200)) == -2            # not a multiple of blk
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
@@ -130,9 +131,9 @@ def test_empty_is_a_noop():
 def test_backward_part_rejects_bad_part():
     p = P()
     for part in (-1, 3, 99):
-        assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 17), FAKE, 1 << 40, None) == -3
-    assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 17), FAKE, 1 << 40, None) == -3
-    assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 17), FAKE, 0, None) == -5
+        assert lib.sagebwd_backward_part(ctypes.byref(p), part, *([FAKE] * 21), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(P(d=96)), 0, *([FAKE] * 21), FAKE, 1 << 40, None) == -3
+    assert lib.sagebwd_backward_part(ctypes.byref(p), 1, *([FAKE] * 21), FAKE, 0, None) == -5
 
 
 def test_binding_rejects_host_tensors():
@@ -155,14 +156,14 @@ def test_q_smooth_arguments():
     # the query mean / key bias pointers are required with q_smooth and ignored (NULL is
     # fine) without; the prologue scratch grows by the queries' block sums
     def pro_with(p, qm, kb):
-        ptrs = [FAKE] * 12 + [qm, kb]
+        ptrs = [FAKE] * 12 + [qm, kb, FAKE, FAKE]
         return lib.sagebwd_quant_prologue(ctypes.byref(p), *ptrs, FAKE, 1 << 40, None)
     assert pro_with(P(q_smooth=1), 0, FAKE) == -1
     assert pro_with(P(q_smooth=1), FAKE, 0) == -1
     assert pro_with(P(q_smooth=1), MIS, FAKE) == -4
     fw = lambda p, kb: lib.sagebwd_forward(ctypes.byref(p), *([FAKE] * 6), kb, FAKE, FAKE, None)
     assert fw(P(q_smooth=1), 0) == -1
-    bw = lambda p, qm, kb: lib.sagebwd_backward(ctypes.byref(p), *([FAKE] * 9), qm, kb, *([FAKE] * 6),
+    bw = lambda p, qm, kb: lib.sagebwd_backward(ctypes.byref(p), *([FAKE] * 9), qm, kb, *([FAKE] * 10),
                                                 FAKE, 1 << 40, None)
     assert bw(P(q_smooth=1), 0, FAKE) == -1
     assert bw(P(q_smooth=1), FAKE, 0) == -1
@@ -171,5 +172,26 @@ def test_q_smooth_arguments():
     assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(q_smooth=1))) == 2 * part
     assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(P(q_smooth=1, k_smooth=0))) == part
     # the q_smooth-only scratch must still be passed
-    assert lib.sagebwd_quant_prologue(ctypes.byref(P(q_smooth=1, k_smooth=0)), *([FAKE] * 14), FAKE,
+    assert lib.sagebwd_quant_prologue(ctypes.byref(P(q_smooth=1, k_smooth=0)), *([FAKE] * 16), FAKE,
                                       part - 1, None) == -5
+
+
+def test_qk_gain_arguments():
+    # with qk_gain the gains (prologue, backward) and their gradients (backward) are required,
+    # and the backward workspace grows by the gains' partial sums
+    def pro_with(p, qg, kg):
+        return lib.sagebwd_quant_prologue(ctypes.byref(p), *([FAKE] * 14), qg, kg, FAKE, 1 << 40, None)
+    assert pro_with(P(qk_gain=1), 0, FAKE) == -1
+    assert pro_with(P(qk_gain=1), FAKE, 0) == -1
+    assert pro_with(P(qk_gain=1), MIS, FAKE) == -4
+
+    def bw(p, qg, kg, dqg, dkg):
+        return lib.sagebwd_backward(ctypes.byref(p), *([FAKE] * 11), qg, kg, *([FAKE] * 6), dqg, dkg,
+                                    FAKE, 1 << 40, None)
+    assert bw(P(qk_gain=1), 0, FAKE, FAKE, FAKE) == -1
+    assert bw(P(qk_gain=1), FAKE, FAKE, FAKE, 0) == -1
+    assert bw(P(qk_gain=1), FAKE, FAKE, MIS, FAKE) == -4
+    up = lambda x: (x + 255) // 256 * 256
+    base = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P()))
+    gains = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(qk_gain=1)))
+    assert gains == base + up(4 * 2 * 4 * 64) + up(4 * 2 * 4 * 64)   # N/64 and N/blk tiles of d floats
