@@ -33,7 +33,7 @@ class Params(ctypes.Structure):
         ("blk", ctypes.c_int32), ("causal", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
-        ("layout", ctypes.c_int32), ("qk_gain", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("qk_gain", ctypes.c_int32), ("normed_grads", ctypes.c_int32),
     ]
 
 

@@ -31,6 +31,7 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (!(p->eps >= 0.0f)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->layout != SAGEBWD_LAYOUT_BHND && p->layout != SAGEBWD_LAYOUT_BNHD) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->qk_gain && !p->qk_norm) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->normed_grads && (!p->qk_norm || p->qk_gain)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
   // (N * d * 4 < 2^31), grids in 2^31 workgroups
@@ -270,7 +271,8 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   }
   a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.x16 = strides16(p);
-  a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0; a.sm_scale = sm_scale_of(p);
+  // normed_grads: the epilogues stop before the RMSNorm backward
+  a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0 && !p->normed_grads; a.sm_scale = sm_scale_of(p);
   return hip_status(sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)), "sagebwd_backward");
 }
 

@@ -70,7 +70,8 @@ typedef enum {
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
                                    B*H > 2^24                                               */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
-                                   layout, eps < 0, qk_gain without qk_norm                 */
+                                   layout, eps < 0, qk_gain or normed_grads without
+                                   qk_norm, normed_grads with qk_gain                       */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
@@ -96,6 +97,9 @@ typedef struct {
                            head and channel (SageBwd article, QK-norm paragraph: RMSNorm per
                            token, here with its weight); the backward also returns their
                            gradients dq_gain, dk_gain [H,d] (sums over batch and tokens)     */
+  int32_t normed_grads; /* nonzero (with qk_norm, without qk_gain): the backward returns dQ,
+                           dK with respect to the normalised Q^, K^ (before smoothing) and
+                           leaves the RMSNorm backward to the caller                         */
 } sagebwd_params;
 
 /* Memory layout of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV; contiguous either way).
@@ -205,7 +209,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 
 /* Backward. Gradients are with respect to the RAW Q, K, V given to the prologue (the
- * RMSNorm backward is applied; K-smoothing adds no term because every row of dS sums to 0).
+ * RMSNorm backward is applied; K-smoothing adds no term because every row of dS sums to 0),
+ * or with normed_grads with respect to the normalised Q^, K^.
  *   Q, K, V       in : dtype [B,H,N,d], the prologue's inputs
  *   Qc, Kc, Qs, Ks, q_rstd, k_rstd in: the prologue's outputs
  *   q_mean, kbias in : the prologue's outputs with q_smooth (ignored, may be NULL, without)

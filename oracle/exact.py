@@ -50,8 +50,12 @@ def _gain_rows(g, lead, BH: int, d: int) -> np.ndarray:
 def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-6,
               sm_scale: Optional[float] = None, k_shift: Optional[np.ndarray] = None,
               row_block: int = 512, want_ds_stats: bool = False,
-              q_gain: Optional[np.ndarray] = None, k_gain: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+              q_gain: Optional[np.ndarray] = None, k_gain: Optional[np.ndarray] = None,
+              normed_grads: bool = False) -> Dict[str, np.ndarray]:
     """Exact attention on [..., N, d] float64 inputs; the backward runs when dO is given.
+
+    normed_grads: dQ, dK are the gradients with respect to the normalised Q^, K^ (the RMSNorm
+    backward is left to the caller).
 
     q_gain, k_gain: optional QK-norm gains [H, d] (the last leading axis of the inputs is H);
     with them the backward also returns dq_gain, dk_gain [H, d].
@@ -125,7 +129,9 @@ def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-
                 stats["ds_max"][:, r0:r1] = np.abs(dS).max(axis=-1)
     out = dict(O=O.reshape(lead + (N, d)), LSE=LSE.reshape(lead + (N,)))
     if have_bwd:
-        if qk_norm:
+        if qk_norm and normed_grads:
+            dq, dk = dqh, dkh
+        elif qk_norm:
             dq = rms_norm_backward(dqh * gq, qn, rq)
             dk = rms_norm_backward(dkh * gk, kn, rk)
             if q_gain is not None or k_gain is not None:

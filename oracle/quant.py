@@ -74,6 +74,7 @@ class Spec:
     bwd_pk: int = 16
     bwd_sk: Optional[int] = None
     q_smooth: bool = False
+    normed_grads: bool = False   # dQ, dK with respect to Q^, K^ (no RMSNorm backward)
 
     def __post_init__(self):
         blk = self.blk
@@ -456,7 +457,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     Kn, k_rstd) when QK-norm is on (Qn, Kn: the normalised tokens before the gains, K before
     smoothing; smoothing adds no term because every dS row sums to zero), then all three are
     rounded to the dtype. With gains, dq_gain = sum over batch and tokens of dQ^ o Qn (and
-    likewise dk_gain), float64 [H, d].
+    likewise dk_gain), float64 [H, d]. With spec.normed_grads the epilogue stops at dQ^, dK^
+    (the gradients with respect to the normalised tokens).
     With q_tiles / k_tiles only pairs whose I is in q_tiles (bwd_tq units) or whose J
     is in k_tiles (bwd_sk units) are visited: dQ is then exact for those query tiles,
     dK and dV for those key tiles, and NaN elsewhere.
@@ -517,7 +519,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             dQh[:, i0:i0 + tq, :] += (sm * sdS * ks[:, j0 // blk])[:, None, None] * (
                 qdS @ kc[:, j0:j0 + sk, :])
     gains = {}
-    if spec.qk_norm:
+    if spec.qk_norm and spec.normed_grads:
+        dQ, dK = dQh, dKh   # gradients with respect to Q^ = g o n and K^ (before smoothing)
+    elif spec.qk_norm:
         # with gains g: X^ = g o n, so dn = g o dX^ and dg = sum over batch and tokens of dX^ o n
         qg, kg = pro.get("q_gain"), pro.get("k_gain")
         Qn, Kn = _flat(pro.get("Qn", pro["Qhat"])), _flat(pro.get("Kn", pro["Khat"]))

@@ -26,12 +26,12 @@ def header_functions() -> list:
     return sorted(set(re.findall(r"^\s*(?:size_t|sagebwd_status|const char\*)\s+(sagebwd_\w+)\s*\(", text, re.M)))
 
 
-def spec_for(w: wl.Workload, dtype: Optional[str] = None) -> oq.Spec:
+def spec_for(w: wl.Workload, dtype: Optional[str] = None, normed_grads: bool = False) -> oq.Spec:
     c = header_constants()
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
                    fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
-                   bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth)
+                   bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth, normed_grads=normed_grads)
 
 
 def rel_l2(a, b) -> float:
@@ -56,10 +56,12 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 
 # ------------------------------------------------------------------------------- GPU side
 
-def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd", qk_gain: bool = False):
+def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd", qk_gain: bool = False,
+               normed_grads: bool = False):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                           dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout, qk_gain=qk_gain)
+                           dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout, qk_gain=qk_gain,
+                           normed_grads=normed_grads)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -76,7 +78,7 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
             pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd",
-            gains=None) -> Dict[str, np.ndarray]:
+            gains=None, normed_grads: bool = False) -> Dict[str, np.ndarray]:
     """Run the HIP path and return host copies (numpy) of everything it produced. With
     layout "bnhd" the 16-bit tensors are handed to the library as [B,N,H,d] (a transposed
     copy of the same values) and its O, dQ, dK, dV are returned transposed back. gains:
@@ -84,7 +86,7 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
     gradients come back as dq_gain, dk_gain."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w, dq_mode, layout, qk_gain=gains is not None)
+    p = params_for(w, dq_mode, layout, qk_gain=gains is not None, normed_grads=normed_grads)
     gq = gk = None
     if gains is not None:
         gq, gk = (torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda:0") for g in gains)

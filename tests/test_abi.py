@@ -13,7 +13,8 @@ lib = _lib.load()  # fails loudly if the library was not built
 
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
-                dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND, qk_gain=0)
+                dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND, qk_gain=0,
+                normed_grads=0)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -71,6 +72,8 @@ def test_invalid_params_rejected(call):
     assert call(P(layout=2)) == -3
     assert call(P(layout=-1)) == -3
     assert call(P(qk_gain=1, qk_norm=0)) == -3   # gains need QK-norm
+    assert call(P(normed_grads=1, qk_norm=0)) == -3
+    assert call(P(normed_grads=1, qk_gain=1)) == -3
     assert call(P(N=200)) == -2            # not a multiple of blk
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2

@@ -123,3 +123,21 @@ def test_repeat_calls_deterministic():
     d = gpu_run(w, x, dq_mode=2)
     assert np.array_equal(c["dK"], d["dK"]) and np.array_equal(c["dV"], d["dV"])
     assert rel_l2(c["dQ"], d["dQ"]) < 1e-3
+
+
+@pytest.mark.parametrize("dq_mode", [0, 2])
+def test_normed_grads(dq_mode):
+    """normed_grads: dQ, dK with respect to the normalised Q^, K^ meet the oracle's bar (O and
+    dV are the default run's, bit for bit)."""
+    w = W["n8192_d128"].with_shape(B=1, H=2, N=384)
+    print(f"[normed_grads] B{w.B} H{w.H} N{w.N} d{w.d} dq_mode={dq_mode}", flush=True)
+    x = host_inputs(w)
+    g = gpu_run(w, x, dq_mode=dq_mode, normed_grads=True)
+    base = gpu_run(w, x, dq_mode=dq_mode)
+    o = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec_for(w, normed_grads=True))
+    for k in ("O", "dV"):
+        assert np.array_equal(g[k], base[k]), k
+    errs = {k: rel_l2(g[k], o[k]) for k in ("dQ", "dK")}
+    print(f"[normed_grads] rel-L2 {errs}", flush=True)
+    for k, e in errs.items():
+        assert e <= 2e-3, (k, e)

@@ -205,3 +205,16 @@ def test_unit_gain_is_no_gain():
     b = exact.attention(Q, K, V, dO, causal=True, qk_norm=True, q_gain=np.ones((2, 8)), k_gain=np.ones((2, 8)))
     for k in ("O", "dQ", "dK", "dV"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_normed_grads_equal_attention_on_normalised_inputs(causal):
+    """The gradients with respect to Q^ = RMSNorm(Q), K^ (normed_grads) are those of plain
+    attention (QK-norm off, itself pinned by finite differences) applied to Q^, K^."""
+    rng = np.random.default_rng(101 + causal)
+    Q, K, V, dO = (_rand(rng, 1, 2, 11, 8) for _ in range(4))
+    a = exact.attention(Q, K, V, dO, causal=causal, qk_norm=True, normed_grads=True)
+    qh, kh = exact.rms_norm(Q, 1e-6)[0], exact.rms_norm(K, 1e-6)[0]
+    b = exact.attention(qh, kh, V, dO, causal=causal, qk_norm=False)
+    for k in ("O", "dQ", "dK", "dV"):
+        assert np.allclose(a[k], b[k], rtol=1e-12, atol=1e-14), k

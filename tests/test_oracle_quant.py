@@ -462,3 +462,21 @@ def test_gain_planted_mistake_is_caught(monkeypatch):
                           dO.astype(np.float64), causal=True, qk_norm=True, eps=spec.eps,
                           q_gain=gq.astype(np.float64), k_gain=gk.astype(np.float64))
     assert _rel(got["dQ"], ref["dQ"]) > 1e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_quant_normed_grads(causal):
+    """normed_grads with identity quantisers: the gradients with respect to Q^, K^ of exact
+    attention (and the RMSNorm backward of them is the default output)."""
+    rng = np.random.default_rng(111 + causal)
+    B, H, N, d = 1, 2, 128, 32
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64", normed_grads=True)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    ref = exact.attention(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), dO.astype(np.float64),
+                          causal=causal, qk_norm=True, eps=spec.eps, normed_grads=True)
+    for name in ("O", "dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 3e-6, name
+    full = oq.run(Q, K, V, dO, oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64"),
+                  tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    assert _rel(got["dQ"], full["dQ"]) > 1e-2     # the RMSNorm backward does change dQ
