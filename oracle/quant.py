@@ -86,8 +86,13 @@ class Spec:
                 raise ValueError(f"{name}={v} must divide blk={blk}")
         if sk % self.bwd_pk != 0:
             raise ValueError("bwd_pk must divide bwd_sk")
-        if self.N % blk != 0:
-            raise ValueError("N must be a multiple of blk")
+        if self.N < 1:
+            raise ValueError("N must be positive")
+
+    @property
+    def Np(self) -> int:
+        """N rounded up to whole blocks: the last block of a head holds N - (Np - blk) tokens."""
+        return -(-self.N // self.blk) * self.blk
 
     @property
     def scale(self) -> float:
@@ -170,7 +175,7 @@ def rms_norm_f32(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
     return x * rstd[..., None], rstd
 
 
-def k_smooth_f32(khat: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
+def k_smooth_f32(khat: np.ndarray, blk: int, n_valid: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """K-smoothing: K~ = K^ - mu, mu = per-channel mean of K^ over the N tokens of a head.
 
     Order: inside each block of blk tokens (a power of two), token t joins group t mod G,
@@ -178,7 +183,9 @@ def k_smooth_f32(khat: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
     the G group sums (tree_f32); then tot = sum of the
     parts in ascending block order (from 0); mu = fl(tot / N); K~ = fl(K^ - mu). The
     pages fix no order; this is the one the GPU's 16 token slots per pass compute.
-    Input [..., N, d]; returns (K~, mu [..., d]).
+    Input [..., Np, d] with Np a multiple of blk; with n_valid < Np the rows from n_valid on
+    are padding (zeros, which add nothing to the sums): mu = fl(tot / n_valid) and those
+    rows of K~ are 0. Returns (K~, mu [..., d]).
     SageBwd article, K-smoothing paragraph (axis: see module docstring).
     Pinned by: test_oracle_quant.py::test_k_smooth_* and the softmax-invariance tests.
     """
@@ -194,8 +201,12 @@ def k_smooth_f32(khat: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
     tot = np.zeros(khat.shape[:-2] + (d,), dtype=F32)
     for b in range(nb):
         tot = tot + part[..., b, :]
-    mu = tot / F32(N)
-    return khat - mu[..., None, :], mu
+    nv = N if n_valid is None else n_valid
+    mu = tot / F32(nv)
+    kt = khat - mu[..., None, :]
+    if nv < N:
+        kt[..., nv:, :] = F32(0.0)
+    return kt, mu
 
 
 def quant_rule_f32(x32: np.ndarray, axes: Tuple[int, ...]) -> Tuple[np.ndarray, np.ndarray]:
@@ -242,6 +253,18 @@ def identity_block_quant(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarra
     return x, np.ones(x.shape[:-2] + (x.shape[-2] // blk,), dtype=np.float64)
 
 
+def _pad_rows(x: np.ndarray, Np: int, value: float = 0.0) -> np.ndarray:
+    """x [..., n, ...] (rows on axis -2 for 4-d tensors, the last axis for [B,H,n]) padded
+    with `value` to Np rows."""
+    axis = -2 if x.ndim == 4 else -1
+    n = x.shape[axis]
+    if n == Np:
+        return x
+    width = [(0, 0)] * x.ndim
+    width[axis] = (0, Np - n)
+    return np.pad(x, width, constant_values=value)
+
+
 def apply_gain_f32(xn: np.ndarray, g: Optional[np.ndarray]) -> np.ndarray:
     """The QK-norm gain: x^ = fl(n * g[h, c]) for n [B,H,N,d] (the normalised tokens) and
     g [H, d] float32 (one IEEE product per element); g None leaves n unchanged (gain 1)."""
@@ -263,9 +286,9 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
     tokens before the gain Qn, Kn and after it Qhat, Khat (float32), which the RMSNorm
     backward and the gains' gradients need, and the gains (q_gain, k_gain; None = 1).
     """
-    Q = np.asarray(Q, dtype=F32)
-    K = np.asarray(K, dtype=F32)
-    V = np.asarray(V, dtype=F32)
+    # a ragged last block: pad every head to Np rows with zero tokens, which change no block
+    # absmax and no sum; the means divide by the N valid tokens (k_smooth_f32)
+    Q, K, V = (_pad_rows(np.asarray(x, dtype=F32), spec.Np) for x in (Q, K, V))
     if spec.qk_norm:
         Qn, q_rstd = rms_norm_f32(Q, spec.eps)
         Kn, k_rstd = rms_norm_f32(K, spec.eps)
@@ -277,13 +300,13 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
         Kh, k_rstd = K, np.ones(K.shape[:-1], dtype=F32)
         Qn, Kn = Qh, Kh
     if spec.k_smooth:
-        Kt, mu = k_smooth_f32(Kh, spec.blk)
+        Kt, mu = k_smooth_f32(Kh, spec.blk, spec.N)
     else:
         Kt, mu = Kh, np.zeros(K.shape[:-2] + (K.shape[-1],), dtype=F32)
     if spec.q_smooth:
         # Q-smoothing (SageBwd article, Q-smoothing paragraph): the queries' per-channel mean,
         # taken like the keys' (same order), is subtracted before quantising
-        Qt, mu_q = k_smooth_f32(Qh, spec.blk)
+        Qt, mu_q = k_smooth_f32(Qh, spec.blk, spec.N)
     else:
         Qt, mu_q = Qh, np.zeros(Q.shape[:-2] + (Q.shape[-1],), dtype=F32)
     Qc, Qs = block_quant(Qt, spec.blk)
@@ -359,6 +382,8 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
       m   = m'
     then O = acc / l (rounded to the dtype) and LSE = m + ln l (natural log, float32).
     Codes may be given as integers or, with identity_tile_quant, as real values.
+    With a ragged last block (spec.N < Np rows of codes) keys from N on are masked and the
+    padding query rows take no part in any tile (their P~ is 0).
     Returns (O [B,H,N,d] float64 of dtype-rounded values, LSE [B,H,N] float32); with
     q_tiles only those query tiles are computed (rows of other tiles are NaN).
     Pinned by: test_oracle_quant.py identity and lossless reductions to oracle.exact.
@@ -366,6 +391,7 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
     B, H, N, d = Qc.shape
     blk, tq, tk = spec.blk, spec.fwd_tq, spec.tk
     sm = spec.scale
+    nv = spec.N
     q = _flat(Qc).astype(np.float64)
     k = _flat(Kc).astype(np.float64)
     v = _flat(Vc).astype(np.float64)
@@ -395,18 +421,21 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
                 s = s + sm * kb[:, None, j0:j0 + tk]
             if spec.causal:
                 s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
+            s = np.where(cols[None, None, :] >= nv, -np.inf, s)
             m_new = np.maximum(m, s.max(axis=-1))
             Pt = np.exp(s - m_new[..., None])
+            Pt = np.where(rows[None, :, None] < nv, Pt, 0.0)
             alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
             l = l * alpha + Pt.sum(axis=-1)
             qP, sP = tile_quant(Pt)
             pv = qP @ v[:, j0:j0 + tk, :]
             acc = acc * alpha[..., None] + (sP * vs[:, j0 // blk])[:, None, None] * pv
             m = m_new
-        O[:, i0:i0 + tq, :] = acc / l[..., None]
-        LSE[:, i0:i0 + tq] = m + np.log(l)
+        with np.errstate(divide="ignore", invalid="ignore"):   # padding rows: l = 0, dropped below
+            O[:, i0:i0 + tq, :] = acc / l[..., None]
+            LSE[:, i0:i0 + tq] = m + np.log(l)
     O = round_to_dtype(O, spec.dtype)
-    return O.reshape(B, H, N, d), LSE.astype(F32).reshape(B, H, N)
+    return O.reshape(B, H, N, d)[:, :, :nv], LSE.astype(F32).reshape(B, H, N)[:, :, :nv]
 
 
 def backward_pre(O, dO, spec: Spec, block_quant: BlockQuant = quant_blocks_f32):
@@ -467,6 +496,11 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     B, H, N, d = pro["Qc"].shape
     blk, tq, sk, pk = spec.blk, spec.bwd_tq, spec.sk, spec.bwd_pk
     sm = spec.scale
+    # a ragged last block: the padding rows (from spec.N on) are zero tokens with LSE = +inf,
+    # so their P is 0, and keys from spec.N on are masked
+    nv = spec.N
+    V, dO, O = (_pad_rows(np.asarray(x), N) for x in (V, dO, O))
+    LSE = _pad_rows(np.asarray(LSE, dtype=F32), N, np.inf)
     D, dOc, dOs = backward_pre(O, dO, spec, block_quant=block_quant)
     qc = _flat(pro["Qc"]).astype(np.float64)
     kc = _flat(pro["Kc"]).astype(np.float64)
@@ -504,6 +538,7 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
                 s = s + sm * kb[:, None, j0:j0 + sk]
             if spec.causal:
                 s = np.where(cols[None, None, :] > rows[None, :, None], -np.inf, s)
+            s = np.where(cols[None, None, :] >= nv, -np.inf, s)
             P = np.exp(s - lse[:, i0:i0 + tq, None])
             dP = do[:, i0:i0 + tq, :] @ vf[:, j0:j0 + sk, :].transpose(0, 2, 1)
             dS = P * (dP - Df[:, i0:i0 + tq, None])
@@ -547,9 +582,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
         dK = np.where(kmask[None, :, None], dK, np.nan)
         dV = np.where(kmask[None, :, None], dV, np.nan)
     out = dict(
-        dQ=round_to_dtype(dQ, spec.dtype).reshape(B, H, N, d),
-        dK=round_to_dtype(dK, spec.dtype).reshape(B, H, N, d),
-        dV=round_to_dtype(dV, spec.dtype).reshape(B, H, N, d),
+        dQ=round_to_dtype(dQ, spec.dtype).reshape(B, H, N, d)[:, :, :nv],
+        dK=round_to_dtype(dK, spec.dtype).reshape(B, H, N, d)[:, :, :nv],
+        dV=round_to_dtype(dV, spec.dtype).reshape(B, H, N, d)[:, :, :nv],
         D=D, dOc=dOc, dOs=dOs,
     )
     out.update(gains)

@@ -480,3 +480,47 @@ def test_identity_quant_normed_grads(causal):
     full = oq.run(Q, K, V, dO, oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64"),
                   tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
     assert _rel(got["dQ"], full["dQ"]) > 1e-2     # the RMSNorm backward does change dQ
+
+
+# ------------------------------------------------------------------- ragged N (N % blk != 0)
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,blk,tiles", [(100, 64, {}), (200, 128, dict(fwd_tk=64, bwd_tq=64, bwd_sk=64)),
+                                         (65, 64, {})])
+def test_identity_quant_ragged_n(causal, N, blk, tiles):
+    """A last block holding N mod blk tokens: with identity quantisers the tiled path equals
+    exact attention on the N tokens (the padding keys are masked, the padding queries take no
+    part), with QK-norm and K-smoothing on."""
+    rng = np.random.default_rng(121 + N + causal)
+    B, H, d = 1, 2, 32
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    K = (K + 3 * rng.standard_normal((1, H, 1, d))).astype(F32)
+    spec = oq.Spec(N=N, d=d, blk=blk, causal=causal, qk_norm=True, k_smooth=True, dtype="f64", **tiles)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    for name in ("O", "dQ", "dK", "dV"):
+        assert got[name].shape == (B, H, N, d), name
+        assert _rel(got[name], ref[name]) < 3e-6, name
+    assert got["Qc"].shape == (B, H, spec.Np, d)
+
+
+def test_ragged_block_quant_is_the_rule_on_valid_tokens():
+    """The ragged last block's codes and scale are the INT8 rule over its valid tokens alone;
+    the padding rows hold code 0; the K mean is over the N tokens and leaves the padding 0."""
+    rng = np.random.default_rng(131)
+    B, H, N, d, blk = 1, 2, 150, 16, 64
+    Q, K, V = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(3))
+    spec = oq.Spec(N=N, d=d, blk=blk, causal=True, qk_norm=True, k_smooth=True)
+    pro = oq.prologue(Q, K, V, spec)
+    Np = spec.Np
+    assert Np == 192
+    last = slice(128, N)
+    qv, sv = oq.quant_rule_f32(V[:, :, last, :], axes=(2, 3))
+    np.testing.assert_array_equal(pro["Vc"][:, :, last, :], qv)
+    np.testing.assert_array_equal(pro["Vs"][:, :, 2], sv)
+    assert not np.any(pro["Vc"][:, :, N:, :]) and not np.any(pro["Kc"][:, :, N:, :]) and not np.any(pro["Qc"][:, :, N:, :])
+    kt = pro["Kc"].astype(np.float64) * np.repeat(pro["Ks"], blk, axis=-1)[..., None]
+    # the smoothed keys average to ~0 over the valid tokens (up to the INT8 rounding)
+    assert np.max(np.abs(kt[:, :, :N].mean(axis=2))) < 0.02
+    kh = oq.rms_norm_f32(K, spec.eps)[0].astype(np.float64)
+    assert np.allclose(pro["k_mean"], kh.mean(axis=2), atol=1e-6)
