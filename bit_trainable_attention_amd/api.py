@@ -64,11 +64,16 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def padded_n(p: _lib.Params) -> int:
+    """Tokens per head of the library's own arrays: N rounded up to whole blocks."""
+    return -(-p.N // p.blk) * p.blk
+
+
 def _shapes(p: _lib.Params):
-    bhnd = (p.B, p.H, p.N, p.d)
-    x16 = (p.B, p.N, p.H, p.d) if p.layout == _lib.LAYOUT_BNHD else bhnd
-    return dict(x=bhnd, x16=x16, xt=(p.B, p.H, p.d, p.N), s=(p.B, p.H, p.N // p.blk), r=(p.B, p.H, p.N),
-                m=(p.B, p.H, p.d))
+    Np = padded_n(p)
+    x16 = (p.B, p.N, p.H, p.d) if p.layout == _lib.LAYOUT_BNHD else (p.B, p.H, p.N, p.d)
+    return dict(x=(p.B, p.H, Np, p.d), x16=x16, xt=(p.B, p.H, p.d, Np), s=(p.B, p.H, Np // p.blk),
+                r=(p.B, p.H, Np), m=(p.B, p.H, p.d))
 
 
 def sagebwd_prologue_workspace_bytes(p: _lib.Params) -> int:
@@ -89,10 +94,10 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     """Byte offsets of the backward workspace regions, as documented in include/sagebwd.h."""
     def up(x):
         return (x + 255) // 256 * 256
-    bh, nt, nb = p.B * p.H, p.N // 64, p.N // p.blk
+    bh, nt, nb = p.B * p.H, padded_n(p) // 64, padded_n(p) // p.blk
     r = p.blk // 64
     tiles = nb * nt - r * nb * (nb - 1) // 2 if p.causal else nb * nt
-    off = {"packet_bytes": PACKET_BYTES[p.d], "packets": 0, "tiles_per_head": tiles}
+    off = {"packet_bytes": PACKET_BYTES[p.d], "packets": 0, "tiles_per_head": tiles, "tiles_per_head_q": nt}
     after = up(bh * nt * PACKET_BYTES[p.d])
     ktp, dsp, dsm = up(bh * nb * p.d * p.blk), up(bh * tiles * 64 * p.blk), up(bh * tiles * (p.blk // 64) * 4)
     spill = p.dq_mode == 1 or (p.dq_mode == 0 and ktp + dsp + dsm <= SPILL_LIMIT)
@@ -104,7 +109,7 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
         off["total"] = after + ktp + dsp + dsm
     else:
         off["dq_acc"] = after
-        off["total"] = after + up(4 * bh * p.N * p.d)
+        off["total"] = after + up(4 * bh * padded_n(p) * p.d)
     if p.qk_gain:
         off["gq"] = off["total"]
         off["gk"] = off["gq"] + up(4 * bh * nt * p.d)

@@ -32,15 +32,24 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->layout != SAGEBWD_LAYOUT_BHND && p->layout != SAGEBWD_LAYOUT_BNHD) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->qk_gain && !p->qk_norm) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->normed_grads && (!p->qk_norm || p->qk_gain)) return SAGEBWD_ERR_UNSUPPORTED;
-  if (p->N % p->blk != 0) return SAGEBWD_ERR_SHAPE;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
-  // (N * d * 4 < 2^31), grids in 2^31 workgroups
+  // (Np * d * 4 < 2^31), grids in 2^31 workgroups
   if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 22)) return SAGEBWD_ERR_SHAPE;
-  if ((long long)p->B * p->H * (p->N / p->blk) * 3 >= (1LL << 31)) return SAGEBWD_ERR_SHAPE;
+  if ((long long)p->B * p->H * ((p->N + p->blk - 1) / p->blk) * 3 >= (1LL << 31)) return SAGEBWD_ERR_SHAPE;
   return SAGEBWD_OK;
 }
 
 bool empty(const sagebwd_params* p) { return p->B == 0 || p->H == 0 || p->N == 0; }
+
+// Tokens per head of the library's own arrays: N rounded up to whole quantisation blocks.
+int padded_n(const sagebwd_params* p) { return (p->N + p->blk - 1) / p->blk * p->blk; }
+
+// The parameters with N replaced by the padded length (for sizes and grids).
+sagebwd_params padded(const sagebwd_params* p) {
+  sagebwd_params q = *p;
+  q.N = padded_n(p);
+  return q;
+}
 
 sagebwd::Strides16 strides16(const sagebwd_params* p) {
   const long long d = p->d, N = p->N, H = p->H;
@@ -48,7 +57,7 @@ sagebwd::Strides16 strides16(const sagebwd_params* p) {
   return {H * N * d, N * d, (int)d, p->H};
 }
 
-size_t elems(const sagebwd_params* p) { return (size_t)p->B * p->H * p->N * p->d; }
+size_t elems(const sagebwd_params* p) { return (size_t)p->B * p->H * padded_n(p) * p->d; }
 
 float sm_scale_of(const sagebwd_params* p) {
   return p->sm_scale > 0.0f ? p->sm_scale : 1.0f / __builtin_sqrtf((float)p->d);
@@ -71,7 +80,9 @@ struct BwdLayout {
   size_t pk, dq, ktp, dsp, dsm, gq, gk, total;
 };
 
-BwdLayout bwd_layout(const sagebwd_params* p) {
+BwdLayout bwd_layout(const sagebwd_params* praw) {
+  const sagebwd_params pp = padded(praw);
+  const sagebwd_params* p = &pp;
   BwdLayout L{};
   const size_t bh = (size_t)p->B * p->H;
   L.pk = 0;
@@ -106,7 +117,7 @@ BwdLayout bwd_layout(const sagebwd_params* p) {
 // Prologue scratch: the keys' per-block channel sums (K-smoothing), then the queries'
 // (Q-smoothing), each 256-byte aligned.
 size_t prologue_part_bytes(const sagebwd_params* p) {
-  return round_up(4 * (size_t)p->B * p->H * (p->N / p->blk) * p->d);
+  return round_up(4 * (size_t)p->B * p->H * (padded_n(p) / p->blk) * p->d);
 }
 
 }  // namespace
@@ -187,7 +198,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
     a.kbias = kbias;
     a.qpart = reinterpret_cast<float*>(ws + (p->k_smooth ? prologue_part_bytes(p) : 0));
   }
-  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.x16 = strides16(p);
   a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.q_smooth = p->q_smooth != 0;
   a.eps = p->eps;
@@ -208,7 +219,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
   a.q_smooth = p->q_smooth != 0;
   a.kbias = a.q_smooth ? kbias : nullptr;
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
-  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.x16 = strides16(p);
   a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
   return hip_status(sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)), "sagebwd_forward");
@@ -269,7 +280,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   } else {
     a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
   }
-  a.BH = p->B * p->H; a.N = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
   a.x16 = strides16(p);
   // normed_grads: the epilogues stop before the RMSNorm backward
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0 && !p->normed_grads; a.sm_scale = sm_scale_of(p);

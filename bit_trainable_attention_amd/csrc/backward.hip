@@ -156,13 +156,18 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * j + k;                       // token inside the tile
       const size_t tok = tok0 + kPq * q + r;
-      const size_t row16 = a.x16.row(bh, blk_id * BLK + kPq * q + r);
+      const int n = blk_id * BLK + kPq * q + r;      // token of the head
+      const bool valid = n < a.Nv;                   // (padding of a ragged last block: zeros)
+      const size_t row16 = a.x16.row(bh, valid ? n : 0);
       const unsigned short* dsrc = a.dO + row16 + c0;
       const unsigned short* osrc = a.O + row16 + c0;
       float part = 0.0f;
       if constexpr (CW == 8) {
-        const u16x8 dv = *reinterpret_cast<const u16x8*>(dsrc);
-        const u16x8 ov = *reinterpret_cast<const u16x8*>(osrc);
+        u16x8 dv = u16x8{}, ov = u16x8{};
+        if (valid) {
+          dv = *reinterpret_cast<const u16x8*>(dsrc);
+          ov = *reinterpret_cast<const u16x8*>(osrc);
+        }
         *reinterpret_cast<u16x8*>(pk + P::bDO + r * 2 * D + 16 * swz_do<D>(r, ch)) = dv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -170,8 +175,11 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
           part = __builtin_fmaf(x[q][k][i], to_f32<DT>(ov[i]), part);
         }
       } else {
-        const u16x4 dv = *reinterpret_cast<const u16x4*>(dsrc);
-        const u16x4 ov = *reinterpret_cast<const u16x4*>(osrc);
+        u16x4 dv = u16x4{}, ov = u16x4{};
+        if (valid) {
+          dv = *reinterpret_cast<const u16x4*>(dsrc);
+          ov = *reinterpret_cast<const u16x4*>(osrc);
+        }
         *reinterpret_cast<u16x4*>(pk + P::bDO + r * 2 * D + 16 * swz_do<D>(r, ch >> 1) + 8 * (ch & 1)) = dv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -184,7 +192,8 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
       const float dsum = row_sum16(part);
       if (ch == 0) {
         reinterpret_cast<float*>(pk + P::bDV)[r] = dsum;
-        reinterpret_cast<float*>(pk + P::bLSE)[r] = a.lse[tok] * kLog2e;
+        // a padding query gets lse = +inf, so its P = 2^(s - lse) is 0 everywhere
+        reinterpret_cast<float*>(pk + P::bLSE)[r] = valid ? a.lse[tok] * kLog2e : INFINITY;
       }
     }
   }
@@ -363,9 +372,11 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
   for (int c = 0; c < KCH; ++c) kreg[c] = *reinterpret_cast<const i32x4*>(a.Kc + (hrow + key) * D + 64 * c + 16 * g);
   u16x8 vreg[HCH];
-  const size_t krow16 = a.x16.row(bh, key);   // this lane's key row of the 16-bit tensors
+  const bool kvalid = key < a.Nv;              // (padding keys of a ragged last block: zeros)
+  const size_t krow16 = a.x16.row(bh, kvalid ? key : 0);   // this lane's key row of the 16-bit tensors
 #pragma unroll
-  for (int c = 0; c < HCH; ++c) vreg[c] = *reinterpret_cast<const u16x8*>(a.V + krow16 + 32 * c + 8 * g);
+  for (int c = 0; c < HCH; ++c)
+    vreg[c] = kvalid ? *reinterpret_cast<const u16x8*>(a.V + krow16 + 32 * c + 8 * g) : u16x8{};
   if constexpr (!SPILL) {
     // K^T codes of the block for dQ = dS K: [D][BLK], chunk j of row c at slot swz<BLK>(c, j)
     for (int ch = tid; ch < BLK * D / 16; ch += NT) {
@@ -476,7 +487,7 @@ void bwd_main(BackwardArgs a) {
     for (int r = 0; r < 4; ++r) {
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], c2, QS ? kb2 - lse2[r] : -lse2[r]));
       if constexpr (decltype(masked)::value) {
-        if (key > q0 + 16 * t + 4 * g + r) p = 0.0f;
+        if ((a.causal && key > q0 + 16 * t + 4 * g + r) || !kvalid) p = 0.0f;
       }
       pf[t][r] = p;
       dsf[t][r] = p * (dp[t][r] - dvv[r]);
@@ -597,7 +608,8 @@ void bwd_main(BackwardArgs a) {
       const int step = qt - qt0;
       const int bofs = (step & 1) * L::kBuf;   // byte offset of this tile's buffer
       phase_sdp(bofs);
-      if (a.causal && k0 + 16 * w + 15 > q0) {   // diagonal tiles: mask keys above the queries
+      // diagonal tiles mask keys above the queries; the waves holding padding keys mask those
+      if ((a.causal && k0 + 16 * w + 15 > q0) || k0 + 16 * w + 15 >= a.Nv) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) elem_tile(lds + bofs, t, q0, std::true_type{});
       } else {
@@ -682,12 +694,14 @@ void bwd_main(BackwardArgs a) {
     }
   }
   unsigned short* dvrow = a.dV + krow16;
+  if (kvalid) {
 #pragma unroll
-  for (int n = 0; n < NCT; ++n) {
-    u16x4 v;
+    for (int n = 0; n < NCT; ++n) {
+      u16x4 v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dv[n][r]);
-    *reinterpret_cast<u16x4*>(dvrow + 16 * n + 4 * g) = v;
+      for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dv[n][r]);
+      *reinterpret_cast<u16x4*>(dvrow + 16 * n + 4 * g) = v;
+    }
   }
   unsigned short* dkrow = a.dK + krow16;
   if (a.qk_norm) {
@@ -700,7 +714,7 @@ void bwd_main(BackwardArgs a) {
     float dot = 0.0f;
 #pragma unroll
     for (int n = 0; n < NCT; ++n) {
-      const u16x4 kv = *reinterpret_cast<const u16x4*>(krow + 16 * n + 4 * g);
+      const u16x4 kv = kvalid ? *reinterpret_cast<const u16x4*>(krow + 16 * n + 4 * g) : u16x4{};
       f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f};
       if (gain) gv = *reinterpret_cast<const f32x4*>(gain + 16 * n + 4 * g);
 #pragma unroll
@@ -740,12 +754,14 @@ void bwd_main(BackwardArgs a) {
       }
     }
   }
+  if (kvalid) {
 #pragma unroll
-  for (int n = 0; n < NCT; ++n) {
-    u16x4 v;
+    for (int n = 0; n < NCT; ++n) {
+      u16x4 v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dk[n][r]);
-    *reinterpret_cast<u16x4*>(dkrow + 16 * n + 4 * g) = v;
+      for (int r = 0; r < 4; ++r) v[r] = from_f32<DT>(dk[n][r]);
+      *reinterpret_cast<u16x4*>(dkrow + 16 * n + 4 * g) = v;
+    }
   }
 }
 
@@ -772,6 +788,7 @@ __device__ __forceinline__ void dq_tile_epilogue(const BackwardArgs& a, int bh, 
     gp[i] = 0.0f;
   }
   for (int r = threadIdx.x / CPR; r < kPq; r += RPP) {
+    if (q0 + r >= a.Nv) break;   // padding rows of a ragged last block (and every later row)
     const size_t tok = hrow + q0 + r;
     const size_t row16 = a.x16.row(bh, q0 + r);
     float v[8];

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
   const int w = wave_id(), l = lane_id(), g = l >> 5, lq = l & 31;
   const int q0 = qt * kRowsPerBlock;
   const int q0w = q0 + w * kRowsPerWave;
-  const bool active = q0w < a.N;
+  const bool active = q0w < a.Nv;   // (rows from Nv on are the padding of a ragged last block)
   const int qrow = q0w + lq;  // this lane's query row
 
   // Q codes of this lane's query, as the B operand (contraction slots 16g..16g+15 of each
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
     const int8_t* kl = lds[kt & 1];
     const int8_t* vl = lds[kt & 1] + L::kBytesK;
     // One key tile. DIAG: the tile crosses this wave's causal diagonal (keys above it are
-    // masked); every other visited tile is wholly visible and carries no masking work.
+    // masked) or holds padding keys (from Nv on, a ragged last block); every other visited
+    // tile is wholly visible and carries no masking work.
     auto tile = [&](auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
       // (LLVM's interleaving strategy 1 on this block and on the PV block: measured 1-5%
@@ -188,7 +189,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
             for (int i = 0; i < 4; ++i) {
               float v = __builtin_fmaf((float)s[t][4 * j + i], cq, bq[i]);
               if constexpr (DIAG) {
-                if (k0 + 32 * t + 8 * j + 4 * g + i > qrow) v = -INFINITY;
+                const int key = k0 + 32 * t + 8 * j + 4 * g + i;
+                if ((a.causal && key > qrow) || key >= a.Nv) v = -INFINITY;
               }
               tf[t][4 * j + i] = v;
               fm = fmaxf(fm, v);
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-              if (key > qrow) s[t][r] = INT32_MIN;
+              if ((a.causal && key > qrow) || key >= a.Nv) s[t][r] = INT32_MIN;
             }
         }
         int rmax = INT32_MIN;
@@ -226,7 +228,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       // P~ tile absmax a = max over rows of 2^(rowmax - m'); in log2 it is one wave max.
       // The quantisation factor 127/a is folded into the exponent, so the exponential
       // yields P~ * 127/a directly and its nearest-even integer is the code.
-      const float pa_log = wave_max(rowmax - m_new);
+      // (padding rows of a ragged last block take no part in the tile's absmax)
+      const float pa_log = wave_max(qrow < a.Nv ? rowmax - m_new : -INFINITY);
       const float bias = kLog2_127 - pa_log - m_new;
       const float sP = __builtin_amdgcn_exp2f(pa_log) * (1.0f / 127.0f);
 
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       mo = mo_new;
     };
     if (active && (!a.causal || k0 <= q0w + kRowsPerWave - 1)) {
-      if (a.causal && k0 + BLK - 1 > q0w) tile(std::true_type{});
+      if ((a.causal && k0 + BLK - 1 > q0w) || k0 + BLK > a.Nv) tile(std::true_type{});
       else tile(std::false_type{});
     }
     wait_vmcnt<0>();   // the next tile's copies (the only vector-memory operations in the loop)
@@ -300,6 +303,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 
   if (!active) return;
   const float ltot = lsum_run + __shfl_xor(lsum_run, 32);
+  if (qrow >= a.Nv) return;   // padding rows: nothing to store
   const float linv = 1.0f / ltot;
   unsigned short* orow = a.O + a.x16.row(bh, qrow);
 #pragma unroll

@@ -33,6 +33,7 @@ struct PrologueArgs {
   int BH, N, D, BLK, dtype;
   int qk_norm, k_smooth, q_smooth;
   float eps;
+  int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 
@@ -45,6 +46,7 @@ struct ForwardArgs {
   int BH, N, D, BLK, dtype;
   int causal, q_smooth;
   float sm_scale;
+  int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 
@@ -69,6 +71,7 @@ struct BackwardArgs {
   int BH, N, D, BLK, dtype;
   int causal, qk_norm, q_smooth;
   float sm_scale;
+  int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 

@@ -63,13 +63,26 @@ __device__ __forceinline__ void load_chunk(const unsigned short* __restrict__ sr
   }
 }
 
-// blk_src: the block's first token row; rows are sn elements apart
+// blk_src: the block's first token row; rows are sn elements apart; rows from nvalid on
+// (a ragged last block) are zero tokens and are not read
 template <int DT, int D, int BLK>
-__device__ __forceinline__ void load_slice(const unsigned short* __restrict__ blk_src, int sn, Slice<D, BLK>& s,
-                                           int j, int ch) {
+__device__ __forceinline__ void load_slice(const unsigned short* __restrict__ blk_src, int sn, int nvalid,
+                                           Slice<D, BLK>& s, int j, int ch) {
+  if (nvalid >= BLK) {   // a whole block (uniform branch): unguarded loads
 #pragma unroll
-  for (int p = 0; p < Slice<D, BLK>::P; ++p)
-    load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * sn + ch * Slice<D, BLK>::CW, s.x[p]);
+    for (int p = 0; p < Slice<D, BLK>::P; ++p)
+      load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * sn + ch * Slice<D, BLK>::CW, s.x[p]);
+    return;
+  }
+#pragma unroll
+  for (int p = 0; p < Slice<D, BLK>::P; ++p) {
+    if (16 * p + j < nvalid) {
+      load_chunk<DT, Slice<D, BLK>::CW>(blk_src + (size_t)(16 * p + j) * sn + ch * Slice<D, BLK>::CW, s.x[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Slice<D, BLK>::CW; ++i) s.x[p][i] = 0.0f;
+    }
+  }
 }
 
 // Sum of the 16 lanes of each row by the pairwise tree (xor 1, xor 2, half mirror, mirror).
@@ -182,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
   S s;
-  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + a.x16.row(bh, blk_id * BLK), a.x16.sn, s,
-                         j, ch);
+  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + a.x16.row(bh, blk_id * BLK), a.x16.sn,
+                         a.Nv - blk_id * BLK, s, j, ch);
 
   if (tensor == 2) {
     // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token].
@@ -284,15 +297,15 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
   const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
   S s;
-  load_slice<DT, D, BLK>((is_q ? a.Q : a.K) + a.x16.row(bh, blk_id * BLK), a.x16.sn, s, j, ch);
+  load_slice<DT, D, BLK>((is_q ? a.Q : a.K) + a.x16.row(bh, blk_id * BLK), a.x16.sn, a.Nv - blk_id * BLK, s, j, ch);
   // mean of the head's keys (or queries) per channel; every workgroup of the head computes the
   // same value, the one of block 0 stores it
   const bool smooth = is_q || a.k_smooth;
   if (smooth) {
-    head_mean<D>((is_q ? a.qpart : a.kpart) + (size_t)bh * nb * D, nb, a.N, mean);
+    head_mean<D>((is_q ? a.qpart : a.kpart) + (size_t)bh * nb * D, nb, a.Nv, mean);
     if (blk_id == 0 && threadIdx.x < D) (is_q ? a.q_mean : a.k_mean)[(size_t)bh * D + threadIdx.x] = mean[threadIdx.x];
   }
-  if (!is_q && a.q_smooth) head_mean<D>(a.qpart + (size_t)bh * nb * D, nb, a.N, qmean);
+  if (!is_q && a.q_smooth) head_mean<D>(a.qpart + (size_t)bh * nb * D, nb, a.Nv, qmean);
   __syncthreads();
   float mu[S::CW], gn[S::CW];
   const float* gain = a.qk_norm ? (is_q ? a.q_gain : a.k_gain) : nullptr;
@@ -305,10 +318,11 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
     const float r = a.qk_norm ? rstd[tok0 + 16 * p + j] : 1.0f;
+    const bool valid = blk_id * BLK + 16 * p + j < a.Nv;   // padding tokens stay 0 (uniform but the last block)
 #pragma unroll
     for (int i = 0; i < S::CW; ++i) {
       const float xh = (s.x[p][i] * r) * gn[i];   // gn = 1 without gains: exact
-      s.x[p][i] = xh - mu[i];
+      s.x[p][i] = valid ? xh - mu[i] : 0.0f;
     }
   }
   const float amax = slice_absmax<D, BLK>(s, red);

@@ -39,6 +39,11 @@
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors), contiguous,
  *     16-byte aligned. Shapes are given in [B,H,N,d] order, last index fastest, except that
  *     the 16-bit tensors follow sagebwd_params.layout ([B,N,H,d] with SAGEBWD_LAYOUT_BNHD).
+ *   - N need not be a multiple of blk: the last quantisation block of a head then holds
+ *     N mod blk tokens (its absmax, and the means, cover those tokens only). The 16-bit
+ *     tensors hold exactly N tokens per head; every array of the library's own (codes,
+ *     scales, statistics, lse) holds Np = N rounded up to a multiple of blk, the tokens from
+ *     N on being padding (codes 0; their lse and statistics are not meaningful).
  *   - The caller owns every buffer. The library allocates nothing, keeps no state between
  *     calls, never synchronises, and is re-entrant; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream). Calls sharing a workspace must be
@@ -67,8 +72,7 @@ extern "C" {
 typedef enum {
   SAGEBWD_OK = 0,
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
-  SAGEBWD_ERR_SHAPE = -2,       /* negative size, N not a multiple of blk, N > 2^22, or
-                                   B*H > 2^24                                               */
+  SAGEBWD_ERR_SHAPE = -2,       /* negative size, N > 2^22, or B*H > 2^24                  */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
                                    layout, eps < 0, qk_gain or normed_grads without
                                    qk_norm, normed_grads with qk_gain                       */
@@ -81,7 +85,7 @@ typedef enum { SAGEBWD_FP16 = 0, SAGEBWD_BF16 = 1 } sagebwd_dtype;
 
 typedef struct {
   int32_t B, H, N, d;   /* batch, heads, tokens, head dim (d in {64, 128})                  */
-  int32_t blk;          /* quantisation block, tokens (64 or 128); N % blk == 0             */
+  int32_t blk;          /* quantisation block, tokens (64 or 128)                            */
   int32_t causal;       /* nonzero: key j is visible to query i iff j <= i                  */
   int32_t qk_norm;      /* nonzero: RMSNorm Q and K per token (gain 1 unless qk_gain)       */
   int32_t k_smooth;     /* nonzero: subtract K's per-channel mean before quantising         */
@@ -112,7 +116,7 @@ typedef enum { SAGEBWD_LAYOUT_BHND = 0, SAGEBWD_LAYOUT_BNHD = 1 } sagebwd_layout
  * of INT8 dS codes once to the workspace and contracts them with K in a query-major pass
  * (plain stores, O(N^2/2) bytes of scratch per head when causal). SAGEBWD_DQ_ATOMIC adds
  * each tile's float32 dQ contribution with atomics (O(N) scratch, but the atomic traffic is
- * (N/blk) * N * d * 4 bytes per head). SAGEBWD_DQ_AUTO picks SPILL while its scratch is at
+ * (Np/blk) * Np * d * 4 bytes per head). SAGEBWD_DQ_AUTO picks SPILL while its scratch is at
  * most SAGEBWD_DQ_AUTO_SPILL_LIMIT bytes, else ATOMIC. Both give the same dQ up to float32
  * summation order. SPILL also needs one head's dS tiles (T * 64 * blk bytes, T below) under
  * 4 GiB: AUTO picks ATOMIC beyond that, and an explicit SPILL is rejected
@@ -121,7 +125,7 @@ typedef enum { SAGEBWD_DQ_AUTO = 0, SAGEBWD_DQ_SPILL = 1, SAGEBWD_DQ_ATOMIC = 2 
 #define SAGEBWD_DQ_AUTO_SPILL_LIMIT (16ull << 30)
 
 /* Bytes of scratch sagebwd_quant_prologue needs: the per-block channel sums of the
- * normalised keys, float32 [B,H,N/blk,d], when k_smooth is on, then (256-byte aligned) those
+ * normalised keys, float32 [B,H,Np/blk,d], when k_smooth is on, then (256-byte aligned) those
  * of the normalised queries when q_smooth is on (0 when both are off). Returns 0 for
  * invalid params. */
 size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
@@ -130,15 +134,15 @@ size_t sagebwd_prologue_workspace_bytes(const sagebwd_params* p);
  * and scales. The codes, scales and statistics are the "quantised views" both passes reuse
  * (the Full-Stack FP4 page, section 2.4, reuses quantised Q, K, V between the passes).
  *   Q, K, V  in : dtype [B,H,N,d]
- *   Qc, Kc   out: int8 [B,H,N,d]   codes of Q^ (of Q~ = Q^ - q_mean with q_smooth) and of
+ *   Qc, Kc   out: int8 [B,H,Np,d]  codes of Q^ (of Q~ = Q^ - q_mean with q_smooth) and of
  *                                  K~ = K^ - mean (smoothed keys)
- *   Vtc      out: int8 [B,H,d,N]   codes of V, stored TRANSPOSED (channel-major)
- *   Qs,Ks,Vs out: float32 [B,H,N/blk]  block scales
- *   q_rstd, k_rstd out: float32 [B,H,N]  1/sqrt(mean(x^2)+eps) per token (1 if !qk_norm)
+ *   Vtc      out: int8 [B,H,d,Np]  codes of V, stored TRANSPOSED (channel-major)
+ *   Qs,Ks,Vs out: float32 [B,H,Np/blk]  block scales
+ *   q_rstd, k_rstd out: float32 [B,H,Np]  1/sqrt(mean(x^2)+eps) per token (1 if !qk_norm)
  *   k_mean   out: float32 [B,H,d]  the subtracted mean (0 if !k_smooth)
  *   q_mean   out: float32 [B,H,d]  the subtracted query mean (q_smooth only; else ignored,
  *                                  may be NULL)
- *   kbias    out: float32 [B,H,N]  b_k = Ks * (Kc_k . q_mean), float32 sum over channels
+ *   kbias    out: float32 [B,H,Np] b_k = Ks * (Kc_k . q_mean), float32 sum over channels
  *                                  (q_smooth only; else ignored, may be NULL)
  *   q_gain, k_gain in: float32 [H,d]  QK-norm gains (qk_gain only; else ignored, may be NULL)
  *   workspace   : >= sagebwd_prologue_workspace_bytes(p) bytes (may be NULL if that is 0)
@@ -166,7 +170,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
  *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs, and its kbias with q_smooth (each
  *            score is then sm_scale * (Q~ K~^T + b_k); kbias ignored, may be NULL, without)
  *   O   out: dtype [B,H,N,d]
- *   lse out: float32 [B,H,N], natural-log logsumexp of each row of the scaled scores */
+ *   lse out: float32 [B,H,Np], natural-log logsumexp of each row of the scaled scores */
 sagebwd_status sagebwd_forward(const sagebwd_params* p,
                                const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
                                const float* Qs, const float* Ks, const float* Vs,
@@ -174,7 +178,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
 
 /* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
  * boundary, in this order; "chunk" = 16 bytes):
- *   packets [B,H,N/64] x P bytes     P = 17408 for d = 64, 33792 for d = 128: for each head
+ *   packets [B,H,Np/64] x P bytes     P = 17408 for d = 64, 33792 for d = 128: for each head
  *           and each 64-token tile, the tile's data in the order the key-block kernel copies
  *           it into LDS (r = token inside the tile, c = channel):
  *     [0, 64d)      Q codes [64][d]; chunk j of row r stored at chunk
@@ -188,11 +192,11 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *     [+256, +512)  D = rowsum(dO o O), float32 [64]
  *     [+512, +516)  the Q block scale; [+516, +520) the dO block scale (float32); padding
  * then, with dq_mode ATOMIC:
- *   dq_acc  float32 [B,H,N,d]        dQ of the normalised queries, accumulated
+ *   dq_acc  float32 [B,H,Np,d]       dQ of the normalised queries, accumulated
  * or, with dq_mode SPILL (T = tiles per head = nb*nt - (blk/64)*nb*(nb-1)/2 when causal,
- * nb*nt otherwise, nb = N/blk, nt = N/64; tile (kb, t) of key block kb and query tile t has
+ * nb*nt otherwise, nb = Np/blk, nt = Np/64; tile (kb, t) of key block kb and query tile t has
  * index kb*nt - (blk/64)*kb*(kb-1)/2 + t - kb*blk/64 when causal, kb*nt + t otherwise):
- *   ktp     [B,H,N/blk] x d*blk      K codes of each key block, channel-major [d][blk];
+ *   ktp     [B,H,Np/blk] x d*blk      K codes of each key block, channel-major [d][blk];
  *                                    chunk j of row c stored at chunk j^(c&7) (blk = 128)
  *                                    or j^((c>>1)&3) (blk = 64)
  *   dsp     [B,H,T] x 64*blk         INT8 dS codes of each tile, key-major [blk][64]:
@@ -203,8 +207,8 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p,
  *   dsm     float32 [B,H,T,blk/64]   per 64 keys of the tile (one dS scale tile):
  *                                    sm_scale * (dS tile scale) * (K block scale)
  * then, with qk_gain:
- *   gq      float32 [B,H,N/64,d]     partial dq_gain of each 64-query tile
- *   gk      float32 [B,H,N/blk,d]    partial dk_gain of each key block
+ *   gq      float32 [B,H,Np/64,d]    partial dq_gain of each 64-query tile
+ *   gk      float32 [B,H,Np/blk,d]   partial dk_gain of each key block
  * Returns 0 for invalid params. */
 size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p);
 

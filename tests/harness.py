@@ -110,7 +110,7 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
             res[k] = v.cpu().numpy()
     if "forward" in stages:
         res["O"] = back(O).float().cpu().numpy().astype(np.float64)
-        res["LSE"] = lse.cpu().numpy()
+        res["LSE"] = lse[:, :, :w.N].cpu().numpy()      # (rows from N on: padding)
     if "backward" in stages:
         for k in ("dQ", "dK", "dV"):
             res[k] = back(g[k]).float().cpu().numpy().astype(np.float64)
@@ -118,7 +118,7 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
             res["dq_gain"] = g["dq_gain"].cpu().numpy().astype(np.float64)
             res["dk_gain"] = g["dk_gain"].cpu().numpy().astype(np.float64)
         lay = api.backward_workspace_layout(p)
-        npk = w.B * w.H * (w.N // 64) * lay["packet_bytes"]   # only the packet region is decoded
+        npk = w.B * w.H * lay["tiles_per_head_q"] * lay["packet_bytes"]   # only the packet region is decoded
         ws = g["workspace"][:npk].cpu().numpy()
         res.update(decode_packets(ws, lay, w))
     return res
@@ -127,7 +127,8 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
 def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[str, np.ndarray]:
     """Read the dO codes (channel-major, natural token order), the dO block scales and D
     back out of the backward workspace's tile packets (layout in include/sagebwd.h)."""
-    d, P, nt = w.d, lay["packet_bytes"], w.N // 64
+    Np = -(-w.N // w.blk) * w.blk
+    d, P, nt = w.d, lay["packet_bytes"], Np // 64
     pk = ws[lay["packets"]:lay["packets"] + w.B * w.H * nt * P].reshape(w.B, w.H, nt, P)
     rows = pk[..., 192 * d:256 * d].view(np.int8).reshape(w.B, w.H, nt, d, 4, 16)  # [.., c, slot, 16]
     c = np.arange(d)
@@ -136,9 +137,9 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
     u = np.arange(64)
     pos = 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
     codes = logical[..., pos]                                                         # [B,H,nt,d,64]
-    dOtc = np.moveaxis(codes, 2, 3).reshape(w.B, w.H, d, w.N)
+    dOtc = np.moveaxis(codes, 2, 3).reshape(w.B, w.H, d, Np)
     base = 256 * d
-    Dv = pk[..., base + 256:base + 512].copy().view(np.float32).reshape(w.B, w.H, w.N)
+    Dv = pk[..., base + 256:base + 512].copy().view(np.float32).reshape(w.B, w.H, Np)
     sdo_tiles = pk[..., base + 516:base + 520].copy().view(np.float32).reshape(w.B, w.H, nt)
     dOs = sdo_tiles[..., :: w.blk // 64]
     return {"dOtc": dOtc, "dOs": dOs, "Dvec": Dv}

@@ -74,7 +74,6 @@ def test_invalid_params_rejected(call):
     assert call(P(qk_gain=1, qk_norm=0)) == -3   # gains need QK-norm
     assert call(P(normed_grads=1, qk_norm=0)) == -3
     assert call(P(normed_grads=1, qk_gain=1)) == -3
-    assert call(P(N=200)) == -2            # not a multiple of blk
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
     assert call(P(B=1 << 13, H=1 << 12)) == -2
