@@ -30,6 +30,11 @@ What is computed, in the order of the SageBwd article:
      subtracted before quantising; every score gets back the per-key bias
      b_k = (K mu_Q)_k (key_bias), and dK^ gets dK_bias = (dS^T 1) mu_Q^T
      (q_smooth_dk_bias); dQ is unchanged.
+  8. Optional FP8 recipe (Spec.fmt = "fp8"; SageBwd article, precision split paragraph,
+     where the FP8 alternative of the quantised products is named): every quantiser of
+     steps 3-5 keeps its tile and its absmax rule but maps onto e4m3 (OCP float8 e4m3fn,
+     largest finite 448) instead of [-127, 127]: scale a / 448, code e4m3_rne(x * 448 / a).
+     The products are formed from the codes' values exactly as in the INT8 recipe.
 
 Precision: steps 1-3 are float32, one IEEE operation at a time, round to nearest
 even, in the order written (sums run over channels, or over tokens, in ascending
@@ -75,6 +80,7 @@ class Spec:
     bwd_sk: Optional[int] = None
     q_smooth: bool = False
     normed_grads: bool = False   # dQ, dK with respect to Q^, K^ (no RMSNorm backward)
+    fmt: str = "int8"            # encoding of the six quantised products' operands: "int8" | "fp8"
 
     def __post_init__(self):
         blk = self.blk
@@ -244,6 +250,84 @@ def quant_blocks_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
     return q.reshape(x.shape), s
 
 
+# ----------------------------------------------------------------------------
+# The FP8 recipe (e4m3, OCP "FN" variant: bias 7, 3 mantissa bits, max 448, no infinity).
+# ----------------------------------------------------------------------------
+
+FP8_MAX = 448.0
+
+
+def e4m3_encode(x32: np.ndarray) -> np.ndarray:
+    """float32 -> e4m3 bit patterns (uint8), round to nearest even, from the format's
+    definition: normals (1 + m/8) * 2^(e - 7) for e = 1..15 (e = 15, m = 7 is NaN, so the
+    largest finite value is 1.75 * 2^8 = 448), subnormals m/8 * 2^-6; the sign is kept (also
+    on zero). |x| must stay below 464, the midpoint between 448 and the next step (the NaN
+    pattern): fl(x * fl(448 / a)) can exceed 448 by an ulp, and rounds to 448.
+    Pinned by: test_oracle_quant.py::test_e4m3_* (torch's float8_e4m3fn conversion, round
+    trips of every finite code, hand-made ties)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    if np.any(np.abs(x) >= 464.0):
+        raise ValueError("e4m3 input at or beyond 464 (overflows 448)")
+    sign = np.signbit(x).astype(np.uint8) << 7
+    a = np.abs(x)
+    f, E = np.frexp(a)                       # a = f * 2^E, f in [0.5, 1)
+    e = E - 1                                # a = (2f) * 2^e, 2f in [1, 2)
+    normal = (a > 0) & (e >= -6)             # zero (frexp exponent 0) takes the subnormal path
+    # normals: mantissa steps of 2^(e-3); subnormals: steps of 2^-9
+    step = np.where(normal, np.exp2(e - 3.0), 2.0 ** -9)
+    q = np.rint(a / step)                    # exact division by a power of two; RNE
+    code = np.zeros(x.shape, dtype=np.int64)
+    # normal: q in [8, 16]; q == 16 rounds up into the next binade
+    qn = q.astype(np.int64)
+    en = np.where(qn >= 16, e + 1, e)
+    mn = np.where(qn >= 16, 0, qn - 8)
+    code = np.where(normal, ((en + 7) << 3) | mn, qn)   # subnormal: q in [0, 8] (8 = min normal)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """e4m3 bit patterns -> float64 values."""
+    c = np.asarray(code).astype(np.int64) & 0xFF
+    s = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return s * v
+
+
+def quant_rule_fp8_f32(x32: np.ndarray, axes: Tuple[int, ...]) -> Tuple[np.ndarray, np.ndarray]:
+    """The FP8 rule: symmetric absmax over `axes`, scale s = fl(a / 448), inv = fl(448 / a),
+    code = e4m3_rne(fl(x * inv)) (an all-zero block: scale 0, codes 0). Returns (codes as
+    uint8 e4m3 bit patterns, scales float32 with `axes` removed)."""
+    x32 = np.asarray(x32, dtype=F32)
+    a = np.max(np.abs(x32), axis=axes, keepdims=True)
+    zero = a == 0
+    a_safe = np.where(zero, F32(1.0), a)
+    s = np.where(zero, F32(0.0), a_safe / F32(FP8_MAX)).astype(F32)
+    inv = np.where(zero, F32(0.0), F32(FP8_MAX) / a_safe).astype(F32)
+    return e4m3_encode((x32 * inv).astype(F32)), np.squeeze(s, axis=axes)
+
+
+def quant_blocks_fp8_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-block FP8 quantisation of [..., N, d]: one scale per blk tokens x d channels."""
+    x = np.asarray(x, dtype=F32)
+    N, d = x.shape[-2], x.shape[-1]
+    xb = x.reshape(x.shape[:-2] + (N // blk, blk, d))
+    nd = xb.ndim
+    q, s = quant_rule_fp8_f32(xb, axes=(nd - 2, nd - 1))
+    return q.reshape(x.shape), s
+
+
+def code_values(codes: np.ndarray) -> np.ndarray:
+    """Values of codes as float64: e4m3 bit patterns (uint8) are decoded, INT8 codes and
+    identity "codes" are taken as they are."""
+    codes = np.asarray(codes)
+    if codes.dtype == np.uint8:
+        return e4m3_decode(codes)
+    return codes.astype(np.float64)
+
+
 BlockQuant = Callable[[np.ndarray, int], Tuple[np.ndarray, np.ndarray]]
 
 
@@ -341,6 +425,15 @@ def key_bias(Kc, Ks, mu_q, blk: int) -> np.ndarray:
 TileQuant = Callable[[np.ndarray], Tuple[np.ndarray, np.ndarray]]
 
 
+def fp8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise each tile x[h] with the FP8 rule, deciding in float32; codes returned as their
+    float64 values, scales as float64 [BH]."""
+    x32 = np.asarray(x, dtype=np.float64).astype(F32)
+    axes = tuple(range(1, x32.ndim))
+    q, s = quant_rule_fp8_f32(x32, axes)
+    return e4m3_decode(q), s.astype(np.float64)
+
+
 def int8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise each tile x[h] (leading axis = head) with the INT8 rule, deciding in float32.
 
@@ -392,9 +485,9 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
     blk, tq, tk = spec.blk, spec.fwd_tq, spec.tk
     sm = spec.scale
     nv = spec.N
-    q = _flat(Qc).astype(np.float64)
-    k = _flat(Kc).astype(np.float64)
-    v = _flat(Vc).astype(np.float64)
+    q = code_values(_flat(Qc))
+    k = code_values(_flat(Kc))
+    v = code_values(_flat(Vc))
     qs = _flat(np.asarray(Qs, dtype=np.float64))
     ks = _flat(np.asarray(Ks, dtype=np.float64))
     vs = _flat(np.asarray(Vs, dtype=np.float64))
@@ -502,11 +595,11 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     V, dO, O = (_pad_rows(np.asarray(x), N) for x in (V, dO, O))
     LSE = _pad_rows(np.asarray(LSE, dtype=F32), N, np.inf)
     D, dOc, dOs = backward_pre(O, dO, spec, block_quant=block_quant)
-    qc = _flat(pro["Qc"]).astype(np.float64)
-    kc = _flat(pro["Kc"]).astype(np.float64)
+    qc = code_values(_flat(pro["Qc"]))
+    kc = code_values(_flat(pro["Kc"]))
     qs = _flat(np.asarray(pro["Qs"], dtype=np.float64))
     ks = _flat(np.asarray(pro["Ks"], dtype=np.float64))
-    doc = _flat(dOc).astype(np.float64)
+    doc = code_values(_flat(dOc))
     dos = _flat(np.asarray(dOs, dtype=np.float64))
     do = _flat(np.asarray(dO, dtype=F32)).astype(np.float64)
     vf = _flat(np.asarray(V, dtype=F32)).astype(np.float64)
@@ -603,11 +696,17 @@ def q_smooth_dk_bias(qdS, sdS, mu_q, sm: float) -> np.ndarray:
     return sm * csum[:, :, None] * np.asarray(mu_q, np.float64)[:, None, :]
 
 
-def run(Q, K, V, dO, spec: Spec, tile_quant: TileQuant = int8_tile_quant,
-        block_quant: BlockQuant = quant_blocks_f32, q_gain: Optional[np.ndarray] = None,
+def run(Q, K, V, dO, spec: Spec, tile_quant: Optional[TileQuant] = None,
+        block_quant: Optional[BlockQuant] = None, q_gain: Optional[np.ndarray] = None,
         k_gain: Optional[np.ndarray] = None):
     """Prologue -> forward -> backward on whole tensors. Returns one dict of everything
-    (with gains [H, d] also their gradients dq_gain, dk_gain)."""
+    (with gains [H, d] also their gradients dq_gain, dk_gain). The quantisers default to the
+    recipe of spec.fmt: the INT8 rule, or the FP8 (e4m3) rule with absmax/448 scales."""
+    fp8 = spec.fmt == "fp8"
+    if tile_quant is None:
+        tile_quant = fp8_tile_quant if fp8 else int8_tile_quant
+    if block_quant is None:
+        block_quant = quant_blocks_fp8_f32 if fp8 else quant_blocks_f32
     pro = prologue(Q, K, V, spec, block_quant=block_quant, q_gain=q_gain, k_gain=k_gain)
     O, LSE = forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec,
                      tile_quant=tile_quant, kbias=pro["kbias"] if spec.q_smooth else None)

@@ -524,3 +524,107 @@ def test_ragged_block_quant_is_the_rule_on_valid_tokens():
     assert np.max(np.abs(kt[:, :, :N].mean(axis=2))) < 0.02
     kh = oq.rms_norm_f32(K, spec.eps)[0].astype(np.float64)
     assert np.allclose(pro["k_mean"], kh.mean(axis=2), atol=1e-6)
+
+
+# ------------------------------------------------------------------- FP8 (e4m3) recipe
+
+def test_e4m3_matches_torch_conversion():
+    """The oracle's own e4m3 encoding (written from the format's definition) equals torch's
+    float8_e4m3fn conversion (round to nearest even) on every representable value, every
+    midpoint between neighbours and random values across the whole range."""
+    torch = pytest.importorskip("torch")
+    vals = oq.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = np.unique(vals[np.isfinite(vals)])
+    mids = (fin[:-1] + fin[1:]) / 2
+    rng = np.random.default_rng(141)
+    rnd = rng.uniform(-448, 448, 20000) * np.exp2(rng.integers(-16, 1, 20000))
+    x = np.concatenate([fin, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf), rnd]).astype(F32)
+    x = x[np.abs(x) <= 448]
+    mine = oq.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch writes -0 for negative values rounding to zero, as the oracle does
+    assert np.array_equal(mine, ref), int(np.sum(mine != ref))
+
+
+def test_e4m3_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # all but NaN
+    assert np.array_equal(oq.e4m3_encode(oq.e4m3_decode(codes).astype(F32)), codes)
+    assert oq.e4m3_decode(np.array([0x7E], np.uint8))[0] == 448.0
+    assert oq.e4m3_decode(np.array([0x01], np.uint8))[0] == 2.0 ** -9
+    # ties go to the even mantissa: 17 -> 16, 19 -> 20, 2^-10 (half the smallest subnormal) -> 0
+    got = oq.e4m3_decode(oq.e4m3_encode(np.array([17.0, 19.0, 2.0 ** -10, 3 * 2.0 ** -10], F32)))
+    np.testing.assert_array_equal(got, [16.0, 20.0, 0.0, 2.0 ** -8])
+    # an ulp above 448 (x * fl(448 / a) can land there) still rounds to 448; 464 is refused
+    just_above = np.nextafter(F32(448.0), F32(np.inf))
+    assert oq.e4m3_encode(np.array([just_above, -just_above], F32)).tolist() == [0x7E, 0xFE]
+    with pytest.raises(ValueError):
+        oq.e4m3_encode(np.array([464.0], F32))
+    # signed zeros
+    assert oq.e4m3_encode(np.array([0.0, -0.0], F32)).tolist() == [0x00, 0x80]
+
+
+def test_fp8_rule_properties():
+    """Every non-zero block has a code of magnitude 448 (the absmax element); each value is
+    within half a step of the code's value times the scale."""
+    rng = np.random.default_rng(143)
+    x = (rng.standard_normal((2, 3, 256, 16)) * np.exp2(rng.integers(-8, 8, (2, 3, 1, 1)))).astype(F32)
+    q, s = oq.quant_blocks_fp8_f32(x, 64)
+    v = oq.e4m3_decode(q).reshape(2, 3, 4, 64, 16)
+    assert np.all(np.max(np.abs(v), axis=(-2, -1)) == 448.0)
+    deq = v * s[..., None, None]
+    xb = x.reshape(2, 3, 4, 64, 16).astype(np.float64)
+    # relative step of e4m3 is 2^-3 for normals; subnormals have an absolute step 2^-9 * s
+    err = np.abs(deq - xb)
+    bound = np.maximum(np.abs(xb) * 2.0 ** -4, 2.0 ** -10 * s[..., None, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_lossless_block_quant_equals_exact(causal):
+    """Inputs that the FP8 rule represents exactly (e4m3 values times a per-block power of two,
+    each block holding a +-448 element), identity tiles: the FP8 path equals exact attention,
+    which pins the decode of the codes and which block scale multiplies which product."""
+    rng = np.random.default_rng(145)
+    shape, blk = (1, 2, 256, 16), 64
+    vals = oq.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+
+    def lossless(emin, emax):
+        B, H, N, d = shape
+        c = rng.choice(fin, size=shape)
+        c.reshape(B, H, N // blk, blk * d)[..., 0] = 448.0 * rng.choice([-1, 1], (B, H, N // blk))
+        e = rng.integers(emin, emax + 1, (B, H, N // blk))
+        return (c * np.repeat(np.exp2(e.astype(np.float64)), blk, axis=-1)[..., None]).astype(F32), e
+    Q, eq = lossless(-12, -10)
+    K, _ = lossless(-12, -10)
+    V, ev = lossless(-9, -6)
+    dO, _ = lossless(-9, -6)
+    spec = oq.Spec(N=256, d=16, blk=blk, causal=causal, qk_norm=False, k_smooth=False, dtype="f64", fmt="fp8")
+    pro = oq.prologue(Q, K, V, spec, block_quant=oq.quant_blocks_fp8_f32)
+    np.testing.assert_array_equal(pro["Qs"], np.exp2(eq).astype(F32))
+    np.testing.assert_array_equal(pro["Vs"], np.exp2(ev).astype(F32))
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    assert _rel(got["O"], ref["O"]) < 1e-12
+    for name in ("dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 2e-6, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_close_to_exact(causal):
+    """The FP8 recipe end to end stays close to exact attention (3 mantissa bits: looser than
+    INT8's, still far from what an indexing error would give)."""
+    rng = np.random.default_rng(147)
+    B, H, N, d = 1, 2, 256, 64
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(np.float16).astype(F32) for _ in range(4))
+    spec = oq.Spec(N=N, d=d, blk=64, causal=causal, qk_norm=True, k_smooth=True, dtype="f64", fmt="fp8")
+    got = oq.run(Q, K, V, dO, spec)
+    assert got["Qc"].dtype == np.uint8
+    ref = _exact_all(Q, K, V, dO, spec)
+
+    def cos(a, b):
+        a = a.ravel(); b = b.ravel()
+        return a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+    assert cos(got["O"], ref["O"]) > 0.995
+    for name in ("dQ", "dK", "dV"):
+        assert cos(got[name], ref[name]) > 0.98, name
