@@ -13,6 +13,7 @@ SAGEBWD_FP16 = 0
 SAGEBWD_BF16 = 1
 DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
+FMT_INT8, FMT_FP8 = 0, 1   # sagebwd_fmt
 
 # Quantisation tile shapes of the kernels (include/sagebwd.h); the backward's P and dS tiles
 # span one query block (blk rows) by BWD_P_TILE_K and min(blk, BWD_DS_TILE_K) keys.
@@ -34,6 +35,7 @@ class Params(ctypes.Structure):
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
         ("layout", ctypes.c_int32), ("qk_gain", ctypes.c_int32), ("normed_grads", ctypes.c_int32),
+        ("fmt", ctypes.c_int32),
     ]
 
 

@@ -20,14 +20,16 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
                 dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0,
                 q_smooth: bool = False, layout: str = "bhnd", qk_gain: bool = False,
-                normed_grads: bool = False) -> _lib.Params:
+                normed_grads: bool = False, fmt: str = "int8") -> _lib.Params:
     """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics; layout of the 16-bit tensors:
     "bhnd" [B,H,N,d] or "bnhd" [B,N,H,d]; qk_gain: learnable QK-norm gains [H,d];
-    normed_grads: dQ, dK with respect to the normalised Q^, K^ (include/sagebwd.h)."""
+    normed_grads: dQ, dK with respect to the normalised Q^, K^; fmt: code format of the
+    six quantised products, "int8" or "fp8" (e4m3) (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
     lay = {"bhnd": _lib.LAYOUT_BHND, "bnhd": _lib.LAYOUT_BNHD}[layout]
     return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode,
-                       int(q_smooth), lay, int(qk_gain), int(normed_grads))
+                       int(q_smooth), lay, int(qk_gain), int(normed_grads),
+                       {"int8": _lib.FMT_INT8, "fp8": _lib.FMT_FP8}[fmt])
 
 
 def sagebwd_status_string(status: int) -> str:

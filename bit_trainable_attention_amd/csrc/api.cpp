@@ -32,6 +32,8 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->layout != SAGEBWD_LAYOUT_BHND && p->layout != SAGEBWD_LAYOUT_BNHD) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->qk_gain && !p->qk_norm) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->normed_grads && (!p->qk_norm || p->qk_gain)) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->fmt != SAGEBWD_FMT_INT8 && p->fmt != SAGEBWD_FMT_FP8) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->fmt == SAGEBWD_FMT_FP8 && p->q_smooth) return SAGEBWD_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
   // (Np * d * 4 < 2^31), grids in 2^31 workgroups
   if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 22)) return SAGEBWD_ERR_SHAPE;
@@ -199,6 +201,7 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
     a.qpart = reinterpret_cast<float*>(ws + (p->k_smooth ? prologue_part_bytes(p) : 0));
   }
   a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.fmt = p->fmt;
   a.x16 = strides16(p);
   a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.q_smooth = p->q_smooth != 0;
   a.eps = p->eps;
@@ -220,6 +223,7 @@ sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const 
   a.kbias = a.q_smooth ? kbias : nullptr;
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
   a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.fmt = p->fmt;
   a.x16 = strides16(p);
   a.causal = p->causal != 0; a.sm_scale = sm_scale_of(p);
   return hip_status(sagebwd::launch_forward(a, static_cast<hipStream_t>(stream)), "sagebwd_forward");
@@ -281,6 +285,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
     a.dq_acc = reinterpret_cast<float*>(ws + L.dq);
   }
   a.BH = p->B * p->H; a.N = padded_n(p); a.Nv = p->N; a.D = p->d; a.BLK = p->blk; a.dtype = p->dtype;
+  a.fmt = p->fmt;
   a.x16 = strides16(p);
   // normed_grads: the epilogues stop before the RMSNorm backward
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0 && !p->normed_grads; a.sm_scale = sm_scale_of(p);

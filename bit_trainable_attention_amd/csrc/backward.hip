@@ -201,10 +201,12 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   const float am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = am > 0.0f ? 127.0f / am : 0.0f;
+  const bool fp8 = a.fmt == FMT_FP8;
+  const float M = fp8 ? 448.0f : 127.0f;
+  const float inv = am > 0.0f ? M / am : 0.0f;
   if (tid < NQ) {
     int8_t* pk = pk0 + tid * P::kBytes;
-    *reinterpret_cast<float*>(pk + P::bSDO) = am > 0.0f ? am / 127.0f : 0.0f;
+    *reinterpret_cast<float*>(pk + P::bSDO) = am > 0.0f ? am / M : 0.0f;
     *reinterpret_cast<float*>(pk + P::bSQ) = a.Qs[(size_t)bh * nb + blk_id];
   }
 
@@ -227,8 +229,7 @@ __global__ __launch_bounds__(256) void bwd_pre(BackwardArgs a) {
 #pragma unroll
     for (int i = 0; i < CW; ++i)
       *reinterpret_cast<unsigned*>(tt + (q * D + c0 + i) * TR + wpos) =
-          pack4_lo_bytes(quant_word(x[q][0][i], inv), quant_word(x[q][1][i], inv), quant_word(x[q][2][i], inv),
-                         quant_word(x[q][3][i], inv));
+          code_word(fp8, x[q][0][i], x[q][1][i], x[q][2][i], x[q][3][i], inv);
   __syncthreads();
   write_rows(P::bDOT);
   __syncthreads();
@@ -332,7 +333,7 @@ struct BwdLds {
   static constexpr int kMinBlocks = BLK == 64 ? 2 : 1;   // workgroups per CU
 };
 
-template <int DT, int D, int BLK, bool SPILL, bool QS>
+template <int DT, int D, int BLK, bool SPILL, bool QS, int FMT>
 __global__ __launch_bounds__((BwdLds<D, BLK, SPILL>::NW * 64), (BwdLds<D, BLK, SPILL>::kMinBlocks))
 void bwd_main(BackwardArgs a) {
   using L = BwdLds<D, BLK, SPILL>;
@@ -442,7 +443,8 @@ void bwd_main(BackwardArgs a) {
 
   // ---- the phases of one query tile; state carried between them (registers)
   float sQ = 0.0f, sdO = 0.0f, c2 = 0.0f;
-  i32x4 s[NS];
+  using C = Codes<FMT>;
+  typename C::acc4 s[NS];
   f32x4 dp[NS];
   float dsf[NS][4];
   i32x4 qtr[NH][NCT];
@@ -461,12 +463,16 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       const int8_t* pb = lds + (t / 4) * P::kBytes;
-      s[t] = i32x4{};
-#pragma unroll
-      for (int c = 0; c < KCH; ++c) {
+      s[t] = typename C::acc4{};
+      auto aq = [&](int c) {
         const int cq = D == 128 ? c ^ (t & 1) : c;   // (t % 4) & 1 == t & 1
-        const i32x4 aq = *reinterpret_cast<const i32x4*>(pb + (qb ^ (64 * cq)) + 16 * (t % 4) * D);
-        s[t] = mfma_i8_16x16x64(aq, kreg[c], s[t]);
+        return *reinterpret_cast<const i32x4*>(pb + (qb ^ (64 * cq)) + 16 * (t % 4) * D);
+      };
+      if constexpr (FMT == FMT_FP8 && KCH == 2) {
+        s[t] = C::mma16x2(aq(0), aq(1), kreg[0], kreg[1], s[t]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) s[t] = C::mma16(aq(c), kreg[c], s[t]);
       }
       dp[t] = f32x4{};
 #pragma unroll
@@ -512,25 +518,24 @@ void bwd_main(BackwardArgs a) {
     // ---- P codes on this wave's TQ x 16 tile, then dV^T += dO^T P (int32 over the TQ rows)
     {
       const float pa = fmaxf(pm, FLT_MIN);
-      const float pinv = 127.0f * __builtin_amdgcn_rcpf(pa);
-      const float sv = pa * (1.0f / 127.0f) * sdO;
+      const float pinv = C::kMax * __builtin_amdgcn_rcpf(pa);
+      const float sv = pa * (1.0f / C::kMax) * sdO;
       i32x4 pc[NH];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float* v = pf[4 * h + t];
-          pc[h][t] = (int)pack4_lo_bytes(quant_word_fma(v[0], pinv), quant_word_fma(v[1], pinv),
-                                         quant_word_fma(v[2], pinv), quant_word_fma(v[3], pinv));
+          pc[h][t] = (int)tile_code_word<FMT>(v[0], v[1], v[2], v[3], pinv);
         }
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        i32x4 acc = i32x4{};
+        typename C::acc4 acc{};
+        auto ao = [&](int h) { return *reinterpret_cast<const i32x4*>(buf + h * P::kBytes + oT + 16 * n * kPq); };
+        // (FP8: two K = 32 products per 64 rows; joining the two 64-row halves into one
+        // K = 128 product needs 8-register operand copies that spill at d = 128)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const i32x4 ao = *reinterpret_cast<const i32x4*>(buf + h * P::kBytes + oT + 16 * n * kPq);
-          acc = mfma_i8_16x16x64(ao, pc[h], acc);
-        }
+        for (int h = 0; h < NH; ++h) acc = C::mma16(ao(h), pc[h], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
       }
@@ -556,17 +561,17 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
     for (int i = 1; i < 4; ++i) da = fmaxf(da, redD[(step & 1) * NW + wg0 + i]);
     da = fmaxf(da, FLT_MIN);
-    const float dinv = 127.0f * __builtin_amdgcn_rcpf(da);
-    const float sdS = da * (1.0f / 127.0f);
+    const float dinv = C::kMax * __builtin_amdgcn_rcpf(da);
+    const float sdS = da * (1.0f / C::kMax);
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float* v = dsf[4 * h + t];
-        dc[h][t] = (int)pack4_lo_bytes(quant_word_fma(v[0], dinv), quant_word_fma(v[1], dinv),
-                                       quant_word_fma(v[2], dinv), quant_word_fma(v[3], dinv));
+        dc[h][t] = (int)tile_code_word<FMT>(v[0], v[1], v[2], v[3], dinv);
       }
     if constexpr (QS) {
+      static_assert(FMT == FMT_INT8, "Q-smoothing sums INT8 codes");
       int isum = 0;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
@@ -578,9 +583,9 @@ void bwd_main(BackwardArgs a) {
       const float sk = smc * sdS * sQ;
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
-        i32x4 acc = i32x4{};
+        typename C::acc4 acc{};
 #pragma unroll
-        for (int h = 0; h < NH; ++h) acc = mfma_i8_16x16x64(qtr[h][n], dc[h], acc);
+        for (int h = 0; h < NH; ++h) acc = C::mma16(qtr[h][n], dc[h], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(sk, (float)acc[r], dk[n][r]);
       }
@@ -642,7 +647,7 @@ void bwd_main(BackwardArgs a) {
           float m = redD[(step & 1) * NW + 4 * kc];
 #pragma unroll
           for (int i = 1; i < 4; ++i) m = fmaxf(m, redD[(step & 1) * NW + 4 * kc + i]);
-          sc[kc] = smc * (fmaxf(m, FLT_MIN) * (1.0f / 127.0f)) * sK;
+          sc[kc] = smc * (fmaxf(m, FLT_MIN) * (1.0f / C::kMax)) * sK;
         }
         lds_barrier();
         f32x4 accf[NCT];
@@ -659,7 +664,7 @@ void bwd_main(BackwardArgs a) {
           for (int n = 0; n < NCT; ++n) {
             const int c = 16 * n + lr;
             const i32x4 bk = *reinterpret_cast<const i32x4*>(lds + L::offKT + c * BLK + 16 * swz<BLK>(c, 4 * kc + g));
-            const i32x4 acc = mfma_i8_16x16x64(as, bk, i32x4{});
+            const auto acc = C::mma16(as, bk, typename C::acc4{});
 #pragma unroll
             for (int r = 0; r < 4; ++r) accf[n][r] = __builtin_fmaf(sc[kc], (float)acc[r], accf[n][r]);
           }
@@ -853,8 +858,9 @@ struct DqLds {
   static constexpr int kBytes0 = kBuf > kPq * D * 4 ? kBuf : kPq * D * 4;
 };
 
-template <int DT, int D, int BLK>
+template <int DT, int D, int BLK, int FMT>
 __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
+  using C = Codes<FMT>;
   using L = DqLds<D, BLK>;
   constexpr int NCT = D / 16;                       // 16-channel tiles of dQ
   constexpr int NPW = NCT / 4;                      // ... per wave
@@ -946,7 +952,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
         const i32x4 as = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
         for (int n = 0; n < NPW; ++n) {
-          const i32x4 acc = mfma_i8_16x16x64(as, kt[n][kc], i32x4{});
+          const auto acc = C::mma16(as, kt[n][kc], typename C::acc4{});
 #pragma unroll
           for (int r = 0; r < 4; ++r) dq[qs][n][r] = __builtin_fmaf(m, (float)acc[r], dq[qs][n][r]);
         }
@@ -1027,20 +1033,32 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 1) {
-    auto go = [&](auto spill_c, auto qs_c) {
+    auto go = [&](auto spill_c, auto qs_c, auto fmt_c) {
       constexpr bool SP = decltype(spill_c)::value, QSV = decltype(qs_c)::value;
+      constexpr int FM = decltype(fmt_c)::value;
       using L = BwdLds<D, BLK, SP>;
-      return launch_kernel(&bwd_main<DT, D, BLK, SP, QSV>, dim3((unsigned)(nb * a.BH)), dim3(L::NW * 64), st, a);
+      return launch_kernel(&bwd_main<DT, D, BLK, SP, QSV, FM>, dim3((unsigned)(nb * a.BH)), dim3(L::NW * 64), st,
+                           a);
     };
     using T = std::true_type;
     using F = std::false_type;
-    const hipError_t e = a.spill ? (a.q_smooth ? go(T{}, T{}) : go(T{}, F{})) : (a.q_smooth ? go(F{}, T{}) : go(F{}, F{}));
+    using I8 = std::integral_constant<int, FMT_INT8>;
+    using F8 = std::integral_constant<int, FMT_FP8>;
+    hipError_t e;
+    if (a.fmt == FMT_FP8) {   // (Q-smoothing takes INT8 codes only; the API refuses it with FP8)
+      if (a.q_smooth) return hipErrorInvalidValue;
+      e = a.spill ? go(T{}, F{}, F8{}) : go(F{}, F{}, F8{});
+    } else {
+      e = a.spill ? (a.q_smooth ? go(T{}, T{}, I8{}) : go(T{}, F{}, I8{}))
+                  : (a.q_smooth ? go(F{}, T{}, I8{}) : go(F{}, F{}, I8{}));
+    }
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 2) {
     const dim3 tiles((unsigned)((long long)(a.N / kPq) * a.BH));
-    const hipError_t e = a.spill ? launch_kernel(&bwd_dq<DT, D, BLK>, tiles, dim3(256), st, a)
-                                 : launch_kernel(&dq_finalize<DT, D>, tiles, dim3(256), st, a);
+    const hipError_t e = !a.spill            ? launch_kernel(&dq_finalize<DT, D>, tiles, dim3(256), st, a)
+                         : a.fmt == FMT_FP8 ? launch_kernel(&bwd_dq<DT, D, BLK, FMT_FP8>, tiles, dim3(256), st, a)
+                                            : launch_kernel(&bwd_dq<DT, D, BLK, FMT_INT8>, tiles, dim3(256), st, a);
     if (e != hipSuccess) return e;
     if (a.q_gain) return launch_kernel(&gain_reduce<D>, dim3((unsigned)a.x16.H, 2), dim3(128), st, a);
   }

@@ -1,4 +1,4 @@
-// Device-side building blocks shared by the HIP kernels of the SageBwd-style INT8 attention.
+// Device-side building blocks shared by the HIP kernels of the SageBwd-style quantised attention.
 // gfx950 (CDNA4) only: 64-lane wavefronts, MFMA matrix cores.
 #pragma once
 
@@ -10,6 +10,7 @@ namespace sagebwd {
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -162,6 +163,88 @@ __device__ __forceinline__ unsigned quant_word(float x, float inv) {
 // once by the fused multiply-add with 1.5 * 2^23 (|x * inv| <= 127.5); low byte = code.
 __device__ __forceinline__ unsigned quant_word_fma(float x, float inv) {
   return __float_as_uint(__builtin_fmaf(x, inv, 12582912.0f));
+}
+
+// ---------------------------------------------------------------- code formats
+// The six quantised products take one-byte codes in one of two formats, with the same
+// byte layouts everywhere: INT8 (codes in [-127, 127], scale absmax/127, int32 products)
+// or FP8 e4m3 (OCP float8 e4m3fn, largest finite 448, scale absmax/448, float32 products).
+enum { FMT_INT8 = 0, FMT_FP8 = 1 };
+
+template <int FMT> struct Codes;
+
+template <> struct Codes<FMT_INT8> {
+  using acc4 = i32x4;
+  using acc16 = i32x16;
+  static constexpr float kMax = 127.0f;
+  static constexpr float kLog2Max = 6.988684686772166f;   // log2(127)
+  __device__ static __forceinline__ acc4 mma16(i32x4 a, i32x4 b, acc4 c) { return mfma_i8_16x16x64(a, b, c); }
+  __device__ static __forceinline__ acc4 mma16x2(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, acc4 c) {
+    return mfma_i8_16x16x64(a1, b1, mfma_i8_16x16x64(a0, b0, c));
+  }
+  __device__ static __forceinline__ acc16 mma32x2(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, acc16 c) {
+    return mfma_i8_32x32x32(a1, b1, mfma_i8_32x32x32(a0, b0, c));
+  }
+};
+
+// FP8 products. Each lane's 16 operand bytes of an INT8 product (one contraction slot per
+// byte, paired identically in A and B) feed the FP8 forms unchanged: two 8-byte halves make
+// two K = 32 (16 x 16) or K = 16 (32 x 32) products, or the 16 bytes of two consecutive
+// INT8 chunks concatenate into the 32 bytes of one K = 128 / K = 64 scaled product (scale
+// exponents 127 = 2^0, both operands e4m3). A and B see the same slot assignment in every
+// case, so the sum over the contraction is unchanged. The hardware keeps subnormal codes;
+// its float32 accumulation is not exact (errors near 2^-16 of the sum of |terms| were
+// measured), unlike the exact int32 sums of the INT8 form.
+template <> struct Codes<FMT_FP8> {
+  using acc4 = f32x4;
+  using acc16 = f32x16;
+  static constexpr float kMax = 448.0f;
+  static constexpr float kLog2Max = 8.807354922057604f;   // log2(448)
+  __device__ static __forceinline__ long half(i32x4 v, int h) {
+    return __builtin_bit_cast(long, i32x2{v[2 * h], v[2 * h + 1]});
+  }
+  __device__ static __forceinline__ acc4 mma16(i32x4 a, i32x4 b, acc4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(half(a, 0), half(b, 0), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(half(a, 1), half(b, 1), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ acc4 mma16x2(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, acc4 c) {
+    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+  __device__ static __forceinline__ acc16 mma32x2(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, acc16 c) {
+    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// e4m3 codes of four values already multiplied by the inverse scale (|x| < 464), round to
+// nearest even (v_cvt_pk_fp8_f32), byte i <- x_i.
+__device__ __forceinline__ unsigned fp8_word(float x0, float x1, float x2, float x3) {
+  const unsigned w = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)w, true);
+}
+
+// Codes of four values under inverse scale inv, the rule of the prologue: fl(x * inv)
+// rounded to the format (nearest even); byte i <- x_i.
+__device__ __forceinline__ unsigned code_word(bool fp8, float x0, float x1, float x2, float x3, float inv) {
+#pragma clang fp contract(off)
+  if (fp8) return fp8_word(x0 * inv, x1 * inv, x2 * inv, x3 * inv);
+  return pack4_lo_bytes(quant_word(x0, inv), quant_word(x1, inv), quant_word(x2, inv), quant_word(x3, inv));
+}
+
+// In-kernel tile codes (P, dS): INT8 rounds the exact product x * inv once; FP8 rounds
+// fl(x * inv) to e4m3.
+template <int FMT>
+__device__ __forceinline__ unsigned tile_code_word(float x0, float x1, float x2, float x3, float inv) {
+  if constexpr (FMT == FMT_FP8) {
+#pragma clang fp contract(off)
+    return fp8_word(x0 * inv, x1 * inv, x2 * inv, x3 * inv);
+  } else {
+    return pack4_lo_bytes(quant_word_fma(x0, inv), quant_word_fma(x1, inv), quant_word_fma(x2, inv),
+                          quant_word_fma(x3, inv));
+  }
 }
 
 // ---------------------------------------------------------------- LDS staging helpers

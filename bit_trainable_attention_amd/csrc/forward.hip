@@ -9,7 +9,8 @@
 //   LDS by buffer->LDS copies: K codes token-major and V^T codes channel-major, both with
 //   their 16-byte chunks XOR-swizzled by row (swz_f) so the MFMA operand reads spread over
 //   the banks (the copies take the permutation on their source addresses).
-//   S^T = K Q^T with v_mfma_i32_32x32x32_i8: lane l holds query l%32 and 16 keys per
+//   S^T = K Q^T with v_mfma_i32_32x32x32_i8 (FP8 codes: v_mfma_scale_f32_32x32x64_f8f6f4 on
+//   two 32-channel chunks at once): lane l holds query l%32 and 16 keys per
 //   32-key subtile, so the row max / row sum are lane-local plus one exchange with lane
 //   l^32 (v_permlane32_swap). The quantised P~^T becomes the B operand of O^T = V^T P~^T
 //   after two v_permlane32_swap per subtile, which put keys 16g..16g+15 in lane group g,
@@ -19,13 +20,15 @@
 // exponent is t * sm*log2e + (row terms); the tile's BLK biases ride in LDS after K and V^T.
 // Per key tile (the online-softmax step and the P~ quantisation tile, 32 rows x BLK keys):
 //   m' = max(m, rowmax s); P~ = 2^(s*log2e - m'); a = max P~ over the wave's tile;
-//   codes = rne(P~ * (127/a)); l = l*alpha + u*sum P~; O = O*alpha + u*(a/127)*sV*int(PV),
+//   codes = rne(P~ * (M/a)); l = l*alpha + u*sum P~; O = O*alpha + u*(a/M)*sV*(PV of codes),
+// with M = 127 for INT8 codes and 448 for FP8 (e4m3) codes,
 // with O and l kept relative to a reference r that lags m: r' = m' when some row of the wave
 // has m' > r + 8 (and on the first tile), else r' = r; alpha = 2^(r - r'), u = 2^(m' - r').
 // Most tiles then leave r alone and skip the O rescale; the codes and the final O and LSE are
 // the same as with r = m (only rounding differs).
-// P~ * 127/a is produced by one exponential, 2^(s*log2e - m' + log2(127/a)), and rounded and
-// packed by v_cvt_pk_u8_f32 (nearest even); only tiles on the diagonal carry masking work.
+// P~ * M/a is produced by one exponential, 2^(s*log2e - m' + log2(M/a)), and rounded and
+// packed by v_cvt_pk_u8_f32 (INT8) or v_cvt_pk_fp8_f32 (FP8), both nearest even; only tiles
+// on the diagonal carry masking work.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,7 +43,6 @@ constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLog2_127 = 6.988684686772166f;  // log2(127)
 constexpr float kLazy = 8.0f;  // O and l may lag the running max by up to 2^kLazy
 
 // Chunk swizzle of the K and V^T tiles, rows of RB bytes (an involution in j). The operand
@@ -97,9 +99,11 @@ __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int 
 
 }  // namespace
 
-template <int DT, int D, int BLK, bool QS>
+template <int DT, int D, int BLK, bool QS, int FMT>
 __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
   using L = FwdLds<D, BLK, QS>;
+  using C = Codes<FMT>;
+  static_assert(FMT == FMT_INT8 || !QS, "Q-smoothing takes INT8 codes only");
   constexpr int NSUB = BLK / 32;  // 32-key subtiles per key tile
   constexpr int DC = D / 32;      // 32-channel chunks
   __shared__ __attribute__((aligned(16))) int8_t lds[2][L::kBytes];
@@ -159,17 +163,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       // (LLVM's interleaving strategy 1 on this block and on the PV block: measured 1-5%
       // faster than the default schedule)
       __builtin_amdgcn_iglp_opt(1);
-      // ---- S^T = K Q^T (exact int32)
-      i32x16 s[NSUB];
+      // ---- S^T = K Q^T (exact int32 for INT8 codes, float32 for FP8 codes)
+      typename C::acc16 s[NSUB];
 #pragma unroll
       for (int t = 0; t < NSUB; ++t) {
-        s[t] = i32x16{};
+        s[t] = typename C::acc16{};
+        const int kr = 32 * t + lq;
+        auto ak = [&](int kk) { return *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz_f<D>(kr, 2 * kk + g)); };
 #pragma unroll
-        for (int kk = 0; kk < DC; ++kk) {
-          const int kr = 32 * t + lq;
-          const i32x4 ak = *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz_f<D>(kr, 2 * kk + g));
-          s[t] = mfma_i8_32x32x32(ak, qreg[kk], s[t]);
-        }
+        for (int kk = 0; kk < DC; kk += 2) s[t] = C::mma32x2(ak(kk), ak(kk + 1), qreg[kk], qreg[kk + 1], s[t]);
       }
       const float c2 = (sQ * sK) * (a.sm_scale * kLog2e);
       [[maybe_unused]] const float c3 = a.sm_scale * kLog2e;
@@ -198,6 +200,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
           }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(fm), __float_as_int(fm), false, false);
         rowmax = fmaxf(__int_as_float((int)sw[0]), __int_as_float((int)sw[1])) * c3;
+      } else if constexpr (FMT == FMT_FP8) {
+        if constexpr (DIAG) {
+#pragma unroll
+          for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+              if ((a.causal && key > qrow) || key >= a.Nv) s[t][r] = -INFINITY;
+            }
+        }
+        float rmax = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[t][r]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(rmax), __float_as_int(rmax), false, false);
+          rmax = fmaxf(__int_as_float((int)sw[0]), __int_as_float((int)sw[1]));
+        }
+        // (c2 is 0 for an all-zero block: a row with no visible key stays at -inf)
+        rowmax = rmax == -INFINITY ? -INFINITY : rmax * c2;
       } else {
         if constexpr (DIAG) {
 #pragma unroll
@@ -226,12 +249,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(mo - mo_new);   // 1 exactly when not moved
       const float up = __builtin_amdgcn_exp2f(m_new - mo_new);   // P~ in units of 2^mo_new
       // P~ tile absmax a = max over rows of 2^(rowmax - m'); in log2 it is one wave max.
-      // The quantisation factor 127/a is folded into the exponent, so the exponential
-      // yields P~ * 127/a directly and its nearest-even integer is the code.
+      // The quantisation factor M/a is folded into the exponent, so the exponential
+      // yields P~ * M/a directly and its nearest-even code is the code.
       // (padding rows of a ragged last block take no part in the tile's absmax)
       const float pa_log = wave_max(qrow < a.Nv ? rowmax - m_new : -INFINITY);
-      const float bias = kLog2_127 - pa_log - m_new;
-      const float sP = __builtin_amdgcn_exp2f(pa_log) * (1.0f / 127.0f);
+      const float bias = C::kLog2Max - pa_log - m_new;
+      const float sP = __builtin_amdgcn_exp2f(pa_log) * (1.0f / C::kMax);
 
       float tsum = 0.0f;
       i32x4 pc[NSUB];
@@ -247,15 +270,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
               x = __builtin_fmaf(tf[t][4 * j + i], c3, bias);   // -inf stays -inf (masked)
             } else {
               x = __builtin_fmaf((float)s[t][4 * j + i], c2, bias);
-              if constexpr (DIAG) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
+              if constexpr (DIAG && FMT == FMT_FP8) x = s[t][4 * j + i] == -INFINITY ? -INFINITY : x;
+              if constexpr (DIAG && FMT == FMT_INT8) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
             }
             u[i] = __builtin_amdgcn_exp2f(x);
             tsum += u[i];
           }
-          unsigned wd = __builtin_amdgcn_cvt_pk_u8_f32(u[0], 0, 0u);
-          wd = __builtin_amdgcn_cvt_pk_u8_f32(u[1], 1, wd);
-          wd = __builtin_amdgcn_cvt_pk_u8_f32(u[2], 2, wd);
-          pc[t][j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, wd);
+          if constexpr (FMT == FMT_FP8) {
+            pc[t][j] = (int)fp8_word(u[0], u[1], u[2], u[3]);
+          } else {
+            unsigned wd = __builtin_amdgcn_cvt_pk_u8_f32(u[0], 0, 0u);
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(u[1], 1, wd);
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(u[2], 2, wd);
+            pc[t][j] = (int)__builtin_amdgcn_cvt_pk_u8_f32(u[3], 3, wd);
+          }
         }
       // word j of lane group g holds keys 8j + 4g .. +3; group 0 needs keys 0..15 and group
       // 1 keys 16..31: swap words (0, 2) and (1, 3) across the lane halves
@@ -265,11 +293,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         const auto x13 = __builtin_amdgcn_permlane32_swap(pc[t][1], pc[t][3], false, false);
         pc[t] = i32x4{(int)x02[0], (int)x02[1], (int)x13[0], (int)x13[1]};
       }
-      // l accumulates P~ before quantisation: sum(P~ * 127/a) * a/127
+      // l accumulates P~ before quantisation: sum(P~ * M/a) * a/M
       lsum_run = lsum_run * alpha + tsum * (sP * up);
 
       __builtin_amdgcn_iglp_opt(1);
-      // ---- O^T = O^T * alpha + (a/127) sV (V^T P~^T), int32 over the BLK keys of one V block.
+      // ---- O^T = O^T * alpha + (a/M) sV (V^T P~^T) over the BLK keys of one V block.
       // O is rescaled only when its reference moved.
       const float spv = (sP * sV) * up;
       if (moved) {
@@ -280,13 +308,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       }
 #pragma unroll
       for (int ct = 0; ct < DC; ++ct) {
-        i32x16 acc = i32x16{};
+        typename C::acc16 acc{};
+        const int vr = 32 * ct + lq;
+        auto av = [&](int t) { return *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz_f<BLK>(vr, 2 * t + g)); };
 #pragma unroll
-        for (int t = 0; t < NSUB; ++t) {
-          const int vr = 32 * ct + lq;
-          const i32x4 av = *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz_f<BLK>(vr, 2 * t + g));
-          acc = mfma_i8_32x32x32(av, pc[t], acc);
-        }
+        for (int t = 0; t < NSUB; t += 2) acc = C::mma32x2(av(t), av(t + 1), pc[t], pc[t + 1], acc);
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[ct][r] = __builtin_fmaf(spv, (float)acc[r], o[ct][r]);
       }
@@ -322,8 +348,10 @@ template <int DT, int D, int BLK>
 static hipError_t launch_forward_t(const ForwardArgs& a, hipStream_t st) {
   const long long nq = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
   const dim3 grid((unsigned)(nq * a.BH)), block(kWaves * 64);
-  return a.q_smooth ? launch_kernel(&fwd_kernel<DT, D, BLK, true>, grid, block, st, a)
-                    : launch_kernel(&fwd_kernel<DT, D, BLK, false>, grid, block, st, a);
+  if (a.fmt == FMT_FP8)   // (Q-smoothing takes INT8 codes only; the API refuses it with FP8)
+    return a.q_smooth ? hipErrorInvalidValue : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_FP8>, grid, block, st, a);
+  return a.q_smooth ? launch_kernel(&fwd_kernel<DT, D, BLK, true, FMT_INT8>, grid, block, st, a)
+                    : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_INT8>, grid, block, st, a);
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st) {

@@ -34,6 +34,7 @@ struct PrologueArgs {
   int qk_norm, k_smooth, q_smooth;
   float eps;
   int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
+  int fmt;                           // code format: FMT_INT8 or FMT_FP8
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 
@@ -47,6 +48,7 @@ struct ForwardArgs {
   int causal, q_smooth;
   float sm_scale;
   int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
+  int fmt;                           // code format: FMT_INT8 or FMT_FP8
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 
@@ -72,6 +74,7 @@ struct BackwardArgs {
   int causal, qk_norm, q_smooth;
   float sm_scale;
   int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
+  int fmt;                           // code format: FMT_INT8 or FMT_FP8
   Strides16 x16;                     // layout of the 16-bit tensors
 };
 

@@ -149,21 +149,22 @@ __device__ __forceinline__ float slice_absmax(const Slice<D, BLK>& s, float* red
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Codes of the thread's values under the block's absmax a, token-major; scale a/127.
+// Codes of the thread's values under the block's absmax a, token-major; scale a/M with
+// M = 127 (INT8) or 448 (FP8 e4m3).
 template <int D, int BLK>
-__device__ __forceinline__ void quant_slice_token_major(const Slice<D, BLK>& s, float a, int8_t* __restrict__ blk_codes,
-                                                        float* __restrict__ scale_out, int j, int ch) {
+__device__ __forceinline__ void quant_slice_token_major(const Slice<D, BLK>& s, float a, bool fp8,
+                                                        int8_t* __restrict__ blk_codes, float* __restrict__ scale_out,
+                                                        int j, int ch) {
   using S = Slice<D, BLK>;
-  const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-  if (threadIdx.x == 0) *scale_out = a > 0.0f ? a / 127.0f : 0.0f;
+  const float M = fp8 ? 448.0f : 127.0f;
+  const float inv = a > 0.0f ? M / a : 0.0f;
+  if (threadIdx.x == 0) *scale_out = a > 0.0f ? a / M : 0.0f;
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
     int8_t* dst = blk_codes + (size_t)(16 * p + j) * D + ch * S::CW;
-    const unsigned w0 = pack4_lo_bytes(quant_word(s.x[p][0], inv), quant_word(s.x[p][1], inv),
-                                       quant_word(s.x[p][2], inv), quant_word(s.x[p][3], inv));
+    const unsigned w0 = code_word(fp8, s.x[p][0], s.x[p][1], s.x[p][2], s.x[p][3], inv);
     if constexpr (S::CW == 8) {
-      const unsigned w1 = pack4_lo_bytes(quant_word(s.x[p][4], inv), quant_word(s.x[p][5], inv),
-                                         quant_word(s.x[p][6], inv), quant_word(s.x[p][7], inv));
+      const unsigned w1 = code_word(fp8, s.x[p][4], s.x[p][5], s.x[p][6], s.x[p][7], inv);
       *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
     } else {
       *reinterpret_cast<unsigned*>(dst) = w0;
@@ -201,13 +202,18 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   if (tensor == 2) {
     // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token].
     const float amax = slice_absmax<D, BLK>(s, lds.red);
-    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-    if (threadIdx.x == 0) a.Vs[sidx] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    const bool fp8 = a.fmt == FMT_FP8;
+    const float M = fp8 ? 448.0f : 127.0f;
+    const float inv = amax > 0.0f ? M / amax : 0.0f;
+    if (threadIdx.x == 0) a.Vs[sidx] = amax > 0.0f ? amax / M : 0.0f;
 #pragma unroll
     for (int p = 0; p < S::P; ++p)
 #pragma unroll
-      for (int i = 0; i < S::CW; ++i)
-        lds.vt[ch * S::CW + i][16 * p + j] = (int8_t)quant_word(s.x[p][i], inv);
+      for (int i = 0; i < S::CW; i += 4) {
+        const unsigned wd = code_word(fp8, s.x[p][i], s.x[p][i + 1], s.x[p][i + 2], s.x[p][i + 3], inv);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lds.vt[ch * S::CW + i + u][16 * p + j] = (int8_t)(wd >> (8 * u));
+      }
     __syncthreads();
     constexpr int kRowChunks = BLK / 16;
     for (int e = threadIdx.x; e < D * kRowChunks; e += kThreads) {
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   }
   if (tensor == 1 && a.q_smooth) return;   // the keys' codes and biases come from pass2
   const float amax = slice_absmax<D, BLK>(s, lds.red);
-  quant_slice_token_major<D, BLK>(s, amax, (tensor == 0 ? a.Qc : a.Kc) + tok0 * D,
+  quant_slice_token_major<D, BLK>(s, amax, a.fmt == FMT_FP8, (tensor == 0 ? a.Qc : a.Kc) + tok0 * D,
                                   (tensor == 0 ? a.Qs : a.Ks) + sidx, j, ch);
 }
 
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void prologue_pass2(PrologueArgs a) {
     }
   }
   const float amax = slice_absmax<D, BLK>(s, red);
-  quant_slice_token_major<D, BLK>(s, amax, (is_q ? a.Qc : a.Kc) + tok0 * D, (is_q ? a.Qs : a.Ks) + sidx, j, ch);
+  quant_slice_token_major<D, BLK>(s, amax, a.fmt == FMT_FP8, (is_q ? a.Qc : a.Kc) + tok0 * D, (is_q ? a.Qs : a.Ks) + sidx, j, ch);
   if (is_q || !a.q_smooth) return;
   // key bias b = Ks * (codes . q_mean): the codes as quant_slice_token_major made them
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;

@@ -74,8 +74,9 @@ typedef enum {
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N > 2^22, or B*H > 2^24                  */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
-                                   layout, eps < 0, qk_gain or normed_grads without
-                                   qk_norm, normed_grads with qk_gain                       */
+                                   layout or fmt, eps < 0, qk_gain or normed_grads
+                                   without qk_norm, normed_grads with qk_gain, FP8 with
+                                   q_smooth                                                 */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
@@ -104,7 +105,18 @@ typedef struct {
   int32_t normed_grads; /* nonzero (with qk_norm, without qk_gain): the backward returns dQ,
                            dK with respect to the normalised Q^, K^ (before smoothing) and
                            leaves the RMSNorm backward to the caller                         */
+  int32_t fmt;          /* sagebwd_fmt of the six quantised products' codes (INT8 or FP8)     */
 } sagebwd_params;
+
+/* Code format of the six quantised products (SageBwd article, precision-split paragraph,
+ * which names FP8 as the alternative low-bit format of the same split). SAGEBWD_FMT_INT8:
+ * codes in [-127, 127], scale absmax/127, int32 products (the method as described above).
+ * SAGEBWD_FMT_FP8: OCP float8 e4m3fn codes (bias 7, subnormals kept, largest finite 448),
+ * scale absmax/448, codes = e4m3 round-to-nearest-even of fl(x * (448/absmax)); the same
+ * blocks, tiles, byte layouts and buffer sizes, products accumulated by the FP8 matrix
+ * cores in float32 (not exactly). In-kernel tiles (P~, P, dS) round fl(x * 448/absmax) with
+ * the hardware reciprocal. FP8 is not available with q_smooth (SAGEBWD_ERR_UNSUPPORTED). */
+typedef enum { SAGEBWD_FMT_INT8 = 0, SAGEBWD_FMT_FP8 = 1 } sagebwd_fmt;
 
 /* Memory layout of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV; contiguous either way).
  * BHND is [B,H,N,d]; BNHD is [B,N,H,d], the layout a fused QKV projection produces, read and

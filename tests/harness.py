@@ -26,12 +26,13 @@ def header_functions() -> list:
     return sorted(set(re.findall(r"^\s*(?:size_t|sagebwd_status|const char\*)\s+(sagebwd_\w+)\s*\(", text, re.M)))
 
 
-def spec_for(w: wl.Workload, dtype: Optional[str] = None, normed_grads: bool = False) -> oq.Spec:
+def spec_for(w: wl.Workload, dtype: Optional[str] = None, normed_grads: bool = False, fmt: str = "int8") -> oq.Spec:
     c = header_constants()
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
                    fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
-                   bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth, normed_grads=normed_grads)
+                   bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth, normed_grads=normed_grads,
+                   fmt=fmt)
 
 
 def rel_l2(a, b) -> float:
@@ -57,11 +58,11 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 # ------------------------------------------------------------------------------- GPU side
 
 def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd", qk_gain: bool = False,
-               normed_grads: bool = False):
+               normed_grads: bool = False, fmt: str = "int8"):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
                            dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout, qk_gain=qk_gain,
-                           normed_grads=normed_grads)
+                           normed_grads=normed_grads, fmt=fmt)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -78,15 +79,16 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
             pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd",
-            gains=None, normed_grads: bool = False) -> Dict[str, np.ndarray]:
+            gains=None, normed_grads: bool = False, fmt: str = "int8") -> Dict[str, np.ndarray]:
     """Run the HIP path and return host copies (numpy) of everything it produced. With
     layout "bnhd" the 16-bit tensors are handed to the library as [B,N,H,d] (a transposed
     copy of the same values) and its O, dQ, dK, dV are returned transposed back. gains:
     optional (q_gain, k_gain) float32 [H, d] arrays (learnable QK-norm gains); their
-    gradients come back as dq_gain, dk_gain."""
+    gradients come back as dq_gain, dk_gain. fmt: "int8" or "fp8" codes (FP8 codes come back
+    as their uint8 bit patterns, like the oracle's)."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w, dq_mode, layout, qk_gain=gains is not None, normed_grads=normed_grads)
+    p = params_for(w, dq_mode, layout, qk_gain=gains is not None, normed_grads=normed_grads, fmt=fmt)
     gq = gk = None
     if gains is not None:
         gq, gk = (torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda:0") for g in gains)
@@ -121,6 +123,10 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
         npk = w.B * w.H * lay["tiles_per_head_q"] * lay["packet_bytes"]   # only the packet region is decoded
         ws = g["workspace"][:npk].cpu().numpy()
         res.update(decode_packets(ws, lay, w))
+    if fmt == "fp8":
+        for k in ("Qc", "Kc", "Vtc", "dOtc"):
+            if k in res:
+                res[k] = res[k].view(np.uint8)
     return res
 
 

@@ -14,7 +14,7 @@ lib = _lib.load()  # fails loudly if the library was not built
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
                 dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND, qk_gain=0,
-                normed_grads=0)
+                normed_grads=0, fmt=_lib.FMT_INT8)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -74,6 +74,9 @@ def test_invalid_params_rejected(call):
     assert call(P(qk_gain=1, qk_norm=0)) == -3   # gains need QK-norm
     assert call(P(normed_grads=1, qk_norm=0)) == -3
     assert call(P(normed_grads=1, qk_gain=1)) == -3
+    assert call(P(fmt=2)) == -3
+    assert call(P(fmt=-1)) == -3
+    assert call(P(fmt=_lib.FMT_FP8, q_smooth=1)) == -3   # Q-smoothing sums INT8 codes
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
     assert call(P(B=1 << 13, H=1 << 12)) == -2
@@ -197,3 +200,13 @@ def test_qk_gain_arguments():
     base = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P()))
     gains = lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(qk_gain=1)))
     assert gains == base + up(4 * 2 * 4 * 64) + up(4 * 2 * 4 * 64)   # N/64 and N/blk tiles of d floats
+
+
+def test_fp8_workspace_sizes_equal_int8():
+    # FP8 codes keep the INT8 byte layouts: every buffer and workspace has the same size
+    for kw in (dict(), dict(dq_mode=2), dict(k_smooth=0), dict(N=200)):
+        a, b = P(**kw), P(fmt=_lib.FMT_FP8, **kw)
+        assert lib.sagebwd_backward_workspace_bytes(ctypes.byref(a)) == \
+            lib.sagebwd_backward_workspace_bytes(ctypes.byref(b))
+        assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(a)) == \
+            lib.sagebwd_prologue_workspace_bytes(ctypes.byref(b))
