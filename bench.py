@@ -60,7 +60,7 @@ def traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, heads: int):
+def cpu_baseline(w, x, heads: int, fmt: str = "int8"):
     """The plain CPU oracle (as it stands) on `heads` heads of the same workload."""
     from threadpoolctl import threadpool_info
     from oracle import quant as oq
@@ -69,7 +69,7 @@ def cpu_baseline(w, x, heads: int):
     ws = w.with_shape(B=1, H=heads)
     sl = lambda a: np.ascontiguousarray(a.reshape((-1,) + a.shape[2:])[:heads].reshape((1, heads) + a.shape[2:]))
     Qf, Kf, Vf, dOf = (wl.bits_to_f32(sl(x[k]), w.dtype) for k in ("Q", "K", "V", "dO"))
-    spec = spec_for(ws)
+    spec = spec_for(ws, fmt=fmt)
     t0 = time.perf_counter()
     oq.run(Qf, Kf, Vf, dOf, spec)
     dt = time.perf_counter() - t0
@@ -101,6 +101,8 @@ def main():
                     help="time the Q-smoothing variant on the same inputs (default: off, as the metric)")
     ap.add_argument("--layout", default="bhnd", choices=("bhnd", "bnhd"),
                     help="memory layout of the 16-bit tensors handed to the library (default [B,H,N,d])")
+    ap.add_argument("--fmt", default="int8", choices=("int8", "fp8"),
+                    help="code format of the six quantised products (default INT8, as the metric)")
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
@@ -124,7 +126,7 @@ def main():
         f"qk_norm={w.qk_norm} k_smooth={w.k_smooth} blk={w.blk}")
     x = wl.make_inputs(w)
     p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                        q_smooth=w.q_smooth, layout=args.layout)
+                        q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt)
     dev = torch.device("cuda:0")
     Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
     if args.layout == "bnhd":
@@ -183,7 +185,7 @@ def main():
     ops_main = 10 * w.d * pairs       # bwd_main: recomputed QK^T, dV, dK, dQ (INT8) + dP (FP16)
     ach_main = ops_main / (stage_ms["bwd_main"] * 1e-3) / 1e12
     peak_main = weighted_peak(4, 1)
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile() if args.fmt == "int8" else None   # (counters of the INT8 kernel)
     # each stage's own ideal: MFMA-bound stages at their dense peaks, the others at 8 TB/s of
     # their algorithmic HBM bytes (E = B*H*N*d elements: prologue reads Q,K,V and writes three
     # code tensors; bwd_pre reads dO, O, Qc, Kc and writes the packets and K^T codes; the dQ pass
@@ -211,7 +213,7 @@ def main():
             for t in (qg, kg, vg):
                 t.grad = None
             o = sagebwd_attention(qg, kg, vg, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
-                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth, layout=args.layout)
+                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt)
             o.backward(dO)
 
         for _ in range(2):
@@ -229,7 +231,8 @@ def main():
         del qg, kg, vg
 
     out = {
-        "metric": "INT8 attention fwd+bwd TOPS at B2 H16 N8192 d128 causal; % of MFMA peak",
+        "metric": ("INT8" if args.fmt == "int8" else "FP8 (e4m3)")
+        + " attention fwd+bwd TOPS at B2 H16 N8192 d128 causal; % of MFMA peak",
         "value": round(value, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -239,12 +242,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp16",
+        "dtype": "int8+fp16" if args.fmt == "int8" else "fp8e4m3+fp16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} H{w.H} N{w.N} d{w.d} causal {w.dtype} QK-norm "
                                f"K-smoothing blk{w.blk}{' Q-smoothing' if w.q_smooth else ''} (prologue+fwd+bwd)",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal, "blk": w.blk,
-                   "dtype": w.dtype, "q_smooth": w.q_smooth, "layout": args.layout, "parallelism": "single GPU"},
+                   "dtype": w.dtype, "q_smooth": w.q_smooth, "layout": args.layout, "fmt": args.fmt,
+                   "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak_step, 4),
         "step_ms": {k: round(v, 4) for k, v in step_stats.items()},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
@@ -257,7 +261,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_heads} head(s)...")
-        cb = cpu_baseline(w, x, args.cpu_heads)
+        cb = cpu_baseline(w, x, args.cpu_heads, args.fmt)
         log(f"[bench] CPU oracle: {cb['seconds']:.1f} s, {cb['value']:.5f} TOPS, {cb['cores']} threads")
         cb.pop("seconds")
         out["cpu_baseline"] = cb

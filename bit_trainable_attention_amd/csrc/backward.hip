@@ -449,6 +449,17 @@ void bwd_main(BackwardArgs a) {
   float dsf[NS][4];
   i32x4 qtr[NH][NCT];
   i32x4 dc[NH];
+  // FP8 with two 64-row halves: the Q^T operands and dS codes of both halves as one 32-byte
+  // operand per lane, so dK takes one K = 128 product without operand copies. (dV keeps two
+  // K = 32 products per half, and so does dK in the atomic dQ mode: 32-byte operands there
+  // push the kernel past 256 registers.)
+  constexpr bool P8 = FMT == FMT_FP8 && NH == 2 && SPILL;
+  [[maybe_unused]] i32x8 qtr8[NCT];
+  [[maybe_unused]] i32x8 dc8;
+  auto dch = [&](int h) -> i32x4 {
+    if constexpr (P8) return i32x4{dc8[4 * h], dc8[4 * h + 1], dc8[4 * h + 2], dc8[4 * h + 3]};
+    else return dc[h];
+  };
 
   // S = Q K~^T and dP = dO V^T for the 16-row sub-tiles of the tile at byte offset bofs
   // (LLVM's interleaving strategy 1 for this block: measured 1.7-2.6% faster than the
@@ -532,8 +543,6 @@ void bwd_main(BackwardArgs a) {
       for (int n = 0; n < NCT; ++n) {
         typename C::acc4 acc{};
         auto ao = [&](int h) { return *reinterpret_cast<const i32x4*>(buf + h * P::kBytes + oT + 16 * n * kPq); };
-        // (FP8: two K = 32 products per 64 rows; joining the two 64-row halves into one
-        // K = 128 product needs 8-register operand copies that spill at d = 128)
 #pragma unroll
         for (int h = 0; h < NH; ++h) acc = C::mma16(ao(h), pc[h], acc);
 #pragma unroll
@@ -549,7 +558,11 @@ void bwd_main(BackwardArgs a) {
       for (int h = 0; h < NH; ++h) {
         const i32x2 x0 = lds_read_tr8(pn + h * P::kBytes);
         const i32x2 x1 = lds_read_tr8(pn + h * P::kBytes + 32 * D);
-        qtr[h][n] = i32x4{x0[0], x0[1], x1[0], x1[1]};
+        if constexpr (P8) {
+          qtr8[n][4 * h] = x0[0]; qtr8[n][4 * h + 1] = x0[1]; qtr8[n][4 * h + 2] = x1[0]; qtr8[n][4 * h + 3] = x1[1];
+        } else {
+          qtr[h][n] = i32x4{x0[0], x0[1], x1[0], x1[1]};
+        }
       }
     }
   };
@@ -568,7 +581,9 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float* v = dsf[4 * h + t];
-        dc[h][t] = (int)tile_code_word<FMT>(v[0], v[1], v[2], v[3], dinv);
+        const int wd = (int)tile_code_word<FMT>(v[0], v[1], v[2], v[3], dinv);
+        if constexpr (P8) dc8[4 * h + t] = wd;
+        else dc[h][t] = wd;
       }
     if constexpr (QS) {
       static_assert(FMT == FMT_INT8, "Q-smoothing sums INT8 codes");
@@ -584,8 +599,12 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
       for (int n = 0; n < NCT; ++n) {
         typename C::acc4 acc{};
+        if constexpr (P8) {
+          acc = C::mma16w(qtr8[n], dc8, acc);
+        } else {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) acc = C::mma16(qtr[h][n], dc[h], acc);
+          for (int h = 0; h < NH; ++h) acc = C::mma16(qtr[h][n], dc[h], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) dk[n][r] = __builtin_fmaf(sk, (float)acc[r], dk[n][r]);
       }
@@ -597,7 +616,7 @@ void bwd_main(BackwardArgs a) {
       const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt * NH);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        *reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq + 16 * swz_ds(kl, g)) = dc[h];
+        *reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq + 16 * swz_ds(kl, g)) = dch(h);
         if (l == 0) a.dsm[(ti + h) * KD + dg] = smc * sdS * sK;   // every wave of the group stores the same value
       }
     }
@@ -639,7 +658,7 @@ void bwd_main(BackwardArgs a) {
         int8_t* dst = lds + bofs;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-          *reinterpret_cast<i32x4*>(dst + kl * TQ + 16 * swz<TQ>(kl, 4 * h + g)) = dc[h];
+          *reinterpret_cast<i32x4*>(dst + kl * TQ + 16 * swz<TQ>(kl, 4 * h + g)) = dch(h);
         // the scale of every 64-key dS tile of the block
         float sc[KD];
 #pragma unroll

@@ -212,6 +212,10 @@ template <> struct Codes<FMT_FP8> {
     const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
+  // operands already held as 32 bytes per lane
+  __device__ static __forceinline__ acc4 mma16w(i32x8 a, i32x8 b, acc4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
   __device__ static __forceinline__ acc16 mma32x2(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1, acc16 c) {
     const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
