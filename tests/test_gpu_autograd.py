@@ -22,7 +22,7 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _wrapper_run(w, x, layout):
+def _wrapper_run(w, x, layout, fmt="int8"):
     import torch
     from bit_trainable_attention_amd.autograd import sagebwd_attention
     q, k, v, dO = (to_device(x[n], w.dtype) for n in ("Q", "K", "V", "dO"))
@@ -30,7 +30,7 @@ def _wrapper_run(w, x, layout):
         q, k, v, dO = (t.transpose(1, 2).contiguous() for t in (q, k, v, dO))
     q, k, v = (t.requires_grad_() for t in (q, k, v))
     O, lse = sagebwd_attention(q, k, v, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth, blk=w.blk,
-                               eps=w.eps, sm_scale=w.sm_scale, layout=layout, return_lse=True)
+                               eps=w.eps, sm_scale=w.sm_scale, layout=layout, return_lse=True, fmt=fmt)
     O.backward(dO)
     torch.cuda.synchronize()
     out = {"O": O, "dQ": q.grad, "dK": k.grad, "dV": v.grad}
@@ -51,6 +51,17 @@ def test_wrapper_equals_c_abi(name, w):
         got = _wrapper_run(w, x, layout)
         for n in ("O", "LSE", "dQ", "dK", "dV"):
             assert np.array_equal(got[n], direct[n]), (layout, n, float(np.max(np.abs(got[n] - direct[n]))))
+
+
+def test_wrapper_fp8_equals_c_abi():
+    """fmt="fp8" reaches the library through the wrapper: the same bits as the C ABI's FP8 run."""
+    name, w = CASES[0]
+    _say(f"[autograd] {name}: FP8 wrapper")
+    x = host_inputs(w)
+    direct = gpu_run(w, x, fmt="fp8")
+    got = _wrapper_run(w, x, "bhnd", fmt="fp8")
+    for n in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(got[n], direct[n]), (n, float(np.max(np.abs(got[n] - direct[n]))))
 
 
 def test_wrapper_meets_oracle_bar():
