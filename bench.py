@@ -182,25 +182,36 @@ def main():
     ops = w.algorithmic_ops()
     value = ops / (ms_per_step * 1e-3) / 1e12
     peak_step = weighted_peak(6, 1)
-    ops_main = 10 * w.d * pairs       # bwd_main: recomputed QK^T, dV, dK, dQ (INT8) + dP (FP16)
+    # bwd_main's products depend on where dQ = dS K runs: with the dS spill (the default at this
+    # size) bwd_main does the recomputed QK^T, dV, dK (INT8) and dP (FP16), 8*d ops per visible
+    # pair against a 3:1 INT8/FP16 peak, and the dQ pass does dQ (2*d INT8 ops per pair); with
+    # float32 atomics bwd_main does all five (10*d, 4:1) and the dQ pass only the epilogue
+    spill = bool(api.backward_workspace_layout(p)["spill"])
+    n_i8_main = 3 if spill else 4
+    ops_main = (2 * n_i8_main + 2) * w.d * pairs
     ach_main = ops_main / (stage_ms["bwd_main"] * 1e-3) / 1e12
-    peak_main = weighted_peak(4, 1)
+    peak_main = weighted_peak(n_i8_main, 1)
+    ops_dq = 2 * w.d * pairs if spill else 0
     traffic = traffic_from_profile() if args.fmt == "int8" else None   # (counters of the INT8 kernel)
-    # each stage's own ideal: MFMA-bound stages at their dense peaks, the others at 8 TB/s of
-    # their algorithmic HBM bytes (E = B*H*N*d elements: prologue reads Q,K,V and writes three
-    # code tensors; bwd_pre reads dO, O, Qc, Kc and writes the packets and K^T codes; the dQ pass
-    # reads one dS byte per visible pair, the K^T codes and Q, and writes dQ)
+    # each stage's own ideal: the stages with products at their dense MFMA peaks (forward: QK^T
+    # and PV in INT8; bwd_main as above; the dQ pass: dS K in INT8), the others at 8 TB/s of
+    # their algorithmic HBM bytes (E = B*H*N*d elements: the prologue reads Q, K, V and writes
+    # three code tensors, 9E; bwd_pre reads dO, O, Qc, Kc and writes the packets, 11E). The dS
+    # spill is the dQ pass's working traffic, not algorithmic bytes; without it the dQ pass is
+    # the RMSNorm backward over the float32 accumulator (reads 4E + Q 2E, writes dQ 2E)
     E = w.B * w.H * w.N * w.d
     hbm = 8e12
     stage_ideal_ms = {"prologue": 9 * E / hbm * 1e3, "forward": 4 * w.d * pairs / (PEAK_I8 * 1e12) * 1e3,
                       "bwd_pre": 11 * E / hbm * 1e3, "bwd_main": ops_main / (peak_main * 1e12) * 1e3,
-                      "bwd_dq": (pairs + 5 * E) / hbm * 1e3}
+                      "bwd_dq": ops_dq / (PEAK_I8 * 1e12) * 1e3 if spill else 8 * E / hbm * 1e3}
     log(f"[bench] {ms_per_step:.3f} ms/step, {value:.1f} TOPS = {100 * value / peak_step:.1f}% of the "
         f"{peak_step:.0f} TOPS INT8/FP16 (6:1) dense peak; stages (ms): "
         + ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
     fwd_ops = 4 * w.d * pairs
     log(f"[bench] forward {fwd_ops / (stage_ms['forward'] * 1e-3) / 1e12:.1f} TOPS (INT8 peak {PEAK_I8:.0f}); "
-        f"bwd_main {ach_main:.1f} TOPS (4:1 INT8/FP16 peak {peak_main:.0f})")
+        f"bwd_main {ach_main:.1f} TOPS ({n_i8_main}:1 INT8/FP16 peak {peak_main:.0f}); dQ pass "
+        + (f"{ops_dq / (stage_ms['bwd_dq'] * 1e-3) / 1e12:.1f} TOPS (INT8 peak {PEAK_I8:.0f})" if spill
+           else "epilogue only (atomic dQ)"))
 
     autograd_ms = None
     if not args.no_autograd:
@@ -255,7 +266,12 @@ def main():
         "stages_frac_of_ideal": {k: round(stage_ideal_ms[k] / stage_ms[k], 4) for k in stage_ms},
         "roofline": {"kernel": "bwd_main", "bound": "mfma", "achieved": round(ach_main, 2),
                      "peak": round(peak_main, 1), "unit": "TFLOP/s", "frac": round(ach_main / peak_main, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "ops_per_pair": (2 * n_i8_main + 2) * w.d, "pairs": pairs,
+                     "mix": f"{n_i8_main}:1 INT8:FP16 ({'dS spill: dQ in the dQ pass' if spill else 'atomic dQ'})"},
+        "dq_pass": ({"ops_per_pair": 2 * w.d, "achieved": round(ops_dq / (stage_ms["bwd_dq"] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_I8, "unit": "TOPS", "frac": round(ops_dq / (stage_ms["bwd_dq"] * 1e-3) / 1e12
+                                                                   / PEAK_I8, 4)} if spill else None),
         "cpu_baseline": None,
         "autograd_ms_per_step": None if autograd_ms is None else round(autograd_ms, 4),
     }

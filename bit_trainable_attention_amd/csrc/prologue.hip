@@ -98,10 +98,12 @@ __device__ __forceinline__ float row_tree_sum(float v) {
   return v;
 }
 
-// QK-norm of the thread's tokens in place; lane ch == 0 writes rstd of each token.
+// QK-norm of the thread's tokens in place; lane ch == 0 writes rstd of each token. Tokens
+// from nvalid on (the padding of a ragged last block) are zeros and get rstd = 1, so they stay
+// zero even with eps = 0 (where 1/sqrt(0) would make them 0 * inf = NaN).
 template <int D, int BLK>
 __device__ __forceinline__ void qk_norm_slice(Slice<D, BLK>& s, float eps, float* __restrict__ rstd_out, int j,
-                                              int ch) {
+                                              int ch, int nvalid) {
   using S = Slice<D, BLK>;
 #pragma unroll
   for (int p = 0; p < S::P; ++p) {
@@ -113,7 +115,7 @@ __device__ __forceinline__ void qk_norm_slice(Slice<D, BLK>& s, float eps, float
     }
     const float ss = row_tree_sum(cs);
     const float ms = ss / (float)D;
-    const float r = 1.0f / __builtin_sqrtf(ms + eps);
+    const float r = 16 * p + j < nvalid ? 1.0f / __builtin_sqrtf(ms + eps) : 1.0f;
 #pragma unroll
     for (int i = 0; i < S::CW; ++i) s.x[p][i] = s.x[p][i] * r;
     if (ch == 0) rstd_out[16 * p + j] = r;
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
 
   float* rstd_out = (tensor == 0 ? a.q_rstd : a.k_rstd) + tok0;
   if (a.qk_norm) {
-    qk_norm_slice<D, BLK>(s, a.eps, rstd_out, j, ch);
+    qk_norm_slice<D, BLK>(s, a.eps, rstd_out, j, ch, a.Nv - blk_id * BLK);
     apply_gain_slice<D, BLK>(s, tensor == 0 ? a.q_gain : a.k_gain, bh % a.x16.H, ch);
   } else if (ch == 0) {
 #pragma unroll

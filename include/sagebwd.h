@@ -43,7 +43,8 @@
  *     N mod blk tokens (its absmax, and the means, cover those tokens only). The 16-bit
  *     tensors hold exactly N tokens per head; every array of the library's own (codes,
  *     scales, statistics, lse) holds Np = N rounded up to a multiple of blk, the tokens from
- *     N on being padding (codes 0; their lse and statistics are not meaningful).
+ *     N on being padding (codes 0, rstd 1; their lse and other statistics are not
+ *     meaningful). Padding tokens are never normalised, so eps = 0 is valid with any N.
  *   - The caller owns every buffer. The library allocates nothing, keeps no state between
  *     calls, never synchronises, and is re-entrant; all work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream). Calls sharing a workspace must be
@@ -90,7 +91,8 @@ typedef struct {
   int32_t causal;       /* nonzero: key j is visible to query i iff j <= i                  */
   int32_t qk_norm;      /* nonzero: RMSNorm Q and K per token (gain 1 unless qk_gain)       */
   int32_t k_smooth;     /* nonzero: subtract K's per-channel mean before quantising         */
-  float eps;            /* RMSNorm epsilon (>= 0), e.g. 1e-6                                */
+  float eps;            /* RMSNorm epsilon (>= 0), e.g. 1e-6; with eps = 0 an all-zero
+                           token has no defined norm and its results are unspecified          */
   float sm_scale;       /* softmax scale; <= 0 selects 1/sqrt(d)                            */
   int32_t dtype;        /* sagebwd_dtype of Q, K, V, dO, O, dQ, dK, dV                       */
   int32_t dq_mode;      /* how the backward reduces dQ over key blocks (sagebwd_dq_mode)     */

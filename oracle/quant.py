@@ -376,6 +376,12 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
     if spec.qk_norm:
         Qn, q_rstd = rms_norm_f32(Q, spec.eps)
         Kn, k_rstd = rms_norm_f32(K, spec.eps)
+        if spec.N < spec.Np:
+            # padding tokens are not normalised: rstd 1, values 0 (with eps = 0 their rstd
+            # would be 1/sqrt(0) and 0 * inf would put NaN into every sum over the block)
+            for xn, r in ((Qn, q_rstd), (Kn, k_rstd)):
+                r[..., spec.N:] = F32(1.0)
+                xn[..., spec.N:, :] = F32(0.0)
         Qh, Kh = apply_gain_f32(Qn, q_gain), apply_gain_f32(Kn, k_gain)
     else:
         if q_gain is not None or k_gain is not None:

@@ -23,6 +23,9 @@ CASES = [
     ("d64_bnhd_gains_qsmooth_n257", W["llama325m"].with_shape(B=2, H=2, N=257, q_smooth=True, q_bias_var=4.0),
      0, "bnhd", True),
     ("d64_noncausal_blk128_n65", W["llama325m"].with_shape(B=1, H=2, N=65, blk=128, causal=False), 0, "bhnd", False),
+    # eps = 0: the padding tokens must not be normalised (1/sqrt(0) would turn them into NaN)
+    ("d128_eps0_gains_n200", W["n8192_d128"].with_shape(B=1, H=2, N=200, eps=0.0), 0, "bhnd", True),
+    ("d64_eps0_atomic_n100", W["llama325m"].with_shape(B=1, H=2, N=100, eps=0.0), 2, "bhnd", False),
 ]
 
 

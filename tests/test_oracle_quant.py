@@ -526,6 +526,29 @@ def test_ragged_block_quant_is_the_rule_on_valid_tokens():
     assert np.allclose(pro["k_mean"], kh.mean(axis=2), atol=1e-6)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_eps_zero(causal):
+    """eps = 0 with a ragged last block: the zero padding tokens are not normalised (rstd 1,
+    values 0), so no 0 * inf = NaN reaches the block sums, the K mean or any code; the
+    identity-quantiser path still equals exact attention (eps = 0) on the N real tokens, and
+    the INT8 path stays finite with the padding codes 0."""
+    rng = np.random.default_rng(141 + causal)
+    B, H, N, d, blk = 1, 2, 100, 32, 64
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)).astype(F32) for _ in range(4))
+    K = (K + 2 * rng.standard_normal((1, H, 1, d))).astype(F32)
+    spec = oq.Spec(N=N, d=d, blk=blk, causal=causal, qk_norm=True, k_smooth=True, dtype="f64", eps=0.0)
+    got = oq.run(Q, K, V, dO, spec, tile_quant=oq.identity_tile_quant, block_quant=oq.identity_block_quant)
+    ref = _exact_all(Q, K, V, dO, spec)
+    for name in ("O", "dQ", "dK", "dV"):
+        assert _rel(got[name], ref[name]) < 3e-6, name
+    q = oq.run(Q, K, V, dO, oq.Spec(N=N, d=d, blk=blk, causal=causal, qk_norm=True, k_smooth=True, eps=0.0))
+    for name in ("k_mean", "q_rstd", "k_rstd", "Qs", "Ks", "O", "dQ", "dK", "dV"):
+        assert np.all(np.isfinite(q[name])), name
+    assert np.all(q["q_rstd"][..., N:] == 1) and np.all(q["k_rstd"][..., N:] == 1)
+    assert not np.any(q["Kc"][..., N:, :]) and not np.any(q["Qc"][..., N:, :])
+    assert np.any(q["Kc"][..., :N, :])
+
+
 # ------------------------------------------------------------------- FP8 (e4m3) recipe
 
 def test_e4m3_matches_torch_conversion():
