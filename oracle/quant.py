@@ -30,11 +30,14 @@ What is computed, in the order of the SageBwd article:
      subtracted before quantising; every score gets back the per-key bias
      b_k = (K mu_Q)_k (key_bias), and dK^ gets dK_bias = (dS^T 1) mu_Q^T
      (q_smooth_dk_bias); dQ is unchanged.
-  8. Optional FP8 recipe (Spec.fmt = "fp8"; SageBwd article, precision split paragraph,
-     where the FP8 alternative of the quantised products is named): every quantiser of
-     steps 3-5 keeps its tile and its absmax rule but maps onto e4m3 (OCP float8 e4m3fn,
-     largest finite 448) instead of [-127, 127]: scale a / 448, code e4m3_rne(x * 448 / a).
-     The products are formed from the codes' values exactly as in the INT8 recipe.
+  8. Optional FP8 recipe (Spec.fmt = "fp8"). The SageBwd article's precision split names
+     only INT8 and FP16; FP8 is named by the Full-Stack FP4 page (section 1, problem
+     definition: attention is commonly kept in BF16 or FP8) and by the NVFP4 / Quartet 2
+     page (block-scaled FP8 training; E4M3 as an FP8 format). The recipe keeps the
+     article's split and swaps the format: every quantiser of steps 3-5 keeps its tile and
+     its absmax rule but maps onto e4m3 (OCP float8 e4m3fn, largest finite 448) instead of
+     [-127, 127]: scale a / 448, code e4m3_rne(x * 448 / a). The products are formed from
+     the codes' values exactly as in the INT8 recipe.
 
 Precision: steps 1-3 are float32, one IEEE operation at a time, round to nearest
 even, in the order written (sums run over channels, or over tokens, in ascending
@@ -121,8 +124,11 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     """Round float64 values to fp16 or bf16 (nearest even); return them as float64.
 
     dtype "f64" leaves the values unrounded (used only by the oracle's own pins).
-    bf16 goes through float32 first; the two roundings can only differ from one
-    direct rounding on values within 2^-24 relative of a bf16 tie.
+    fp16 is one rounding of the float64 value. bf16 goes through float32 first; the two
+    roundings can only differ from one direct rounding on values within 2^-24 relative of
+    a bf16 tie.
+    Pinned by: test_oracle_tiles.py::test_round_to_dtype_matches_torch (torch's conversions,
+    ties, subnormals, overflow, and a double-rounding case of each branch).
     """
     x = np.asarray(x, dtype=np.float64)
     if dtype == "f64":  # no rounding: used by the reduction pins
@@ -143,7 +149,9 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def tree_f32(s: np.ndarray) -> np.ndarray:
     """Sum over the last axis (a power of two long) by a pairwise tree over consecutive
-    entries: (s0+s1), (s2+s3), ... then ((s0+s1)+(s2+s3)), ... down to one value, float32."""
+    entries: (s0+s1), (s2+s3), ... then ((s0+s1)+(s2+s3)), ... down to one value, float32.
+    Pinned by: test_oracle_quant.py::test_rms_norm_chunk_tree_order and
+    test_k_smooth_group_tree_order (hand-derived 2^24 absorption cases)."""
     s = np.asarray(s, dtype=F32)
     n = s.shape[-1]
     assert n >= 1 and n & (n - 1) == 0
@@ -162,6 +170,8 @@ def rms_norm_f32(x: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
     this one is the one a 16-lane row of the GPU computes (each lane one chunk, then a
     butterfly across the row).
     ms = fl(ss / d); rstd = fl(1 / fl(sqrt(fl(ms + eps)))); x^ = fl(x * rstd).
+    This order is a frozen part of the bit-exact contract: it is specified here and kernels
+    follow it, never the reverse.
     Returns (x^, rstd). SageBwd article, QK-norm paragraph (RMSNorm per token, gain 1).
     Pinned by: test_oracle_quant.py::test_rms_norm_* (hand example, order, error bound).
     """
@@ -191,7 +201,7 @@ def k_smooth_f32(khat: np.ndarray, blk: int, n_valid: Optional[int] = None) -> T
     pages fix no order; this is the one the GPU's 16 token slots per pass compute.
     Input [..., Np, d] with Np a multiple of blk; with n_valid < Np the rows from n_valid on
     are padding (zeros, which add nothing to the sums): mu = fl(tot / n_valid) and those
-    rows of K~ are 0. Returns (K~, mu [..., d]).
+    rows of K~ are 0. Returns (K~, mu [..., d]). The order is frozen like rms_norm_f32's.
     SageBwd article, K-smoothing paragraph (axis: see module docstring).
     Pinned by: test_oracle_quant.py::test_k_smooth_* and the softmax-invariance tests.
     """
@@ -241,6 +251,9 @@ def quant_blocks_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
 
     SageBwd article, per-block kernels paragraph. Returns (codes [..., N, d] int8,
     scales [..., N // blk] float32).
+    Pinned by: test_oracle_quant.py::test_lossless_block_quant_equals_exact (which block scale
+    multiplies which product), test_ragged_block_quant_is_the_rule_on_valid_tokens and the
+    hand-derived prologue fixtures.
     """
     x = np.asarray(x, dtype=F32)
     N, d = x.shape[-2], x.shape[-1]
@@ -286,7 +299,9 @@ def e4m3_encode(x32: np.ndarray) -> np.ndarray:
 
 
 def e4m3_decode(code: np.ndarray) -> np.ndarray:
-    """e4m3 bit patterns -> float64 values."""
+    """e4m3 bit patterns -> float64 values.
+    Pinned by: test_oracle_quant.py::test_e4m3_round_trip_and_ties (every finite code) and
+    test_e4m3_matches_torch_conversion."""
     c = np.asarray(code).astype(np.int64) & 0xFF
     s = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 15
@@ -299,7 +314,9 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
 def quant_rule_fp8_f32(x32: np.ndarray, axes: Tuple[int, ...]) -> Tuple[np.ndarray, np.ndarray]:
     """The FP8 rule: symmetric absmax over `axes`, scale s = fl(a / 448), inv = fl(448 / a),
     code = e4m3_rne(fl(x * inv)) (an all-zero block: scale 0, codes 0). Returns (codes as
-    uint8 e4m3 bit patterns, scales float32 with `axes` removed)."""
+    uint8 e4m3 bit patterns, scales float32 with `axes` removed).
+    Pinned by: test_oracle_quant.py::test_fp8_rule_properties and
+    test_fp8_lossless_block_quant_equals_exact."""
     x32 = np.asarray(x32, dtype=F32)
     a = np.max(np.abs(x32), axis=axes, keepdims=True)
     zero = a == 0
@@ -310,7 +327,8 @@ def quant_rule_fp8_f32(x32: np.ndarray, axes: Tuple[int, ...]) -> Tuple[np.ndarr
 
 
 def quant_blocks_fp8_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Per-block FP8 quantisation of [..., N, d]: one scale per blk tokens x d channels."""
+    """Per-block FP8 quantisation of [..., N, d]: one scale per blk tokens x d channels.
+    Pinned by: test_oracle_quant.py::test_fp8_lossless_block_quant_equals_exact."""
     x = np.asarray(x, dtype=F32)
     N, d = x.shape[-2], x.shape[-1]
     xb = x.reshape(x.shape[:-2] + (N // blk, blk, d))
@@ -321,7 +339,8 @@ def quant_blocks_fp8_f32(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarra
 
 def code_values(codes: np.ndarray) -> np.ndarray:
     """Values of codes as float64: e4m3 bit patterns (uint8) are decoded, INT8 codes and
-    identity "codes" are taken as they are."""
+    identity "codes" are taken as they are. Pinned by the lossless reductions of both
+    formats (test_oracle_quant.py::test_lossless_block_quant_equals_exact, _fp8_)."""
     codes = np.asarray(codes)
     if codes.dtype == np.uint8:
         return e4m3_decode(codes)
@@ -332,14 +351,16 @@ BlockQuant = Callable[[np.ndarray, int], Tuple[np.ndarray, np.ndarray]]
 
 
 def identity_block_quant(x: np.ndarray, blk: int) -> Tuple[np.ndarray, np.ndarray]:
-    """No quantisation: values pass through as float64 "codes" with block scales 1."""
+    """No quantisation: values pass through as float64 "codes" with block scales 1.
+    Pinned by: test_oracle_quant.py::test_identity_quant_equals_exact (any change to the
+    values breaks the reduction to exact attention)."""
     x = np.asarray(x, dtype=np.float64)
     return x, np.ones(x.shape[:-2] + (x.shape[-2] // blk,), dtype=np.float64)
 
 
 def _pad_rows(x: np.ndarray, Np: int, value: float = 0.0) -> np.ndarray:
     """x [..., n, ...] (rows on axis -2 for 4-d tensors, the last axis for [B,H,n]) padded
-    with `value` to Np rows."""
+    with `value` to Np rows. Pinned by: test_oracle_quant.py::test_identity_quant_ragged_n."""
     axis = -2 if x.ndim == 4 else -1
     n = x.shape[axis]
     if n == Np:
@@ -351,7 +372,9 @@ def _pad_rows(x: np.ndarray, Np: int, value: float = 0.0) -> np.ndarray:
 
 def apply_gain_f32(xn: np.ndarray, g: Optional[np.ndarray]) -> np.ndarray:
     """The QK-norm gain: x^ = fl(n * g[h, c]) for n [B,H,N,d] (the normalised tokens) and
-    g [H, d] float32 (one IEEE product per element); g None leaves n unchanged (gain 1)."""
+    g [H, d] float32 (one IEEE product per element); g None leaves n unchanged (gain 1).
+    Pinned by: test_oracle_quant.py::test_gain_prologue_power_of_two_exact and
+    test_identity_quant_with_gains."""
     if g is None:
         return xn
     return (xn * np.asarray(g, dtype=F32)[None, :, None, :]).astype(F32)
@@ -369,6 +392,9 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
     QK-norm is off), k_mean (float32 [B,H,d], 0 when smoothing is off), the normalised
     tokens before the gain Qn, Kn and after it Qhat, Khat (float32), which the RMSNorm
     backward and the gains' gradients need, and the gains (q_gain, k_gain; None = 1).
+    Pinned by: its steps' pins (rms_norm_f32, k_smooth_f32, quant_blocks_f32), the
+    hand-derived prologue fixtures, test_ragged_eps_zero and the reductions to exact
+    attention with norm, smoothing and gains on.
     """
     # a ragged last block: pad every head to Np rows with zero tokens, which change no block
     # absmax and no sum; the means divide by the N valid tokens (k_smooth_f32)
@@ -433,7 +459,8 @@ TileQuant = Callable[[np.ndarray], Tuple[np.ndarray, np.ndarray]]
 
 def fp8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise each tile x[h] with the FP8 rule, deciding in float32; codes returned as their
-    float64 values, scales as float64 [BH]."""
+    float64 values, scales as float64 [BH].
+    Pinned by: test_oracle_quant.py::test_fp8_close_to_exact (and the rule's own pins)."""
     x32 = np.asarray(x, dtype=np.float64).astype(F32)
     axes = tuple(range(1, x32.ndim))
     q, s = quant_rule_fp8_f32(x32, axes)
@@ -444,6 +471,8 @@ def int8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise each tile x[h] (leading axis = head) with the INT8 rule, deciding in float32.
 
     Returns (codes as float64, scales as float64 [BH]).
+    Pinned by: test_oracle_tiles.py (the exact-rational fixture's codes) and
+    test_oracle_quant.py::test_int8_close_to_exact.
     """
     x32 = np.asarray(x, dtype=np.float64).astype(F32)
     axes = tuple(range(1, x32.ndim))
@@ -452,7 +481,8 @@ def int8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def identity_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """No quantisation: values pass through with scale 1 (used to pin the tiling logic)."""
+    """No quantisation: values pass through with scale 1 (used to pin the tiling logic).
+    Pinned by: test_oracle_quant.py::test_identity_quant_equals_exact."""
     x = np.asarray(x, dtype=np.float64)
     return x, np.ones(x.shape[0], dtype=np.float64)
 
@@ -485,7 +515,10 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
     padding query rows take no part in any tile (their P~ is 0).
     Returns (O [B,H,N,d] float64 of dtype-rounded values, LSE [B,H,N] float32); with
     q_tiles only those query tiles are computed (rows of other tiles are NaN).
-    Pinned by: test_oracle_quant.py identity and lossless reductions to oracle.exact.
+    Pinned by: test_oracle_quant.py identity and lossless reductions to oracle.exact; the
+    tile placement (P~ tile shape, running max per key tile, l before quantisation) by
+    test_oracle_tiles.py (an exact-rational two-tile fixture that other tilings miss, a spy
+    on the quantised tiles, LSE independent of the P~ quantiser).
     """
     B, H, N, d = Qc.shape
     blk, tq, tk = spec.blk, spec.fwd_tq, spec.tk
@@ -541,6 +574,8 @@ def backward_pre(O, dO, spec: Spec, block_quant: BlockQuant = quant_blocks_f32):
     """D = rowsum(dO o O) (float64, O as stored in the dtype) and the per-block INT8 dO.
 
     Returns (D [B,H,N] float64, dOc int8 [B,H,N,d], dOs float32 [B,H,N/blk]).
+    Pinned by: the identity reduction of the backward to exact attention (D enters every dS)
+    and the planted mistake "ds_drop_D" (test_oracle_quant.py).
     """
     O = np.asarray(O, dtype=np.float64)
     dO32 = np.asarray(dO, dtype=F32)
@@ -591,6 +626,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     is in k_tiles (bwd_sk units) are visited: dQ is then exact for those query tiles,
     dK and dV for those key tiles, and NaN elsewhere.
     Returns dict dQ, dK, dV ([B,H,N,d] float64 of dtype-rounded values) plus D, dOc, dOs.
+    Pinned by: test_oracle_quant.py (identity and lossless reductions to oracle.exact,
+    finite-difference-pinned exact gradients, planted mistakes) and, for the P and dS tile
+    placement, test_oracle_tiles.py (exact-rational fixture that other tilings miss, spy).
     """
     B, H, N, d = pro["Qc"].shape
     blk, tq, sk, pk = spec.blk, spec.bwd_tq, spec.sk, spec.bwd_pk
@@ -707,7 +745,8 @@ def run(Q, K, V, dO, spec: Spec, tile_quant: Optional[TileQuant] = None,
         k_gain: Optional[np.ndarray] = None):
     """Prologue -> forward -> backward on whole tensors. Returns one dict of everything
     (with gains [H, d] also their gradients dq_gain, dk_gain). The quantisers default to the
-    recipe of spec.fmt: the INT8 rule, or the FP8 (e4m3) rule with absmax/448 scales."""
+    recipe of spec.fmt: the INT8 rule, or the FP8 (e4m3) rule with absmax/448 scales.
+    Pinned by: the pins of its three steps (prologue, forward, backward)."""
     fp8 = spec.fmt == "fp8"
     if tile_quant is None:
         tile_quant = fp8_tile_quant if fp8 else int8_tile_quant

@@ -283,7 +283,7 @@ def test_pins_pass_unplanted():
 
 
 @pytest.mark.parametrize("mistake", ["rmsnorm_bwd_drop_mean", "rmsnorm_bwd_sign",
-                                     "ds_drop_D", "dk_transposed"])
+                                     "ds_drop_D", "dk_transposed", "tile_scale_dropped"])
 def test_planted_mistake_is_caught(monkeypatch, mistake):
     if mistake == "rmsnorm_bwd_drop_mean":
         monkeypatch.setattr(oq, "rms_norm_backward",
