@@ -41,6 +41,28 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+# Per-row bar next to the whole-tensor rel-L2 bar (2e-3), derived before measuring: a row of
+# an output holds d = 64..128 values whose quantisation errors are averaged, so rows whose
+# error is concentrated (a query attending to a few keys, a key seen by few queries) may sit a
+# few times above the tensor-wide figure; 10x covers that. A localised bug (one wrong value per
+# row, e.g. at a tile edge) moves its row by about one value's share of the row norm, at least
+# 1/sqrt(d) >= 0.088, far above the bar. Rows with a norm below the tensor's RMS row norm are
+# judged against that RMS norm (an absolute floor), so a tiny row's relative noise does not
+# count as a fault.
+ROW_TOL = 2e-2
+
+
+def row_rel_max(a, b) -> float:
+    """max over rows (all axes but the last) of ||a_i - b_i|| / max(||b_i||, RMS_i ||b_i||)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    d = b.shape[-1]
+    a2, b2 = a.reshape(-1, d), b.reshape(-1, d)
+    nb = np.linalg.norm(b2, axis=1)
+    floor = max(float(np.sqrt(np.mean(nb * nb))), 1e-300)
+    return float(np.max(np.linalg.norm(a2 - b2, axis=1) / np.maximum(nb, floor)))
+
+
 def cosine(a, b) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()

@@ -33,6 +33,10 @@ CASES = {
     "d128_blk64_ragged": W["n8192_d128"].with_shape(B=1, H=2, N=200, blk=64, k_outlier_channels=0),
     "d64_blk128_noncausal_bf16": W["bf16_d64"].with_shape(B=1, H=2, N=384, blk=128, causal=False),
     "no_norm_no_smooth": W["tiny"].with_shape(N=320, causal=True, qk_norm=False, k_smooth=False),
+    # the remaining (dtype, d, blk) instantiations the library dispatches
+    "fp16_d64_blk128": W["tiny"].with_shape(B=1, H=2, N=384, blk=128, causal=True, qk_norm=True),
+    "bf16_d128_blk64": W["n8192_d128"].with_shape(B=1, H=2, N=320, blk=64, dtype="bf16"),
+    "bf16_d128_blk128": W["n8192_d128"].with_shape(B=1, H=2, N=512, dtype="bf16"),
 }
 
 

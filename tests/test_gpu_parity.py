@@ -14,7 +14,8 @@ import pytest
 from bit_trainable_attention_amd import workloads as wl
 from oracle import exact
 from oracle import quant as oq
-from tests.harness import check_prologue, cosine, gpu_run, host_inputs, pro_to_device, rel_l2, spec_for
+from tests.harness import (ROW_TOL, check_prologue, cosine, gpu_run, host_inputs, pro_to_device, rel_l2,
+                           row_rel_max, spec_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,6 +33,11 @@ SMALL = {
     "no_norm_no_smooth": W["tiny"].with_shape(N=320, causal=True, qk_norm=False, k_smooth=False),
     "norm_no_smooth_bf16": W["llama325m"].with_shape(B=1, H=2, N=256, k_smooth=False),
     "d128_noncausal": W["n8192_d128"].with_shape(B=1, H=1, N=384, causal=False),
+    # the remaining (dtype, d, blk) instantiations the library dispatches
+    "fp16_d64_blk128": W["tiny"].with_shape(B=1, H=2, N=384, blk=128, causal=True, qk_norm=True),
+    "bf16_d128_blk64": W["n8192_d128"].with_shape(B=1, H=2, N=320, blk=64, dtype="bf16"),
+    "bf16_d128_blk128": W["n8192_d128"].with_shape(B=1, H=2, N=512, dtype="bf16"),
+    "bf16_d128_blk128_noncausal": W["n32768"].with_shape(B=1, H=2, N=256, dtype="bf16", causal=False),
 }
 
 
@@ -56,14 +62,17 @@ def test_end_to_end_small(name):
     lse_err = float(np.max(np.abs(g["LSE"].astype(np.float64) - o["LSE"])))
     ex = exact.attention(x["Qf"], x["Kf"], x["Vf"], x["dOf"], causal=w.causal, qk_norm=w.qk_norm, eps=w.eps)
     cos = {k: cosine(g[k], ex[k]) for k in ("O", "dQ", "dK", "dV")}
-    _say(f"[parity] {name}: rel-L2 vs O-Q {errs}, max|dLSE| {lse_err:.2e}, cosine vs O-X {cos}")
+    rows = {k: row_rel_max(g[k], o[k]) for k in ("O", "dQ", "dK", "dV")}
+    _say(f"[parity] {name}: rel-L2 vs O-Q {errs}, worst row {rows}, max|dLSE| {lse_err:.2e}, cosine vs O-X {cos}")
     assert lse_err < 1e-4 * max(1.0, float(np.max(np.abs(o["LSE"]))))
     for k, e in errs.items():
         assert e <= TOL, (k, e)
+    for k, e in rows.items():
+        assert e <= ROW_TOL, (k, e)
 
 
 @pytest.mark.parametrize("name", ["n8192_d128_small", "d128_blk64_ragged", "d64_blk128_noncausal_bf16",
-                                  "llama325m_small"])
+                                  "llama325m_small", "fp16_d64_blk128", "bf16_d128_blk64", "bf16_d128_blk128"])
 def test_dq_modes(name):
     """dS spill and float32-atomic dQ reductions both meet the bar and agree with each other."""
     w = SMALL[name]
