@@ -23,8 +23,10 @@ BWD_DS_TILE_K = 64
 
 STATUS = {
     0: "SAGEBWD_OK", -1: "SAGEBWD_ERR_NULL", -2: "SAGEBWD_ERR_SHAPE", -3: "SAGEBWD_ERR_UNSUPPORTED",
-    -4: "SAGEBWD_ERR_ALIGN", -5: "SAGEBWD_ERR_WORKSPACE", -6: "SAGEBWD_ERR_HIP",
+    -4: "SAGEBWD_ERR_ALIGN", -5: "SAGEBWD_ERR_WORKSPACE", -6: "SAGEBWD_ERR_HIP", -7: "SAGEBWD_ERR_SCRATCH",
 }
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # SAGEBWD_NOALLOC_SCRATCH_BYTES
 
 
 class Params(ctypes.Structure):
@@ -46,6 +48,7 @@ _ST = ctypes.c_int
 SIGNATURES = {
     "sagebwd_prologue_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
     "sagebwd_quant_prologue": (_ST, [ctypes.POINTER(Params)] + [_P] * 16 + [_P, _SIZE, _P]),
+    "sagebwd_quant_prologue_noalloc": (_ST, [ctypes.POINTER(Params)] + [_P] * 16 + [_P]),
     "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 9 + [_P]),
     "sagebwd_backward_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
     "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 21 + [_P, _SIZE, _P]),

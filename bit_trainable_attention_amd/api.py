@@ -138,6 +138,43 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
     """QK-norm (with the gains [H,d] when p.qk_gain) -> K-smoothing (and Q-smoothing) ->
     per-block INT8 codes/scales. Returns the prologue tensors; with q_smooth also q_mean
     [B,H,d] and kbias [B,H,N]."""
+    out, q_gain, k_gain = _prologue_outputs(p, Q, K, V, out, q_gain, k_gain)
+    dev = Q.device
+    need = sagebwd_prologue_workspace_bytes(p)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().sagebwd_quant_prologue(ctypes.byref(p), *_prologue_ptrs(p, Q, K, V, out, q_gain, k_gain),
+                                            _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _check(st, "sagebwd_quant_prologue")
+    return out
+
+
+def sagebwd_quant_prologue_noalloc(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                                   out: Optional[Dict[str, torch.Tensor]] = None,
+                                   stream: Optional[torch.cuda.Stream] = None,
+                                   q_gain: Optional[torch.Tensor] = None,
+                                   k_gain: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """The allocation-free prologue (include/sagebwd.h): the library's call allocates nothing,
+    its scratch is a static per-device array. Pass preallocated `out` tensors for a call
+    that allocates nothing on this side either (with out=None they are allocated here)."""
+    out, q_gain, k_gain = _prologue_outputs(p, Q, K, V, out, q_gain, k_gain)
+    st = _lib.load().sagebwd_quant_prologue_noalloc(
+        ctypes.byref(p), *_prologue_ptrs(p, Q, K, V, out, q_gain, k_gain), _stream(Q.device, stream))
+    _check(st, "sagebwd_quant_prologue_noalloc")
+    return out
+
+
+def _prologue_ptrs(p, Q, K, V, out, q_gain, k_gain):
+    return [_ptr(Q), _ptr(K), _ptr(V),
+            _ptr(out["Qc"]), _ptr(out["Kc"]), _ptr(out["Vtc"]), _ptr(out["Qs"]), _ptr(out["Ks"]), _ptr(out["Vs"]),
+            _ptr(out["q_rstd"]), _ptr(out["k_rstd"]), _ptr(out["k_mean"]),
+            _ptr(out.get("q_mean") if p.q_smooth else None), _ptr(out.get("kbias") if p.q_smooth else None),
+            _ptr(q_gain), _ptr(k_gain)]
+
+
+def _prologue_outputs(p, Q, K, V, out, q_gain, k_gain):
+    """Check the prologue's inputs and outputs (allocating the outputs when out is None)."""
     dev = Q.device
     sh = _shapes(p)
     dt = _TORCH_DTYPE[p.dtype]
@@ -166,18 +203,7 @@ def sagebwd_quant_prologue(p: _lib.Params, Q: torch.Tensor, K: torch.Tensor, V: 
         wanted += [("q_mean", "m", torch.float32), ("kbias", "r", torch.float32)]
     for name, key, tdt in wanted:
         _want(out[name], name, sh[key], tdt, dev)
-    need = sagebwd_prologue_workspace_bytes(p)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.load().sagebwd_quant_prologue(
-        ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
-        _ptr(out["Qc"]), _ptr(out["Kc"]), _ptr(out["Vtc"]), _ptr(out["Qs"]), _ptr(out["Ks"]), _ptr(out["Vs"]),
-        _ptr(out["q_rstd"]), _ptr(out["k_rstd"]), _ptr(out["k_mean"]),
-        _ptr(out.get("q_mean") if p.q_smooth else None), _ptr(out.get("kbias") if p.q_smooth else None),
-        _ptr(q_gain), _ptr(k_gain), _ptr(workspace), ws_bytes, _stream(dev, stream))
-    _check(st, "sagebwd_quant_prologue")
-    return out
+    return out, q_gain, k_gain
 
 
 def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[torch.Tensor] = None,

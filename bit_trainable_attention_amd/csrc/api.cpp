@@ -135,6 +135,7 @@ const char* sagebwd_status_string(sagebwd_status s) {
     case SAGEBWD_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
     case SAGEBWD_ERR_HIP: return "HIP kernel launch failed";
+    case SAGEBWD_ERR_SCRATCH: return "problem exceeds the allocation-free entry point's static scratch";
   }
   return "unknown status";
 }
@@ -164,11 +165,14 @@ size_t sagebwd_backward_workspace_bytes(const sagebwd_params* p) {
   return L.total;
 }
 
-sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
-                                      int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
-                                      float* q_rstd, float* k_rstd, float* k_mean, float* q_mean,
-                                      float* kbias, const float* q_gain, const float* k_gain, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+// noalloc: the workspace is the current device's static scratch (looked up after every
+// argument check), never the caller's.
+static sagebwd_status prologue_impl(const sagebwd_params* p, const void* Q, const void* K, const void* V,
+                                    int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
+                                    float* q_rstd, float* k_rstd, float* k_mean, float* q_mean, float* kbias,
+                                    const float* q_gain, const float* k_gain, void* workspace,
+                                    size_t workspace_bytes, void* stream, bool noalloc) {
+  const char* who = noalloc ? "sagebwd_quant_prologue_noalloc" : "sagebwd_quant_prologue";
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
   if (empty(p)) return SAGEBWD_OK;
@@ -177,7 +181,16 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
   if (p->q_smooth && (st = check_ptrs(q_mean, kbias)) != SAGEBWD_OK) return st;
   if (p->qk_gain && (st = check_ptrs(q_gain, k_gain)) != SAGEBWD_OK) return st;
   const size_t need = sagebwd_prologue_workspace_bytes(p);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > SAGEBWD_NOALLOC_SCRATCH_BYTES) return SAGEBWD_ERR_SCRATCH;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const hipError_t e = sagebwd::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+      if (e != hipSuccess) return hip_status(e, who);
+      workspace_bytes = SAGEBWD_NOALLOC_SCRATCH_BYTES;
+    }
+  } else if (need > 0) {
     if (!workspace) return SAGEBWD_ERR_NULL;
     if (!aligned16(workspace)) return SAGEBWD_ERR_ALIGN;
     if (workspace_bytes < need) return SAGEBWD_ERR_WORKSPACE;
@@ -205,7 +218,25 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, co
   a.x16 = strides16(p);
   a.qk_norm = p->qk_norm != 0; a.k_smooth = p->k_smooth != 0; a.q_smooth = p->q_smooth != 0;
   a.eps = p->eps;
-  return hip_status(sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)), "sagebwd_quant_prologue");
+  return hip_status(sagebwd::launch_prologue(a, static_cast<hipStream_t>(stream)), who);
+}
+
+sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p, const void* Q, const void* K, const void* V,
+                                      int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs, float* Ks, float* Vs,
+                                      float* q_rstd, float* k_rstd, float* k_mean, float* q_mean,
+                                      float* kbias, const float* q_gain, const float* k_gain, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return prologue_impl(p, Q, K, V, Qc, Kc, Vtc, Qs, Ks, Vs, q_rstd, k_rstd, k_mean, q_mean, kbias, q_gain, k_gain,
+                       workspace, workspace_bytes, stream, false);
+}
+
+sagebwd_status sagebwd_quant_prologue_noalloc(const sagebwd_params* p, const void* Q, const void* K,
+                                              const void* V, int8_t* Qc, int8_t* Kc, int8_t* Vtc, float* Qs,
+                                              float* Ks, float* Vs, float* q_rstd, float* k_rstd, float* k_mean,
+                                              float* q_mean, float* kbias, const float* q_gain,
+                                              const float* k_gain, void* stream) {
+  return prologue_impl(p, Q, K, V, Qc, Kc, Vtc, Qs, Ks, Vs, q_rstd, k_rstd, k_mean, q_mean, kbias, q_gain, k_gain,
+                       nullptr, 0, stream, true);
 }
 
 sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,

@@ -7,6 +7,8 @@
 
 #include <type_traits>
 
+#include "sagebwd.h"
+
 namespace sagebwd {
 
 // Element strides of the 16-bit tensors (Q, K, V, O, dO, dQ, dK, dV): element (b, h, n, c)
@@ -88,6 +90,11 @@ hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, dim3 block, hipStream_
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st);
+// Bytes of the static device scratch of the allocation-free prologue entry point, and the
+// device address of the current device's copy (looked up on the first call per device; the
+// stream, if not null, must belong to the current device).
+constexpr size_t kNoAllocScratchBytes = SAGEBWD_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t st, void** out);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st);
 hipError_t launch_backward(const BackwardArgs& a, int part, hipStream_t st);  // part -1 = all
 size_t packet_bytes(int d);  // bytes of one 64-query backward tile packet

@@ -35,6 +35,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace sagebwd {
 
 namespace {
@@ -363,6 +365,45 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st) {
   if (e != hipSuccess || !(a.k_smooth || a.q_smooth)) return e;
   return launch_kernel(&prologue_pass2<DT, D, BLK>, dim3((unsigned)(nblocks * (a.q_smooth ? 2 : 1))),
                        dim3(kThreads), st, a);
+}
+
+// ---------------------------------------------------------------- allocation-free scratch
+// The allocation-free prologue entry point takes its block-sum scratch from this array: each
+// GPU the library runs on holds its own copy from the first call on it until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory: the device
+// address is looked up once per device (hipGetSymbolAddress, with that device current) and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device ordinal; null until looked up
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t st, void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (st) {
+    // the work is enqueued on st, so the scratch must be the one of st's device, which must
+    // be the current device (the symbol lookup below names the current device's copy)
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return e;
+    if ((int)sdev != dev) return hipErrorInvalidDevice;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t st) {

@@ -80,7 +80,9 @@ typedef enum {
                                    q_smooth                                                 */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
-  SAGEBWD_ERR_HIP = -6          /* a kernel launch failed                                   */
+  SAGEBWD_ERR_HIP = -6,         /* a kernel launch failed                                   */
+  SAGEBWD_ERR_SCRATCH = -7      /* the allocation-free entry point's static scratch is too
+                                   small for the problem                                    */
 } sagebwd_status;
 
 typedef enum { SAGEBWD_FP16 = 0, SAGEBWD_BF16 = 1 } sagebwd_dtype;
@@ -179,6 +181,33 @@ sagebwd_status sagebwd_quant_prologue(const sagebwd_params* p,
                                       const float* q_gain, const float* k_gain,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/* Allocation-free variant of sagebwd_quant_prologue, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, computation and outputs (bit for bit), without the workspace:
+ * the prologue's scratch comes from a static device array of SAGEBWD_NOALLOC_SCRATCH_BYTES
+ * bytes, which each GPU holds from the first call on it until the process ends. The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *   - Problems with sagebwd_prologue_workspace_bytes(p) > SAGEBWD_NOALLOC_SCRATCH_BYTES are
+ *     rejected with SAGEBWD_ERR_SCRATCH, after the argument checks and before any HIP call
+ *     (16 MiB covers e.g. B*H*ceil(N/blk)*d <= 4M, so K-smoothing at B*H = 32, N = 32768,
+ *     d = 128, blk = 128 needs 1 MiB).
+ *   - After the argument checks the call looks up the current device (and, if stream is not
+ *     NULL, the stream's device, which must be the current one: else SAGEBWD_ERR_HIP with
+ *     hipErrorInvalidDevice) and, on the first call per device, the array's device address.
+ *   - Every call on one GPU shares that GPU's array. Calls ordered on one stream are safe;
+ *     calls that may overlap in time on one GPU (other streams, unordered host threads) race
+ *     on it and give undefined results. The kernels write every scratch byte they read
+ *     within the same call, so nothing carries over from an earlier call. */
+#define SAGEBWD_NOALLOC_SCRATCH_BYTES (16ull << 20)
+sagebwd_status sagebwd_quant_prologue_noalloc(const sagebwd_params* p,
+                                              const void* Q, const void* K, const void* V,
+                                              int8_t* Qc, int8_t* Kc, int8_t* Vtc,
+                                              float* Qs, float* Ks, float* Vs,
+                                              float* q_rstd, float* k_rstd, float* k_mean,
+                                              float* q_mean, float* kbias,
+                                              const float* q_gain, const float* k_gain,
+                                              void* stream);
 
 /* Forward: O = softmax(sm_scale * Q^ K~^T [causal mask]) V with INT8 QK^T and PV.
  *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs, and its kbias with q_smooth (each

@@ -2,11 +2,16 @@
 rejects bad arguments before doing anything on a device. No call here reaches a kernel:
 every call either fails validation or is a documented no-op (N == 0)."""
 import ctypes
+import re
 
 import pytest
 
 from bit_trainable_attention_amd import _lib
-from tests.harness import header_constants, header_functions
+from tests.harness import HEADER, header_constants, header_functions
+
+
+def header_path():
+    return HEADER
 
 lib = _lib.load()  # fails loudly if the library was not built
 
@@ -53,6 +58,10 @@ def _prologue(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.sagebwd_quant_prologue(ctypes.byref(p), *([ptr] * 16), ws, ws_bytes, None)
 
 
+def _prologue_noalloc(p, ptr=FAKE):
+    return lib.sagebwd_quant_prologue_noalloc(ctypes.byref(p), *([ptr] * 16), None)
+
+
 def _forward(p, ptr=FAKE):
     return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 9), None)
 
@@ -61,7 +70,7 @@ def _backward(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
     return lib.sagebwd_backward(ctypes.byref(p), *([ptr] * 21), ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("call", [_prologue, _forward, _backward])
+@pytest.mark.parametrize("call", [_prologue, _prologue_noalloc, _forward, _backward])
 def test_invalid_params_rejected(call):
     assert call(P(d=96)) == -3
     assert call(P(d=32)) == -3
@@ -210,3 +219,20 @@ def test_fp8_workspace_sizes_equal_int8():
             lib.sagebwd_backward_workspace_bytes(ctypes.byref(b))
         assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(a)) == \
             lib.sagebwd_prologue_workspace_bytes(ctypes.byref(b))
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The allocation-free prologue refuses a problem whose scratch exceeds the static array,
+    after the argument checks and before any HIP call (on a host without a GPU a HIP call
+    would fail with SAGEBWD_ERR_HIP instead)."""
+    big = P(B=64, H=64, N=32768, d=128, blk=128)       # K block sums: 4096 heads x 256 blocks x 128 x 4 B
+    assert lib.sagebwd_prologue_workspace_bytes(ctypes.byref(big)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert _prologue_noalloc(big) == -7
+    assert lib.sagebwd_status_string(-7).decode() != "unknown status"
+    assert _prologue_noalloc(big, ptr=MIS) == -4         # argument errors still come first
+    assert _prologue_noalloc(big, ptr=0) == -1
+    assert _prologue_noalloc(P(N=0)) == 0                # an empty problem enqueues nothing
+    # a problem at the limit passes the size check (and would then look up the device)
+    text = open(header_path()).read()
+    m = re.search(r"#define\s+SAGEBWD_NOALLOC_SCRATCH_BYTES\s+\((\d+)ull\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
