@@ -327,9 +327,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
     __syncthreads();
   }
 
-  if (!active) return;
+  // padding rows of a ragged last block (from Nv to the padded length N): lse = +inf, the
+  // backward's convention for queries that see no key (their P is 0); no O row exists
+  const bool pad_row = qrow >= a.Nv && qrow < a.N;
+  if (!active) {
+    if (g == 0 && pad_row) a.lse[(size_t)bh * a.N + qrow] = INFINITY;
+    return;
+  }
   const float ltot = lsum_run + __shfl_xor(lsum_run, 32);
-  if (qrow >= a.Nv) return;   // padding rows: nothing to store
+  if (qrow >= a.Nv) {
+    if (g == 0 && pad_row) a.lse[(size_t)bh * a.N + qrow] = INFINITY;
+    return;
+  }
   const float linv = 1.0f / ltot;
   unsigned short* orow = a.O + a.x16.row(bh, qrow);
 #pragma unroll

@@ -43,7 +43,7 @@
  *     N mod blk tokens (its absmax, and the means, cover those tokens only). The 16-bit
  *     tensors hold exactly N tokens per head; every array of the library's own (codes,
  *     scales, statistics, lse) holds Np = N rounded up to a multiple of blk, the tokens from
- *     N on being padding (codes 0, rstd 1; their lse and other statistics are not
+ *     N on being padding (codes 0, rstd 1, lse +inf; their other statistics are not
  *     meaningful). Padding tokens are never normalised, so eps = 0 is valid with any N.
  *   - The caller owns every buffer. The library allocates nothing, keeps no state between
  *     calls, never synchronises, and is re-entrant; all work is enqueued on `stream`
@@ -213,7 +213,8 @@ sagebwd_status sagebwd_quant_prologue_noalloc(const sagebwd_params* p,
  *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs, and its kbias with q_smooth (each
  *            score is then sm_scale * (Q~ K~^T + b_k); kbias ignored, may be NULL, without)
  *   O   out: dtype [B,H,N,d]
- *   lse out: float32 [B,H,Np], natural-log logsumexp of each row of the scaled scores */
+ *   lse out: float32 [B,H,Np], natural-log logsumexp of each row of the scaled scores
+ *            (+inf for the padding rows from N on) */
 sagebwd_status sagebwd_forward(const sagebwd_params* p,
                                const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
                                const float* Qs, const float* Ks, const float* Vs,
