@@ -103,6 +103,8 @@ def main():
                     help="memory layout of the 16-bit tensors handed to the library (default [B,H,N,d])")
     ap.add_argument("--fmt", default="int8", choices=("int8", "fp8"),
                     help="code format of the six quantised products (default INT8, as the metric)")
+    ap.add_argument("--dq-mode", default="auto", choices=("auto", "spill", "atomic"),
+                    help="how the backward reduces dQ over key blocks (default: the library's choice)")
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
@@ -126,7 +128,8 @@ def main():
         f"qk_norm={w.qk_norm} k_smooth={w.k_smooth} blk={w.blk}")
     x = wl.make_inputs(w)
     p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
-                        q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt)
+                        q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt,
+                        dq_mode={"auto": 0, "spill": 1, "atomic": 2}[args.dq_mode])
     dev = torch.device("cuda:0")
     Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
     if args.layout == "bnhd":

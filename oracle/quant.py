@@ -39,6 +39,14 @@ What is computed, in the order of the SageBwd article:
      [-127, 127]: scale a / 448, code e4m3_rne(x * 448 / a). The products are formed from
      the codes' values exactly as in the INT8 recipe.
 
+  9. Optional Q-Attn precision split (Spec.split = "qattn"; Full-Stack FP4 page, section
+     2.4, mixed-precision attention): the robust paths, QK^T (forward and recomputed) and
+     the dS products dQ = dS K, dK = dS^T Q, stay low-bit (the codes of spec.fmt); the
+     softmax-sensitive paths PV, P^T dO and dO V^T run in 16 bits: P~ and P are rounded to
+     the inputs' 16-bit type (half_round_tile), and V and dO enter with their own 16-bit
+     values (identity_block_quant), with float accumulation. The quantised views of Q and K
+     are reused by both passes as before.
+
 Precision: steps 1-3 are float32, one IEEE operation at a time, round to nearest
 even, in the order written (sums run over channels, or over tokens, in ascending
 index order). Everything after the prologue is float64, except that each in-kernel
@@ -83,7 +91,8 @@ class Spec:
     bwd_sk: Optional[int] = None
     q_smooth: bool = False
     normed_grads: bool = False   # dQ, dK with respect to Q^, K^ (no RMSNorm backward)
-    fmt: str = "int8"            # encoding of the six quantised products' operands: "int8" | "fp8"
+    fmt: str = "int8"            # encoding of the low-bit products' operands: "int8" | "fp8"
+    split: str = "sagebwd"       # which products are low-bit: "sagebwd" (six of seven) | "qattn"
 
     def __post_init__(self):
         blk = self.blk
@@ -97,6 +106,8 @@ class Spec:
             raise ValueError("bwd_pk must divide bwd_sk")
         if self.N < 1:
             raise ValueError("N must be positive")
+        if self.split not in ("sagebwd", "qattn"):
+            raise ValueError(f"split={self.split!r}")
 
     @property
     def Np(self) -> int:
@@ -382,7 +393,8 @@ def apply_gain_f32(xn: np.ndarray, g: Optional[np.ndarray]) -> np.ndarray:
 
 def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
              block_quant: BlockQuant = quant_blocks_f32, q_gain: Optional[np.ndarray] = None,
-             k_gain: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+             k_gain: Optional[np.ndarray] = None,
+             v_block_quant: Optional[BlockQuant] = None) -> Dict[str, np.ndarray]:
     """QK-norm (with optional gains [H, d]) -> K-smoothing -> per-block INT8 quantisation
     of Q^, K~, V.
 
@@ -427,7 +439,7 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
         Qt, mu_q = Qh, np.zeros(Q.shape[:-2] + (Q.shape[-1],), dtype=F32)
     Qc, Qs = block_quant(Qt, spec.blk)
     Kc, Ks = block_quant(Kt, spec.blk)
-    Vc, Vs = block_quant(V, spec.blk)
+    Vc, Vs = (block_quant if v_block_quant is None else v_block_quant)(V, spec.blk)
     out = dict(Qc=Qc, Kc=Kc, Vc=Vc, Qs=Qs, Ks=Ks, Vs=Vs, q_rstd=q_rstd, k_rstd=k_rstd,
                k_mean=mu, q_mean=mu_q, Qhat=Qh, Khat=Kh, Qn=Qn, Kn=Kn, q_gain=q_gain, k_gain=k_gain)
     out["kbias"] = key_bias(Kc, Ks, mu_q, spec.blk) if spec.q_smooth else np.zeros(K.shape[:-1])
@@ -478,6 +490,20 @@ def int8_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     axes = tuple(range(1, x32.ndim))
     q, s = quant_rule_f32(x32, axes)
     return q.astype(np.float64), s.astype(np.float64)
+
+
+def half_round_tile(dtype: str) -> TileQuant:
+    """The Q-Attn split's 16-bit operand for P~ and P: every value rounded to the 16-bit type
+    dtype (nearest even) after rounding to float32, the precision the kernels hold P in; scale
+    1 (no tile scale: P <= 1 fits both 16-bit types). dtype "f64" keeps the values (for pins).
+    Pinned by: test_oracle_qattn.py (reduction to exact attention on the dequantised Q, K;
+    rounding on vs off) and round_to_dtype's pins."""
+    def q(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        x = np.asarray(x, dtype=np.float64)
+        if dtype != "f64":
+            x = round_to_dtype(x.astype(F32).astype(np.float64), dtype)
+        return x, np.ones(x.shape[0], dtype=np.float64)
+    return q
 
 
 def identity_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
@@ -597,7 +623,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
              tile_quant: TileQuant = int8_tile_quant,
              block_quant: BlockQuant = quant_blocks_f32,
              q_tiles: Optional[Sequence[int]] = None,
-             k_tiles: Optional[Sequence[int]] = None):
+             k_tiles: Optional[Sequence[int]] = None,
+             p_quant: Optional[TileQuant] = None,
+             do_quant: Optional[BlockQuant] = None):
     """Backward with recomputed INT8 QK^T, FP dP = dO V^T and INT8 dV, dK, dQ.
 
     pro: the prologue's dict (codes, scales, rstd, Qhat, Khat). Q, K, V, dO: float32
@@ -625,6 +653,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     With q_tiles / k_tiles only pairs whose I is in q_tiles (bwd_tq units) or whose J
     is in k_tiles (bwd_sk units) are visited: dQ is then exact for those query tiles,
     dK and dV for those key tiles, and NaN elsewhere.
+    p_quant (default tile_quant) quantises the P tiles of dV and do_quant (default
+    block_quant) the dO blocks: the Q-Attn split passes the 16-bit rounding and the
+    identity, so dV = round16(P)^T dO.
     Returns dict dQ, dK, dV ([B,H,N,d] float64 of dtype-rounded values) plus D, dOc, dOs.
     Pinned by: test_oracle_quant.py (identity and lossless reductions to oracle.exact,
     finite-difference-pinned exact gradients, planted mistakes) and, for the P and dS tile
@@ -638,7 +669,9 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     nv = spec.N
     V, dO, O = (_pad_rows(np.asarray(x), N) for x in (V, dO, O))
     LSE = _pad_rows(np.asarray(LSE, dtype=F32), N, np.inf)
-    D, dOc, dOs = backward_pre(O, dO, spec, block_quant=block_quant)
+    D, dOc, dOs = backward_pre(O, dO, spec, block_quant=block_quant if do_quant is None else do_quant)
+    if p_quant is None:
+        p_quant = tile_quant
     qc = code_values(_flat(pro["Qc"]))
     kc = code_values(_flat(pro["Kc"]))
     qs = _flat(np.asarray(pro["Qs"], dtype=np.float64))
@@ -681,7 +714,7 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             dS = P * (dP - Df[:, i0:i0 + tq, None])
             qdS, sdS = tile_quant(dS)
             for p0 in range(0, sk, pk):
-                qP, sP = tile_quant(P[:, :, p0:p0 + pk])
+                qP, sP = p_quant(P[:, :, p0:p0 + pk])
                 dV[:, j0 + p0:j0 + p0 + pk, :] += (sP * dos[:, i0 // blk])[:, None, None] * (
                     qP.transpose(0, 2, 1) @ doc[:, i0:i0 + tq, :])
             dKh[:, j0:j0 + sk, :] += (sm * sdS * qs[:, i0 // blk])[:, None, None] * (
@@ -752,10 +785,16 @@ def run(Q, K, V, dO, spec: Spec, tile_quant: Optional[TileQuant] = None,
         tile_quant = fp8_tile_quant if fp8 else int8_tile_quant
     if block_quant is None:
         block_quant = quant_blocks_fp8_f32 if fp8 else quant_blocks_f32
-    pro = prologue(Q, K, V, spec, block_quant=block_quant, q_gain=q_gain, k_gain=k_gain)
+    qattn = spec.split == "qattn"
+    # Q-Attn: PV, P^T dO in 16 bits (P~, P rounded to the dtype; V, dO their own values)
+    half = half_round_tile(spec.dtype) if qattn else None
+    pro = prologue(Q, K, V, spec, block_quant=block_quant, q_gain=q_gain, k_gain=k_gain,
+                   v_block_quant=identity_block_quant if qattn else None)
     O, LSE = forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec,
-                     tile_quant=tile_quant, kbias=pro["kbias"] if spec.q_smooth else None)
-    g = backward(pro, Q, K, V, O, LSE, dO, spec, tile_quant=tile_quant, block_quant=block_quant)
+                     tile_quant=half if qattn else tile_quant,
+                     kbias=pro["kbias"] if spec.q_smooth else None)
+    g = backward(pro, Q, K, V, O, LSE, dO, spec, tile_quant=tile_quant, block_quant=block_quant,
+                 p_quant=half if qattn else None, do_quant=identity_block_quant if qattn else None)
     out = dict(pro)
     out.update(O=O, LSE=LSE)
     out.update(g)
