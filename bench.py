@@ -103,6 +103,9 @@ def main():
                     help="memory layout of the 16-bit tensors handed to the library (default [B,H,N,d])")
     ap.add_argument("--fmt", default="int8", choices=("int8", "fp8"),
                     help="code format of the six quantised products (default INT8, as the metric)")
+    ap.add_argument("--split", default="sagebwd", choices=("sagebwd", "qattn"),
+                    help="precision split: six of seven products quantised (default, the metric) or the "
+                         "Q-Attn split (QK^T and the dS products quantised, PV, P^T dO, dO V^T in 16 bits)")
     ap.add_argument("--dq-mode", default="auto", choices=("auto", "spill", "atomic"),
                     help="how the backward reduces dQ over key blocks (default: the library's choice)")
     ap.add_argument("--no-autograd", action="store_true",
@@ -129,14 +132,14 @@ def main():
     x = wl.make_inputs(w)
     p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
                         q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt,
-                        dq_mode={"auto": 0, "spill": 1, "atomic": 2}[args.dq_mode])
+                        dq_mode={"auto": 0, "spill": 1, "atomic": 2}[args.dq_mode], split=args.split)
     dev = torch.device("cuda:0")
     Q, K, V, dO = (to_device(x[k]) for k in ("Q", "K", "V", "dO"))
     if args.layout == "bnhd":
         Q, K, V, dO = (t.transpose(1, 2).contiguous() for t in (Q, K, V, dO))
     pro = api.sagebwd_quant_prologue(p, Q, K, V)
     pro_ws = torch.empty(max(api.sagebwd_prologue_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
-    O, lse = api.sagebwd_forward(p, pro)
+    O, lse = api.sagebwd_forward(p, pro, V=V)
     grads = {n: torch.empty_like(Q) for n in ("dQ", "dK", "dV")}
     bws = torch.empty(api.sagebwd_backward_workspace_bytes(p), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -155,7 +158,7 @@ def main():
         ev[0].record()
         api.sagebwd_quant_prologue(p, Q, K, V, out=pro, workspace=pro_ws)
         ev[1].record()
-        api.sagebwd_forward(p, pro, O=O, lse=lse)
+        api.sagebwd_forward(p, pro, O=O, lse=lse, V=V)
         ev[2].record()
         for part in range(3):
             api.sagebwd_backward_part(p, part, Q, K, V, pro, O, lse, dO, grads, bws)
@@ -227,7 +230,8 @@ def main():
             for t in (qg, kg, vg):
                 t.grad = None
             o = sagebwd_attention(qg, kg, vg, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
-                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt)
+                                  blk=w.blk, eps=w.eps, q_smooth=w.q_smooth, layout=args.layout, fmt=args.fmt,
+                                  split=args.split)
             o.backward(dO)
 
         for _ in range(2):

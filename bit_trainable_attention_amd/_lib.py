@@ -14,12 +14,14 @@ SAGEBWD_BF16 = 1
 DQ_AUTO, DQ_SPILL, DQ_ATOMIC = 0, 1, 2
 LAYOUT_BHND, LAYOUT_BNHD = 0, 1
 FMT_INT8, FMT_FP8 = 0, 1   # sagebwd_fmt
+SPLIT_SAGEBWD, SPLIT_QATTN = 0, 1   # sagebwd_split
 
 # Quantisation tile shapes of the kernels (include/sagebwd.h); the backward's P and dS tiles
 # span one query block (blk rows) by BWD_P_TILE_K and min(blk, BWD_DS_TILE_K) keys.
 FWD_TILE_Q = 32
 BWD_P_TILE_K = 16
 BWD_DS_TILE_K = 64
+QATTN_FWD_TILE_K = 64
 
 STATUS = {
     0: "SAGEBWD_OK", -1: "SAGEBWD_ERR_NULL", -2: "SAGEBWD_ERR_SHAPE", -3: "SAGEBWD_ERR_UNSUPPORTED",
@@ -37,7 +39,7 @@ class Params(ctypes.Structure):
         ("k_smooth", ctypes.c_int32), ("eps", ctypes.c_float), ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("q_smooth", ctypes.c_int32),
         ("layout", ctypes.c_int32), ("qk_gain", ctypes.c_int32), ("normed_grads", ctypes.c_int32),
-        ("fmt", ctypes.c_int32),
+        ("fmt", ctypes.c_int32), ("split", ctypes.c_int32),
     ]
 
 
@@ -49,7 +51,7 @@ SIGNATURES = {
     "sagebwd_prologue_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
     "sagebwd_quant_prologue": (_ST, [ctypes.POINTER(Params)] + [_P] * 16 + [_P, _SIZE, _P]),
     "sagebwd_quant_prologue_noalloc": (_ST, [ctypes.POINTER(Params)] + [_P] * 16 + [_P]),
-    "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 9 + [_P]),
+    "sagebwd_forward": (_ST, [ctypes.POINTER(Params)] + [_P] * 10 + [_P]),
     "sagebwd_backward_workspace_bytes": (_SIZE, [ctypes.POINTER(Params)]),
     "sagebwd_backward": (_ST, [ctypes.POINTER(Params)] + [_P] * 21 + [_P, _SIZE, _P]),
     "sagebwd_backward_part": (_ST, [ctypes.POINTER(Params), ctypes.c_int32] + [_P] * 21 + [_P, _SIZE, _P]),

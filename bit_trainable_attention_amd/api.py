@@ -20,16 +20,18 @@ _TORCH_DTYPE = {_lib.SAGEBWD_FP16: torch.float16, _lib.SAGEBWD_BF16: torch.bfloa
 def make_params(B: int, H: int, N: int, d: int, blk: int, causal: bool, qk_norm: bool, k_smooth: bool,
                 dtype: str, eps: float = 1e-6, sm_scale: float = 0.0, dq_mode: int = 0,
                 q_smooth: bool = False, layout: str = "bhnd", qk_gain: bool = False,
-                normed_grads: bool = False, fmt: str = "int8") -> _lib.Params:
+                normed_grads: bool = False, fmt: str = "int8", split: str = "sagebwd") -> _lib.Params:
     """dq_mode: 0 auto, 1 dS spill, 2 float32 atomics; layout of the 16-bit tensors:
     "bhnd" [B,H,N,d] or "bnhd" [B,N,H,d]; qk_gain: learnable QK-norm gains [H,d];
     normed_grads: dQ, dK with respect to the normalised Q^, K^; fmt: code format of the
-    six quantised products, "int8" or "fp8" (e4m3) (include/sagebwd.h)."""
+    quantised products, "int8" or "fp8" (e4m3); split: "sagebwd" (six of seven products
+    quantised) or "qattn" (QK^T and the dS products) (include/sagebwd.h)."""
     dt = {"fp16": _lib.SAGEBWD_FP16, "bf16": _lib.SAGEBWD_BF16}[dtype]
     lay = {"bhnd": _lib.LAYOUT_BHND, "bnhd": _lib.LAYOUT_BNHD}[layout]
     return _lib.Params(B, H, N, d, blk, int(causal), int(qk_norm), int(k_smooth), eps, sm_scale, dt, dq_mode,
                        int(q_smooth), lay, int(qk_gain), int(normed_grads),
-                       {"int8": _lib.FMT_INT8, "fp8": _lib.FMT_FP8}[fmt])
+                       {"int8": _lib.FMT_INT8, "fp8": _lib.FMT_FP8}[fmt],
+                       {"sagebwd": _lib.SPLIT_SAGEBWD, "qattn": _lib.SPLIT_QATTN}[split])
 
 
 def sagebwd_status_string(status: int) -> str:
@@ -208,12 +210,19 @@ def _prologue_outputs(p, Q, K, V, out, q_gain, k_gain):
 
 def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None,
-                    stream: Optional[torch.cuda.Stream] = None):
-    """INT8 forward from the prologue tensors (and their kbias with q_smooth). Returns (O, lse)."""
+                    stream: Optional[torch.cuda.Stream] = None, V: Optional[torch.Tensor] = None):
+    """Forward from the prologue tensors (and their kbias with q_smooth). With the Q-Attn split
+    the raw V (the prologue's input) is required: PV runs in 16 bits. Returns (O, lse)."""
     dev = pro["Qc"].device
     sh = _shapes(p)
-    wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Vtc", "xt", torch.int8),
-              ("Qs", "s", torch.float32), ("Ks", "s", torch.float32), ("Vs", "s", torch.float32)]
+    qattn = p.split == _lib.SPLIT_QATTN
+    wanted = [("Qc", "x", torch.int8), ("Kc", "x", torch.int8), ("Qs", "s", torch.float32), ("Ks", "s", torch.float32)]
+    if not qattn:
+        wanted += [("Vtc", "xt", torch.int8), ("Vs", "s", torch.float32)]
+    else:
+        if V is None:
+            raise ValueError("the Q-Attn split's forward needs the raw V")
+        _want(V, "V", sh["x16"], _TORCH_DTYPE[p.dtype], dev)
     if p.q_smooth:
         wanted.append(("kbias", "r", torch.float32))
     for name, key, tdt in wanted:
@@ -227,7 +236,7 @@ def sagebwd_forward(p: _lib.Params, pro: Dict[str, torch.Tensor], O: Optional[to
     st = _lib.load().sagebwd_forward(
         ctypes.byref(p), _ptr(pro["Qc"]), _ptr(pro["Kc"]), _ptr(pro["Vtc"]),
         _ptr(pro["Qs"]), _ptr(pro["Ks"]), _ptr(pro["Vs"]), _ptr(pro["kbias"] if p.q_smooth else None),
-        _ptr(O), _ptr(lse), _stream(dev, stream))
+        _ptr(V if qattn else None), _ptr(O), _ptr(lse), _stream(dev, stream))
     _check(st, "sagebwd_forward")
     return O, lse
 

@@ -31,7 +31,7 @@ class SageBwdAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, q_gain, k_gain, causal: bool, qk_norm: bool, k_smooth: bool, blk: int,
                 eps: float, sm_scale: float, dq_mode: int, q_smooth: bool, layout: str, normed_grads: bool,
-                fmt: str):
+                fmt: str, split: str):
         if q.dtype not in _DTYPES:
             raise TypeError(f"q, k, v must be float16 or bfloat16, got {q.dtype}")
         if q.dim() != 4:
@@ -45,11 +45,11 @@ class SageBwdAttention(torch.autograd.Function):
             raise ValueError("q_gain and k_gain go together")
         p = api.make_params(B, H, N, d, blk, causal, qk_norm, k_smooth, _DTYPES[q.dtype], eps=eps,
                             sm_scale=sm_scale, dq_mode=dq_mode, q_smooth=q_smooth, layout=layout,
-                            qk_gain=gained, normed_grads=normed_grads, fmt=fmt)
+                            qk_gain=gained, normed_grads=normed_grads, fmt=fmt, split=split)
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         gains = (q_gain.detach().float().contiguous(), k_gain.detach().float().contiguous()) if gained else (None, None)
         pro = api.sagebwd_quant_prologue(p, q, k, v, q_gain=gains[0], k_gain=gains[1])
-        O, lse = api.sagebwd_forward(p, pro)
+        O, lse = api.sagebwd_forward(p, pro, V=v)
         ctx.params = p
         ctx.saved_names = _SAVED_QS if q_smooth else _SAVED
         ctx.gain_dtypes = (q_gain.dtype, k_gain.dtype) if gained else None
@@ -67,7 +67,7 @@ class SageBwdAttention(torch.autograd.Function):
         dgq = dgk = None
         if ctx.gain_dtypes:
             dgq, dgk = g["dq_gain"].to(ctx.gain_dtypes[0]), g["dk_gain"].to(ctx.gain_dtypes[1])
-        return (g["dQ"], g["dK"], g["dV"], dgq, dgk) + (None,) * 12
+        return (g["dQ"], g["dK"], g["dV"], dgq, dgk) + (None,) * 13
 
 
 def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
@@ -76,7 +76,7 @@ def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
                       dq_mode: int = 0, q_smooth: bool = False, q_gain: Optional[torch.Tensor] = None,
                       k_gain: Optional[torch.Tensor] = None,
                       normed_grads: bool = False,
-                      fmt: str = "int8") -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
+                      fmt: str = "int8", split: str = "sagebwd") -> Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]:
     """SageBwd-style INT8 attention with gradients (see the module docstring).
 
     sm_scale <= 0 selects 1/sqrt(d); q_smooth selects the Q-smoothing variant (the query
@@ -84,14 +84,18 @@ def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     q_gain, k_gain: optional learnable QK-norm gains [H, d] (both or neither; they receive
     gradients). normed_grads: q.grad and k.grad become the gradients with respect to the
     normalised Q^, K^ (for a caller that applies its own RMSNorm backward). fmt: "int8" or
-    "fp8" (e4m3 codes for the six quantised products; not with q_smooth). The lse returned with return_lse is float32 [B, H, N] (natural log) and
-    carries no gradient.
+    "fp8" (e4m3 codes for the quantised products; not with q_smooth). split: "sagebwd" (six of
+    the seven products quantised) or "qattn" (the Full-Stack FP4 page's split: QK^T and the dS
+    products quantised, PV, P^T dO and dO V^T in 16 bits; not with q_smooth). The lse returned
+    with return_lse is float32 [B, H, N] (natural log) and carries no gradient.
     """
     if fmt not in ("int8", "fp8"):
         raise ValueError(f"fmt must be 'int8' or 'fp8', got {fmt!r}")
+    if split not in ("sagebwd", "qattn"):
+        raise ValueError(f"split must be 'sagebwd' or 'qattn', got {split!r}")
     if layout not in ("bhnd", "bnhd"):
         raise ValueError(f"layout must be 'bhnd' or 'bnhd', got {layout!r}")
     O, lse = SageBwdAttention.apply(q, k, v, q_gain, k_gain, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
                                     float(eps), float(sm_scale), int(dq_mode), bool(q_smooth), layout,
-                                    bool(normed_grads), str(fmt))
+                                    bool(normed_grads), str(fmt), str(split))
     return (O, lse) if return_lse else O

@@ -34,6 +34,8 @@ sagebwd_status check_params(const sagebwd_params* p) {
   if (p->normed_grads && (!p->qk_norm || p->qk_gain)) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->fmt != SAGEBWD_FMT_INT8 && p->fmt != SAGEBWD_FMT_FP8) return SAGEBWD_ERR_UNSUPPORTED;
   if (p->fmt == SAGEBWD_FMT_FP8 && p->q_smooth) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->split != SAGEBWD_SPLIT_SAGEBWD && p->split != SAGEBWD_SPLIT_QATTN) return SAGEBWD_ERR_UNSUPPORTED;
+  if (p->split == SAGEBWD_SPLIT_QATTN && p->q_smooth) return SAGEBWD_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels: byte offsets inside one head's arrays fit in 31 bits
   // (Np * d * 4 < 2^31), grids in 2^31 workgroups
   if ((long long)p->B * p->H > (1LL << 24) || p->N > (1 << 22)) return SAGEBWD_ERR_SHAPE;
@@ -131,7 +133,7 @@ const char* sagebwd_status_string(sagebwd_status s) {
     case SAGEBWD_OK: return "ok";
     case SAGEBWD_ERR_NULL: return "null pointer argument";
     case SAGEBWD_ERR_SHAPE: return "invalid shape (negative size, or N not a multiple of blk)";
-    case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype, dq_mode, layout, eps or gains)";
+    case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype, dq_mode, layout, fmt, split, eps or gains)";
     case SAGEBWD_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
     case SAGEBWD_ERR_HIP: return "HIP kernel launch failed";
@@ -240,16 +242,24 @@ sagebwd_status sagebwd_quant_prologue_noalloc(const sagebwd_params* p, const voi
 }
 
 sagebwd_status sagebwd_forward(const sagebwd_params* p, const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
-                               const float* Qs, const float* Ks, const float* Vs, const float* kbias, void* O,
-                               float* lse, void* stream) {
+                               const float* Qs, const float* Ks, const float* Vs, const float* kbias,
+                               const void* V, void* O, float* lse, void* stream) {
   sagebwd_status st = check_params(p);
   if (st != SAGEBWD_OK) return st;
   if (empty(p)) return SAGEBWD_OK;
-  st = check_ptrs(Qc, Kc, Vtc, Qs, Ks, Vs, O, lse);
+  const bool qattn = p->split == SAGEBWD_SPLIT_QATTN;
+  st = qattn ? check_ptrs(Qc, Kc, Qs, Ks, V, O, lse) : check_ptrs(Qc, Kc, Vtc, Qs, Ks, Vs, O, lse);
   if (st != SAGEBWD_OK) return st;
   if (p->q_smooth && (st = check_ptrs(kbias)) != SAGEBWD_OK) return st;
   ForwardArgs a{};
-  a.Qc = Qc; a.Kc = Kc; a.Vtc = Vtc; a.Qs = Qs; a.Ks = Ks; a.Vs = Vs;
+  a.Qc = Qc; a.Kc = Kc; a.Qs = Qs; a.Ks = Ks;
+  a.qattn = qattn;
+  if (qattn) {
+    a.V = static_cast<const unsigned short*>(V);
+  } else {
+    a.Vtc = Vtc;
+    a.Vs = Vs;
+  }
   a.q_smooth = p->q_smooth != 0;
   a.kbias = a.q_smooth ? kbias : nullptr;
   a.O = static_cast<unsigned short*>(O); a.lse = lse;
@@ -320,6 +330,7 @@ static sagebwd_status backward_impl(const sagebwd_params* p, int part, const voi
   a.x16 = strides16(p);
   // normed_grads: the epilogues stop before the RMSNorm backward
   a.causal = p->causal != 0; a.qk_norm = p->qk_norm != 0 && !p->normed_grads; a.sm_scale = sm_scale_of(p);
+  a.qattn = p->split == SAGEBWD_SPLIT_QATTN;
   return hip_status(sagebwd::launch_backward(a, part, static_cast<hipStream_t>(stream)), "sagebwd_backward");
 }
 

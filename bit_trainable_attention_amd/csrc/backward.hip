@@ -333,9 +333,10 @@ struct BwdLds {
   static constexpr int kMinBlocks = BLK == 64 ? 2 : 1;   // workgroups per CU
 };
 
-template <int DT, int D, int BLK, bool SPILL, bool QS, int FMT>
+template <int DT, int D, int BLK, bool SPILL, bool QS, int FMT, bool QA>
 __global__ __launch_bounds__((BwdLds<D, BLK, SPILL>::NW * 64), (BwdLds<D, BLK, SPILL>::kMinBlocks))
 void bwd_main(BackwardArgs a) {
+  static_assert(!(QS && QA), "Q-smoothing is not combined with the Q-Attn split");
   using L = BwdLds<D, BLK, SPILL>;
   using P = Packet<D>;
   constexpr int NW = L::NW;        // waves per workgroup
@@ -512,9 +513,46 @@ void bwd_main(BackwardArgs a) {
   };
 
   // the tile maxima (|dS| maximum to the workgroup), P codes and dV, and the Q^T operands of
-  // dK: every remaining read of the tile's buffer
+  // dK: every remaining read of the tile's buffer. With the Q-Attn split (QA) P is not
+  // quantised: dV^T += dO^T P runs in 16 bits, P rounded to the dtype as the B operand
+  // (slots 4t' + r of lane group g: rows 16t + 4g + r of sub-tiles t = 2u, 2u + 1) and dO^T
+  // as the A operand by transposing reads of the packet's row-major dO (four rows 16t + 4g ..
+  // + 3 per read, channels 16n .. 16n + 15).
   auto phase_post = [&](int bofs, int step) {
     const int8_t* buf = lds + bofs;
+    if constexpr (QA) {
+      float dm = fabsf(dsf[0][0]);
+#pragma unroll
+      for (int i = 1; i < 4 * NS; i += 2)
+        dm = fmaxf(fmaxf(dm, fabsf(dsf[i / 4][i % 4])), i + 1 < 4 * NS ? fabsf(dsf[(i + 1) / 4][(i + 1) % 4]) : 0.0f);
+      dm = wave_max_nonneg(dm);
+      if (l == 0) redD[(step & 1) * NW + w] = dm;
+      const int jl = l & 15, kr = jl >> 2, qq = jl & 3;
+      // P as 16-bit B operands first (the float P registers are then free)
+      u16x8 bp[NS / 2];
+#pragma unroll
+      for (int u = 0; u < NS / 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bp[u][r] = from_f32<DT>(pf[2 * u][r]);
+          bp[u][4 + r] = from_f32<DT>(pf[2 * u + 1][r]);
+        }
+#pragma unroll
+      for (int n = 0; n < NCT; ++n) {
+        const int ch = 2 * n + (qq >> 1);
+        auto rd = [&](int t) {
+          const int row = 16 * (t % 4) + 4 * g + kr;   // row of packet t / 4
+          return lds_read_tr16(buf + (t / 4) * P::kBytes + P::bDO + row * 2 * D + 16 * swz_do<D>(row, ch) +
+                               8 * (qq & 1));
+        };
+#pragma unroll
+        for (int u = 0; u < NS / 2; ++u) {
+          const u16x4 a0 = rd(2 * u), a1 = rd(2 * u + 1);
+          const u16x8 ad = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          dv[n] = mfma_16b_16x16x32<DT>(ad, bp[u], dv[n]);
+        }
+      }
+    } else {
     // ---- tile maxima (chains of three-input maxima; the |dS| maximum goes to the workgroup)
     float pm = pf[0][0], dm = fabsf(dsf[0][0]);
 #pragma unroll
@@ -548,6 +586,7 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) dv[n][r] = __builtin_fmaf(sv, (float)acc[r], dv[n][r]);
       }
+    }
     }
     // ---- Q^T operands of dK (after the next barrier the buffer is refilled)
     const int qa = bofs + oQT;
@@ -1052,24 +1091,28 @@ static hipError_t launch_backward_t(const BackwardArgs& a, int part, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (part < 0 || part == 1) {
-    auto go = [&](auto spill_c, auto qs_c, auto fmt_c) {
-      constexpr bool SP = decltype(spill_c)::value, QSV = decltype(qs_c)::value;
+    auto go = [&](auto spill_c, auto qs_c, auto fmt_c, auto qa_c) {
+      constexpr bool SP = decltype(spill_c)::value, QSV = decltype(qs_c)::value, QAV = decltype(qa_c)::value;
       constexpr int FM = decltype(fmt_c)::value;
       using L = BwdLds<D, BLK, SP>;
-      return launch_kernel(&bwd_main<DT, D, BLK, SP, QSV, FM>, dim3((unsigned)(nb * a.BH)), dim3(L::NW * 64), st,
-                           a);
+      return launch_kernel(&bwd_main<DT, D, BLK, SP, QSV, FM, QAV>, dim3((unsigned)(nb * a.BH)), dim3(L::NW * 64),
+                           st, a);
     };
     using T = std::true_type;
     using F = std::false_type;
     using I8 = std::integral_constant<int, FMT_INT8>;
     using F8 = std::integral_constant<int, FMT_FP8>;
     hipError_t e;
-    if (a.fmt == FMT_FP8) {   // (Q-smoothing takes INT8 codes only; the API refuses it with FP8)
-      if (a.q_smooth) return hipErrorInvalidValue;
-      e = a.spill ? go(T{}, F{}, F8{}) : go(F{}, F{}, F8{});
+    // (Q-smoothing takes INT8 codes and the SageBwd split only; the API refuses the others)
+    if (a.q_smooth && (a.fmt != FMT_INT8 || a.qattn)) return hipErrorInvalidValue;
+    if (a.qattn) {
+      if (a.fmt == FMT_FP8) e = a.spill ? go(T{}, F{}, F8{}, T{}) : go(F{}, F{}, F8{}, T{});
+      else e = a.spill ? go(T{}, F{}, I8{}, T{}) : go(F{}, F{}, I8{}, T{});
+    } else if (a.fmt == FMT_FP8) {
+      e = a.spill ? go(T{}, F{}, F8{}, F{}) : go(F{}, F{}, F8{}, F{});
     } else {
-      e = a.spill ? (a.q_smooth ? go(T{}, T{}, I8{}) : go(T{}, F{}, I8{}))
-                  : (a.q_smooth ? go(F{}, T{}, I8{}) : go(F{}, F{}, I8{}));
+      e = a.spill ? (a.q_smooth ? go(T{}, T{}, I8{}, F{}) : go(T{}, F{}, I8{}, F{}))
+                  : (a.q_smooth ? go(F{}, T{}, I8{}, F{}) : go(F{}, F{}, I8{}, F{}));
     }
     if (e != hipSuccess) return e;
   }

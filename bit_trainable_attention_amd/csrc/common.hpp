@@ -79,6 +79,17 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const int8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
 }
 
+// Transposing LDS read of 16-bit values (ds_read_b64_tr_b16). Inside each group of 16 lanes,
+// lanes 4k .. 4k+3 name the four 8-byte quarters of "row" k (k = 0..3, 16 values per row) and
+// lane j of the group receives value j of every row: result element k = value (j % 4) at the
+// address of lane 4k + j/4 (checked on the hardware). Reading four rows of a row-major 16-bit
+// tile thus hands each lane one column: the transposed operand of a 16-bit MFMA.
+__device__ __forceinline__ u16x4 lds_read_tr16(const void* p) {
+  typedef short s16x4 __attribute__((vector_size(8)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
@@ -132,6 +143,13 @@ __device__ __forceinline__ int rows_max(float v) {
   const int b = __float_as_int(v);
   return max(max(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
              max(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmax_dpp<0xB1>(x);
+  x = fmax_dpp<0x4E>(x);
+  x = fmax_dpp<0x124>(x);
+  x = fmax_dpp<0x128>(x);
+  return __int_as_float(rows_max(x));
 }
 __device__ __forceinline__ void wave_max2_nonneg(float& x, float& y) {
   x = fmax_dpp<0xB1>(x);  y = fmax_dpp<0xB1>(y);    // lane ^ 1

@@ -55,13 +55,29 @@ __device__ __forceinline__ int swz_f(int r, int j) {
   else return j ^ ((r >> 2) & 3);
 }
 
-template <int D, int BLK, bool QS = false>
+// Chunk swizzle of the Q-Attn split's 16-bit V rows (2D bytes, 16-byte chunks). The PV
+// operand reads (ds_read_b64_tr_b16) name 8 rows x 64 bytes at once (rows 4g + k, channel
+// bytes 32cg .. 32cg + 31, two groups cg); XORing the chunk with bits of the row lets those 32
+// chunks cover every bank group exactly twice (256-byte rows: row bits 0-1 into chunk bits
+// 2-3; 128-byte rows, two per bank cycle: row bit 1 into chunk bit 2).
+template <int D>
+__device__ __forceinline__ int swz_v16(int r, int j) {
+  if constexpr (D == 128) return j ^ ((r & 3) << 2);
+  else return j ^ (((r >> 1) & 1) << 2);
+}
+
+// One key tile's LDS. SageBwd split: TK = BLK keys (one quantisation block of K and V), K
+// codes and V^T codes. Q-Attn split (QA): TK = 64 keys, K codes and the tile's 16-bit V rows
+// (the PV product runs in 16 bits; the online-softmax step is the 64-key tile).
+template <int D, int BLK, bool QS = false, bool QA = false>
 struct FwdLds {
-  static constexpr int kBytesK = BLK * D;   // K codes [BLK][D], chunk j of row r at swz_f<D>(r, j)
-  static constexpr int kBytesV = D * BLK;   // V^T codes [D][BLK], chunk j of row c at swz_f<BLK>(c, j)
+  static constexpr int TK = QA ? 64 : BLK;
+  static constexpr int kBytesK = TK * D;                 // K codes [TK][D], chunk j of row r at swz_f<D>(r, j)
+  static constexpr int kBytesV = QA ? TK * 2 * D         // V [TK][D] 16-bit, chunk j of row r at swz_v16<D>(r, j)
+                                    : D * BLK;           // V^T codes [D][BLK], chunk j of row c at swz_f<BLK>(c, j)
   static constexpr int kBytesKV = kBytesK + kBytesV;
   static constexpr int kBytes = kBytesKV + (QS ? 1024 : 0);   // (QS) key biases f32 [BLK], one 1 KB copy
-  static constexpr int kCopies = kBytesKV / 1024;            // 1 KB copies of K and V^T per tile
+  static constexpr int kCopies = kBytesKV / 1024;            // 1 KB copies of K and V per tile
   static constexpr int kCopiesPerWave = kCopies / kWaves;
   static_assert(kCopies % kWaves == 0, "copies per wave");
 };
@@ -69,12 +85,21 @@ struct FwdLds {
 // Copies of key tile k0 into an LDS tile buffer: copy cp = w + kWaves*i moves LDS bytes
 // [1024 cp, 1024 cp + 1024); lane l fills the chunk at 1024 cp + 16 l and reads the logical
 // chunk that the swizzle puts there.
-template <int D, int BLK, bool QS>
+template <int D, int BLK, bool QS, bool QA>
 __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int k0, int8_t* dst, int w, int l) {
-  using L = FwdLds<D, BLK, QS>;
+  using L = FwdLds<D, BLK, QS, QA>;
   const int8_t* kh = a.Kc + (size_t)bh * a.N * D;     // this head's K codes
-  const int8_t* vh = a.Vtc + (size_t)bh * D * a.N;    // this head's V^T codes
   const uint32_t hbytes = (uint32_t)a.N * D;
+  // (QA) the tile's 16-bit V rows, read through a descriptor based at row k0 whose range ends
+  // after the last real token (the 16-bit tensors hold exactly Nv tokens): rows past it read
+  // as zeros
+  [[maybe_unused]] const unsigned short* vrow0 = nullptr;
+  [[maybe_unused]] uint32_t vbytes = 0;
+  if constexpr (QA) {
+    vrow0 = a.V + a.x16.row((int)bh, k0);
+    const int rows = min(L::TK, a.Nv - k0);
+    vbytes = rows > 0 ? (uint32_t)((rows - 1) * a.x16.sn + D) * 2u : 0u;
+  }
 #pragma unroll
   for (int i = 0; i < L::kCopiesPerWave; ++i) {
     const int cp = w + kWaves * i;
@@ -83,7 +108,13 @@ __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int 
       const int r = e / (D / 16), pc = e % (D / 16);
       const int j = swz_f<D>(r, pc);                    // the swizzle is an involution
       buffer_to_lds16(kh, hbytes, dst + cp * 1024, (uint32_t)((k0 + r) * D + 16 * j), 0u);
+    } else if constexpr (QA) {
+      const int ev = e - L::kBytesK / 16;
+      const int r = ev / (D / 8), pc = ev % (D / 8);
+      const int j = swz_v16<D>(r, pc);
+      buffer_to_lds16(vrow0, vbytes, dst + cp * 1024, (uint32_t)(r * a.x16.sn * 2 + 16 * j), 0u);
     } else {
+      const int8_t* vh = a.Vtc + (size_t)bh * D * a.N;    // this head's V^T codes
       const int ev = e - L::kBytesK / 16;
       const int c = ev / (BLK / 16), pc = ev % (BLK / 16);
       const int j = swz_f<BLK>(c, pc);
@@ -99,12 +130,14 @@ __device__ __forceinline__ void issue_tile(const ForwardArgs& a, size_t bh, int 
 
 }  // namespace
 
-template <int DT, int D, int BLK, bool QS, int FMT>
+template <int DT, int D, int BLK, bool QS, int FMT, bool QA>
 __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
-  using L = FwdLds<D, BLK, QS>;
+  using L = FwdLds<D, BLK, QS, QA>;
   using C = Codes<FMT>;
   static_assert(FMT == FMT_INT8 || !QS, "Q-smoothing takes INT8 codes only");
-  constexpr int NSUB = BLK / 32;  // 32-key subtiles per key tile
+  static_assert(!(QS && QA), "Q-smoothing is not combined with the Q-Attn split");
+  constexpr int TK = L::TK;       // keys per tile (one online-softmax step)
+  constexpr int NSUB = TK / 32;   // 32-key subtiles per key tile
   constexpr int DC = D / 32;      // 32-channel chunks
   __shared__ __attribute__((aligned(16))) int8_t lds[2][L::kBytes];
 
@@ -129,7 +162,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
     sQ = a.Qs[(size_t)bh * nb + q0w / BLK];
   }
   const int last_row = min(q0 + kRowsPerBlock, a.N) - 1;
-  const int n_kt = a.causal ? last_row / BLK + 1 : nb;
+  const int n_kt = a.causal ? last_row / TK + 1 : a.N / TK;
 
   // m: running row max (the reference of P~); mo: the reference of O and l, which follows m
   // only when some row of the wave has moved more than kLazy past it (and on the first tile)
@@ -138,21 +171,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
   for (int ct = 0; ct < DC; ++ct) o[ct] = f32x16{};
 
-  issue_tile<D, BLK, QS>(a, bh, 0, lds[0], w, l);
+  issue_tile<D, BLK, QS, QA>(a, bh, 0, lds[0], w, l);
   wait_vmcnt<0>();
   __syncthreads();
-  // block scales of the current key tile, loaded one tile ahead
-  float sK_n = a.Ks[(size_t)bh * nb], sV_n = a.Vs[(size_t)bh * nb];
+  // block scales of the current key tile, loaded one tile ahead (QA: V is not quantised)
+  float sK_n = a.Ks[(size_t)bh * nb], sV_n = QA ? 1.0f : a.Vs[(size_t)bh * nb];
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const bool has_next = kt + 1 < n_kt;
-    if (has_next) issue_tile<D, BLK, QS>(a, bh, (kt + 1) * BLK, lds[(kt + 1) & 1], w, l);
+    if (has_next) issue_tile<D, BLK, QS, QA>(a, bh, (kt + 1) * TK, lds[(kt + 1) & 1], w, l);
     const float sK = sK_n, sV = sV_n;
     if (has_next) {
-      sK_n = a.Ks[(size_t)bh * nb + kt + 1];
-      sV_n = a.Vs[(size_t)bh * nb + kt + 1];
+      sK_n = a.Ks[(size_t)bh * nb + (kt + 1) * TK / BLK];
+      if constexpr (!QA) sV_n = a.Vs[(size_t)bh * nb + kt + 1];
     }
-    const int k0 = kt * BLK;
+    const int k0 = kt * TK;
     const int8_t* kl = lds[kt & 1];
     const int8_t* vl = lds[kt & 1] + L::kBytesK;
     // One key tile. DIAG: the tile crosses this wave's causal diagonal (keys above it are
@@ -244,10 +277,61 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
         if constexpr (DIAG) rowmax = rmax == INT32_MIN ? -INFINITY : rowmax;
       }
       const float m_new = fmaxf(m, rowmax);
-      const bool moved = __builtin_amdgcn_ballot_w64(m_new > mo + kLazy) != 0;
+      // (QA: the reference follows the running max exactly, so the 16-bit P~ are taken, and
+      // rounded, against it as in the definition)
+      const bool moved = __builtin_amdgcn_ballot_w64(m_new > mo + (QA ? 0.0f : kLazy)) != 0;
       const float mo_new = moved ? m_new : mo;
       const float alpha = __builtin_amdgcn_exp2f(mo - mo_new);   // 1 exactly when not moved
       const float up = __builtin_amdgcn_exp2f(m_new - mo_new);   // P~ in units of 2^mo_new
+      if constexpr (QA) {
+        // ---- P~ = 2^(s*c2 - m') rounded to the 16-bit type: the B operand of the 16-bit PV
+        //      (register r of subtile t holds key 8*(r/4) + 4g + r%4: r = 0..7 feed the first
+        //      16-key product, r = 8..15 the second, with the same key slots in V^T's reads)
+        float tsum = 0.0f;
+        u16x8 pb[NSUB][2];
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = __builtin_fmaf((float)s[t][4 * j + i], c2, -m_new);
+              if constexpr (DIAG && FMT == FMT_FP8) x = s[t][4 * j + i] == -INFINITY ? -INFINITY : x;
+              if constexpr (DIAG && FMT == FMT_INT8) x = s[t][4 * j + i] == INT32_MIN ? -INFINITY : x;
+              const float u = __builtin_amdgcn_exp2f(x);
+              tsum += u;
+              pb[t][j >> 1][4 * (j & 1) + i] = from_f32<DT>(u);
+            }
+        lsum_run = lsum_run * alpha + tsum;
+        __builtin_amdgcn_iglp_opt(1);
+        if (moved) {
+#pragma unroll
+          for (int ct = 0; ct < DC; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+        }
+        // ---- O^T += V^T P~^T in 16 bits, float32 accumulation. V^T's A operand (row =
+        //      channel 32ct + 16cg + jl, key slots of lane group g) comes from the row-major V
+        //      tile by two transposing reads of four key rows each.
+        const int cg = (l >> 4) & 1, jl = l & 15, kr = jl >> 2, qq = jl & 3;
+#pragma unroll
+        for (int ct = 0; ct < DC; ++ct) {
+          const int ch = 4 * ct + 2 * cg + (qq >> 1);
+#pragma unroll
+          for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int ra = 32 * t + 16 * h + 4 * g + kr, rb = ra + 8;
+              const u16x4 a0 = lds_read_tr16(vl + ra * 2 * D + 16 * swz_v16<D>(ra, ch) + 8 * (qq & 1));
+              const u16x4 a1 = lds_read_tr16(vl + rb * 2 * D + 16 * swz_v16<D>(rb, ch) + 8 * (qq & 1));
+              const u16x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+              o[ct] = mfma_16b_32x32x16<DT>(av, pb[t][h], o[ct]);
+            }
+        }
+        m = m_new;
+        mo = mo_new;
+        return;
+      }
       // P~ tile absmax a = max over rows of 2^(rowmax - m'); in log2 it is one wave max.
       // The quantisation factor M/a is folded into the exponent, so the exponential
       // yields P~ * M/a directly and its nearest-even code is the code.
@@ -320,7 +404,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
       mo = mo_new;
     };
     if (active && (!a.causal || k0 <= q0w + kRowsPerWave - 1)) {
-      if ((a.causal && k0 + BLK - 1 > q0w) || k0 + BLK > a.Nv) tile(std::true_type{});
+      if ((a.causal && k0 + TK - 1 > q0w) || k0 + TK > a.Nv) tile(std::true_type{});
       else tile(std::false_type{});
     }
     wait_vmcnt<0>();   // the next tile's copies (the only vector-memory operations in the loop)
@@ -357,10 +441,14 @@ template <int DT, int D, int BLK>
 static hipError_t launch_forward_t(const ForwardArgs& a, hipStream_t st) {
   const long long nq = (a.N + kRowsPerBlock - 1) / kRowsPerBlock;
   const dim3 grid((unsigned)(nq * a.BH)), block(kWaves * 64);
-  if (a.fmt == FMT_FP8)   // (Q-smoothing takes INT8 codes only; the API refuses it with FP8)
-    return a.q_smooth ? hipErrorInvalidValue : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_FP8>, grid, block, st, a);
-  return a.q_smooth ? launch_kernel(&fwd_kernel<DT, D, BLK, true, FMT_INT8>, grid, block, st, a)
-                    : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_INT8>, grid, block, st, a);
+  // (Q-smoothing takes INT8 codes and the SageBwd split only; the API refuses the others)
+  if (a.q_smooth && (a.fmt != FMT_INT8 || a.qattn)) return hipErrorInvalidValue;
+  if (a.qattn)
+    return a.fmt == FMT_FP8 ? launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_FP8, true>, grid, block, st, a)
+                            : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_INT8, true>, grid, block, st, a);
+  if (a.fmt == FMT_FP8) return launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_FP8, false>, grid, block, st, a);
+  return a.q_smooth ? launch_kernel(&fwd_kernel<DT, D, BLK, true, FMT_INT8, false>, grid, block, st, a)
+                    : launch_kernel(&fwd_kernel<DT, D, BLK, false, FMT_INT8, false>, grid, block, st, a);
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t st) {

@@ -44,6 +44,8 @@ struct ForwardArgs {
   const int8_t *Qc, *Kc, *Vtc;
   const float *Qs, *Ks, *Vs;
   const float* kbias;                // [BH, N] (Q-smoothing only)
+  const unsigned short* V;           // 16-bit V, layout x16 (Q-Attn split only)
+  int qattn;                         // Q-Attn split: PV in 16 bits from V
   unsigned short* O;                 // [BH, N, D]
   float* lse;                        // [BH, N]
   int BH, N, D, BLK, dtype;
@@ -78,6 +80,7 @@ struct BackwardArgs {
   int Nv;                            // valid tokens per head (N = Nv rounded up to blk)
   int fmt;                           // code format: FMT_INT8 or FMT_FP8
   Strides16 x16;                     // layout of the 16-bit tensors
+  int qattn;                         // Q-Attn split: dV = P^T dO in 16 bits
 };
 
 // Enqueue one kernel and return the status of this launch itself (hipLaunchKernel reports

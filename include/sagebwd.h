@@ -69,15 +69,17 @@ extern "C" {
 #define SAGEBWD_FWD_TILE_Q 32
 #define SAGEBWD_BWD_P_TILE_K 16
 #define SAGEBWD_BWD_DS_TILE_K 64
+/* Q-Attn split: keys per forward tile (the online-softmax step; P~ is not quantised there) */
+#define SAGEBWD_QATTN_FWD_TILE_K 64
 
 typedef enum {
   SAGEBWD_OK = 0,
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
   SAGEBWD_ERR_SHAPE = -2,       /* negative size, N > 2^22, or B*H > 2^24                  */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
-                                   layout or fmt, eps < 0, qk_gain or normed_grads
-                                   without qk_norm, normed_grads with qk_gain, FP8 with
-                                   q_smooth                                                 */
+                                   layout or fmt or split, eps < 0, qk_gain or
+                                   normed_grads without qk_norm, normed_grads with qk_gain,
+                                   q_smooth with FP8 or with the Q-Attn split               */
   SAGEBWD_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                         */
   SAGEBWD_ERR_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes() figure    */
   SAGEBWD_ERR_HIP = -6,         /* a kernel launch failed                                   */
@@ -109,8 +111,24 @@ typedef struct {
   int32_t normed_grads; /* nonzero (with qk_norm, without qk_gain): the backward returns dQ,
                            dK with respect to the normalised Q^, K^ (before smoothing) and
                            leaves the RMSNorm backward to the caller                         */
-  int32_t fmt;          /* sagebwd_fmt of the six quantised products' codes (INT8 or FP8)     */
+  int32_t fmt;          /* sagebwd_fmt of the quantised products' codes (INT8 or FP8)         */
+  int32_t split;        /* sagebwd_split: which of the seven products are quantised          */
 } sagebwd_params;
+
+/* Precision split of attention's seven products.
+ * SAGEBWD_SPLIT_SAGEBWD (SageBwd article, precision-split paragraph): six products quantised
+ *   (forward QK^T and PV; backward recomputed QK^T, dV = P^T dO, dK = dS^T Q, dQ = dS K),
+ *   dP = dO V^T in the 16-bit input type.
+ * SAGEBWD_SPLIT_QATTN (Full-Stack FP4 page, section 2.4, mixed-precision attention): the
+ *   robust paths stay quantised, QK^T (forward and recomputed) and the dS products dK and dQ;
+ *   the softmax-sensitive paths PV, P^T dO and dO V^T run on the 16-bit MFMA in the inputs'
+ *   16-bit type (the page's BF16 is the bf16 inputs' type; fp16 inputs use fp16): P~ and P are
+ *   rounded to it (nearest even) and V and dO enter with their own values, float32
+ *   accumulation. The forward's key tile is SAGEBWD_QATTN_FWD_TILE_K keys (the running max
+ *   moves once per tile and P~ = exp(s - running max) exactly, no lagging reference); the
+ *   forward reads the raw V (sagebwd_forward's V argument) and ignores the V codes; the
+ *   backward's P and dS tiles are as above, P only rounded. Not with q_smooth. */
+typedef enum { SAGEBWD_SPLIT_SAGEBWD = 0, SAGEBWD_SPLIT_QATTN = 1 } sagebwd_split;
 
 /* Code format of the six quantised products (SageBwd article, precision-split paragraph,
  * which names FP8 as the alternative low-bit format of the same split). SAGEBWD_FMT_INT8:
@@ -212,13 +230,16 @@ sagebwd_status sagebwd_quant_prologue_noalloc(const sagebwd_params* p,
 /* Forward: O = softmax(sm_scale * Q^ K~^T [causal mask]) V with INT8 QK^T and PV.
  *   inputs : the prologue's Qc, Kc, Vtc, Qs, Ks, Vs, and its kbias with q_smooth (each
  *            score is then sm_scale * (Q~ K~^T + b_k); kbias ignored, may be NULL, without)
+ *   V   in : dtype [B,H,N,d] (layout as Q): the raw values, read by the Q-Attn split's
+ *            16-bit PV (Vtc and Vs are then ignored and may be NULL); ignored, may be NULL,
+ *            with the SageBwd split
  *   O   out: dtype [B,H,N,d]
  *   lse out: float32 [B,H,Np], natural-log logsumexp of each row of the scaled scores
  *            (+inf for the padding rows from N on) */
 sagebwd_status sagebwd_forward(const sagebwd_params* p,
                                const int8_t* Qc, const int8_t* Kc, const int8_t* Vtc,
                                const float* Qs, const float* Ks, const float* Vs,
-                               const float* kbias, void* O, float* lse, void* stream);
+                               const float* kbias, const void* V, void* O, float* lse, void* stream);
 
 /* Bytes of scratch sagebwd_backward needs. Layout (each region starts on a 256-byte
  * boundary, in this order; "chunk" = 16 bytes):

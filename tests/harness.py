@@ -26,13 +26,16 @@ def header_functions() -> list:
     return sorted(set(re.findall(r"^\s*(?:size_t|sagebwd_status|const char\*)\s+(sagebwd_\w+)\s*\(", text, re.M)))
 
 
-def spec_for(w: wl.Workload, dtype: Optional[str] = None, normed_grads: bool = False, fmt: str = "int8") -> oq.Spec:
+def spec_for(w: wl.Workload, dtype: Optional[str] = None, normed_grads: bool = False, fmt: str = "int8",
+             split: str = "sagebwd") -> oq.Spec:
     c = header_constants()
+    qa = split == "qattn"
     return oq.Spec(N=w.N, d=w.d, blk=w.blk, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth,
                    dtype=dtype or w.dtype, eps=w.eps, sm_scale=w.sm_scale,
-                   fwd_tq=c["FWD_TILE_Q"], fwd_tk=w.blk, bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
+                   fwd_tq=c["FWD_TILE_Q"], fwd_tk=min(w.blk, c["QATTN_FWD_TILE_K"]) if qa else w.blk,
+                   bwd_tq=w.blk, bwd_pk=c["BWD_P_TILE_K"],
                    bwd_sk=min(w.blk, c["BWD_DS_TILE_K"]), q_smooth=w.q_smooth, normed_grads=normed_grads,
-                   fmt=fmt)
+                   fmt=fmt, split=split)
 
 
 def rel_l2(a, b) -> float:
@@ -80,11 +83,11 @@ def host_inputs(w: wl.Workload) -> Dict[str, np.ndarray]:
 # ------------------------------------------------------------------------------- GPU side
 
 def params_for(w: wl.Workload, dq_mode: int = 0, layout: str = "bhnd", qk_gain: bool = False,
-               normed_grads: bool = False, fmt: str = "int8"):
+               normed_grads: bool = False, fmt: str = "int8", split: str = "sagebwd"):
     from bit_trainable_attention_amd import api
     return api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps,
                            dq_mode=dq_mode, q_smooth=w.q_smooth, layout=layout, qk_gain=qk_gain,
-                           normed_grads=normed_grads, fmt=fmt)
+                           normed_grads=normed_grads, fmt=fmt, split=split)
 
 
 def to_device(bits: np.ndarray, dtype: str):
@@ -101,7 +104,8 @@ def f32_to_device_dtype(x: np.ndarray, dtype: str):
 
 def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forward", "backward"),
             pro_in=None, O_in=None, lse_in=None, dq_mode: int = 0, layout: str = "bhnd",
-            gains=None, normed_grads: bool = False, fmt: str = "int8") -> Dict[str, np.ndarray]:
+            gains=None, normed_grads: bool = False, fmt: str = "int8",
+            split: str = "sagebwd") -> Dict[str, np.ndarray]:
     """Run the HIP path and return host copies (numpy) of everything it produced. With
     layout "bnhd" the 16-bit tensors are handed to the library as [B,N,H,d] (a transposed
     copy of the same values) and its O, dQ, dK, dV are returned transposed back. gains:
@@ -110,7 +114,7 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
     as their uint8 bit patterns, like the oracle's)."""
     import torch
     from bit_trainable_attention_amd import api
-    p = params_for(w, dq_mode, layout, qk_gain=gains is not None, normed_grads=normed_grads, fmt=fmt)
+    p = params_for(w, dq_mode, layout, qk_gain=gains is not None, normed_grads=normed_grads, fmt=fmt, split=split)
     gq = gk = None
     if gains is not None:
         gq, gk = (torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).to("cuda:0") for g in gains)
@@ -125,7 +129,7 @@ def gpu_run(w: wl.Workload, x: Dict[str, np.ndarray], stages=("prologue", "forwa
         pro = api.sagebwd_quant_prologue(p, Q, K, V, q_gain=gq, k_gain=gk)
     O, lse = O_in, lse_in
     if "forward" in stages:
-        O, lse = api.sagebwd_forward(p, pro)
+        O, lse = api.sagebwd_forward(p, pro, V=V)
     if "backward" in stages:
         g = api.sagebwd_backward(p, Q, K, V, pro, O, lse, dO, q_gain=gq, k_gain=gk)
     torch.cuda.synchronize()
@@ -173,11 +177,12 @@ def decode_packets(ws: np.ndarray, lay: Dict[str, int], w: wl.Workload) -> Dict[
     return {"dOtc": dOtc, "dOs": dOs, "Dvec": Dv}
 
 
-def check_prologue(g: Dict[str, np.ndarray], o: Dict[str, np.ndarray]) -> None:
+def check_prologue(g: Dict[str, np.ndarray], o: Dict[str, np.ndarray], check_v: bool = True) -> None:
     """The GPU prologue's codes, scales, rstd and K mean (and query mean with Q-smoothing)
     equal the oracle's bit for bit; the key bias (float32 on the GPU, any summation order)
-    is within float32 rounding of the oracle's float64 value."""
-    keys = ["Qc", "Kc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean"]
+    is within float32 rounding of the oracle's float64 value. check_v False skips the V codes
+    (the Q-Attn split's oracle keeps V's own values; the products never read the V codes)."""
+    keys = ["Qc", "Kc", "Qs", "Ks", "q_rstd", "k_rstd", "k_mean"] + (["Vs"] if check_v else [])
     if "kbias" in g:
         keys.append("q_mean")
         kb = np.asarray(o["kbias"], np.float64)
@@ -187,7 +192,9 @@ def check_prologue(g: Dict[str, np.ndarray], o: Dict[str, np.ndarray]) -> None:
     for k in keys:
         assert g[k].dtype == o[k].dtype, k
         assert np.array_equal(g[k], o[k]), (k, int(np.sum(g[k] != o[k])))
-    assert np.array_equal(g["Vtc"], np.swapaxes(o["Vc"], -1, -2)), int(np.sum(g["Vtc"] != np.swapaxes(o["Vc"], -1, -2)))
+    if check_v:
+        assert np.array_equal(g["Vtc"], np.swapaxes(o["Vc"], -1, -2)), \
+            int(np.sum(g["Vtc"] != np.swapaxes(o["Vc"], -1, -2)))
 
 
 def pro_to_device(pro: Dict[str, np.ndarray]):

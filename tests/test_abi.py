@@ -19,7 +19,7 @@ lib = _lib.load()  # fails loudly if the library was not built
 def P(**kw):
     base = dict(B=1, H=2, N=256, d=64, blk=64, causal=1, qk_norm=1, k_smooth=1, eps=1e-6, sm_scale=0.0,
                 dtype=_lib.SAGEBWD_FP16, dq_mode=0, q_smooth=0, layout=_lib.LAYOUT_BHND, qk_gain=0,
-                normed_grads=0, fmt=_lib.FMT_INT8)
+                normed_grads=0, fmt=_lib.FMT_INT8, split=_lib.SPLIT_SAGEBWD)
     base.update(kw)
     return _lib.Params(**base)
 
@@ -37,8 +37,8 @@ def test_exports_every_header_symbol():
 
 def test_header_tile_constants_match_binding():
     c = header_constants()
-    assert (c["FWD_TILE_Q"], c["BWD_P_TILE_K"], c["BWD_DS_TILE_K"]) == \
-        (_lib.FWD_TILE_Q, _lib.BWD_P_TILE_K, _lib.BWD_DS_TILE_K)
+    assert (c["FWD_TILE_Q"], c["BWD_P_TILE_K"], c["BWD_DS_TILE_K"], c["QATTN_FWD_TILE_K"]) == \
+        (_lib.FWD_TILE_Q, _lib.BWD_P_TILE_K, _lib.BWD_DS_TILE_K, _lib.QATTN_FWD_TILE_K)
 
 
 def test_status_strings():
@@ -63,7 +63,7 @@ def _prologue_noalloc(p, ptr=FAKE):
 
 
 def _forward(p, ptr=FAKE):
-    return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 9), None)
+    return lib.sagebwd_forward(ctypes.byref(p), *([ptr] * 10), None)
 
 
 def _backward(p, ptr=FAKE, ws=FAKE, ws_bytes=1 << 40):
@@ -86,6 +86,9 @@ def test_invalid_params_rejected(call):
     assert call(P(fmt=2)) == -3
     assert call(P(fmt=-1)) == -3
     assert call(P(fmt=_lib.FMT_FP8, q_smooth=1)) == -3   # Q-smoothing sums INT8 codes
+    assert call(P(split=2)) == -3
+    assert call(P(split=-1)) == -3
+    assert call(P(split=_lib.SPLIT_QATTN, q_smooth=1)) == -3
     assert call(P(B=-1)) == -2
     assert call(P(N=-64)) == -2
     assert call(P(B=1 << 13, H=1 << 12)) == -2
@@ -95,7 +98,7 @@ def test_invalid_params_rejected(call):
 
 
 def test_null_params_rejected():
-    assert lib.sagebwd_forward(None, *([FAKE] * 9), None) == -1
+    assert lib.sagebwd_forward(None, *([FAKE] * 10), None) == -1
     assert lib.sagebwd_backward_workspace_bytes(None) == 0
     assert lib.sagebwd_prologue_workspace_bytes(None) == 0
 
@@ -175,7 +178,7 @@ def test_q_smooth_arguments():
     assert pro_with(P(q_smooth=1), 0, FAKE) == -1
     assert pro_with(P(q_smooth=1), FAKE, 0) == -1
     assert pro_with(P(q_smooth=1), MIS, FAKE) == -4
-    fw = lambda p, kb: lib.sagebwd_forward(ctypes.byref(p), *([FAKE] * 6), kb, FAKE, FAKE, None)
+    fw = lambda p, kb: lib.sagebwd_forward(ctypes.byref(p), *([FAKE] * 6), kb, FAKE, FAKE, FAKE, None)
     assert fw(P(q_smooth=1), 0) == -1
     bw = lambda p, qm, kb: lib.sagebwd_backward(ctypes.byref(p), *([FAKE] * 9), qm, kb, *([FAKE] * 10),
                                                 FAKE, 1 << 40, None)
@@ -236,3 +239,14 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     text = open(header_path()).read()
     m = re.search(r"#define\s+SAGEBWD_NOALLOC_SCRATCH_BYTES\s+\((\d+)ull\s*<<\s*(\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_qattn_forward_needs_raw_v():
+    """The Q-Attn split's forward reads the raw 16-bit V (its PV is 16-bit) and not the V codes:
+    a null V is an argument error, misaligned V too."""
+    qa = P(split=_lib.SPLIT_QATTN)
+    fw = lambda p, vtc, vs, v: lib.sagebwd_forward(ctypes.byref(p), FAKE, FAKE, vtc, FAKE, FAKE, vs, None, v,
+                                                   FAKE, FAKE, None)
+    assert fw(qa, FAKE, FAKE, 0) == -1
+    assert fw(qa, FAKE, FAKE, MIS) == -4
+    assert fw(P(), FAKE, 0, FAKE) == -1       # the SageBwd split still needs the V codes
