@@ -33,7 +33,8 @@
  *   P  (backward)  : blk query rows (one query block) x SAGEBWD_BWD_P_TILE_K keys.
  *   dS (backward)  : blk query rows x SAGEBWD_BWD_DS_TILE_K keys.
  * Every tile lies inside one blk x blk block, so the block scales factor out of each
- * integer product.
+ * integer product. The tile shapes are compile-time constants of the kernels (the macros
+ * below); the caller cannot choose them.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors), contiguous,
