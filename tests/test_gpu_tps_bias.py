@@ -13,9 +13,15 @@ g_k = mean_{i<k} g_q(dO_i) is compared with g_exact(mean_{i<k} dO_i):
 
 Independent zero-mean rounding errors shrink like 1/sqrt(k); a bias does not. Fitting
 err_k^2 = b^2 + v / k at k = 1 and k = 64 splits the two. The test prints the curve and the
-fit for the INT8 and FP8 recipes. It asserts only what averaging must give when the noise
-term dominates one batch (err_64 below err_1), that the single-batch error is not smaller than
-the fitted floor, and that every figure is finite.
+fit for the INT8 and FP8 recipes, for the GPU path and for the quantised oracle on the same
+batches, and asserts:
+  - the oracle shows the mechanism: err_64 stays above 1.5x the pure 1/sqrt(k) decay
+    err_1 / 8, i.e. a floor b > 0 that averaging does not remove;
+  - the GPU curve is the oracle's: by the triangle inequality and the parity bar (rel-L2 of
+    each batch's gradients within `bar` of the oracle's: 2e-3 INT8, 1e-2 FP8),
+    |err_k(GPU) - err_k(oracle)| <= bar * mean_{i<k} ||g_oracle(dO_i)|| / ||g_exact(S)||,
+    and the fitted floors agree within the bound this gives at k = 64;
+  - err_64 below err_1, the single-batch error not below the fitted floor, all finite.
 """
 import sys
 
@@ -24,7 +30,8 @@ import pytest
 
 from bit_trainable_attention_amd import workloads as wl
 from oracle import exact
-from tests.harness import gpu_run, host_inputs
+from oracle import quant as oq
+from tests.harness import gpu_run, host_inputs, spec_for
 
 pytestmark = pytest.mark.gpu
 
@@ -58,17 +65,50 @@ def test_tps_bias_curve(fmt):
         e = exact.attention(x["Qf"], x["Kf"], x["Vf"], dO, causal=w.causal, qk_norm=w.qk_norm, eps=w.eps)
         return np.concatenate([e[k].ravel() for k in ("dQ", "dK", "dV")])
 
+    # the quantised oracle on the same batches (prologue and forward do not depend on dO)
+    spec = spec_for(w, fmt=fmt)
+    tq = oq.fp8_tile_quant if fmt == "fp8" else oq.int8_tile_quant
+    bq = oq.quant_blocks_fp8_f32 if fmt == "fp8" else oq.quant_blocks_f32
+    pro = oq.prologue(x["Qf"], x["Kf"], x["Vf"], spec, block_quant=bq)
+    O, L = oq.forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec, tile_quant=tq)
+    ograds = []
+    for i in range(kmax):
+        g = oq.backward(pro, x["Qf"], x["Kf"], x["Vf"], O, L, dos[i].astype(np.float32), spec, tile_quant=tq,
+                        block_quant=bq)
+        ograds.append(np.concatenate([g[k].ravel() for k in ("dQ", "dK", "dV")]))
+
     ref_norm = np.linalg.norm(g_exact(S))
-    errs = {}
-    for k in KS:
-        gk = np.mean(grads[:k], axis=0)
-        errs[k] = float(np.linalg.norm(gk - g_exact(np.mean(dos[:k], axis=0))) / ref_norm)
-    # err_k^2 = b^2 + v/k from k = 1 and k = kmax
-    v = (errs[1] ** 2 - errs[kmax] ** 2) / (1.0 - 1.0 / kmax)
-    b2 = errs[kmax] ** 2 - v / kmax
-    b = float(np.sqrt(max(b2, 0.0)))
-    _say(f"[tps] {fmt}: err_k {errs}; fitted bias floor {b:.3e}, noise term sqrt(v) {np.sqrt(max(v, 0.0)):.3e} "
+
+    def curve(gs):
+        out = {}
+        for k in KS:
+            gk = np.mean(gs[:k], axis=0)
+            out[k] = float(np.linalg.norm(gk - g_exact(np.mean(dos[:k], axis=0))) / ref_norm)
+        return out
+
+    def floor(e):   # err_k^2 = b^2 + v/k from k = 1 and k = kmax
+        v = (e[1] ** 2 - e[kmax] ** 2) / (1.0 - 1.0 / kmax)
+        return float(np.sqrt(max(e[kmax] ** 2 - v / kmax, 0.0))), float(np.sqrt(max(v, 0.0)))
+
+    errs, oerrs = curve(grads), curve(ograds)
+    b, sv = floor(errs)
+    ob, osv = floor(oerrs)
+    _say(f"[tps] {fmt}: GPU err_k {errs}; fitted bias floor {b:.3e}, noise term sqrt(v) {sv:.3e} "
          f"(1/sqrt(k) prediction at k={kmax}: {errs[1] / np.sqrt(kmax):.3e})")
-    assert all(np.isfinite(e) for e in errs.values())
+    _say(f"[tps] {fmt}: oracle err_k {oerrs}; fitted bias floor {ob:.3e}, noise term sqrt(v) {osv:.3e}")
+    assert all(np.isfinite(e) for e in list(errs.values()) + list(oerrs.values()))
     assert errs[kmax] < errs[1]
     assert errs[1] >= b
+    # the mechanism, on the oracle: a floor that averaging does not remove
+    assert oerrs[kmax] > 1.5 * oerrs[1] / np.sqrt(kmax), oerrs
+    # the GPU follows the oracle within the parity bar carried through the averages
+    bar = 1e-2 if fmt == "fp8" else 2e-3
+    gnorm = np.array([np.linalg.norm(g) for g in ograds]) / ref_norm
+    for k in KS:
+        tol = bar * float(np.mean(gnorm[:k]))
+        assert abs(errs[k] - oerrs[k]) <= tol, (k, errs[k], oerrs[k], tol)
+    # floors: b^2 = (kmax e_kmax^2 - e_1^2) / (kmax - 1) moves by at most this much when every
+    # e_k moves by at most tol (first order, e_k >= b)
+    tol_b = bar * float(np.mean(gnorm)) * (kmax * errs[kmax] + errs[1]) / ((kmax - 1) * max(b, 1e-12))
+    _say(f"[tps] {fmt}: floors GPU {b:.4e} vs oracle {ob:.4e} (bound {tol_b:.2e})")
+    assert abs(b - ob) <= tol_b, (b, ob, tol_b)
