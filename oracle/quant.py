@@ -517,6 +517,15 @@ def identity_tile_quant(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 # Forward and backward (float64 after the prologue).
 # ----------------------------------------------------------------------------
 
+def lowbit_product(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The product of two code operands (batched matmul, float64). INT8 code products are
+    exact integers and FP8 code products exact in float64, so this is the plain product; it
+    is one function so that a test can model a matrix core's inexact accumulation in its
+    place (tests/test_oracle_fp8_model.py). Used for QK^T (both passes), PV, dV, dK and dQ.
+    Pinned by: the lossless reductions (test_lossless_block_quant_equals_exact, _fp8_)."""
+    return a @ b
+
+
 def _flat(a: np.ndarray, nlead: int = 2) -> np.ndarray:
     return a.reshape((-1,) + a.shape[nlead:])
 
@@ -573,7 +582,7 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
             if spec.causal and j0 > i0 + tq - 1:
                 break
             cols = np.arange(j0, j0 + tk)
-            S = qi @ k[:, j0:j0 + tk, :].transpose(0, 2, 1)
+            S = lowbit_product(qi, k[:, j0:j0 + tk, :].transpose(0, 2, 1))
             s = S * (sq * ks[:, j0 // blk] * sm)[:, None, None]
             if kb is not None:
                 s = s + sm * kb[:, None, j0:j0 + tk]
@@ -586,7 +595,7 @@ def forward(Qc, Kc, Vc, Qs, Ks, Vs, spec: Spec, tile_quant: TileQuant = int8_til
             alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
             l = l * alpha + Pt.sum(axis=-1)
             qP, sP = tile_quant(Pt)
-            pv = qP @ v[:, j0:j0 + tk, :]
+            pv = lowbit_product(qP, v[:, j0:j0 + tk, :])
             acc = acc * alpha[..., None] + (sP * vs[:, j0 // blk])[:, None, None] * pv
             m = m_new
         with np.errstate(divide="ignore", invalid="ignore"):   # padding rows: l = 0, dropped below
@@ -702,7 +711,7 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
                 if not ((qsel is not None and it in qsel) or (ksel is not None and jt in ksel)):
                     continue
             cols = np.arange(j0, j0 + sk)
-            S = qc[:, i0:i0 + tq, :] @ kc[:, j0:j0 + sk, :].transpose(0, 2, 1)
+            S = lowbit_product(qc[:, i0:i0 + tq, :], kc[:, j0:j0 + sk, :].transpose(0, 2, 1))
             s = S * (qs[:, i0 // blk] * ks[:, j0 // blk] * sm)[:, None, None]
             if qsm:
                 s = s + sm * kb[:, None, j0:j0 + sk]
@@ -716,13 +725,13 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             for p0 in range(0, sk, pk):
                 qP, sP = p_quant(P[:, :, p0:p0 + pk])
                 dV[:, j0 + p0:j0 + p0 + pk, :] += (sP * dos[:, i0 // blk])[:, None, None] * (
-                    qP.transpose(0, 2, 1) @ doc[:, i0:i0 + tq, :])
+                    lowbit_product(qP.transpose(0, 2, 1), doc[:, i0:i0 + tq, :]))
             dKh[:, j0:j0 + sk, :] += (sm * sdS * qs[:, i0 // blk])[:, None, None] * (
-                qdS.transpose(0, 2, 1) @ qc[:, i0:i0 + tq, :])
+                lowbit_product(qdS.transpose(0, 2, 1), qc[:, i0:i0 + tq, :]))
             if qsm:
                 dKh[:, j0:j0 + sk, :] += q_smooth_dk_bias(qdS, sdS, muq, sm)
             dQh[:, i0:i0 + tq, :] += (sm * sdS * ks[:, j0 // blk])[:, None, None] * (
-                qdS @ kc[:, j0:j0 + sk, :])
+                lowbit_product(qdS, kc[:, j0:j0 + sk, :]))
     gains = {}
     if spec.qk_norm and spec.normed_grads:
         dQ, dK = dQh, dKh   # gradients with respect to Q^ = g o n and K^ (before smoothing)
