@@ -28,8 +28,11 @@ COMMON = [
     "-Wall", "-Wno-unused-result",
 ]
 # per-file extras: the prologue is specified operation by operation (no FMA contraction); the
-# attention kernels take maxima of finite values only, so max needs no NaN-quieting of its inputs
-EXTRA = {"prologue.hip": ["-ffp-contract=off"], "backward.hip": ["-fno-honor-nans"]}
+# attention kernels take maxima of finite values only, so max needs no NaN-quieting of its inputs;
+# the backward's MFMAs write VGPRs (the dQ pass otherwise lands its products in AGPRs and reads
+# each one back with v_accvgpr_read before converting it: a third VALU op per element)
+EXTRA = {"prologue.hip": ["-ffp-contract=off"],
+         "backward.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["api.cpp", "prologue.hip", "forward.hip", "backward.hip"]
 
 
