@@ -829,28 +829,27 @@ void bwd_main(BackwardArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dQ epilogue
-// One 64-query tile of dQ^ (query rows q0 .. q0 + 63 of head bh, q0 = 64 qt): RMSNorm backward
-// with the gain (Q^ = g o n, n = Q * rstd: dn = g o dQ^, dQ = rstd * (dn - n * mean_c(dn o n)),
-// g = 1 without gains), rounding to the dtype, and with gains the tile's partial of dq_gain
-// (dQ^ o n summed over the rows in a fixed order). 256 threads; D/8 lanes per row, 8
-// channels each; row(r, c, v) fills v[0..7] with dQ^ of tile row r, channels c .. c + 7.
-// gred: 8 KB of LDS the caller no longer needs once every row has been read.
+// Rows [r0, r1) of one 64-query tile of dQ^ (query rows q0 + r, q0 = 64 qt, of head bh):
+// RMSNorm backward with the gain (Q^ = g o n, n = Q * rstd: dn = g o dQ^, dQ = rstd * (dn -
+// n * mean_c(dn o n)), g = 1 without gains), rounding to the dtype, and with gains each
+// thread's share of the tile's dq_gain partial (dQ^ o n) added into gp[8]. 256 threads; D/8
+// lanes per row, 8 channels each, so EPI_ROWS = 256 / (D/8) rows per round; row(r, c, v) fills
+// v[0..7] with dQ^ of tile row r, channels c .. c + 7. r0 and r1 are multiples of EPI_ROWS.
+template <int D>
+constexpr int kEpiRows = 256 / (D / 8);
+
 template <int DT, int D, typename RowF>
-__device__ __forceinline__ void dq_tile_epilogue(const BackwardArgs& a, int bh, int qt, RowF&& row, float* gred) {
-  constexpr int CPR = D / 8;                        // lanes per row, 8 channels each
-  constexpr int RPP = 256 / CPR;                    // rows per pass
-  static_assert(RPP * D * 4 == 8192, "gain partials take 8 KB");
+__device__ __forceinline__ void dq_epilogue_rows(const BackwardArgs& a, int bh, int qt, int r0, int r1, RowF&& row,
+                                                 float* gp) {
+  constexpr int CPR = D / 8;                        // lanes per row
   const size_t hrow = (size_t)bh * a.N;
   const int q0 = qt * kPq;
   const int c = (threadIdx.x % CPR) * 8;
   const float* gain = (a.qk_norm && a.q_gain) ? a.q_gain + (size_t)(bh % a.x16.H) * D + c : nullptr;
-  float gv[8], gp[8];
+  float gv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    gv[i] = gain ? gain[i] : 1.0f;
-    gp[i] = 0.0f;
-  }
-  for (int r = threadIdx.x / CPR; r < kPq; r += RPP) {
+  for (int i = 0; i < 8; ++i) gv[i] = gain ? gain[i] : 1.0f;
+  for (int r = r0 + (int)threadIdx.x / CPR; r < r1; r += kEpiRows<D>) {
     if (q0 + r >= a.Nv) break;   // padding rows of a ragged last block (and every later row)
     const size_t tok = hrow + q0 + r;
     const size_t row16 = a.x16.row(bh, q0 + r);
@@ -881,16 +880,23 @@ __device__ __forceinline__ void dq_tile_epilogue(const BackwardArgs& a, int bh, 
     }
     *reinterpret_cast<u16x8*>(a.dQ + row16 + c) = out;
   }
-  if (gain) {
-    __syncthreads();   // every row has been read: gred may overlap the rows' source
+}
+
+// (gains) The tile's dq_gain partial from the threads' gp: summed over the threads of each
+// channel in a fixed order through gred (kEpiRows * D floats of LDS the caller no longer
+// needs), written to gq_part. Every thread of the workgroup calls it.
+template <int D>
+__device__ __forceinline__ void dq_gain_partial(const BackwardArgs& a, int bh, int qt, const float* gp, float* gred) {
+  constexpr int CPR = D / 8;
+  const int c = (threadIdx.x % CPR) * 8;
+  __syncthreads();   // every row has been read: gred may overlap the rows' source
 #pragma unroll
-    for (int i = 0; i < 8; ++i) gred[(threadIdx.x / CPR) * D + c + i] = gp[i];
-    __syncthreads();
-    if (threadIdx.x < D) {
-      float t = gred[threadIdx.x];
-      for (int i = 1; i < RPP; ++i) t += gred[i * D + threadIdx.x];
-      a.gq_part[((size_t)bh * (a.N / kPq) + qt) * D + threadIdx.x] = t;
-    }
+  for (int i = 0; i < 8; ++i) gred[(threadIdx.x / CPR) * D + c + i] = gp[i];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = gred[threadIdx.x];
+    for (int i = 1; i < kEpiRows<D>; ++i) t += gred[i * D + threadIdx.x];
+    a.gq_part[((size_t)bh * (a.N / kPq) + qt) * D + threadIdx.x] = t;
   }
 }
 
@@ -912,8 +918,10 @@ struct DqLds {
   static constexpr int bM = kTile;                  // then its dQ multipliers (one per 64 keys)
   static constexpr int kBuf = kTile + 1024;         // one ring slot
   static constexpr int kCopiesPerWave = kTile / 1024 / 4;
-  // slot 0 also holds the epilogue's dQ^ tile [64][D] f32
-  static constexpr int kBytes0 = kBuf > kPq * D * 4 ? kBuf : kPq * D * 4;
+  // slot 0 also stages the epilogue's dQ^ rows, kEpiRows<D> at a time [kEpiRows][D] f32 (and
+  // the gain partials' reduction of the same size)
+  static constexpr int kEpi = kEpiRows<D> * D * 4;
+  static constexpr int kBytes0 = kBuf > kEpi ? kBuf : kEpi;
 };
 
 template <int DT, int D, int BLK, int FMT>
@@ -1033,19 +1041,29 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
   wait_vmcnt<0>();
   lds_barrier();
 
-  // ---- epilogue: dQ^ tile to LDS [64][D] f32, then RMSNorm backward row by row
+  // ---- epilogue: the dQ^ rows go through slot 0 kEpiRows at a time (lane group g holds rows
+  //      16g + 4qs + r), then the RMSNorm backward row by row
+  constexpr int ER = kEpiRows<D>;
   float* t = reinterpret_cast<float*>(slot0);
+  float gp[8] = {};
 #pragma unroll
-  for (int qs = 0; qs < 4; ++qs)
+  for (int p = 0; p < kPq / ER; ++p) {
+    if (16 * g >= p * ER && 16 * g < (p + 1) * ER) {
 #pragma unroll
-    for (int n = 0; n < NPW; ++n)
+      for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[(16 * g + 4 * qs + r) * D + 16 * (NPW * w + n) + lr] = dq[qs][n][r];
-  __syncthreads();
-  dq_tile_epilogue<DT, D>(a, bh, qt, [&](int r, int c, float* v) {
+        for (int n = 0; n < NPW; ++n)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = t[r * D + c + i];
-  }, t);
+          for (int r = 0; r < 4; ++r) t[(16 * g + 4 * qs + r - p * ER) * D + 16 * (NPW * w + n) + lr] = dq[qs][n][r];
+    }
+    __syncthreads();
+    dq_epilogue_rows<DT, D>(a, bh, qt, p * ER, (p + 1) * ER, [&](int r, int c, float* v) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = t[(r - p * ER) * D + c + i];
+    }, gp);
+    __syncthreads();
+  }
+  if (a.qk_norm && a.q_gain) dq_gain_partial<D>(a, bh, qt, gp, t);
 }
 
 // ------------------------------------------------------------------------------ dq_finalize
@@ -1055,12 +1073,14 @@ template <int DT, int D>
 __global__ __launch_bounds__(256) void dq_finalize(BackwardArgs a) {
   const int ntile = a.N / kPq;
   const int bh = blockIdx.x / ntile, qt = blockIdx.x % ntile;
-  __shared__ float gred[2048];
+  __shared__ float gred[kEpiRows<D> * D];
   const float* src = a.dq_acc + ((size_t)bh * a.N + (size_t)qt * kPq) * D;
-  dq_tile_epilogue<DT, D>(a, bh, qt, [&](int r, int c, float* v) {
+  float gp[8] = {};
+  dq_epilogue_rows<DT, D>(a, bh, qt, 0, kPq, [&](int r, int c, float* v) {
     *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src + (size_t)r * D + c);
     *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + (size_t)r * D + c + 4);
-  }, gred);
+  }, gp);
+  if (a.qk_norm && a.q_gain) dq_gain_partial<D>(a, bh, qt, gp, gred);
 }
 
 // ------------------------------------------------------------------------------ gain_reduce
