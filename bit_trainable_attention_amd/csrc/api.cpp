@@ -132,7 +132,7 @@ const char* sagebwd_status_string(sagebwd_status s) {
   switch (s) {
     case SAGEBWD_OK: return "ok";
     case SAGEBWD_ERR_NULL: return "null pointer argument";
-    case SAGEBWD_ERR_SHAPE: return "invalid shape (negative size, or N not a multiple of blk)";
+    case SAGEBWD_ERR_SHAPE: return "invalid shape (negative size, N > 2^22, B*H > 2^24, or too many quantisation blocks)";
     case SAGEBWD_ERR_UNSUPPORTED: return "unsupported option (d, blk, dtype, dq_mode, layout, fmt, split, eps or gains)";
     case SAGEBWD_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SAGEBWD_ERR_WORKSPACE: return "workspace too small";

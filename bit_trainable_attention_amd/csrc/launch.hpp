@@ -107,8 +107,6 @@ long long spill_tiles_per_head(int N, int blk, int causal);
 // combinations (dtype in {fp16, bf16}, d in {64, 128}, blk in {64, 128}).
 template <typename F>
 hipError_t dispatch_dt_d_blk(int dtype, int d, int blk, F&& f) {
-  using I = std::integral_constant<int, 0>;
-  (void)sizeof(I);
 #define SAGEBWD_CASE(DTV, DV, BV)                                                    \
   if (dtype == DTV && d == DV && blk == BV)                                          \
     return f(std::integral_constant<int, DTV>{}, std::integral_constant<int, DV>{},  \

@@ -76,7 +76,8 @@ extern "C" {
 typedef enum {
   SAGEBWD_OK = 0,
   SAGEBWD_ERR_NULL = -1,        /* a required pointer is NULL                               */
-  SAGEBWD_ERR_SHAPE = -2,       /* negative size, N > 2^22, or B*H > 2^24                  */
+  SAGEBWD_ERR_SHAPE = -2,       /* negative size, N > 2^22, B*H > 2^24, or 3*B*H*ceil(N/blk)
+                                   >= 2^31 (the prologue's workgroups)                      */
   SAGEBWD_ERR_UNSUPPORTED = -3, /* d or blk not in {64, 128}, unknown dtype, dq_mode or
                                    layout or fmt or split, eps < 0, qk_gain or
                                    normed_grads without qk_norm, normed_grads with qk_gain,
