@@ -104,7 +104,9 @@ def backward_workspace_layout(p: _lib.Params) -> Dict[str, int]:
     off = {"packet_bytes": PACKET_BYTES[p.d], "packets": 0, "tiles_per_head": tiles, "tiles_per_head_q": nt}
     after = up(bh * nt * PACKET_BYTES[p.d])
     ktp, dsp, dsm = up(bh * nb * p.d * p.blk), up(bh * tiles * 64 * p.blk), up(bh * tiles * (p.blk // 64) * 4)
-    spill = p.dq_mode == 1 or (p.dq_mode == 0 and ktp + dsp + dsm <= SPILL_LIMIT)
+    # one head's dS tiles must stay below 4 GiB (the dQ pass addresses them with 32-bit offsets)
+    fits = tiles * 64 * p.blk < (1 << 32)
+    spill = fits and (p.dq_mode == 1 or (p.dq_mode == 0 and ktp + dsp + dsm <= SPILL_LIMIT))
     off["spill"] = int(spill)
     if spill:
         off["ktp"] = after

@@ -137,6 +137,19 @@ def test_spill_needs_per_head_tiles_below_4gib():
     assert lib.sagebwd_backward_workspace_bytes(ctypes.byref(P(dq_mode=1, B=1, H=1, N=65536, d=128, blk=128))) > 0
 
 
+@pytest.mark.parametrize("kw", [
+    dict(), dict(dq_mode=2), dict(causal=0), dict(N=200), dict(d=128, blk=128), dict(qk_gain=1),
+    dict(B=1, H=1, N=65536, d=128, blk=128), dict(B=1, H=1, N=131072, d=128, blk=128),
+    dict(B=1, H=1, N=131072, d=128, blk=128, causal=0, dq_mode=2)])
+def test_binding_layout_matches_library(kw):
+    # the binding's documented workspace offsets (which tests use to decode the packets)
+    # end where the library's workspace size says, in both dQ modes and past the spill limit
+    from bit_trainable_attention_amd import api
+    p = P(**kw)
+    lay = api.backward_workspace_layout(p)
+    assert lay["total"] == lib.sagebwd_backward_workspace_bytes(ctypes.byref(p))
+
+
 def test_empty_is_a_noop():
     # N == 0 (or B == 0 / H == 0): nothing is enqueued and pointers are not inspected
     for p in (P(N=0), P(B=0), P(H=0)):
