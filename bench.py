@@ -113,7 +113,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention shards over heads with no communication; see DESIGN.md).", file=sys.stderr)
+              "(the attention shards over heads with no communication between them).", file=sys.stderr)
         sys.exit(2)
 
     import torch

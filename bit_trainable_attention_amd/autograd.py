@@ -98,4 +98,8 @@ def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
     O, lse = SageBwdAttention.apply(q, k, v, q_gain, k_gain, bool(causal), bool(qk_norm), bool(k_smooth), int(blk),
                                     float(eps), float(sm_scale), int(dq_mode), bool(q_smooth), layout,
                                     bool(normed_grads), str(fmt), str(split))
-    return (O, lse) if return_lse else O
+    if not return_lse:
+        return O
+    # the library's lse holds N rounded up to whole blocks (padding rows +inf): the first N
+    N = q.shape[1] if layout == "bnhd" else q.shape[2]
+    return O, lse[..., :N]

@@ -15,6 +15,7 @@ CASES = [
     ("tiny", W["tiny"]),
     ("bf16_d64_causal", W["bf16_d64"].with_shape(B=1, H=2, N=512)),
     ("d128_causal", W["n8192_d128"].with_shape(B=1, H=2, N=384)),
+    ("ragged", W["tiny"].with_shape(B=1, H=2, N=200)),
 ]
 
 
@@ -37,6 +38,7 @@ def _wrapper_run(w, x, layout, fmt="int8"):
     if layout == "bnhd":
         out = {n: t.transpose(1, 2) for n, t in out.items()}
     res = {n: t.detach().float().cpu().numpy().astype(np.float64) for n, t in out.items()}
+    assert tuple(lse.shape) == (w.B, w.H, w.N), tuple(lse.shape)
     res["LSE"] = lse.cpu().numpy()
     return res
 

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
 
-Bars (SageBwd-style the benchmark spec): INT8 codes, scales and the prologue statistics are
+Bars: INT8 codes, scales and the prologue statistics are
 bit-exact; O, dQ, dK, dV reach rel-L2 <= 2e-3 against the quantised oracle. Shapes here are
 small enough for the oracle to run whole: several tiles in every direction, a query count
 that leaves the forward's last 128-row workgroup half full, both dtypes, both head dims,
