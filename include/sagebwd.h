@@ -132,8 +132,10 @@ typedef struct {
  *   backward's P and dS tiles are as above, P only rounded. Not with q_smooth. */
 typedef enum { SAGEBWD_SPLIT_SAGEBWD = 0, SAGEBWD_SPLIT_QATTN = 1 } sagebwd_split;
 
-/* Code format of the six quantised products (SageBwd article, precision-split paragraph,
- * which names FP8 as the alternative low-bit format of the same split). SAGEBWD_FMT_INT8:
+/* Code format of the quantised products. The SageBwd article's precision split names only
+ * INT8 and FP16; FP8 attention is named by the Full-Stack FP4 page (section 1, problem
+ * definition: attention kept in BF16 or FP8), and block-scaled FP8 training with the E4M3
+ * format by the NVFP4 / Quartet 2 page. SAGEBWD_FMT_INT8:
  * codes in [-127, 127], scale absmax/127, int32 products (the method as described above).
  * SAGEBWD_FMT_FP8: OCP float8 e4m3fn codes (bias 7, subnormals kept, largest finite 448),
  * scale absmax/448, codes = e4m3 round-to-nearest-even of fl(x * (448/absmax)); the same
