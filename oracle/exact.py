@@ -15,9 +15,10 @@ constant to S, which softmax ignores (pinned by test_oracle_exact.py).
 
 Rows are processed in blocks of query rows so that long sequences never hold the
 N x N matrix; each row of the softmax is computed whole, as the definition says.
-Pinned by: central finite differences (test_oracle_exact.py::test_grad_fd_*), the
-library attention routine (test_forward_matches_sdpa), closed forms (uniform keys,
-single key), and the dS structure (row sums zero, RMS(dS) bound).
+Pinned by: central finite differences (test_oracle_exact.py::test_grad_fd,
+test_gain_grad_fd), torch's float64 RMSNorm and attention routine under autograd
+(test_matches_torch_autograd, test_gain_matches_torch_autograd), closed forms (identical
+keys, single key), and the dS structure (row sums zero, RMS(dS) bound).
 """
 from __future__ import annotations
 
@@ -27,20 +28,26 @@ import numpy as np
 
 
 def rms_norm(x: np.ndarray, eps: float):
-    """y = x / sqrt(mean_c x^2 + eps); returns (y, rstd) in float64."""
+    """y = x / sqrt(mean_c x^2 + eps); returns (y, rstd) in float64.
+    Pinned by: torch's rms_norm in test_matches_torch_autograd (qk_norm on: O and LSE to
+    1e-11)."""
     x = np.asarray(x, dtype=np.float64)
     rstd = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
     return x * rstd[..., None], rstd
 
 
 def rms_norm_backward(dy: np.ndarray, y: np.ndarray, rstd: np.ndarray) -> np.ndarray:
-    """Backward of y = x * rstd(x): dx = rstd * (dy - y * mean_c(dy * y))."""
+    """Backward of y = x * rstd(x): dx = rstd * (dy - y * mean_c(dy * y)).
+    Pinned by: finite differences of dQ, dK with qk_norm on (test_grad_fd) and torch
+    autograd through rms_norm (test_matches_torch_autograd)."""
     r = rstd[..., None]
     return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
 
 
 def _gain_rows(g, lead, BH: int, d: int) -> np.ndarray:
-    """A gain [H, d] (or None -> ones) as [BH, 1, d] for inputs with leading dims (.., H)."""
+    """A gain [H, d] (or None -> ones) as [BH, 1, d] for inputs with leading dims (.., H).
+    Pinned by: test_gain_grad_fd, test_gain_matches_torch_autograd (per-head gains on H = 2
+    and 3) and test_unit_gain_is_no_gain."""
     if g is None:
         return np.ones((BH, 1, d))
     g = np.asarray(g, dtype=np.float64)
@@ -65,6 +72,12 @@ def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-
     want_ds_stats: also return, per query row, sqrt(mean_j dS_ij^2) over the row's
     visible keys ("ds_rms"), sqrt(sum_j dS_ij^2) ("ds_l2"), max_j |dP_ij| ("dp_max"),
     the row sum of dS ("ds_rowsum") and max_j |dS_ij| ("ds_max").
+
+    Pinned by: test_grad_fd (every gradient against central differences of loss(), both
+    masks, QK-norm on and off), test_matches_torch_autograd (O, LSE, dQ, dK, dV against
+    torch's float64 attention), test_closed_form_identical_keys / _single_key,
+    test_k_smoothing_invariance (k_shift), test_ds_structure and test_ds_rms_falls_with_sqrt_n
+    (want_ds_stats), test_gain_* (gains), test_normed_grads_equal_attention_on_normalised_inputs.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -148,6 +161,8 @@ def attention(Q, K, V, dO=None, *, causal: bool, qk_norm: bool, eps: float = 1e-
 
 
 def loss(Q, K, V, dO, **kw) -> float:
-    """L = sum(dO o O): its gradient w.r.t. (Q, K, V) is what attention(..., dO) returns."""
+    """L = sum(dO o O): its gradient w.r.t. (Q, K, V) is what attention(..., dO) returns.
+    Pinned by: test_matches_torch_autograd (O itself against torch); the finite differences
+    in test_grad_fd difference this function."""
     out = attention(Q, K, V, None, **kw)
     return float(np.sum(np.asarray(dO, np.float64) * out["O"]))

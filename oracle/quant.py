@@ -527,6 +527,7 @@ def lowbit_product(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def _flat(a: np.ndarray, nlead: int = 2) -> np.ndarray:
+    """Merge the first nlead axes into one (a reshape: no arithmetic, nothing to pin)."""
     return a.reshape((-1,) + a.shape[nlead:])
 
 
