@@ -22,7 +22,10 @@
 //          K: rstd; with K-smoothing, the block's per-channel sums of K^ (group t mod 16 in
 //             ascending order, then the pairwise tree over the 16 groups); with neither
 //             smoothing, codes;
-//          V: block absmax, codes written channel-major (V^T) through an LDS byte tile.
+//          V: block absmax, codes written channel-major (V^T): here thread (j, ch) holds
+//             the BLK/16 consecutive tokens from (BLK/16)*j, transposes its code bytes in
+//             registers (4 x 4 blocks, v_perm_b32) and stores each channel's run of token
+//             codes into an LDS tile, whose rows leave in 16-byte chunks.
 // pass2  (either smoothing) one workgroup per (head, block) for K, and with Q-smoothing one
 //          more per (head, block) for Q: the head's mean (block sums in ascending block
 //          order, / N; every workgroup of the head computes it, block 0's stores it),
@@ -85,6 +88,42 @@ __device__ __forceinline__ void load_slice(const unsigned short* __restrict__ bl
       for (int i = 0; i < Slice<D, BLK>::CW; ++i) s.x[p][i] = 0.0f;
     }
   }
+}
+
+// As load_slice, but thread (j, ch) takes the P consecutive tokens P*j .. P*j + P - 1
+// (slot p = token P*j + p): the V layout, whose codes leave channel-major.
+template <int DT, int D, int BLK>
+__device__ __forceinline__ void load_slice_consec(const unsigned short* __restrict__ blk_src, int sn, int nvalid,
+                                                  Slice<D, BLK>& s, int j, int ch) {
+  using S = Slice<D, BLK>;
+  if (nvalid >= BLK) {
+#pragma unroll
+    for (int p = 0; p < S::P; ++p) load_chunk<DT, S::CW>(blk_src + (size_t)(S::P * j + p) * sn + ch * S::CW, s.x[p]);
+    return;
+  }
+#pragma unroll
+  for (int p = 0; p < S::P; ++p) {
+    if (S::P * j + p < nvalid) {
+      load_chunk<DT, S::CW>(blk_src + (size_t)(S::P * j + p) * sn + ch * S::CW, s.x[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::CW; ++i) s.x[p][i] = 0.0f;
+    }
+  }
+}
+
+// 4 x 4 byte transpose: r[t] holds bytes (b0 .. b3) of row t; out[c] gets byte c of rows
+// 0 .. 3 (byte t of out[c] = byte c of r[t]). v_perm_b32 selects bytes 0-3 of its second
+// operand and 4-7 of its first.
+__device__ __forceinline__ void transpose4x4_bytes(const unsigned (&r)[4], unsigned (&out)[4]) {
+  const unsigned e01 = __builtin_amdgcn_perm(r[1], r[0], 0x06020400u);   // r0.b0 r1.b0 r0.b2 r1.b2
+  const unsigned o01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030501u);   // r0.b1 r1.b1 r0.b3 r1.b3
+  const unsigned e23 = __builtin_amdgcn_perm(r[3], r[2], 0x06020400u);
+  const unsigned o23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030501u);
+  out[0] = __builtin_amdgcn_perm(e23, e01, 0x05040100u);
+  out[2] = __builtin_amdgcn_perm(e23, e01, 0x07060302u);
+  out[1] = __builtin_amdgcn_perm(o23, o01, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(o23, o01, 0x07060302u);
 }
 
 // Sum of the 16 lanes of each row by the pairwise tree (xor 1, xor 2, half mirror, mirror).
@@ -181,9 +220,17 @@ struct Pass1Lds {
   float red[kThreads / 64];
   union {
     float gs[16][D];                               // K: group sums per token slot
-    int8_t vt[D][BLK + 16];                        // V: codes, channel-major
+    int8_t vt[D][BLK];                             // V: codes, channel-major, chunk q of row c
+                                                   // at chunk q ^ vt_swz(c)
   };
 };
+
+// The V tile's 16-byte chunk swizzle: the channel rows that one write instruction of the
+// 16 channel groups touches start on the same bank, so each group's chunk is rotated.
+template <int D, int BLK>
+__device__ __forceinline__ int vt_swz(int c) {
+  return (c / Slice<D, BLK>::CW) & (BLK / 16 - 1);
+}
 
 }  // namespace
 
@@ -200,33 +247,53 @@ __global__ __launch_bounds__(kThreads) void prologue_pass1(PrologueArgs a) {
   const int j = threadIdx.x >> 4, ch = threadIdx.x & 15;
 
   S s;
-  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : tensor == 1 ? a.K : a.V) + a.x16.row(bh, blk_id * BLK), a.x16.sn,
-                         a.Nv - blk_id * BLK, s, j, ch);
-
   if (tensor == 2) {
-    // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token].
+    // V: quantise the raw values; codes stored channel-major: Vtc[bh][c][token]. Thread
+    // (j, ch) holds the P consecutive tokens P*j .. of its CW channels, so after a 4 x 4
+    // byte transpose of its code words each of its channels has P consecutive token codes,
+    // which go to the LDS tile in one store.
+    load_slice_consec<DT, D, BLK>(a.V + a.x16.row(bh, blk_id * BLK), a.x16.sn, a.Nv - blk_id * BLK, s, j, ch);
     const float amax = slice_absmax<D, BLK>(s, lds.red);
     const bool fp8 = a.fmt == FMT_FP8;
     const float M = fp8 ? 448.0f : 127.0f;
     const float inv = amax > 0.0f ? M / amax : 0.0f;
     if (threadIdx.x == 0) a.Vs[sidx] = amax > 0.0f ? amax / M : 0.0f;
+    constexpr int TG = S::P / 4;    // groups of four tokens
+    constexpr int CG = S::CW / 4;   // groups of four channels
+    unsigned ct[S::CW][TG];         // ct[i][g]: tokens P*j + 4g .. + 3 of channel ch*CW + i
 #pragma unroll
-    for (int p = 0; p < S::P; ++p)
+    for (int g = 0; g < TG; ++g)
 #pragma unroll
-      for (int i = 0; i < S::CW; i += 4) {
-        const unsigned wd = code_word(fp8, s.x[p][i], s.x[p][i + 1], s.x[p][i + 2], s.x[p][i + 3], inv);
+      for (int q = 0; q < CG; ++q) {
+        unsigned r[4], o[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lds.vt[ch * S::CW + i + u][16 * p + j] = (int8_t)(wd >> (8 * u));
+        for (int t = 0; t < 4; ++t) {
+          const float* x = s.x[4 * g + t] + 4 * q;
+          r[t] = code_word(fp8, x[0], x[1], x[2], x[3], inv);
+        }
+        transpose4x4_bytes(r, o);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ct[4 * q + c][g] = o[c];
       }
+    const int t0 = S::P * j;   // first token of the thread: chunk t0 / 16, byte t0 % 16
+#pragma unroll
+    for (int i = 0; i < S::CW; ++i) {
+      const int c = ch * S::CW + i;
+      int8_t* dst = &lds.vt[c][16 * ((t0 >> 4) ^ vt_swz<D, BLK>(c)) + (t0 & 15)];
+      if constexpr (TG == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(ct[i][0], ct[i][1]);
+      else *reinterpret_cast<unsigned*>(dst) = ct[i][0];
+    }
     __syncthreads();
     constexpr int kRowChunks = BLK / 16;
     for (int e = threadIdx.x; e < D * kRowChunks; e += kThreads) {
       const int c = e / kRowChunks, q = e % kRowChunks;
       *reinterpret_cast<i32x4*>(a.Vtc + ((size_t)bh * D + c) * a.N + (size_t)blk_id * BLK + 16 * q) =
-          *reinterpret_cast<const i32x4*>(&lds.vt[c][16 * q]);
+          *reinterpret_cast<const i32x4*>(&lds.vt[c][16 * (q ^ vt_swz<D, BLK>(c))]);
     }
     return;
   }
+  load_slice<DT, D, BLK>((tensor == 0 ? a.Q : a.K) + a.x16.row(bh, blk_id * BLK), a.x16.sn, a.Nv - blk_id * BLK, s,
+                         j, ch);
 
   float* rstd_out = (tensor == 0 ? a.q_rstd : a.k_rstd) + tok0;
   if (a.qk_norm) {
