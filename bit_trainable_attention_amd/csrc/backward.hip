@@ -655,7 +655,10 @@ void bwd_main(BackwardArgs a) {
       const long long ti = (long long)bh * a.spill_tiles + spill_tile_index(a.N, BLK, a.causal, kb, qt * NH);
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        *reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq + 16 * swz_ds(kl, g)) = dch(h);
+        // (non-temporal: the spill is read once, by the dQ pass, and must not push the packets,
+        // which every key block reads again, out of L2)
+        __builtin_nontemporal_store(dch(h), reinterpret_cast<i32x4*>(a.dsp + (ti + h) * (kPq * BLK) + kl * kPq +
+                                                                      16 * swz_ds(kl, g)));
         if (l == 0) a.dsm[(ti + h) * KD + dg] = smc * sdS * sK;   // every wave of the group stores the same value
       }
     }
@@ -904,8 +907,9 @@ __device__ __forceinline__ void dq_gain_partial(const BackwardArgs& a, int bh, i
 // Query-major dQ pass over the spilled dS^T tiles: one workgroup (4 waves) per (head, 64-query
 // tile). For every key block up to the diagonal and each of its 64-key dS tiles,
 // dQ^ += m * (dS_codes . K_codes) runs on v_mfma_i32_16x16x64_i8 with float32 accumulation in
-// registers (m = sm_scale * s_dS * s_K of that 64-key tile). The tile's dS^T codes [BLK][64] stream through a ring of three LDS buffers
-// (buffer->LDS copies issued two key blocks ahead) and are read back query-major with
+// registers (m = sm_scale * s_dS * s_K of that 64-key tile). The tile's dS^T codes [BLK][64]
+// stream through a ring of three LDS buffers (buffer->LDS copies issued two key blocks ahead,
+// non-temporal, so that the stream leaves the K^T codes in L2) and are read back query-major with
 // transposing reads: the A operand (rows = queries, contraction = keys). Wave w computes all
 // 64 queries against its own NPW 16-channel tiles, so it needs only those channels of the
 // block's K^T codes (the B operand), which it loads straight into registers one key block
@@ -962,7 +966,7 @@ __global__ __launch_bounds__(256) void bwd_dq(BackwardArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int cp = w + 4 * j;
-      buffer_to_lds16(dsh, dsh_bytes, dst + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
+      buffer_to_lds16<kCpolNT>(dsh, dsh_bytes, dst + cp * 1024, 16 * l, (uint32_t)(ti * (kPq * BLK)) + cp * 1024);
     }
     if (w == 3) buffer_to_lds4(dmh, (uint32_t)(a.spill_tiles * 4 * KC), dst + L::bM, 4 * l, (uint32_t)(ti * 4 * KC));
   };

@@ -293,12 +293,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // bodies are compiled for the device only:
 // this compiler's host pass cannot type-check the LDS-DMA builtin and, instead of reporting
 // it, silently omits the host launch stubs of kernels that reach it.
+// CPOL: the load's cache policy bits; kCpolNT marks data read once (a stream), which the
+// caches then keep from displacing data that is read again.
+constexpr int kCpolNT = 2;
+template <int CPOL = 0>
 __device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t bytes, int8_t* lds, uint32_t voff,
                                                 uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                                                       0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, CPOL);
 #endif
 }
 
