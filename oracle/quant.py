@@ -412,8 +412,10 @@ def prologue(Q: np.ndarray, K: np.ndarray, V: np.ndarray, spec: Spec,
     # absmax and no sum; the means divide by the N valid tokens (k_smooth_f32)
     Q, K, V = (_pad_rows(np.asarray(x, dtype=F32), spec.Np) for x in (Q, K, V))
     if spec.qk_norm:
-        Qn, q_rstd = rms_norm_f32(Q, spec.eps)
-        Kn, k_rstd = rms_norm_f32(K, spec.eps)
+        # (with eps = 0 the zero padding rows divide by zero here; they are replaced just below)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            Qn, q_rstd = rms_norm_f32(Q, spec.eps)
+            Kn, k_rstd = rms_norm_f32(K, spec.eps)
         if spec.N < spec.Np:
             # padding tokens are not normalised: rstd 1, values 0 (with eps = 0 their rstd
             # would be 1/sqrt(0) and 0 * inf would put NaN into every sum over the block)
