@@ -125,3 +125,42 @@ def test_full_shape_long_sequence_sampled():
     assert cos["O"] >= 0.995 and cos["O_all"] >= 0.995, cos
     for k in ("dQ", "dK", "dV", "dQ_all", "dK_all", "dV_all"):
         assert cos[k] >= 0.98, (k, cos)
+
+
+@pytest.mark.parametrize("fmt,split", [("fp8", "sagebwd"), ("int8", "qattn")])
+def test_full_shape_variants(fmt, split):
+    """The FP8 recipe and the Q-Attn split at the bench shape (B2 H16 N8192 d128), in the launch
+    configuration `bench.py --fmt fp8` / `--split qattn` times: the HIP path on every head, the
+    oracle with the same recipe on one sampled head (its prologue codes bit for bit; O, dQ, dK,
+    dV within rel-L2 1e-2 for FP8 codes and 2e-3 for INT8 codes; cosine vs exact float64
+    attention 0.995 / 0.98)."""
+    w = wl.WORKLOADS["n8192_d128"]
+    bh = 19
+    _say(f"[full] {w.name} fmt={fmt} split={split}: B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU on all heads")
+    x = host_inputs(w)
+    g = gpu_run(w, x, fmt=fmt, split=split)
+    spec = spec_for(w.with_shape(B=1, H=1), fmt=fmt, split=split)
+    xh = {k: _head(x[k], w, bh) for k in ("Qf", "Kf", "Vf", "dOf")}
+    _say(f"[full] {w.name} fmt={fmt} split={split}: oracle on head {bh}")
+    o = oq.run(xh["Qf"], xh["Kf"], xh["Vf"], xh["dOf"], spec)
+    for k in ("Qc", "Kc", "Qs", "Ks"):
+        assert np.array_equal(_head(g[k], w, bh), o[k]), k
+    if split == "sagebwd":
+        assert np.array_equal(_head(g["Vtc"], w, bh), np.swapaxes(o["Vc"], -1, -2))
+        assert np.array_equal(_head(g["Vs"], w, bh), o["Vs"])
+    errs = {k: rel_l2(_head(g[k], w, bh), o[k]) for k in ("O", "dQ", "dK", "dV")}
+    rows = {k: row_rel_max(_head(g[k], w, bh), o[k]) for k in ("O", "dQ", "dK", "dV")}
+    lse = float(np.max(np.abs(_head(g["LSE"], w, bh).astype(np.float64) - o["LSE"])))
+    ex = exact.attention(xh["Qf"], xh["Kf"], xh["Vf"], xh["dOf"], causal=w.causal, qk_norm=w.qk_norm, eps=w.eps)
+    cos = {k: cosine(_head(g[k], w, bh), ex[k]) for k in ("O", "dQ", "dK", "dV")}
+    _say(f"[full] {w.name} fmt={fmt} split={split} head {bh}: rel-L2 {errs}, worst row {rows}, "
+         f"max|dLSE| {lse:.2e}, cosine vs exact {cos}")
+    tol = 1e-2 if fmt == "fp8" else TOL
+    assert lse < 1e-4 * max(1.0, float(np.max(np.abs(o["LSE"]))))
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+    for k, e in rows.items():
+        assert e <= (5 if fmt == "fp8" else 1) * ROW_TOL, (k, e)
+    assert cos["O"] >= 0.995, cos
+    for k in ("dQ", "dK", "dV"):
+        assert cos[k] >= 0.98, (k, cos)
