@@ -127,18 +127,28 @@ def test_full_shape_long_sequence_sampled():
         assert cos[k] >= 0.98, (k, cos)
 
 
-@pytest.mark.parametrize("fmt,split", [("fp8", "sagebwd"), ("int8", "qattn")])
-def test_full_shape_variants(fmt, split):
-    """The FP8 recipe and the Q-Attn split at the bench shape (B2 H16 N8192 d128), in the launch
-    configuration `bench.py --fmt fp8` / `--split qattn` times: the HIP path on every head, the
-    oracle with the same recipe on one sampled head (its prologue codes bit for bit; O, dQ, dK,
-    dV within rel-L2 1e-2 for FP8 codes and 2e-3 for INT8 codes; cosine vs exact float64
-    attention 0.995 / 0.98)."""
-    w = wl.WORKLOADS["n8192_d128"]
+VARIANTS = [  # (fmt, split, q_smooth, layout, dq_mode): the bench's --fmt, --split, --q-smooth,
+    ("fp8", "sagebwd", False, "bhnd", 0),   # --layout and --dq-mode options
+    ("int8", "qattn", False, "bhnd", 0),
+    ("int8", "sagebwd", True, "bhnd", 0),
+    ("int8", "sagebwd", False, "bnhd", 0),
+    ("int8", "sagebwd", False, "bhnd", 2),
+]
+
+
+@pytest.mark.parametrize("fmt,split,q_smooth,layout,dq_mode", VARIANTS)
+def test_full_shape_variants(fmt, split, q_smooth, layout, dq_mode):
+    """The bench's variants at the bench shape (B2 H16 N8192 d128), in the launch configuration
+    `bench.py --fmt fp8` / `--split qattn` / `--q-smooth` / `--layout bnhd` / `--dq-mode atomic`
+    times: the HIP path on every head, the oracle with the same recipe on one sampled head (its
+    prologue codes bit for bit; O, dQ, dK, dV within rel-L2 1e-2 for FP8 codes and 2e-3 for
+    INT8 codes; cosine vs exact float64 attention 0.995 / 0.98)."""
+    w = wl.WORKLOADS["n8192_d128"].with_shape(q_smooth=q_smooth)
     bh = 19
-    _say(f"[full] {w.name} fmt={fmt} split={split}: B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU on all heads")
+    _say(f"[full] {w.name} fmt={fmt} split={split} q_smooth={q_smooth} layout={layout} dq_mode={dq_mode}: "
+         f"B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU on all heads")
     x = host_inputs(w)
-    g = gpu_run(w, x, fmt=fmt, split=split)
+    g = gpu_run(w, x, fmt=fmt, split=split, layout=layout, dq_mode=dq_mode)
     spec = spec_for(w.with_shape(B=1, H=1), fmt=fmt, split=split)
     xh = {k: _head(x[k], w, bh) for k in ("Qf", "Kf", "Vf", "dOf")}
     _say(f"[full] {w.name} fmt={fmt} split={split}: oracle on head {bh}")
