@@ -673,6 +673,11 @@ void bwd_main(BackwardArgs a) {
       const int q0 = qt * TQ;
       const int step = qt - qt0;
       const int bofs = (step & 1) * L::kBuf;   // byte offset of this tile's buffer
+      // Issue priority: waves w and w + 4 share a SIMD, and without priorities the older one
+      // leads every phase, then waits at the barrier while the younger one finishes alone.
+      // The younger four lead S/dP, the elementwise work and dK; the older ones lead the
+      // phase before the barrier (B2 H16 N8192 d128: 1.050/1.052 -> 1.036/1.035 ms).
+      if (w >= 4) __builtin_amdgcn_s_setprio(2);
       phase_sdp(bofs);
       // diagonal tiles mask keys above the queries; the waves holding padding keys mask those
       if ((a.causal && k0 + 16 * w + 15 > q0) || k0 + 16 * w + 15 >= a.Nv) {
@@ -682,11 +687,13 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
         for (int t = 0; t < NS; ++t) elem_tile(lds + bofs, t, q0, std::false_type{});
       }
+      if (w >= 4) __builtin_amdgcn_s_setprio(0);
       phase_post(bofs, step);
       // the copies of tile qt+1 (issued one step ago) must have landed before the barrier
       // that publishes them; issued after them: last step's stores or atomics
       wait_vmcnt<kStores>();
       lds_barrier();
+      if (w >= 4) __builtin_amdgcn_s_setprio(2);
       if constexpr (SPILL) {
         if (qt + 2 < ntq) issue(qt + 2, lds + bofs);
       }
