@@ -567,7 +567,10 @@ void bwd_main(BackwardArgs a) {
     // ---- P codes on this wave's TQ x 16 tile, then dV^T += dO^T P (int32 over the TQ rows)
     {
       const float pa = fmaxf(pm, FLT_MIN);
-      const float pinv = C::kMax * __builtin_amdgcn_rcpf(pa);
+      // (an all-zero tile, e.g. 16 padding keys: kMax / FLT_MIN overflows to +inf and 0 * inf
+      // would make NaN codes, which FP8 products carry on; the clamp keeps 0 * pinv = 0 and
+      // |x| * pinv <= kMax)
+      const float pinv = fminf(C::kMax * __builtin_amdgcn_rcpf(pa), FLT_MAX);
       const float sv = pa * (1.0f / C::kMax) * sdO;
       i32x4 pc[NH];
 #pragma unroll
@@ -613,7 +616,9 @@ void bwd_main(BackwardArgs a) {
 #pragma unroll
     for (int i = 1; i < 4; ++i) da = fmaxf(da, redD[(step & 1) * NW + wg0 + i]);
     da = fmaxf(da, FLT_MIN);
-    const float dinv = C::kMax * __builtin_amdgcn_rcpf(da);
+    // (clamped as pinv above: an all-zero dS tile, e.g. 64 padding keys of a ragged block,
+    // must give codes 0, not 0 * inf = NaN)
+    const float dinv = fminf(C::kMax * __builtin_amdgcn_rcpf(da), FLT_MAX);
     const float sdS = da * (1.0f / C::kMax);
 #pragma unroll
     for (int h = 0; h < NH; ++h)

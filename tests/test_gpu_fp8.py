@@ -37,6 +37,9 @@ CASES = {
     "fp16_d64_blk128": W["tiny"].with_shape(B=1, H=2, N=384, blk=128, causal=True, qk_norm=True),
     "bf16_d128_blk64": W["n8192_d128"].with_shape(B=1, H=2, N=320, blk=64, dtype="bf16"),
     "bf16_d128_blk128": W["n8192_d128"].with_shape(B=1, H=2, N=512, dtype="bf16"),
+    # a ragged last block whose second 64-key group is all padding: that dS tile is all zero
+    # (its inverse scale must not become inf, or the FP8 codes turn NaN and so does dQ)
+    "d128_blk128_padding_dS_tile": W["n8192_d128"].with_shape(B=1, H=2, N=300),
 }
 
 
