@@ -668,8 +668,19 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     p_quant (default tile_quant) quantises the P tiles of dV and do_quant (default
     block_quant) the dO blocks: the Q-Attn split passes the 16-bit rounding and the
     identity, so dV = round16(P)^T dO.
-    Returns dict dQ, dK, dV ([B,H,N,d] float64 of dtype-rounded values) plus D, dOc, dOs.
-    Pinned by: test_oracle_quant.py (identity and lossless reductions to oracle.exact,
+    Returns dict dQ, dK, dV ([B,H,N,d] float64 of dtype-rounded values) plus D, dOc, dOs, and
+    dQ_code_step, dK_code_step ([B,H,N] float64): for each row of dQ (dK), an upper bound on
+    how far one unit of one of its dS codes moves that row (L2), in the row's own units. A dS
+    code is decided by rounding a float at a grid point, so an implementation whose dS differs
+    from this one in the last float32 bits (another exp, LSE or summation order) may land on
+    the neighbouring code at a near-tie; for integer codes one unit is one such step. Per tile,
+    one unit at (i, j) adds sm * sdS * sK(J) * Kc_j to dQ^_i and sm * sdS * (sQ(I) * Qc_i
+    (+ mu_Q with Q-smoothing)) to dK^_j; the bound takes the largest key (query) row norm of the
+    tile and the largest over the row's tiles, then the RMSNorm backward's factor rstd * max|g|
+    (its map is rstd times a contraction, mean(y^2) <= 1, applied to g o dX^).
+    Pinned by: test_oracle_code_step.py (a planted one-unit code change is matched exactly on
+    a single tile and stays within the bound on many tiles, with and without QK-norm, gains and
+    Q-smoothing); test_oracle_quant.py (identity and lossless reductions to oracle.exact,
     finite-difference-pinned exact gradients, planted mistakes) and, for the P and dS tile
     placement, test_oracle_tiles.py (exact-rational fixture that other tilings miss, spy).
     """
@@ -701,6 +712,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
     dQh = np.zeros((BH, N, d))
     dKh = np.zeros((BH, N, d))
     dV = np.zeros((BH, N, d))
+    stepQ = np.zeros((BH, N))
+    stepK = np.zeros((BH, N))
     qsel = None if q_tiles is None else set(q_tiles)
     ksel = None if k_tiles is None else set(k_tiles)
     for it in range(N // tq):
@@ -725,6 +738,13 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             dP = do[:, i0:i0 + tq, :] @ vf[:, j0:j0 + sk, :].transpose(0, 2, 1)
             dS = P * (dP - Df[:, i0:i0 + tq, None])
             qdS, sdS = tile_quant(dS)
+            kmax = np.linalg.norm(kc[:, j0:j0 + sk, :], axis=2).max(axis=1)
+            qrow = qs[:, i0 // blk][:, None, None] * qc[:, i0:i0 + tq, :]
+            if qsm:
+                qrow = qrow + muq[:, None, :]
+            qmax = np.linalg.norm(qrow, axis=2).max(axis=1)
+            stepQ[:, i0:i0 + tq] = np.maximum(stepQ[:, i0:i0 + tq], (sm * sdS * ks[:, j0 // blk] * kmax)[:, None])
+            stepK[:, j0:j0 + sk] = np.maximum(stepK[:, j0:j0 + sk], (sm * sdS * qmax)[:, None])
             for p0 in range(0, sk, pk):
                 qP, sP = p_quant(P[:, :, p0:p0 + pk])
                 dV[:, j0 + p0:j0 + p0 + pk, :] += (sP * dos[:, i0 // blk])[:, None, None] * (
@@ -748,6 +768,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
             np.asarray(kg, np.float64), (B, H, d)).reshape(B * H, 1, d)
         dQ = rms_norm_backward(dQh * gq, Qn, _flat(pro["q_rstd"]))
         dK = rms_norm_backward(dKh * gk, Kn, _flat(pro["k_rstd"]))
+        stepQ = stepQ * _flat(np.asarray(pro["q_rstd"], np.float64)) * np.abs(gq).max(axis=2)
+        stepK = stepK * _flat(np.asarray(pro["k_rstd"], np.float64)) * np.abs(gk).max(axis=2)
         if qg is not None or kg is not None:
             gains = dict(dq_gain=(dQh * Qn).reshape(B, H, N, d).sum(axis=(0, 2)),
                          dk_gain=(dKh * Kn).reshape(B, H, N, d).sum(axis=(0, 2)))
@@ -768,6 +790,8 @@ def backward(pro: Dict[str, np.ndarray], Q, K, V, O, LSE, dO, spec: Spec,
         dK=round_to_dtype(dK, spec.dtype).reshape(B, H, N, d)[:, :, :nv],
         dV=round_to_dtype(dV, spec.dtype).reshape(B, H, N, d)[:, :, :nv],
         D=D, dOc=dOc, dOs=dOs,
+        dQ_code_step=stepQ.reshape(B, H, N)[:, :, :nv],
+        dK_code_step=stepK.reshape(B, H, N)[:, :, :nv],
     )
     out.update(gains)
     return out

@@ -55,15 +55,25 @@ def rel_l2(a, b) -> float:
 ROW_TOL = 2e-2
 
 
-def row_rel_max(a, b) -> float:
-    """max over rows (all axes but the last) of ||a_i - b_i|| / max(||b_i||, RMS_i ||b_i||)."""
+def row_norm_floor(b) -> np.ndarray:
+    """Per row (all axes but the last, flattened) of b: max(||b_i||, RMS_i ||b_i||), the
+    denominator of the per-row bar."""
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b.reshape(-1, b.shape[-1]), axis=1)
+    return np.maximum(nb, max(float(np.sqrt(np.mean(nb * nb))), 1e-300))
+
+
+def row_rel(a, b) -> np.ndarray:
+    """Per row (flattened as row_norm_floor) of ||a_i - b_i|| / max(||b_i||, RMS_i ||b_i||)."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     d = b.shape[-1]
-    a2, b2 = a.reshape(-1, d), b.reshape(-1, d)
-    nb = np.linalg.norm(b2, axis=1)
-    floor = max(float(np.sqrt(np.mean(nb * nb))), 1e-300)
-    return float(np.max(np.linalg.norm(a2 - b2, axis=1) / np.maximum(nb, floor)))
+    return np.linalg.norm(a.reshape(-1, d) - b.reshape(-1, d), axis=1) / row_norm_floor(b)
+
+
+def row_rel_max(a, b) -> float:
+    """max over rows (all axes but the last) of ||a_i - b_i|| / max(||b_i||, RMS_i ||b_i||)."""
+    return float(np.max(row_rel(a, b)))
 
 
 def cosine(a, b) -> float:

@@ -34,7 +34,7 @@ def _cases():
     return sorted(CASES.items())
 
 
-def _noisy_product(rng, rel=2.0 ** -16):
+def noisy_product(rng, rel=2.0 ** -16):
     def mm(a, b):
         exact = a @ b
         mag = np.abs(a) @ np.abs(b)
@@ -42,17 +42,21 @@ def _noisy_product(rng, rel=2.0 ** -16):
     return mm
 
 
+def run_modelled(x, spec, seed, **kw):
+    """oracle.quant.run with every low-bit product replaced by the noise model (seeded)."""
+    real = oq.lowbit_product
+    oq.lowbit_product = noisy_product(np.random.default_rng(seed))
+    try:
+        return oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec, **kw)
+    finally:
+        oq.lowbit_product = real
+
+
 def model_discrepancy(w, seed=0):
     x = host_inputs(w)
     spec = spec_for(w, fmt="fp8")
     ref = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec)
-    rng = np.random.default_rng(seed)
-    real = oq.lowbit_product
-    oq.lowbit_product = _noisy_product(rng)
-    try:
-        got = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec)
-    finally:
-        oq.lowbit_product = real
+    got = run_modelled(x, spec, seed)
     return {k: rel_l2(got[k], ref[k]) for k in OUTS}
 
 
@@ -73,7 +77,7 @@ def test_model_is_inert_for_int8_sums():
     spec = spec_for(w, fmt="fp8")
     ref = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec)
     real = oq.lowbit_product
-    oq.lowbit_product = _noisy_product(np.random.default_rng(1), rel=0.0)
+    oq.lowbit_product = noisy_product(np.random.default_rng(1), rel=0.0)
     try:
         got = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec)
     finally:
