@@ -1,9 +1,9 @@
 """A seeded sweep of small configurations through the HIP path, each against the oracle of the
-same recipe: the cross product of the options is too large to list by hand, so 240 cases are
-drawn from it with a fixed generator.
+same recipe: the cross product of the options is too large to list by hand, so 240 cases with
+N up to 700 and 40 with N from 701 to 4096 are drawn from it with fixed generators.
 
 Drawn per case: the input distribution (one of the workloads' bases, which fixes d), dtype, blk,
-B, H, N in 1..700 (mostly ragged), causal, QK-norm, K-smoothing, learnable gains, Q-smoothing,
+B, H, N (mostly ragged), causal, QK-norm, K-smoothing, learnable gains, Q-smoothing,
 the 16-bit layout, the dQ mode, the code format and the precision split, within what the
 library accepts together.
 
@@ -39,7 +39,8 @@ BASES = ("tiny", "bf16_d64", "llama325m", "n8192_d128", "n32768")
 CODE_STEPS = 2
 
 
-def _draw(n_cases: int = 240, seed: int = 20261203):
+def _draw(n_cases: int, seed: int, prefix: str, n_lo: int, n_hi: int, b_max: int, h_max: int):
+    """n_cases configurations; N is uniform in [n_lo, n_hi] (4 in 5) or a multiple of 64 in it."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n_cases):
@@ -48,19 +49,23 @@ def _draw(n_cases: int = 240, seed: int = 20261203):
         q_smooth = bool(rng.random() < 0.2)
         fmt = "fp8" if (not q_smooth and rng.random() < 0.3) else "int8"
         split = "qattn" if (not q_smooth and rng.random() < 0.3) else "sagebwd"
-        n = int(rng.integers(1, 701)) if rng.random() < 0.8 else int(64 * rng.integers(1, 11))
-        w = base.with_shape(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), N=n,
+        n = (int(rng.integers(n_lo, n_hi + 1)) if rng.random() < 0.8
+             else int(64 * rng.integers(-(-n_lo // 64), n_hi // 64 + 1)))
+        w = base.with_shape(B=int(rng.integers(1, b_max + 1)), H=int(rng.integers(1, h_max + 1)), N=n,
                             blk=int(rng.choice([64, 128])), dtype=str(rng.choice(["fp16", "bf16"])),
                             causal=bool(rng.random() < 0.7), qk_norm=qk_norm,
                             k_smooth=bool(rng.random() < 0.8), q_smooth=q_smooth)
         case = dict(w=w, fmt=fmt, split=split, layout=str(rng.choice(["bhnd", "bnhd"])),
                     dq_mode=int(rng.choice([0, 2])), gains=bool(qk_norm and rng.random() < 0.3),
                     gseed=int(rng.integers(1 << 30)))
-        cases.append((f"case{i:03d}", case))
+        cases.append((f"{prefix}{i:03d}", case))
     return cases
 
 
-CASES = _draw()
+# short heads (a handful of tiles per row, most of them ragged), then longer ones (tens of
+# tiles per row, several query and key blocks per workgroup)
+CASES = (_draw(240, 20261203, "case", 1, 700, 2, 3) +
+         _draw(40, 20261204, "mid", 701, 4096, 2, 2))
 
 
 def _fp8_bars(x, spec, ref, kw):
