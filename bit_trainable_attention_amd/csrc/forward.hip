@@ -48,10 +48,11 @@ constexpr float kLazy = 8.0f;  // O and l may lag the running max by up to 2^kLa
 // Chunk swizzle of the K and V^T tiles, rows of RB bytes (an involution in j). The operand
 // reads name rows 32t .. 32t+31 (lane l & 31), one chunk per lane half; on gfx950 they
 // measured ~206 (RB = 128) and ~218 (RB = 64) B/clk per CU with these XORs, against ~117
-// with j ^ (r & 7) and j ^ ((r >> 1) & 3).
+// with j ^ (r & 7) and j ^ ((r >> 1) & 3). The XOR depends on the row only through r & 31,
+// so a read of row block t sits 32 t RB bytes past the same per-lane offset (an immediate).
 template <int RB>
 __device__ __forceinline__ int swz_f(int r, int j) {
-  if constexpr (RB == 128) return j ^ (((r >> 1) ^ (r >> 4)) & 7);
+  if constexpr (RB == 128) return j ^ (((r >> 1) ^ ((r >> 4) & 1)) & 7);
   else return j ^ ((r >> 2) & 3);
 }
 
@@ -150,6 +151,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
   const int q0w = q0 + w * kRowsPerWave;
   const bool active = q0w < a.Nv;   // (rows from Nv on are the padding of a ragged last block)
   const int qrow = q0w + lq;  // this lane's query row
+  // per-lane byte offsets of the K and V^T operand reads inside a 32-row block; row block t of
+  // a tile adds 32 t RB bytes (swz_f depends on the row through r & 31 only)
+  int koff[DC], voff[NSUB];
+#pragma unroll
+  for (int kk = 0; kk < DC; ++kk) koff[kk] = lq * D + 16 * swz_f<D>(lq, 2 * kk + g);
+#pragma unroll
+  for (int t = 0; t < NSUB; ++t) voff[t] = lq * BLK + 16 * swz_f<BLK>(lq, 2 * t + g);
 
   // Q codes of this lane's query, as the B operand (contraction slots 16g..16g+15 of each
   // 32-channel chunk).
@@ -201,8 +209,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
       for (int t = 0; t < NSUB; ++t) {
         s[t] = typename C::acc16{};
-        const int kr = 32 * t + lq;
-        auto ak = [&](int kk) { return *reinterpret_cast<const i32x4*>(kl + kr * D + 16 * swz_f<D>(kr, 2 * kk + g)); };
+        auto ak = [&](int kk) { return *reinterpret_cast<const i32x4*>(kl + koff[kk] + 32 * t * D); };
 #pragma unroll
         for (int kk = 0; kk < DC; kk += 2) s[t] = C::mma32x2(ak(kk), ak(kk + 1), qreg[kk], qreg[kk + 1], s[t]);
       }
@@ -393,8 +400,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fwd_kernel(ForwardArgs a) {
 #pragma unroll
       for (int ct = 0; ct < DC; ++ct) {
         typename C::acc16 acc{};
-        const int vr = 32 * ct + lq;
-        auto av = [&](int t) { return *reinterpret_cast<const i32x4*>(vl + vr * BLK + 16 * swz_f<BLK>(vr, 2 * t + g)); };
+        auto av = [&](int t) { return *reinterpret_cast<const i32x4*>(vl + voff[t] + 32 * ct * BLK); };
 #pragma unroll
         for (int t = 0; t < NSUB; t += 2) acc = C::mma32x2(av(t), av(t + 1), pc[t], pc[t + 1], acc);
 #pragma unroll
