@@ -234,7 +234,9 @@ def main():
                                   split=args.split)
             o.backward(dO)
 
-        for _ in range(2):
+        # (as many warm-up steps as the main timing: the first steps also grow the allocator's
+        # pool for the wrapper's own tensors)
+        for _ in range(max(args.warmup, 5)):
             ag_step()
         n_ag = max(1, min(args.steps, 10))
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

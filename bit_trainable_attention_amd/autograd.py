@@ -55,10 +55,15 @@ class SageBwdAttention(torch.autograd.Function):
         ctx.gain_dtypes = (q_gain.dtype, k_gain.dtype) if gained else None
         ctx.save_for_backward(q, k, v, O, lse, *(pro[n] for n in ctx.saved_names), *(gains if gained else ()))
         ctx.mark_non_differentiable(lse)
+        # lse carries no gradient: without this, autograd would fill a zero tensor for it on
+        # every backward (a kernel launch and a write of B*H*N floats)
+        ctx.set_materialize_grads(False)
         return O, lse
 
     @staticmethod
     def backward(ctx, dO, _dlse):
+        if dO is None:   # O took no part in the loss (grads are not materialised)
+            return (None,) * 17
         q, k, v, O, lse, *saved = ctx.saved_tensors
         pro = dict(zip(ctx.saved_names, saved[:len(ctx.saved_names)]))
         gains = saved[len(ctx.saved_names):] if ctx.gain_dtypes else (None, None)
@@ -67,7 +72,7 @@ class SageBwdAttention(torch.autograd.Function):
         dgq = dgk = None
         if ctx.gain_dtypes:
             dgq, dgk = g["dq_gain"].to(ctx.gain_dtypes[0]), g["dk_gain"].to(ctx.gain_dtypes[1])
-        return (g["dQ"], g["dK"], g["dV"], dgq, dgk) + (None,) * 13
+        return (g["dQ"], g["dK"], g["dV"], dgq, dgk) + (None,) * 12
 
 
 def sagebwd_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
