@@ -1,6 +1,7 @@
 """A seeded sweep of small configurations through the HIP path, each against the oracle of the
 same recipe: the cross product of the options is too large to list by hand, so 240 cases with
-N up to 700 and 40 with N from 701 to 4096 are drawn from it with fixed generators.
+N up to 700 and 40 with N from 701 to 4096 are drawn from it with fixed generators; 30 more
+take heads of one to three tokens through the main variants.
 
 Drawn per case: the input distribution (one of the workloads' bases, which fixes d), dtype, blk,
 B, H, N (mostly ragged), causal, QK-norm, K-smoothing, learnable gains, Q-smoothing,
@@ -62,10 +63,60 @@ def _draw(n_cases: int, seed: int, prefix: str, n_lo: int, n_hi: int, b_max: int
     return cases
 
 
+def _single_tokens():
+    """Heads of one to three tokens: a lone query sees only itself (P = 1, so dS is the small
+    residual dP - D), and nearly every row and key of a block is padding."""
+    variants = {"int8_causal": {}, "int8_full": dict(causal=False), "fp8": dict(fmt="fp8"),
+                "qattn_bnhd": dict(split="qattn", layout="bnhd"), "qsmooth_atomic": dict(q_smooth=True, dq_mode=2)}
+    cases = []
+    for base in ("tiny", "n8192_d128"):
+        for n in (1, 2, 3):
+            for vname, v in variants.items():
+                w = wl.WORKLOADS[base].with_shape(B=1, H=2, N=n, causal=v.get("causal", True),
+                                                  q_smooth=v.get("q_smooth", False))
+                cases.append((f"n{n}_{vname}_{base}", dict(w=w, fmt=v.get("fmt", "int8"), split=v.get("split", "sagebwd"),
+                                                            layout=v.get("layout", "bhnd"), dq_mode=v.get("dq_mode", 0),
+                                                            gains=False, gseed=0)))
+    return cases
+
+
 # short heads (a handful of tiles per row, most of them ragged), then longer ones (tens of
-# tiles per row, several query and key blocks per workgroup)
+# tiles per row, several query and key blocks per workgroup), then heads of one to three tokens
 CASES = (_draw(240, 20261203, "case", 1, 700, 2, 3) +
-         _draw(40, 20261204, "mid", 701, 4096, 2, 2))
+         _draw(40, 20261204, "mid", 701, 4096, 2, 2) + _single_tokens())
+
+
+def _zero_reference_bound(x, spec, o, key, gains):
+    """Bound on ||key|| (dQ or dK) where the oracle's value is exactly zero.
+
+    That happens when dP - D cancels exactly (a lone query in the Q-Attn split: O = V, so
+    dP = D). The kernel sums dP (the matrix core) and D in float32 in their own orders, so a
+    residual of up to gamma_d * sum_c |dO_ic| (|V_jc| + |O_ic|) per pair is a correct result
+    (the standard bound for a d-term float32 dot product, twice). The tile's dS scale follows
+    its largest residual, so the dequantised dS stays within 1.01 times the largest residual E
+    of the head. A row of dK^ (dQ^) is then at most sm * 1.01 * E * the summed norms of the
+    dequantised query (key) code rows it sees, times rstd * max|g| through the RMSNorm backward.
+    """
+    d, n, blk, sm = spec.d, spec.N, spec.blk, spec.scale
+    gamma = d * 2.0 ** -24 / (1.0 - d * 2.0 ** -24)
+    dO, V, O = (np.abs(np.asarray(t, np.float64)) for t in (x["dOf"], x["Vf"], o["O"]))
+    T = dO @ np.swapaxes(V, -1, -2) + (dO * O).sum(-1)[..., None]                    # [B,H,N,N]
+    vis = np.tril(np.ones((n, n), bool)) if spec.causal else np.ones((n, n), bool)
+    E = gamma * np.where(vis, T, 0.0).max(axis=(-1, -2))                               # [B,H]
+    own, other = ("Q", "K") if key == "dQ" else ("K", "Q")
+    codes = np.asarray(o[other + "c"], np.float64)[:, :, :n]
+    scale = np.repeat(np.asarray(o[other + "s"], np.float64), blk, axis=-1)[:, :, :n, None]
+    rows = codes * scale
+    if key == "dK" and spec.q_smooth:
+        rows = rows + np.asarray(o["q_mean"], np.float64)[:, :, None, :]
+    rn = np.linalg.norm(rows, axis=-1)                                                  # [B,H,N]
+    seen = rn @ vis.T.astype(float) if key == "dQ" else rn @ vis.astype(float)          # sum over visible partners
+    bound = sm * 1.01 * E[..., None] * seen
+    if spec.qk_norm and not spec.normed_grads:
+        g = gains[0 if key == "dQ" else 1] if gains is not None else None
+        gmax = 1.0 if g is None else np.abs(np.asarray(g, np.float64)).max(axis=-1)[None, :, None]
+        bound = bound * np.asarray(o[own.lower() + "_rstd"], np.float64)[:, :, :n] * gmax
+    return float(np.sqrt(np.sum(bound ** 2)))
 
 
 def _fp8_bars(x, spec, ref, kw):
@@ -98,18 +149,26 @@ def test_sweep(name, case):
     kw = dict(q_gain=None if gains is None else gains[0], k_gain=None if gains is None else gains[1])
     o = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec, **kw)
     check_prologue(g, o, check_v=split == "sagebwd")
-    keys = OUTS + (("dq_gain", "dk_gain") if gains else ())
+    # an exactly-zero reference (dP - D cancels exactly) takes an absolute bound instead
+    zero = [k for k in ("dQ", "dK") if not np.any(o[k])]
+    for k in zero:
+        norm, bound = float(np.linalg.norm(np.asarray(g[k], np.float64))), _zero_reference_bound(x, spec, o, k, gains)
+        print(f"[sweep] {name}: oracle {k} is exactly 0; ||{k}|| {norm:.3e} within the float32 residual bound {bound:.3e}",
+              flush=True)
+        assert norm <= bound, (k, norm, bound)
+    outs = tuple(k for k in OUTS if k not in zero)
+    keys = outs + (("dq_gain", "dk_gain") if gains else ())
     errs = {k: rel_l2(g[k], o[k]) for k in keys}
     lse = float(np.max(np.abs(g["LSE"].astype(np.float64) - o["LSE"])))
     if fmt == "fp8":
         rel_bar, row_bar, lse_bar = _fp8_bars(x, spec, o, kw)
         rel_bar.update({k: 1e-2 for k in keys if k not in rel_bar})
-        rows = {k: (row_rel_max(g[k], o[k]), row_bar[k]) for k in OUTS}
+        rows = {k: (row_rel_max(g[k], o[k]), row_bar[k]) for k in outs}
     else:
         rel_bar = {k: 2e-3 for k in keys}
         lse_bar = 1e-4 * max(1.0, float(np.max(np.abs(o["LSE"]))))
         rows = {}
-        for k in OUTS:
+        for k in outs:
             r = row_rel(g[k], o[k])
             allow = np.full(r.shape, ROW_TOL)
             if k in ("dQ", "dK"):
