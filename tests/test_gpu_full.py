@@ -13,6 +13,7 @@ import sys
 import numpy as np
 import pytest
 
+from bit_trainable_attention_amd import api
 from bit_trainable_attention_amd import workloads as wl
 from oracle import exact
 from oracle import quant as oq
@@ -74,45 +75,42 @@ def test_full_shape_whole_heads(name, heads):
             assert cos[k] >= 0.98, (k, cos)
 
 
-def test_full_shape_long_sequence_sampled():
-    """N = 32768: sampled query tiles and the last key blocks of one head."""
-    w = wl.WORKLOADS["n32768"]
-    _say(f"[full] n32768: B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU on all heads")
-    x = host_inputs(w)
-    g = gpu_run(w, x)
-    _check_prologue_all_heads(g, x, w)
-    bh = 5
+def _check_sampled_head(w, x, g, bh, q_bwd, exact_cosines):
+    """Head bh of a long-sequence run against the oracle: the forward on exactly the query rows
+    that the sampled pairs need, dQ on the sampled query tiles, dK and dV on the last two key
+    blocks; with exact_cosines also the cosines to exact float64 attention on the whole head."""
+    tag = f"[full] {w.name} N{w.N} head {bh}"
     w1 = w.with_shape(B=1, H=1)
     spec = spec_for(w1)
     xh = {k: _head(x[k], w, bh) for k in ("Qf", "Kf", "Vf", "dOf")}
     pro = oq.prologue(xh["Qf"], xh["Kf"], xh["Vf"], spec)
     N, tq, btq, sk = w.N, spec.fwd_tq, spec.bwd_tq, spec.sk
     k_blocks = [N // sk - 2, N // sk - 1]                   # dK, dV: last two key blocks
-    q_bwd = [3, 170, N // btq - 1]                          # dQ: sampled query tiles (btq rows)
     rows = set(range(k_blocks[0] * sk, N))                  # rows the sampled pairs need O/LSE for
     for it in q_bwd:
         rows |= set(range(it * btq, (it + 1) * btq))
     q_fwd = sorted({r // tq for r in rows})
-    _say(f"[full] n32768 head {bh}: oracle forward on {len(q_fwd)} query tiles")
+    _say(f"{tag}: oracle forward on {len(q_fwd)} query tiles")
     O, L = oq.forward(pro["Qc"], pro["Kc"], pro["Vc"], pro["Qs"], pro["Ks"], pro["Vs"], spec, q_tiles=q_fwd)
-    _say("[full] n32768: oracle backward on the sampled tiles")
+    _say(f"{tag}: oracle backward on the sampled tiles")
     gb = oq.backward(pro, xh["Qf"], xh["Kf"], xh["Vf"], O, L, xh["dOf"], spec, q_tiles=q_bwd, k_tiles=k_blocks)
     r = np.array(sorted(rows))
-    errO = rel_l2(_head(g["O"], w, bh)[..., r, :], O[..., r, :])
     qr = np.concatenate([np.arange(it * btq, (it + 1) * btq) for it in q_bwd])
     kr = np.arange(k_blocks[0] * sk, N)
-    errs = {"O": errO,
+    errs = {"O": rel_l2(_head(g["O"], w, bh)[..., r, :], O[..., r, :]),
             "dQ": rel_l2(_head(g["dQ"], w, bh)[..., qr, :], gb["dQ"][..., qr, :]),
             "dK": rel_l2(_head(g["dK"], w, bh)[..., kr, :], gb["dK"][..., kr, :]),
             "dV": rel_l2(_head(g["dV"], w, bh)[..., kr, :], gb["dV"][..., kr, :])}
     lse = float(np.max(np.abs(_head(g["LSE"], w, bh)[..., r].astype(np.float64) - L[..., r])))
-    _say(f"[full] n32768 head {bh}: rel-L2 {errs}, max|dLSE| {lse:.2e}")
+    _say(f"{tag}: rel-L2 {errs}, max|dLSE| {lse:.2e}")
     assert lse < 1e-4 * max(1.0, float(np.nanmax(np.abs(L[..., r]))))
     for k, e in errs.items():
         assert e <= TOL, (k, e)
+    if not exact_cosines:
+        return
     # cosine vs exact float64 attention on the same rows (the exact oracle streams query row
     # blocks; the whole head at N = 32768 takes it about a minute)
-    _say(f"[full] n32768 head {bh}: exact float64 attention on the whole head")
+    _say(f"{tag}: exact float64 attention on the whole head")
     ex = exact.attention(xh["Qf"], xh["Kf"], xh["Vf"], xh["dOf"], causal=w.causal, qk_norm=w.qk_norm, eps=w.eps,
                          row_block=256)
     cos = {"O": cosine(_head(g["O"], w, bh)[..., r, :], ex["O"][..., r, :]),
@@ -121,10 +119,34 @@ def test_full_shape_long_sequence_sampled():
            "dV": cosine(_head(g["dV"], w, bh)[..., kr, :], ex["dV"][..., kr, :]),
            "dQ_all": cosine(_head(g["dQ"], w, bh), ex["dQ"]), "dK_all": cosine(_head(g["dK"], w, bh), ex["dK"]),
            "dV_all": cosine(_head(g["dV"], w, bh), ex["dV"]), "O_all": cosine(_head(g["O"], w, bh), ex["O"])}
-    _say(f"[full] n32768 head {bh}: cosine vs exact float64 attention {cos}")
+    _say(f"{tag}: cosine vs exact float64 attention {cos}")
     assert cos["O"] >= 0.995 and cos["O_all"] >= 0.995, cos
     for k in ("dQ", "dK", "dV", "dQ_all", "dK_all", "dV_all"):
         assert cos[k] >= 0.98, (k, cos)
+
+
+def test_full_shape_long_sequence_sampled():
+    """N = 32768: sampled query tiles and the last key blocks of one head."""
+    w = wl.WORKLOADS["n32768"]
+    _say(f"[full] n32768: B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU on all heads")
+    x = host_inputs(w)
+    g = gpu_run(w, x)
+    _check_prologue_all_heads(g, x, w)
+    _check_sampled_head(w, x, g, 5, [3, 170, w.N // w.blk - 1], exact_cosines=True)
+
+
+def test_longest_head_atomic_fallback():
+    """One head of N = 131072 (the N = 32768 input distribution): its dS tiles would take
+    ~8.6 GB, past the 4 GiB one head's spill may use, so the automatic dQ mode takes the
+    float32-atomic reduction. Prologue on the whole head, sampled tiles against the oracle."""
+    w = wl.WORKLOADS["n32768"].with_shape(B=1, H=1, N=131072)
+    p = api.make_params(w.B, w.H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+    assert not api.backward_workspace_layout(p)["spill"]
+    _say(f"[full] longest head: B{w.B} H{w.H} N{w.N} d{w.d} blk{w.blk}: GPU (automatic dQ mode: atomic)")
+    x = host_inputs(w)
+    g = gpu_run(w, x)
+    _check_prologue_all_heads(g, x, w)
+    _check_sampled_head(w, x, g, 0, [3, 517, w.N // w.blk - 1], exact_cosines=False)
 
 
 VARIANTS = [  # (fmt, split, q_smooth, layout, dq_mode): the bench's --fmt, --split, --q-smooth,
