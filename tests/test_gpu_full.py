@@ -196,3 +196,43 @@ def test_full_shape_variants(fmt, split, q_smooth, layout, dq_mode):
     assert cos["O"] >= 0.995, cos
     for k in ("dQ", "dK", "dV"):
         assert cos[k] >= 0.98, (k, cos)
+
+
+def test_many_heads_past_32bit_offsets():
+    """2^17 heads of N = 128, d = 128: each 16-bit tensor holds 2^31 elements (4 GiB), past the
+    reach of 32-bit element or byte offsets. Every head receives the same seeded input (one head
+    of the n8192_d128 distribution, copied across heads on the GPU), so every head's codes,
+    scales, O, lse and gradients must equal head 0's bit for bit; head 0 and the last head match
+    the oracle."""
+    import torch
+    from tests.harness import to_device
+    w1 = wl.WORKLOADS["n8192_d128"].with_shape(B=1, H=1, N=128)
+    B, H = 128, 1024
+    w = w1.with_shape(B=B, H=H)
+    x = host_inputs(w1)
+    _say(f"[full] many heads: B{B} H{H} N{w.N} d{w.d} blk{w.blk} ({B * H * w.N * w.d} elements per tensor)")
+    big = {k: to_device(x[k], w.dtype).expand(B, H, w.N, w.d).contiguous() for k in ("Q", "K", "V", "dO")}
+    p = api.make_params(B, H, w.N, w.d, w.blk, w.causal, w.qk_norm, w.k_smooth, w.dtype, eps=w.eps)
+    assert api.backward_workspace_layout(p)["spill"]
+    _say("[full] many heads: prologue, forward, backward")
+    pro = api.sagebwd_quant_prologue(p, big["Q"], big["K"], big["V"])
+    O, lse = api.sagebwd_forward(p, pro, V=big["V"])
+    g = api.sagebwd_backward(p, big["Q"], big["K"], big["V"], pro, O, lse, big["dO"])
+    torch.cuda.synchronize()
+    _say("[full] many heads: every head against head 0")
+    outs = {"O": O, "lse": lse, "dQ": g["dQ"], "dK": g["dK"], "dV": g["dV"],
+            **{k: pro[k] for k in ("Qc", "Kc", "Vtc", "Qs", "Ks", "Vs", "q_rstd", "k_rstd", "k_mean")}}
+    for k, t in outs.items():
+        flat = t.reshape(B * H, -1)
+        assert torch.equal(flat, flat[:1].expand_as(flat)), k
+    _say("[full] many heads: heads 0 and last against the oracle")
+    o = oq.run(x["Qf"], x["Kf"], x["Vf"], x["dOf"], spec_for(w1))
+    for bh in (0, B * H - 1):
+        head = {k: outs[k].reshape(B * H, *outs[k].shape[2:])[bh].float().cpu().numpy() for k in ("O", "dQ", "dK", "dV")}
+        errs = {k: rel_l2(head[k], o[k][0, 0]) for k in head}
+        lse_err = float(np.max(np.abs(lse.reshape(B * H, -1)[bh, :w.N].cpu().numpy().astype(np.float64)
+                                      - o["LSE"][0, 0, :w.N])))
+        _say(f"[full] many heads: head {bh}: rel-L2 {errs}, max|dLSE| {lse_err:.2e}")
+        assert lse_err < 1e-4 * max(1.0, float(np.max(np.abs(o["LSE"]))))
+        for k, e in errs.items():
+            assert e <= TOL, (k, e)
