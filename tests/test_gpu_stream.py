@@ -1,0 +1,51 @@
+"""The three calls run on the stream they are given (the header: every call enqueues on its
+stream argument and returns without waiting).
+
+The inputs are written on a side stream behind a queue of unrelated work (a chain of matrix
+products), and the prologue, forward and backward are then called on that stream: the
+prologue through the current-stream default, the backward with the stream passed explicitly.
+A call that ran on any other stream would read its inputs before the copies that fill them
+(PyTorch's side streams do not wait for the null stream), so every output must equal a plain
+run on the default stream bit for bit."""
+import numpy as np
+import pytest
+
+from bit_trainable_attention_amd import workloads as wl
+from tests.harness import host_inputs, params_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _calls(api, p, Q, K, V, dO, stream=None):
+    pro = api.sagebwd_quant_prologue(p, Q, K, V)
+    O, lse = api.sagebwd_forward(p, pro, V=V)
+    g = api.sagebwd_backward(p, Q, K, V, pro, O, lse, dO, stream=stream)
+    return dict(O=O, lse=lse, dQ=g["dQ"], dK=g["dK"], dV=g["dV"], Qc=pro["Qc"], Kc=pro["Kc"], Vtc=pro["Vtc"])
+
+
+def test_calls_follow_the_callers_stream():
+    import torch
+    from bit_trainable_attention_amd import api
+    w = wl.WORKLOADS["n8192_d128"].with_shape(B=1, H=4, N=1024)
+    x = host_inputs(w)
+    p = params_for(w)
+    src = {k: to_device(x[k], w.dtype) for k in ("Q", "K", "V", "dO")}
+    torch.cuda.synchronize()
+    print("[stream] reference run on the default stream", flush=True)
+    ref = _calls(api, p, src["Q"], src["K"], src["V"], src["dO"])
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()          # default priority
+    print("[stream] queued work, input copies and the three calls on a side stream", flush=True)
+    with torch.cuda.stream(side):
+        m = torch.randn(4096, 4096, device="cuda:0") / 64.0
+        for _ in range(16):            # a few milliseconds of unrelated work ahead of the copies
+            m = torch.tanh(m @ m)
+        ins = {k: torch.empty_like(t) for k, t in src.items()}
+        for k in ins:
+            ins[k].copy_(src[k])
+        got = _calls(api, p, ins["Q"], ins["K"], ins["V"], ins["dO"], stream=side)
+    side.synchronize()
+    for k, t in ref.items():
+        assert torch.equal(got[k], t), k
+    assert bool(torch.isfinite(m).all())
