@@ -49,3 +49,40 @@ def test_calls_follow_the_callers_stream():
     for k, t in ref.items():
         assert torch.equal(got[k], t), k
     assert bool(torch.isfinite(m).all())
+
+
+def test_two_problems_at_once_on_two_streams():
+    """Two different problems (shapes, masks, layouts, dQ modes) enqueued alternately on two
+    streams run concurrently; the library keeps no state between calls, so each must equal its
+    own run on the default stream bit for bit (dQ of the float32-atomic mode: within rel-L2 1e-4,
+    since the order in which the atomics land varies and only that float32 rounding moves)."""
+    import torch
+    from bit_trainable_attention_amd import api
+    cases = [(wl.WORKLOADS["n8192_d128"].with_shape(B=1, H=4, N=1024), dict(dq_mode=1)),
+             (wl.WORKLOADS["bf16_d64"].with_shape(B=2, H=2, N=700, causal=False), dict(dq_mode=2, layout="bnhd"))]
+    prepared = []
+    for w, kw in cases:
+        x = host_inputs(w)
+        tr = (lambda t: t.transpose(1, 2).contiguous()) if kw.get("layout") == "bnhd" else (lambda t: t)
+        t = {k: tr(to_device(x[k], w.dtype)) for k in ("Q", "K", "V", "dO")}
+        prepared.append((params_for(w, **kw), t))
+    torch.cuda.synchronize()
+    print("[stream] two problems: references on the default stream", flush=True)
+    refs = [_calls(api, p, t["Q"], t["K"], t["V"], t["dO"]) for p, t in prepared]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    print("[stream] two problems: four rounds on two streams at once", flush=True)
+    for _ in range(4):
+        got = [None, None]
+        for i, ((p, t), s) in enumerate(zip(prepared, streams)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                got[i] = _calls(api, p, t["Q"], t["K"], t["V"], t["dO"], stream=s)
+        for s in streams:
+            s.synchronize()
+        for i in range(2):
+            for k, t in refs[i].items():
+                if i == 1 and k == "dQ":      # float32 atomics: summation order varies
+                    assert float((got[i][k].float() - t.float()).norm() / t.float().norm()) < 1e-4, (i, k)
+                else:
+                    assert torch.equal(got[i][k], t), (i, k)
