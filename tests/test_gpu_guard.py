@@ -2,7 +2,8 @@
 lse; dQ, dK, dV and the gains' gradients) and the backward workspace is placed inside a larger
 device buffer whose bytes before and after it hold a sentinel pattern. After the calls the
 sentinels must be intact (no write past either end of any output) and the outputs must equal
-those of a run on plain tensors bit for bit. Cases: ragged N (the 16-bit tensors hold exactly
+those of a run on plain tensors bit for bit; every call's inputs (Q, K, V, dO, the gains, the
+prologue's outputs as the forward's and backward's inputs, O and lse) must be unchanged. Cases: ragged N (the 16-bit tensors hold exactly
 N tokens, the library's own arrays Np), the in-place [B,N,H,d] layout, gains, both dQ modes,
 Q-smoothing and the FP8 recipe."""
 import numpy as np
@@ -59,14 +60,23 @@ def _run(w, layout, dq_mode, gains, fmt, guard):
                   for _ in range(2))
     G = Guarded()
     ref = api.sagebwd_quant_prologue(p, Q, K, V, q_gain=gq, k_gain=gk)       # shapes only
+    # inputs are never written: snapshots of every call's inputs, compared after the calls
+    before = {"Q": Q.clone(), "K": K.clone(), "V": V.clone(), "dO": dO.clone()}
+    if gains:
+        before.update(q_gain=gq.clone(), k_gain=gk.clone())
+    now = {"Q": Q, "K": K, "V": V, "dO": dO, "q_gain": gq, "k_gain": gk}
     pro = {k: (G.like(v) if guard else torch.empty_like(v)) for k, v in ref.items()}
     need = api.sagebwd_prologue_workspace_bytes(p)
     pws = (G.bytes(need, Q.device) if guard else torch.empty(need, dtype=torch.uint8, device=Q.device)) if need else None
     api.sagebwd_quant_prologue(p, Q, K, V, out=pro, workspace=pws, q_gain=gq, k_gain=gk)
+    before.update({"pro." + k: v.clone() for k, v in pro.items()})
+    now.update({"pro." + k: v for k, v in pro.items()})
     O0, lse0 = api.sagebwd_forward(p, pro)
     O = G.like(O0) if guard else torch.empty_like(O0)
     lse = G.like(lse0) if guard else torch.empty_like(lse0)
     api.sagebwd_forward(p, pro, O=O, lse=lse)
+    before.update(O=O.clone(), lse=lse.clone())
+    now.update(O=O, lse=lse)
     grads = {n: (G.like(Q) if guard else torch.empty_like(Q)) for n in ("dQ", "dK", "dV")}
     if gains:
         for n in ("dq_gain", "dk_gain"):
@@ -78,6 +88,8 @@ def _run(w, layout, dq_mode, gains, fmt, guard):
     torch.cuda.synchronize()
     if guard:
         G.check()
+    for k, t in before.items():   # the prologue's, the forward's and the backward's inputs
+        assert torch.equal(now[k], t), f"input {k} was written"
     def host(t):   # 16-bit tensors as their bit patterns (numpy has no bfloat16)
         return t.view(torch.int16).cpu().numpy() if t.element_size() == 2 else t.cpu().numpy()
 
