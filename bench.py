@@ -112,7 +112,7 @@ def main():
                     help="skip the extra timing of the same step through the autograd wrapper")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the attention shards over heads with no communication between them).", file=sys.stderr)
         sys.exit(2)
 
