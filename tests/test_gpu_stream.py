@@ -7,7 +7,6 @@ prologue through the current-stream default, the backward with the stream passed
 A call that ran on any other stream would read its inputs before the copies that fill them
 (PyTorch's side streams do not wait for the null stream), so every output must equal a plain
 run on the default stream bit for bit."""
-import numpy as np
 import pytest
 
 from bit_trainable_attention_amd import workloads as wl
