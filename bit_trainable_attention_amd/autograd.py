@@ -16,6 +16,7 @@ from __future__ import annotations
 from typing import Optional, Tuple, Union
 
 import torch
+from torch.autograd.function import once_differentiable
 
 from . import api
 
@@ -61,6 +62,7 @@ class SageBwdAttention(torch.autograd.Function):
         return O, lse
 
     @staticmethod
+    @once_differentiable   # the backward runs in the library: no second derivative through it
     def backward(ctx, dO, _dlse):
         if dO is None:   # O took no part in the loss (grads are not materialised)
             return (None,) * 17

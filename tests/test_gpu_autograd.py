@@ -78,3 +78,18 @@ def test_wrapper_meets_oracle_bar():
     assert lse < 1e-4 * max(1.0, float(np.max(np.abs(o["LSE"]))))
     for n, e in errs.items():
         assert e <= 2e-3, (n, e)
+
+
+def test_no_second_derivative():
+    """The backward runs in the library, so it has no derivative of its own: asking for one
+    (create_graph, then differentiating the gradients) raises instead of returning zeros."""
+    import torch
+    from bit_trainable_attention_amd.autograd import sagebwd_attention
+    w = wl.WORKLOADS["tiny"].with_shape(N=128)
+    x = host_inputs(w)
+    q, k, v = (to_device(x[n], w.dtype).requires_grad_() for n in ("Q", "K", "V"))
+    _say("[autograd] second derivative request")
+    o = sagebwd_attention(q, k, v, causal=w.causal, qk_norm=w.qk_norm, k_smooth=w.k_smooth, blk=w.blk, eps=w.eps)
+    (gq,) = torch.autograd.grad(o.float().sum(), q, create_graph=True)
+    with pytest.raises(RuntimeError):
+        gq.float().sum().backward()
