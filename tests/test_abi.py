@@ -263,3 +263,27 @@ def test_qattn_forward_needs_raw_v():
     assert fw(qa, FAKE, FAKE, 0) == -1
     assert fw(qa, FAKE, FAKE, MIS) == -4
     assert fw(P(), FAKE, 0, FAKE) == -1       # the SageBwd split still needs the V codes
+
+
+def test_binding_layout_matches_library_random():
+    # 400 seeded parameter sets (N log-uniform in 1..2^18, so that some spill and some take the
+    # atomic layout; both dQ requests; gains; Q-smoothing; both formats and splits; ragged N):
+    # wherever the library accepts the parameters, the binding's documented workspace layout
+    # ends exactly at the size the library asks for
+    import numpy as np
+    from bit_trainable_attention_amd import api
+    rng = np.random.default_rng(20261204)
+    checked = 0
+    for _ in range(400):
+        d = int(rng.choice([64, 128]))
+        kw = dict(B=int(rng.integers(1, 9)), H=int(rng.integers(1, 17)), N=int(np.exp(rng.uniform(0, np.log(1 << 18)))),
+                  d=d, blk=int(rng.choice([64, 128])), causal=int(rng.integers(2)), dq_mode=int(rng.integers(3)),
+                  qk_gain=int(rng.integers(2)), q_smooth=int(rng.random() < 0.2),
+                  fmt=int(rng.choice([_lib.FMT_INT8, _lib.FMT_FP8])), split=int(rng.choice([_lib.SPLIT_SAGEBWD, _lib.SPLIT_QATTN])))
+        p = P(**kw)
+        n = lib.sagebwd_backward_workspace_bytes(ctypes.byref(p))
+        if n == 0:
+            continue   # a rejected combination (or an explicit spill past its limit)
+        checked += 1
+        assert api.backward_workspace_layout(p)["total"] == n, kw
+    assert checked > 100
