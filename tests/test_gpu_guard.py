@@ -124,3 +124,36 @@ def test_outputs_stay_inside_their_buffers(name, w, layout, dq_mode, gains, fmt)
     # padding queries of a ragged last block get lse = +inf (every output element is written)
     Np = -(-w.N // w.blk) * w.blk
     assert np.all(np.isposinf(a["lse"][..., w.N:Np])) and np.all(np.isfinite(a["lse"][..., :w.N]))
+
+
+@pytest.mark.parametrize("dq_mode", [1, 2])
+def test_nonfinite_inputs_stay_memory_safe(dq_mode):
+    """NaN and infinite inputs give unspecified results (the header), but memory-safe ones: with
+    NaN, +inf and -inf planted in Q, K, V and dO, every output still lands inside its guarded
+    buffer (no kernel indexes memory by a data value), in both dQ modes."""
+    import torch
+    from bit_trainable_attention_amd import api
+    w = W["n8192_d128"].with_shape(B=1, H=2, N=300)
+    print(f"[guard] non-finite inputs: B{w.B} H{w.H} N{w.N} d{w.d} dq_mode={dq_mode}", flush=True)
+    x = host_inputs(w)
+    p = params_for(w, dq_mode=dq_mode)
+    ins = {k: to_device(x[k], w.dtype) for k in ("Q", "K", "V", "dO")}
+    for i, k in enumerate(ins):                     # a NaN, a +inf and a -inf in every input
+        flat = ins[k].view(-1)
+        flat[7 + 100 * i] = float("nan")
+        flat[5000 + 100 * i] = float("inf")
+        flat[-3 - 100 * i] = float("-inf")
+    G = Guarded()
+    ref = api.sagebwd_quant_prologue(p, ins["Q"], ins["K"], ins["V"])
+    pro = {k: G.like(v) for k, v in ref.items()}
+    need = api.sagebwd_prologue_workspace_bytes(p)
+    pws = G.bytes(need, ins["Q"].device) if need else None
+    api.sagebwd_quant_prologue(p, ins["Q"], ins["K"], ins["V"], out=pro, workspace=pws)
+    O0, lse0 = api.sagebwd_forward(p, pro)
+    O, lse = G.like(O0), G.like(lse0)
+    api.sagebwd_forward(p, pro, O=O, lse=lse)
+    grads = {n: G.like(ins["Q"]) for n in ("dQ", "dK", "dV")}
+    bws = G.bytes(api.sagebwd_backward_workspace_bytes(p), ins["Q"].device)
+    api.sagebwd_backward(p, ins["Q"], ins["K"], ins["V"], pro, O, lse, ins["dO"], grads=grads, workspace=bws)
+    torch.cuda.synchronize()
+    G.check()
