@@ -155,6 +155,8 @@ VARIANTS = [  # (fmt, split, q_smooth, layout, dq_mode): the bench's --fmt, --sp
     ("int8", "sagebwd", True, "bhnd", 0),
     ("int8", "sagebwd", False, "bnhd", 0),
     ("int8", "sagebwd", False, "bhnd", 2),
+    ("fp8", "qattn", False, "bnhd", 0),       # combinations: FP8 codes with the Q-Attn split in place
+    ("int8", "sagebwd", True, "bnhd", 2),     # Q-smoothing in place with atomic dQ
 ]
 
 
